@@ -1,0 +1,195 @@
+"""Python binding of the hbmcoll C ABI (``include/hbmcoll.h``).
+
+Argument marshalling only: every step of a collective runs in the gfx950
+kernels of ``libhbmcoll.so``.  PyTorch supplies device memory and the stream.
+There is no fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhbmcoll.so")
+
+OK = 0
+STATUS = {0: "HBMC_OK", 1: "HBMC_ERR_INVALID_ARG", 2: "HBMC_ERR_UNSUPPORTED", 3: "HBMC_ERR_HIP",
+          4: "HBMC_ERR_NOMEM"}
+DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2, "int32": 3, "int8": 4}
+ESIZE = {"fp32": 4, "fp16": 2, "bf16": 2, "int32": 4, "int8": 1}
+OP = {"sum": 0, "prod": 1, "max": 2, "min": 3}
+ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3}
+COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
+MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
+
+# every symbol include/hbmcoll.h declares
+EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
+           "hbmc_all_gather", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
+           "hbmc_plan_items", "hbmc_status_string")
+
+
+class HbmcError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        msg = STATUS.get(code, str(code))
+        try:
+            msg += ": " + load_library().hbmc_status_string(code).decode()
+        except Exception:  # noqa: BLE001 - the code is still reported
+            pass
+        super().__init__(f"{what}: {msg}" if what else msg)
+        self.code = code
+
+
+class Item(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("mode", ctypes.c_int32), ("nsrc", ctypes.c_int32),
+                ("ndst", ctypes.c_int32), ("begin", ctypes.c_uint64), ("count", ctypes.c_uint64),
+                ("rank", ctypes.c_uint8 * 128)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load ``libhbmcoll.so`` (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, ci, u64p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_uint64)
+        L.hbmc_comm_create.restype = ci
+        L.hbmc_comm_create.argtypes = [ci, ci, ci, ci, sz, ctypes.POINTER(vp)]
+        L.hbmc_comm_destroy.restype = ci
+        L.hbmc_comm_destroy.argtypes = [vp]
+        for name in ("hbmc_allreduce", "hbmc_reduce_scatter", "hbmc_all_gather"):
+            f = getattr(L, name)
+            f.restype = ci
+            f.argtypes = [vp, ctypes.POINTER(vp), sz, ci, ci, vp]
+        L.hbmc_run_steps.restype = ci
+        L.hbmc_run_steps.argtypes = [vp, ci, ctypes.POINTER(vp), sz, ci, ci, ci, ci, vp]
+        L.hbmc_plan_info.restype = ci
+        L.hbmc_plan_info.argtypes = [vp, ci, sz, ci, ctypes.POINTER(ci), u64p, u64p]
+        L.hbmc_plan_step_info.restype = ci
+        L.hbmc_plan_step_info.argtypes = [vp, ci, sz, ci, ci, ctypes.POINTER(ci), u64p]
+        L.hbmc_plan_items.restype = ci
+        L.hbmc_plan_items.argtypes = [vp, ci, sz, ci, ctypes.POINTER(Item), sz, ctypes.POINTER(sz)]
+        L.hbmc_status_string.restype = ctypes.c_char_p
+        L.hbmc_status_string.argtypes = [ci]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise HbmcError(rc, what)
+
+
+def _torch_dtype_name(t) -> str:
+    import torch
+    m = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16", torch.int32: "int32",
+         torch.int8: "int8"}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptrs(bufs):
+    """(void*[P], count, dtype) from a list of device tensors or raw addresses."""
+    P = len(bufs)
+    arr = (ctypes.c_void_p * max(P, 1))()
+    if P and hasattr(bufs[0], "data_ptr"):
+        n = bufs[0].numel()
+        dt = _torch_dtype_name(bufs[0])
+        for i, b in enumerate(bufs):
+            if not b.is_cuda or not b.is_contiguous() or b.numel() != n or _torch_dtype_name(b) != dt:
+                raise ValueError("buffers must be contiguous device tensors of one dtype and size")
+            arr[i] = b.data_ptr()
+        return arr, n, dt
+    for i, b in enumerate(bufs):
+        arr[i] = int(b)
+    return arr, None, None
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+class Comm:
+    """A communicator of P logical ranks (P buffers on one GPU)."""
+
+    def __init__(self, nranks: int, algo: str = "ring", servers: int = 0, ranks_per_server: int = 0,
+                 loop_bytes: int = 0):
+        self.P = nranks
+        self.algo = algo
+        self.S, self.M = servers, ranks_per_server
+        self._h = ctypes.c_void_p()
+        _check(load_library().hbmc_comm_create(nranks, ALGO[algo], servers, ranks_per_server, loop_bytes,
+                                               ctypes.byref(self._h)), "hbmc_comm_create")
+
+    # -- lifetime
+    def close(self) -> None:
+        if self._h:
+            _check(load_library().hbmc_comm_destroy(self._h), "hbmc_comm_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # -- collectives
+    def _coll(self, fn, bufs, dtype, op, count, stream):
+        arr, n, dt = _ptrs(bufs)
+        dtype = dtype or dt
+        count = n if count is None else count
+        _check(getattr(load_library(), fn)(self._h, arr, count, DTYPE[dtype], OP[op], _stream(stream)), fn)
+
+    def allreduce(self, bufs, dtype=None, op="sum", *, count=None, stream=None):
+        self._coll("hbmc_allreduce", bufs, dtype, op, count, stream)
+
+    def reduce_scatter(self, bufs, dtype=None, op="sum", *, count=None, stream=None):
+        self._coll("hbmc_reduce_scatter", bufs, dtype, op, count, stream)
+
+    def all_gather(self, bufs, dtype=None, op="sum", *, count=None, stream=None):
+        self._coll("hbmc_all_gather", bufs, dtype, op, count, stream)
+
+    def run_steps(self, coll, bufs, first, last, dtype=None, op="sum", *, count=None, stream=None):
+        arr, n, dt = _ptrs(bufs)
+        dtype = dtype or dt
+        count = n if count is None else count
+        _check(load_library().hbmc_run_steps(self._h, COLL[coll], arr, count, DTYPE[dtype], OP[op], first,
+                                             last, _stream(stream)), "hbmc_run_steps")
+
+    # -- schedule facts (host only)
+    def plan_info(self, coll: str, count: int, dtype: str):
+        n = ctypes.c_int()
+        b = ctypes.c_uint64()
+        r = ctypes.c_uint64()
+        _check(load_library().hbmc_plan_info(self._h, COLL[coll], count, DTYPE[dtype], ctypes.byref(n),
+                                             ctypes.byref(b), ctypes.byref(r)), "hbmc_plan_info")
+        return dict(nsteps=n.value, hbm_bytes=b.value, max_recv_bytes=r.value)
+
+    def step_info(self, coll: str, count: int, dtype: str, step: int):
+        n = ctypes.c_int()
+        b = ctypes.c_uint64()
+        _check(load_library().hbmc_plan_step_info(self._h, COLL[coll], count, DTYPE[dtype], step,
+                                                  ctypes.byref(n), ctypes.byref(b)), "hbmc_plan_step_info")
+        return dict(nitems=n.value, hbm_bytes=b.value)
+
+    def plan_items(self, coll: str, count: int, dtype: str):
+        n = ctypes.c_size_t()
+        L = load_library()
+        _check(L.hbmc_plan_items(self._h, COLL[coll], count, DTYPE[dtype], None, 0, ctypes.byref(n)),
+               "hbmc_plan_items")
+        arr = (Item * max(n.value, 1))()
+        _check(L.hbmc_plan_items(self._h, COLL[coll], count, DTYPE[dtype], arr, n.value, ctypes.byref(n)),
+               "hbmc_plan_items")
+        out = []
+        for it in arr[:n.value]:
+            ranks = list(it.rank[:it.nsrc + it.ndst])
+            out.append(dict(step=it.step, mode=MODE[it.mode], begin=it.begin, count=it.count,
+                            src=ranks[:it.nsrc], dst=ranks[it.nsrc:]))
+        return out

@@ -1,0 +1,39 @@
+// Host <-> kernel interface of one schedule step.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace hbmc {
+
+constexpr int kDevRanks = 64;
+
+// Device addresses of every rank's buffer for one call (kernel argument).
+struct RankPtrs {
+  unsigned char* p[kDevRanks];
+};
+
+// A work item as the kernels read it from device memory: every destination's
+// elements [begin, begin+count) receive the step's combination of the
+// sources' same elements.  rank[0..nsrc) are sources, then ndst destinations.
+struct alignas(16) DevItem {
+  uint64_t begin, count;
+  uint32_t nsrc, ndst, pad0, pad1;
+  uint8_t rank[2 * kDevRanks];
+};
+
+struct StepLaunch {
+  int dtype, op, mode;    // element type, reduce op, Mode of plan.hpp
+  int nsrc, ndst;         // one item shape per step
+  const DevItem* items;   // device table of the step's items
+  int nitems;
+  uint64_t max_count;     // largest item, elements
+  bool aligned;           // every rank buffer has the same 16-byte phase
+  uint32_t phase;         // that phase, bytes
+};
+
+// Enqueue one step on `stream`; returns the launch's error state.
+hipError_t launch_step(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream);
+
+}  // namespace hbmc

@@ -1,0 +1,327 @@
+// Schedule builder (host).  Each collective becomes a list of steps; a step is
+// a set of work items that one fused kernel launch executes for all ranks at
+// once, so every step here is written from the receiving rank's side.
+//
+// Ring ([RING-RHD] "Ring AllReduce带宽最优的环形流水线"; [TOPO]
+// "AllReduce算法实现"): P-1 reduce-scatter steps in which rank r combines the
+// partial of segment (r-t-2) mod P received from rank r-1 with its own
+// (ending with segment r reduced on rank r), then P-1 all-gather steps in
+// which rank r copies segment (r-1-t) mod P from rank r-1.
+//
+// Recursive halving-doubling ([RHD] "算法描述", Table 1): with
+// r = P - 2^floor(log2 P), ranks 2i+1 (i < r) are first merged into 2i;
+// virtual rank v (real rank 2v for v < r, v + r otherwise) halves its window
+// with partner v xor 2^j at step j (keeping the lower half when bit j of v is
+// 0), then doubles it back in reverse; ranks 2i+1 finally receive a copy.
+// Stand-alone reduce-scatter / all-gather for P = 2^k are order-preserving:
+// distances P/2 .. 1 (rank v keeps the aligned block containing segment v),
+// then 1 .. P/2 for the all-gather.
+//
+// Pipeline ([PIPE] "AllGather 算子的 Pipeline 时序编排", "Rank0 视角的传输任务编排",
+// Table 1): rank g = s*M + m; each loop (slice of at most loop_bytes) is split
+// into P blocks.  Reduce-scatter: one intra-server step in which (s,m) folds
+// its server's M contributions to block ((s-1)M+m), then S-1 steps in which
+// (s,m) combines the partial received from (s-1,m) with its server's fold of
+// block ((s-t-2)M+m).  All-gather: S-1 steps in which (s,m) sends block
+// ((s-t)M+m) both to (s+1,m) and to its M-1 server peers (one read, M
+// writes), then one intra-server pass of block ((s+1)M+m).
+#include "plan.hpp"
+
+#include <algorithm>
+
+namespace hbmc {
+namespace {
+
+// Ceiling split of n elements into `parts` contiguous parts.
+struct Split {
+  uint64_t n, parts, q;
+  Split(uint64_t n_, uint64_t parts_) : n(n_), parts(parts_), q(parts_ ? (n_ + parts_ - 1) / parts_ : 0) {}
+  uint64_t at(uint64_t k) const { return std::min(k * q, n); }
+};
+
+inline int wrap(long a, long m) {
+  long r = a % m;
+  return static_cast<int>(r < 0 ? r + m : r);
+}
+
+inline int log2_floor(int p) {
+  int k = 0;
+  while ((2 << k) <= p) ++k;
+  return k;
+}
+
+class Builder {
+ public:
+  explicit Builder(Schedule* s) : sched_(s) {}
+
+  Step& open(Mode mode) {
+    sched_->steps.emplace_back();
+    Step& st = sched_->steps.back();
+    st.mode = mode;
+    return st;
+  }
+
+  // Append an item [base + b, base + e) with the given sources / destinations.
+  static void add(Step& st, uint64_t b, uint64_t e, std::initializer_list<int> src,
+                  std::initializer_list<int> dst) {
+    std::vector<int> s(src), d(dst);
+    add(st, b, e, s, d);
+  }
+  static void add(Step& st, uint64_t b, uint64_t e, const std::vector<int>& src,
+                  const std::vector<int>& dst) {
+    if (e <= b || dst.empty()) return;
+    Item it;
+    it.begin = b;
+    it.count = e - b;
+    it.nsrc = static_cast<int32_t>(src.size());
+    it.ndst = static_cast<int32_t>(dst.size());
+    int k = 0;
+    for (int r : src) it.rank[k++] = static_cast<uint8_t>(r);
+    for (int r : dst) it.rank[k++] = static_cast<uint8_t>(r);
+    st.items.push_back(it);
+  }
+
+ private:
+  Schedule* sched_;
+};
+
+// ---------------------------------------------------------------- ring
+void ring(const Topology& t, Coll coll, uint64_t L, Builder& B) {
+  const int P = t.P;
+  Split seg(L, P);
+  if (coll != kAllGather) {
+    for (int step = 0; step < P - 1; ++step) {
+      Step& st = B.open(kRecvFold);
+      for (int r = 0; r < P; ++r) {
+        int c = wrap(r - step - 2, P);
+        Builder::add(st, seg.at(c), seg.at(c + 1), {wrap(r - 1, P), r}, {r});
+      }
+    }
+  }
+  if (coll != kReduceScatter) {
+    for (int step = 0; step < P - 1; ++step) {
+      Step& st = B.open(kCopy);
+      for (int r = 0; r < P; ++r) {
+        int c = wrap(r - 1 - step, P);
+        Builder::add(st, seg.at(c), seg.at(c + 1), {wrap(r - 1, P)}, {r});
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- RHD
+// First segment of virtual rank v's window after halving steps 0..j.
+inline int hd_window_start(int v, int j, int pp) {
+  int start = 0;
+  for (int i = 0; i <= j; ++i)
+    if ((v >> i) & 1) start += pp >> (i + 1);
+  return start;
+}
+
+void rhd_allreduce(const Topology& t, uint64_t L, Builder& B) {
+  const int P = t.P, k = log2_floor(P), pp = 1 << k, extra = P - pp;
+  auto real = [extra](int v) { return v < extra ? 2 * v : v + extra; };
+  Split seg(L, pp);
+  if (extra > 0) {  // merge part1
+    Step& st = B.open(kRecvFold);
+    for (int i = 0; i < extra; ++i) Builder::add(st, 0, L, {2 * i + 1, 2 * i}, {2 * i});
+  }
+  for (int j = 0; j < k; ++j) {  // halving
+    Step& st = B.open(kRecvFold);
+    const int len = pp >> (j + 1);
+    for (int v = 0; v < pp; ++v) {
+      int a = hd_window_start(v, j, pp);
+      Builder::add(st, seg.at(a), seg.at(a + len), {real(v ^ (1 << j)), real(v)}, {real(v)});
+    }
+  }
+  for (int j = k - 1; j >= 0; --j) {  // doubling
+    Step& st = B.open(kCopy);
+    const int len = pp >> (j + 1);
+    for (int v = 0; v < pp; ++v) {
+      int u = v ^ (1 << j);
+      int a = hd_window_start(u, j, pp);
+      Builder::add(st, seg.at(a), seg.at(a + len), {real(u)}, {real(v)});
+    }
+  }
+  if (extra > 0) {  // restore part1
+    Step& st = B.open(kCopy);
+    for (int i = 0; i < extra; ++i) Builder::add(st, 0, L, {2 * i}, {2 * i + 1});
+  }
+}
+
+void rhd_ordered(const Topology& t, Coll coll, uint64_t L, Builder& B) {
+  const int P = t.P;
+  Split seg(L, P);
+  if (coll == kReduceScatter) {
+    for (int d = P / 2; d >= 1; d /= 2) {
+      Step& st = B.open(kRecvFold);
+      for (int v = 0; v < P; ++v) {
+        int a = v & ~(d - 1);
+        Builder::add(st, seg.at(a), seg.at(a + d), {v ^ d, v}, {v});
+      }
+    }
+  } else {
+    for (int d = 1; d < P; d *= 2) {
+      Step& st = B.open(kCopy);
+      for (int v = 0; v < P; ++v) {
+        int a = (v ^ d) & ~(d - 1);
+        Builder::add(st, seg.at(a), seg.at(a + d), {v ^ d}, {v});
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pipeline
+void pipeline(const Topology& t, Coll coll, uint64_t L, uint32_t esize, Builder& B,
+              Schedule* sched) {
+  const int S = t.S, M = t.M, P = t.P;
+  const uint64_t lb = t.loop_bytes ? t.loop_bytes : (uint64_t(32) << 20);
+  const uint64_t C = std::max<uint64_t>(1, lb / esize);
+  const int rs_steps = (coll != kAllGather) ? S : 0;
+  const int ag_steps = (coll != kReduceScatter) ? S : 0;
+  std::vector<size_t> idx;
+  for (int i = 0; i < rs_steps; ++i) {
+    B.open(i == 0 ? kFold : kRecvFold);
+    idx.push_back(sched->steps.size() - 1);
+  }
+  for (int i = 0; i < ag_steps; ++i) {
+    B.open(kCopy);
+    idx.push_back(sched->steps.size() - 1);
+  }
+  auto g = [M](int s, int m) { return s * M + m; };
+  for (uint64_t base = 0; base < L; base += C) {
+    const uint64_t n = std::min(C, L - base);
+    Split blk(n, P);
+    auto range = [&](int b, uint64_t* lo, uint64_t* hi) {
+      *lo = base + blk.at(b);
+      *hi = base + blk.at(b + 1);
+    };
+    uint64_t lo, hi;
+    int si = 0;
+    if (rs_steps) {
+      Step& st = sched->steps[idx[si++]];
+      for (int s = 0; s < S; ++s)
+        for (int m = 0; m < M; ++m) {
+          if (M == 1) continue;  // a fold of one block onto itself is no work
+          std::vector<int> src;
+          for (int l = 0; l < M; ++l) src.push_back(g(s, l));
+          range(wrap(s - 1, S) * M + m, &lo, &hi);
+          Builder::add(st, lo, hi, src, {g(s, m)});
+        }
+      for (int step = 0; step < S - 1; ++step) {
+        Step& rst = sched->steps[idx[si++]];
+        for (int s = 0; s < S; ++s)
+          for (int m = 0; m < M; ++m) {
+            std::vector<int> src{g(wrap(s - 1, S), m)};
+            for (int l = 0; l < M; ++l) src.push_back(g(s, l));
+            range(wrap(s - step - 2, S) * M + m, &lo, &hi);
+            Builder::add(rst, lo, hi, src, {g(s, m)});
+          }
+      }
+    }
+    if (ag_steps) {
+      for (int step = 0; step < S - 1; ++step) {
+        Step& st = sched->steps[idx[si++]];
+        for (int s = 0; s < S; ++s)
+          for (int m = 0; m < M; ++m) {
+            std::vector<int> dst{g(wrap(s + 1, S), m)};
+            for (int l = 0; l < M; ++l)
+              if (l != m) dst.push_back(g(s, l));
+            range(wrap(s - step, S) * M + m, &lo, &hi);
+            Builder::add(st, lo, hi, {g(s, m)}, dst);
+          }
+      }
+      Step& st = sched->steps[idx[si++]];
+      for (int s = 0; s < S; ++s)
+        for (int m = 0; m < M; ++m) {
+          std::vector<int> dst;
+          for (int l = 0; l < M; ++l)
+            if (l != m) dst.push_back(g(s, l));
+          range(wrap(s + 1, S) * M + m, &lo, &hi);
+          Builder::add(st, lo, hi, {g(s, m)}, dst);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- checks
+// No two items of a step may touch overlapping ranges of one rank where
+// either writes; within an item a destination may only be read on its own
+// range (the in-place local operand).
+bool step_is_race_free(const Step& st) {
+  struct Touch {
+    int rank;
+    uint64_t b, e;
+    size_t item;
+    bool write;
+  };
+  std::vector<Touch> v;
+  for (size_t i = 0; i < st.items.size(); ++i) {
+    const Item& it = st.items[i];
+    for (int k = 0; k < it.nsrc + it.ndst; ++k)
+      v.push_back({it.rank[k], it.begin, it.begin + it.count, i, k >= it.nsrc});
+    for (int a = it.nsrc; a < it.nsrc + it.ndst; ++a)
+      for (int b = a + 1; b < it.nsrc + it.ndst; ++b)
+        if (it.rank[a] == it.rank[b]) return false;  // one destination twice
+  }
+  std::sort(v.begin(), v.end(), [](const Touch& x, const Touch& y) {
+    return x.rank != y.rank ? x.rank < y.rank : x.b < y.b;
+  });
+  for (size_t i = 0; i < v.size(); ++i)
+    for (size_t j = i + 1; j < v.size() && v[j].rank == v[i].rank && v[j].b < v[i].e; ++j)
+      if (v[i].item != v[j].item && (v[i].write || v[j].write)) return false;
+  return true;
+}
+
+}  // namespace
+
+BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint32_t esize,
+                           Schedule* out) {
+  *out = Schedule{};
+  if (topo.P < 1 || topo.P > kMaxRanks || esize == 0) return kBadArg;
+  if (topo.algo == kPipeline && (topo.S < 1 || topo.M < 1 || topo.S * topo.M != topo.P))
+    return kBadArg;
+  const bool pow2 = (topo.P & (topo.P - 1)) == 0;
+  if (topo.algo == kRhd && coll != kAllReduce && !pow2) return kUnsupported;
+  if (topo.P == 1) return kBuilt;
+
+  Builder B(out);
+  switch (topo.algo) {
+    case kRing: ring(topo, coll, count, B); break;
+    case kRhd:
+      if (coll == kAllReduce)
+        rhd_allreduce(topo, count, B);
+      else
+        rhd_ordered(topo, coll, count, B);
+      break;
+    case kPipeline: pipeline(topo, coll, count, esize, B, out); break;
+    default: return kBadArg;
+  }
+
+  std::vector<uint64_t> recv(topo.P, 0);
+  for (Step& st : out->steps) {
+    bool first = true;
+    for (const Item& it : st.items) {
+      if (first) {
+        st.nsrc = it.nsrc;
+        st.ndst = it.ndst;
+        first = false;
+      } else if (it.nsrc != st.nsrc || it.ndst != st.ndst) {
+        return kBadArg;  // the launcher relies on one item shape per step
+      }
+      st.hbm_bytes += uint64_t(it.nsrc + it.ndst) * it.count * esize;
+      st.max_count = std::max(st.max_count, it.count);
+      for (int d = it.nsrc; d < it.nsrc + it.ndst; ++d) {
+        int others = 0;
+        for (int s = 0; s < it.nsrc; ++s) others += it.rank[s] != it.rank[d];
+        recv[it.rank[d]] += uint64_t(others) * it.count * esize;
+      }
+    }
+    if (!step_is_race_free(st)) return kBadArg;
+    out->hbm_bytes += st.hbm_bytes;
+  }
+  out->max_recv_bytes = *std::max_element(recv.begin(), recv.end());
+  return kBuilt;
+}
+
+}  // namespace hbmc

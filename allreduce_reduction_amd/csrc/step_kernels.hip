@@ -1,0 +1,336 @@
+// gfx950 step kernels.  One launch executes one schedule step for all ranks:
+// grid.y indexes the step's work items, grid.x tiles an item's elements.
+//
+// The reduce is the pages' reduce_op(recv, local) over a received block and
+// the local block ([RING-RHD] "Ring AllReduce带宽最优的环形流水线" listing;
+// the vector unit applies sum / product / maximum, section "Ascend950的AIVAICPU
+// 通信引擎与图模式"); a copy is the all-gather's segment transfer.  On one GPU
+// both become HBM streams: a step reads every source block once and writes
+// every destination block once.
+//
+// Data path: every operand of an item sits at the same element offset, and
+// when all rank buffers share one 16-byte phase the item's body is moved as
+// 16-byte vectors (global_load/store_dwordx4), four per thread per operand
+// per tile, with the few head / tail elements done one by one.  Buffers with
+// different phases take an element-wise kernel.
+//
+// Element ops: fp16 / bf16 lanes are widened to fp32, combined and rounded
+// back to nearest even per operation; integers wrap; max / min order -0 below
+// +0 and give the canonical quiet NaN when either operand is NaN.
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "plan.hpp"
+
+namespace hbmc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVecPerThread = 4;
+constexpr uint64_t kTileVecs = uint64_t(kThreads) * kVecPerThread;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { kF32 = 0, kF16 = 1, kBF16 = 2, kI32 = 3, kI8 = 4 };
+enum { kSum = 0, kProd = 1, kMax = 2, kMin = 3 };
+
+template <int DT>
+struct Width {
+  static constexpr uint32_t bytes = (DT == kF32 || DT == kI32) ? 4 : (DT == kI8 ? 1 : 2);
+};
+
+// ------------------------------------------------------------- element ops
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+
+// Monotone map of an IEEE bit pattern (sign bit `sb`) to an unsigned key:
+// negative values reversed below positive ones, so -0 sorts under +0.
+template <uint32_t SB, uint32_t MASK>
+__device__ __forceinline__ uint32_t order_key(uint32_t u) {
+  return (u & SB) ? (~u & MASK) : (u | SB);
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t op_f32(uint32_t a, uint32_t b) {
+  if constexpr (OP == kSum) {
+    return f2u(u2f(a) + u2f(b));
+  } else if constexpr (OP == kProd) {
+    return f2u(u2f(a) * u2f(b));
+  } else {
+    const bool nan = ((a & 0x7fffffffu) > 0x7f800000u) | ((b & 0x7fffffffu) > 0x7f800000u);
+    const uint32_t ka = order_key<0x80000000u, 0xffffffffu>(a);
+    const uint32_t kb = order_key<0x80000000u, 0xffffffffu>(b);
+    const uint32_t r = (OP == kMax) ? (ka >= kb ? a : b) : (ka <= kb ? a : b);
+    return nan ? 0x7fc00000u : r;
+  }
+}
+
+__device__ __forceinline__ float widen_f16(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+__device__ __forceinline__ uint32_t narrow_f16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // v_cvt_f16_f32, nearest even
+}
+__device__ __forceinline__ float widen_bf16(uint32_t h) { return u2f(h << 16); }
+__device__ __forceinline__ uint32_t narrow_bf16(float f) {
+  const uint32_t u = f2u(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet the NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                  // nearest even
+}
+
+// One 16-bit lane (value in the low half of the word).
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t op_h16(uint32_t a, uint32_t b) {
+  if constexpr (OP == kSum || OP == kProd) {
+    const float x = DT == kF16 ? widen_f16(a) : widen_bf16(a);
+    const float y = DT == kF16 ? widen_f16(b) : widen_bf16(b);
+    const float z = OP == kSum ? x + y : x * y;
+    return DT == kF16 ? narrow_f16(z) : narrow_bf16(z);
+  } else {
+    constexpr uint32_t inf = DT == kF16 ? 0x7c00u : 0x7f80u;
+    constexpr uint32_t qnan = DT == kF16 ? 0x7e00u : 0x7fc0u;
+    const bool nan = ((a & 0x7fffu) > inf) | ((b & 0x7fffu) > inf);
+    const uint32_t ka = order_key<0x8000u, 0xffffu>(a);
+    const uint32_t kb = order_key<0x8000u, 0xffffu>(b);
+    const uint32_t r = (OP == kMax) ? (ka >= kb ? a : b) : (ka <= kb ? a : b);
+    return nan ? qnan : r;
+  }
+}
+
+template <int OP>
+__device__ __forceinline__ int op_int(int x, int y) {
+  if constexpr (OP == kSum) return static_cast<int>(static_cast<uint32_t>(x) + static_cast<uint32_t>(y));
+  if constexpr (OP == kProd) return static_cast<int>(static_cast<uint32_t>(x) * static_cast<uint32_t>(y));
+  if constexpr (OP == kMax) return x >= y ? x : y;
+  return x <= y ? x : y;
+}
+
+// The op on one 32-bit word of packed elements.
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t op_word(uint32_t a, uint32_t b) {
+  if constexpr (DT == kF32) {
+    return op_f32<OP>(a, b);
+  } else if constexpr (DT == kF16 || DT == kBF16) {
+    return op_h16<DT, OP>(a & 0xffffu, b & 0xffffu) | (op_h16<DT, OP>(a >> 16, b >> 16) << 16);
+  } else if constexpr (DT == kI32) {
+    return static_cast<uint32_t>(op_int<OP>(static_cast<int>(a), static_cast<int>(b)));
+  } else {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 32; k += 8) {
+      const int x = static_cast<int8_t>(a >> k), y = static_cast<int8_t>(b >> k);
+      r |= (static_cast<uint32_t>(op_int<OP>(x, y)) & 0xffu) << k;
+    }
+    return r;
+  }
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ u32x4 op_vec(u32x4 a, u32x4 b) {
+  u32x4 r;
+  r.x = op_word<DT, OP>(a.x, b.x);
+  r.y = op_word<DT, OP>(a.y, b.y);
+  r.z = op_word<DT, OP>(a.z, b.z);
+  r.w = op_word<DT, OP>(a.w, b.w);
+  return r;
+}
+
+template <uint32_t E>
+__device__ __forceinline__ uint32_t load_elem(const unsigned char* p) {
+  if constexpr (E == 4) return *reinterpret_cast<const uint32_t*>(p);
+  if constexpr (E == 2) return *reinterpret_cast<const uint16_t*>(p);
+  return *p;
+}
+template <uint32_t E>
+__device__ __forceinline__ void store_elem(unsigned char* p, uint32_t v) {
+  if constexpr (E == 4) *reinterpret_cast<uint32_t*>(p) = v;
+  else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(v);
+  else *p = static_cast<unsigned char>(v);
+}
+
+// Combination of an item's sources at one element (byte offset `off`).
+template <int DT, int OP, int MODE>
+__device__ __forceinline__ uint32_t combine_elem(const RankPtrs& ptrs, const DevItem* it, int ns,
+                                                 uint64_t off) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  if constexpr (MODE == kCopy) {
+    return load_elem<E>(ptrs.p[it->rank[0]] + off);
+  } else if constexpr (MODE == kFold) {
+    uint32_t acc = load_elem<E>(ptrs.p[it->rank[0]] + off);
+    for (int s = 1; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(ptrs.p[it->rank[s]] + off));
+    return acc;
+  } else {
+    uint32_t acc = load_elem<E>(ptrs.p[it->rank[1]] + off);
+    for (int s = 2; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(ptrs.p[it->rank[s]] + off));
+    return op_word<DT, OP>(load_elem<E>(ptrs.p[it->rank[0]] + off), acc);
+  }
+}
+
+template <int DT, int OP, int MODE>
+__device__ __forceinline__ void do_elem(const RankPtrs& ptrs, const DevItem* it, int ns, int nd,
+                                        uint64_t elem) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  const uint64_t off = elem * E;
+  const uint32_t v = combine_elem<DT, OP, MODE>(ptrs, it, ns, off);
+  for (int d = 0; d < nd; ++d) store_elem<E>(ptrs.p[it->rank[ns + d]] + off, v);
+}
+
+// ------------------------------------------------------------- kernels
+
+// Vector kernel.  NS / ND > 0 fix the item shape at compile time (all loads
+// of a tile issued before any combine); 0 reads it from the item.
+template <int DT, int OP, int MODE, int NS, int ND>
+__global__ void __launch_bounds__(kThreads)
+step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  const DevItem* it = items + blockIdx.y;
+  const uint64_t begin = it->begin, count = it->count;
+  const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
+  const int nd = ND > 0 ? ND : static_cast<int>(it->ndst);
+
+  uint64_t head = ((16u - ((phase + begin * E) & 15u)) & 15u) / E;
+  if (head > count) head = count;
+  const uint64_t nvec = (count - head) * E / 16;
+  const uint64_t body_end = head + nvec * (16 / E);
+
+  const uint64_t v0 = uint64_t(blockIdx.x) * kTileVecs + threadIdx.x;
+  if (uint64_t(blockIdx.x) * kTileVecs < nvec) {
+    const uint64_t base = (begin + head) * E;
+    u32x4 acc[kVecPerThread];
+    if constexpr (NS > 0 && NS <= 2) {
+      u32x4 x[NS][kVecPerThread];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[s]] + base);
+#pragma unroll
+        for (int u = 0; u < kVecPerThread; ++u) {
+          const uint64_t v = v0 + uint64_t(u) * kThreads;
+          if (v < nvec) x[s][u] = p[v];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kVecPerThread; ++u) {
+        if constexpr (MODE == kCopy) acc[u] = x[0][u];
+        else if constexpr (MODE == kFold) acc[u] = NS == 1 ? x[0][u] : op_vec<DT, OP>(x[0][u], x[NS - 1][u]);
+        else acc[u] = NS == 1 ? x[0][u] : op_vec<DT, OP>(x[0][u], x[1][u]);
+      }
+    } else {
+      const int first = MODE == kRecvFold ? 1 : 0;
+      {
+        const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[first]] + base);
+#pragma unroll
+        for (int u = 0; u < kVecPerThread; ++u) {
+          const uint64_t v = v0 + uint64_t(u) * kThreads;
+          if (v < nvec) acc[u] = p[v];
+        }
+      }
+      if constexpr (MODE != kCopy) {
+        for (int s = first + 1; s < ns; ++s) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[s]] + base);
+#pragma unroll
+          for (int u = 0; u < kVecPerThread; ++u) {
+            const uint64_t v = v0 + uint64_t(u) * kThreads;
+            if (v < nvec) acc[u] = op_vec<DT, OP>(acc[u], p[v]);
+          }
+        }
+        if constexpr (MODE == kRecvFold) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[0]] + base);
+#pragma unroll
+          for (int u = 0; u < kVecPerThread; ++u) {
+            const uint64_t v = v0 + uint64_t(u) * kThreads;
+            if (v < nvec) acc[u] = op_vec<DT, OP>(p[v], acc[u]);
+          }
+        }
+      }
+    }
+    for (int d = 0; d < nd; ++d) {
+      u32x4* q = reinterpret_cast<u32x4*>(ptrs.p[it->rank[ns + d]] + base);
+#pragma unroll
+      for (int u = 0; u < kVecPerThread; ++u) {
+        const uint64_t v = v0 + uint64_t(u) * kThreads;
+        if (v < nvec) q[v] = acc[u];
+      }
+    }
+  }
+
+  // head and tail elements (fewer than 16 bytes each), by the item's first tile
+  if (blockIdx.x == 0) {
+    const uint64_t t = threadIdx.x;
+    if (t < head) do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + t);
+    if (t >= 64 && t - 64 < count - body_end) do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + body_end + (t - 64));
+  }
+}
+
+// Element-wise kernel for buffers whose 16-byte phases differ.
+template <int DT, int OP, int MODE>
+__global__ void __launch_bounds__(kThreads)
+step_elem(RankPtrs ptrs, const DevItem* __restrict__ items) {
+  const DevItem* it = items + blockIdx.y;
+  const uint64_t begin = it->begin, count = it->count;
+  const int ns = static_cast<int>(it->nsrc), nd = static_cast<int>(it->ndst);
+  const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+  for (uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x; i < count; i += stride)
+    do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + i);
+}
+
+// ------------------------------------------------------------- dispatch
+
+template <int DT, int OP>
+hipError_t launch_typed(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  const dim3 block(kThreads);
+  if (!s.aligned) {
+    uint64_t gx = (s.max_count + kThreads - 1) / kThreads;
+    if (gx > 2048) gx = 2048;
+    if (gx < 1) gx = 1;
+    const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
+    switch (s.mode) {
+      case kCopy: hipLaunchKernelGGL((step_elem<DT, OP, kCopy>), grid, block, 0, stream, ptrs, s.items); break;
+      case kFold: hipLaunchKernelGGL((step_elem<DT, OP, kFold>), grid, block, 0, stream, ptrs, s.items); break;
+      default: hipLaunchKernelGGL((step_elem<DT, OP, kRecvFold>), grid, block, 0, stream, ptrs, s.items); break;
+    }
+    return hipGetLastError();
+  }
+  const uint64_t vecs = s.max_count * E / 16 + 1;
+  const uint64_t gx = (vecs + kTileVecs - 1) / kTileVecs;
+  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
+  if (s.mode == kRecvFold && s.nsrc == 2 && s.ndst == 1) {
+    hipLaunchKernelGGL((step_vec<DT, OP, kRecvFold, 2, 1>), grid, block, 0, stream, ptrs, s.items, s.phase);
+  } else if (s.mode == kCopy && s.nsrc == 1 && s.ndst == 1) {
+    hipLaunchKernelGGL((step_vec<DT, kSum, kCopy, 1, 1>), grid, block, 0, stream, ptrs, s.items, s.phase);
+  } else if (s.mode == kCopy) {
+    hipLaunchKernelGGL((step_vec<DT, kSum, kCopy, 1, 0>), grid, block, 0, stream, ptrs, s.items, s.phase);
+  } else if (s.mode == kFold) {
+    hipLaunchKernelGGL((step_vec<DT, OP, kFold, 0, 1>), grid, block, 0, stream, ptrs, s.items, s.phase);
+  } else {
+    hipLaunchKernelGGL((step_vec<DT, OP, kRecvFold, 0, 1>), grid, block, 0, stream, ptrs, s.items, s.phase);
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_op(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream) {
+  switch (s.op) {
+    case kSum: return launch_typed<DT, kSum>(s, ptrs, stream);
+    case kProd: return launch_typed<DT, kProd>(s, ptrs, stream);
+    case kMax: return launch_typed<DT, kMax>(s, ptrs, stream);
+    default: return launch_typed<DT, kMin>(s, ptrs, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream) {
+  if (s.nitems <= 0) return hipSuccess;
+  if (s.ndst > 1 && s.mode != kCopy) return hipErrorInvalidValue;  // no such schedule step
+  switch (s.dtype) {
+    case kF32: return launch_op<kF32>(s, ptrs, stream);
+    case kF16: return launch_op<kF16>(s, ptrs, stream);
+    case kBF16: return launch_op<kBF16>(s, ptrs, stream);
+    case kI32: return launch_op<kI32>(s, ptrs, stream);
+    default: return launch_op<kI8>(s, ptrs, stream);
+  }
+}
+
+}  // namespace hbmc

@@ -1,0 +1,160 @@
+/*
+ * hbmcoll -- AllReduce dataflow of P logical ranks kept as P buffers in one
+ * GPU's HBM (gfx950).  C ABI: plain pointers and sizes, no C++ or torch types.
+ *
+ * Pages cited (titles as printed):
+ *   [RING-RHD]  "HCCL Ring AllReduce 与 Recursive Halving-Doubling 对比" (mhpn.cn/news/973985)
+ *   [TOPO]      HCCL topology-aware routing article (hwcomputing.csdn.net)
+ *   [RHD]       "HCCL RHD（Recursive Halving-Doubling）算法深度解析" (mhpn.cn/news/2258316)
+ *   [PIPE]      "HCCL Pipeline分级流水算法深度解析：原理、时序编排与耗时模型" (lpnh.cn/news/2272425)
+ *
+ * Common rules for every call below:
+ *   - Return HBMC_OK on success, otherwise an error code; outputs come back
+ *     through out-parameters (the pages' result-code convention, [RING-RHD]
+ *     section "Ascend950的AIVAICPU通信引擎与图模式", HcclGraphBuild listing).
+ *   - Collectives are in place: bufs[r] is rank r's device buffer of `count`
+ *     elements of `dtype` on the current device; the P buffers must not
+ *     overlap and must be aligned to the element size.  Buffers whose 16-byte
+ *     phases differ are accepted and take a slower element-wise path.
+ *   - Collectives are asynchronous and ordered on `stream` (a hipStream_t;
+ *     NULL is the default stream), like the pages' stream-ordered operations
+ *     with wait/event completion ([TOPO] section "梯度同步与计算重叠").  They
+ *     return after enqueueing; a device fault surfaces at the caller's next
+ *     synchronisation of that stream.
+ *   - The caller owns the buffers and the stream; the communicator owns its
+ *     cached schedules and their device tables.  A communicator is not
+ *     thread-safe; calls that overlap on one communicator from several host
+ *     threads race.
+ *   - count == 0 and P == 1 are valid and enqueue nothing.
+ */
+#ifndef HBMCOLL_H
+#define HBMCOLL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hbmc_comm* hbmc_comm_t;
+
+typedef enum {
+  HBMC_OK = 0,
+  HBMC_ERR_INVALID_ARG = 1, /* null / aliased / misaligned buffers, bad P, count*e overflow,
+                               S*M != P, enum out of range, step range out of bounds      */
+  HBMC_ERR_UNSUPPORTED = 2, /* RHD reduce_scatter / all_gather with P not a power of two   */
+  HBMC_ERR_HIP = 3,         /* a HIP call or kernel launch failed                          */
+  HBMC_ERR_NOMEM = 4        /* host or device allocation failed                            */
+} hbmc_status_t;
+
+/* element types (the pages' HcclDataType) */
+typedef enum { HBMC_FP32 = 0, HBMC_FP16 = 1, HBMC_BF16 = 2, HBMC_INT32 = 3, HBMC_INT8 = 4 } hbmc_dtype_t;
+
+/* reduce ops (the pages' HcclReduceOp: addition, multiplication, maximum;
+ * minimum added).  fp16/bf16 are widened to fp32, combined and rounded back to
+ * nearest even after every operation; integers wrap; max/min order -0 below
+ * +0 and return the canonical quiet NaN if either operand is NaN. */
+typedef enum { HBMC_SUM = 0, HBMC_PROD = 1, HBMC_MAX = 2, HBMC_MIN = 3 } hbmc_op_t;
+
+/* algorithms.  RING: [RING-RHD] "Ring AllReduce带宽最优的环形流水线".
+ * RHD: [RHD] "算法描述" and Table 1 (non-power-of-two P merges the first 2r
+ * ranks into r, r = P - 2^floor(log2 P), and restores them at the end).
+ * PIPELINE: [PIPE] -- S servers x M ranks, inter-server ring, intra-server
+ * full mesh, sliced into loops.  ENV: take the algorithm from the environment
+ * variable HBMC_ALGO ("ring", "rhd" or "H-D_R", "pipeline"), the way the
+ * pages' HCCL_ALGO selects an algorithm ([RHD] "RHD 在 HCCL 中的定位与启用方式"). */
+typedef enum { HBMC_ALGO_RING = 0, HBMC_ALGO_RHD = 1, HBMC_ALGO_PIPELINE = 2, HBMC_ALGO_ENV = 3 } hbmc_algo_t;
+
+typedef enum { HBMC_COLL_ALLREDUCE = 0, HBMC_COLL_REDUCE_SCATTER = 1, HBMC_COLL_ALL_GATHER = 2 } hbmc_coll_t;
+
+/*
+ * Create a communicator of `nranks` logical ranks (1..64) using `algo`.
+ * For HBMC_ALGO_PIPELINE, servers * ranks_per_server must equal nranks and
+ * loop_bytes is the per-loop slice ([PIPE] "源码中的流水执行印证": the
+ * executor slices the data into loops bounded by its buffer limits); 0 selects
+ * 32 MiB.  Other algorithms ignore servers, ranks_per_server and loop_bytes.
+ * Touches no device state.  *out receives the handle.
+ */
+hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_per_server,
+                               size_t loop_bytes, hbmc_comm_t* out);
+
+/* Free the communicator and its device tables.  The caller must have
+ * synchronised every stream that still runs one of its collectives. */
+hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
+
+/*
+ * AllReduce, Y[j] = op over ranks i of X_i[j] ([RING-RHD] "AllReduce的数学抽象与问题定义").
+ * On completion every bufs[r][0..count) holds Y, computed in the order the
+ * communicator's schedule implies (bit-identical for every rank).
+ */
+hbmc_status_t hbmc_allreduce(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
+                             hbmc_op_t op, void* stream);
+
+/*
+ * ReduceScatter.  The vector is split into P segments by the ceiling split
+ * (segment k = [min(k q, count), min((k+1) q, count)), q = ceil(count / P),
+ * [TOPO] "AllReduce算法实现"); for the pipeline each loop is split that way.
+ * On completion bufs[r] holds Y on segment r (each loop's block r for the
+ * pipeline); its other segments are unspecified.
+ */
+hbmc_status_t hbmc_reduce_scatter(hbmc_comm_t comm, void* const bufs[], size_t count,
+                                  hbmc_dtype_t dtype, hbmc_op_t op, void* stream);
+
+/*
+ * AllGather.  On entry bufs[r] holds rank r's contribution on segment r (as
+ * reduce_scatter leaves it); on completion every buffer holds all segments.
+ * `op` is validated but unused, so all three collectives share one signature.
+ */
+hbmc_status_t hbmc_all_gather(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
+                              hbmc_op_t op, void* stream);
+
+/*
+ * Run only schedule steps [first_step, last_step) of a collective (every
+ * loop's steps with those indices for the pipeline).  Running [0, k) and then
+ * [k, nsteps) equals the whole collective.  For step-by-step checking and
+ * per-step timing.  Returns HBMC_ERR_INVALID_ARG for an empty or
+ * out-of-range step interval.
+ */
+hbmc_status_t hbmc_run_steps(hbmc_comm_t comm, hbmc_coll_t coll, void* const bufs[], size_t count,
+                             hbmc_dtype_t dtype, hbmc_op_t op, int first_step, int last_step,
+                             void* stream);
+
+/*
+ * Schedule facts, computed on the host without touching the device:
+ * number of steps (launches), algorithmic HBM bytes of the whole collective
+ * (every distinct block a step reads counted once, every block it writes
+ * once), and the largest number of bytes any rank receives from other ranks.
+ * Any out-pointer may be NULL.
+ */
+hbmc_status_t hbmc_plan_info(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, hbmc_dtype_t dtype,
+                             int* nsteps, uint64_t* hbm_bytes, uint64_t* max_recv_bytes);
+
+/* The same for one step: its work items and algorithmic HBM bytes. */
+hbmc_status_t hbmc_plan_step_info(hbmc_comm_t comm, hbmc_coll_t coll, size_t count,
+                                  hbmc_dtype_t dtype, int step, int* nitems, uint64_t* hbm_bytes);
+
+/* One work item of a step: every destination rank's range
+ * [begin, begin+count) receives, for mode COPY the source, for mode FOLD the
+ * left fold of op over the sources in order, and for mode RECV_FOLD
+ * op(source 0, left fold over sources 1..).  rank[0..nsrc) are the sources,
+ * rank[nsrc..nsrc+ndst) the destinations. */
+enum { HBMC_MODE_COPY = 0, HBMC_MODE_FOLD = 1, HBMC_MODE_RECV_FOLD = 2 };
+typedef struct {
+  int32_t step, mode, nsrc, ndst;
+  uint64_t begin, count;
+  uint8_t rank[128];
+} hbmc_item_t;
+
+/* Copy out every work item of a collective's schedule (host only).  Writes
+ * at most `cap` items and sets *n_items to the total. */
+hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, hbmc_dtype_t dtype,
+                              hbmc_item_t* out, size_t cap, size_t* n_items);
+
+/* Static text for a status code. */
+const char* hbmc_status_string(hbmc_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

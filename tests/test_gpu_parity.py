@@ -1,0 +1,182 @@
+"""GPU parity: the C-ABI library on gfx950 against the CPU oracle, bit for bit.
+
+Every case uploads seeded inputs, runs one collective through the C ABI, and
+compares every rank's buffer with the oracle's replay of the same schedule
+(NaNs of sum / prod compared as a class; max / min NaNs bit-exactly).
+Sizes span several 4096-element tiles with ragged tails, segments shorter
+than one vector, empty segments (L < P) and L = 0.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import allreduce_reduction_amd as hc
+import oracle
+import refops
+import synth
+from gpu_util import strided_buffers, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["fp32", "fp16", "bf16", "int32", "int8"]
+OPS = ["sum", "prod", "max", "min"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_inputs(dtype, op, P, L, seed):
+    if dtype in ("int32", "int8"):
+        lo, hi = (-(2 ** 20), 2 ** 20) if dtype == "int32" else (-128, 127)
+        if op == "prod":
+            lo, hi = -3, 3
+        return [synth.generate(dtype, L, synth.UNIFORM_INT, lo, hi, seed=seed, stream=70, rank=r)
+                for r in range(P)]
+    xs = [synth.generate(dtype, L, synth.NORMAL, 1.0, seed=seed, stream=71, rank=r) for r in range(P)]
+    if op == "prod":
+        xs = [refops.from_f32(dtype, (1.0 + 0.05 * refops.to_f64(dtype, x)).astype(np.float32)) for x in xs]
+    return xs
+
+
+def comm_for(algo, P, loop_bytes=0):
+    if algo == "pipeline":
+        # prefer two or more servers with several ranks each
+        shapes = [(P // M, M) for M in (8, 4, 3, 2) if P % M == 0]
+        S, M = next((sm for sm in shapes if sm[0] >= 2), shapes[0] if shapes else (P, 1))
+        return hc.Comm(P, "pipeline", S, M, loop_bytes), S, M
+    return hc.Comm(P, algo), 1, 1
+
+
+def check_case(algo, coll, dtype, op, P, L, seed, loop_bytes=0):
+    say(f"case algo={algo} coll={coll} dtype={dtype} op={op} P={P} L={L} seed={seed}")
+    comm, S, M = comm_for(algo, P, loop_bytes)
+    with comm:
+        xs = make_inputs(dtype, op, P, L, seed)
+        dev = [to_dev(x, dtype) for x in xs]
+        getattr(comm, coll)(dev, dtype, op)
+        torch.cuda.synchronize()
+        want = [x.copy() for x in xs]
+        oracle.run(coll, algo, want, dtype, op, S=S, M=M, loop_bytes=loop_bytes)
+        for r in range(P):
+            got = to_host(dev[r], dtype)
+            refops.assert_same(dtype, got, want[r], f"{algo} {coll} {dtype} {op} P={P} L={L} rank {r}")
+            if op in ("max", "min") and dtype in refops.FLOATS:
+                assert np.array_equal(got.view(np.uint8), want[r].view(np.uint8))
+
+
+LS = [0, 1, 5, 1000, 3 * 4096 + 7, 50_001]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("coll", ["allreduce", "reduce_scatter", "all_gather"])
+@pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
+def test_parity(algo, coll, dtype):
+    rng = np.random.default_rng(zlib.crc32(f"{algo}/{coll}/{dtype}".encode()))
+    Ps = [2, 3, 5, 8] if not (algo == "rhd" and coll != "allreduce") else [2, 4, 8]
+    for op in OPS:
+        for P in Ps:
+            L = int(rng.choice(LS))
+            check_case(algo, coll, dtype, op, P, L, seed=int(rng.integers(1 << 30)),
+                       loop_bytes=(8192 if algo == "pipeline" else 0))
+
+
+@pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
+def test_parity_many_ranks(algo):
+    for P in (13, 16, 32, 64):
+        if algo == "pipeline" and P == 13:
+            continue
+        for dtype, op in (("fp32", "sum"), ("bf16", "sum"), ("int8", "max")):
+            check_case(algo, "allreduce", dtype, op, P, 20_000 + P, seed=P, loop_bytes=16384)
+
+
+@pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
+def test_parity_small_and_empty_segments(algo):
+    for P in (3, 5, 8, 16):
+        for L in range(0, P + 3):
+            check_case(algo, "allreduce", "fp16", "sum", P, L, seed=L)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("phases", ["same_nonzero", "different"])
+def test_unaligned_buffers(dtype, phases):
+    """Buffers at odd element offsets: a shared 16-byte phase takes the vector
+    kernel with head/tail elements, differing phases the element-wise kernel."""
+    esz = np.dtype(refops.STORAGE[dtype]).itemsize
+    for algo in ("ring", "rhd"):
+        P, L = 5, 3 * 4096 + 11
+        say(f"case unaligned {phases} algo={algo} dtype={dtype} P={P} L={L}")
+        xs = make_inputs(dtype, "sum", P, L, seed=3)
+        if phases == "same_nonzero":
+            offs = [max(1, 4 // esz) if esz < 16 else 0] * P
+        else:
+            offs = [r % max(2, 16 // esz) for r in range(P)]
+        views, backing = strided_buffers(xs, dtype, offs)
+        with hc.Comm(P, algo) as comm:
+            comm.allreduce(views, dtype, "sum")
+            torch.cuda.synchronize()
+        want = [x.copy() for x in xs]
+        oracle.run("allreduce", algo, want, dtype, "sum")
+        for r in range(P):
+            refops.assert_same(dtype, to_host(views[r], dtype), want[r], f"rank {r}")
+        # nothing outside the rank ranges was written
+        mask = torch.ones_like(backing, dtype=torch.bool)
+        for v in views:
+            off = (v.data_ptr() - backing.data_ptr()) // esz
+            mask[off:off + L] = False
+        assert int((backing[mask] != 0).sum()) == 0
+
+
+@pytest.mark.parametrize("algo,coll,P", [("ring", "allreduce", 8), ("rhd", "allreduce", 5),
+                                         ("rhd", "allreduce", 8), ("rhd", "reduce_scatter", 8),
+                                         ("pipeline", "allreduce", 8), ("ring", "all_gather", 6)])
+def test_step_by_step(algo, coll, P):
+    """Every rank's whole buffer after every step equals the oracle's replay state."""
+    dtype, L = "bf16", 4 * 4096 + 13
+    comm, S, M = comm_for(algo, P, loop_bytes=4096)
+    with comm:
+        xs = make_inputs(dtype, "sum", P, L, seed=11)
+        dev = [to_dev(x, dtype) for x in xs]
+        nsteps = comm.plan_info(coll, L, dtype)["nsteps"]
+        assert nsteps == oracle.num_steps(coll, algo, P, S, M)
+        want = [x.copy() for x in xs]
+        for s in range(nsteps):
+            say(f"case step-by-step algo={algo} coll={coll} P={P} step={s}")
+            comm.run_steps(coll, dev, s, s + 1, dtype, "sum")
+            torch.cuda.synchronize()
+            oracle.run(coll, algo, want, dtype, "sum", S=S, M=M, loop_bytes=4096, first_step=s,
+                       last_step=s + 1)
+            for r in range(P):
+                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"after step {s}, rank {r}")
+
+
+def test_single_rank_and_zero_count_leave_buffers_alone():
+    x = synth.generate("fp32", 1000, synth.NORMAL, 1.0, seed=1)
+    t = to_dev(x, "fp32")
+    with hc.Comm(1, "ring") as c:
+        c.allreduce([t], "fp32", "sum")
+    with hc.Comm(4, "ring") as c:
+        bufs = [to_dev(x, "fp32") for _ in range(4)]
+        c.allreduce(bufs, "fp32", "sum", count=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(t, "fp32"), x)
+    assert all(np.array_equal(to_host(b, "fp32"), x) for b in bufs)
+
+
+def test_non_default_stream():
+    P, L = 8, 100_000
+    xs = make_inputs("fp32", "sum", P, L, seed=5)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dev = [to_dev(x, "fp32") for x in xs]
+        with hc.Comm(P, "ring") as c:
+            c.allreduce(dev, "fp32", "sum")
+            s.synchronize()
+    want = [x.copy() for x in xs]
+    oracle.run("allreduce", "ring", want, "fp32", "sum")
+    for r in range(P):
+        refops.assert_same("fp32", to_host(dev[r], "fp32"), want[r])
