@@ -41,6 +41,7 @@ struct Plan {
 
 struct hbmc_comm {
   Topology topo;
+  bool xcd_split = false;
   std::map<std::tuple<int, uint64_t, int>, std::unique_ptr<Plan>> plans;
 };
 
@@ -174,6 +175,7 @@ hbmc_status_t run(hbmc_comm* c, int coll, void* const bufs[], size_t count, int 
     L.max_count = step.max_count;
     L.aligned = aligned;
     L.phase = phase;
+    L.xcd_split = c->xcd_split;
     if (launch_step(L, ptrs, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
   }
   return HBMC_OK;
@@ -212,6 +214,8 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
   hbmc_comm* c = new (std::nothrow) hbmc_comm;
   if (!c) return HBMC_ERR_NOMEM;
   c->topo = t;
+  const char* xs = std::getenv("HBMC_XCD_SPLIT");
+  c->xcd_split = xs && xs[0] == '1';
   *out = c;
   return HBMC_OK;
 }

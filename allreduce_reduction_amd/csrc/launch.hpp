@@ -31,6 +31,7 @@ struct StepLaunch {
   uint64_t max_count;     // largest item, elements
   bool aligned;           // every rank buffer has the same 16-byte phase
   uint32_t phase;         // that phase, bytes
+  bool xcd_split;         // give each XCD one contiguous range of tiles
 };
 
 // Enqueue one step on `stream`; returns the launch's error state.

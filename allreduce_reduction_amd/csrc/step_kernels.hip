@@ -10,9 +10,11 @@
 //
 // Data path: every operand of an item sits at the same element offset, and
 // when all rank buffers share one 16-byte phase the item's body is moved as
-// 16-byte vectors (global_load/store_dwordx4), four per thread per operand
-// per tile, with the few head / tail elements done one by one.  Buffers with
-// different phases take an element-wise kernel.
+// 16-byte vectors (global_load/store_dwordx4 with the nontemporal hint): one
+// wave per workgroup and one vector per lane per operand, i.e. 1 KiB tiles of
+// every operand per workgroup, which measured fastest for streams far larger
+// than the caches; the few head / tail elements are done one by one.  Buffers
+// with different phases take an element-wise kernel.
 //
 // Element ops: fp16 / bf16 lanes are widened to fp32, combined and rounded
 // back to nearest even per operation; integers wrap; max / min order -0 below
@@ -25,9 +27,10 @@
 namespace hbmc {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;
+constexpr int kThreads = 64;        // vector kernel: one wave per workgroup
+constexpr int kVecPerThread = 1;    // 16-byte vectors per lane per operand
 constexpr uint64_t kTileVecs = uint64_t(kThreads) * kVecPerThread;
+constexpr int kElemThreads = 256;   // element-wise kernel
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -136,6 +139,9 @@ __device__ __forceinline__ u32x4 op_vec(u32x4 a, u32x4 b) {
   return r;
 }
 
+__device__ __forceinline__ u32x4 load_vec(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_vec(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
 template <uint32_t E>
 __device__ __forceinline__ uint32_t load_elem(const unsigned char* p) {
   if constexpr (E == 4) return *reinterpret_cast<const uint32_t*>(p);
@@ -180,11 +186,26 @@ __device__ __forceinline__ void do_elem(const RankPtrs& ptrs, const DevItem* it,
 
 // Vector kernel.  NS / ND > 0 fix the item shape at compile time (all loads
 // of a tile issued before any combine); 0 reads it from the item.
+// Workgroup -> (item, tile).  Workgroups are dealt to the 8 XCDs round-robin
+// by linear id; with `xcd_split` each XCD instead walks one contiguous range
+// of the step's tiles.
+__device__ __forceinline__ void wg_tile(bool xcd_split, uint32_t* item, uint32_t* tile) {
+  uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
+  if (xcd_split) {
+    const uint32_t per = (gridDim.x * gridDim.y) / 8;
+    lin = (lin % 8) * per + lin / 8;
+  }
+  *item = lin / gridDim.x;
+  *tile = lin % gridDim.x;
+}
+
 template <int DT, int OP, int MODE, int NS, int ND>
 __global__ void __launch_bounds__(kThreads)
-step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase) {
+step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint32_t xcd_split) {
   constexpr uint32_t E = Width<DT>::bytes;
-  const DevItem* it = items + blockIdx.y;
+  uint32_t item, tile;
+  wg_tile(xcd_split != 0, &item, &tile);
+  const DevItem* it = items + item;
   const uint64_t begin = it->begin, count = it->count;
   const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
   const int nd = ND > 0 ? ND : static_cast<int>(it->ndst);
@@ -194,8 +215,8 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase) {
   const uint64_t nvec = (count - head) * E / 16;
   const uint64_t body_end = head + nvec * (16 / E);
 
-  const uint64_t v0 = uint64_t(blockIdx.x) * kTileVecs + threadIdx.x;
-  if (uint64_t(blockIdx.x) * kTileVecs < nvec) {
+  const uint64_t v0 = uint64_t(tile) * kTileVecs + threadIdx.x;
+  if (uint64_t(tile) * kTileVecs < nvec) {
     const uint64_t base = (begin + head) * E;
     u32x4 acc[kVecPerThread];
     if constexpr (NS > 0 && NS <= 2) {
@@ -206,7 +227,7 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase) {
 #pragma unroll
         for (int u = 0; u < kVecPerThread; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
-          if (v < nvec) x[s][u] = p[v];
+          if (v < nvec) x[s][u] = load_vec(p + v);
         }
       }
 #pragma unroll
@@ -222,7 +243,7 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase) {
 #pragma unroll
         for (int u = 0; u < kVecPerThread; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
-          if (v < nvec) acc[u] = p[v];
+          if (v < nvec) acc[u] = load_vec(p + v);
         }
       }
       if constexpr (MODE != kCopy) {
@@ -231,7 +252,7 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase) {
 #pragma unroll
           for (int u = 0; u < kVecPerThread; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
-            if (v < nvec) acc[u] = op_vec<DT, OP>(acc[u], p[v]);
+            if (v < nvec) acc[u] = op_vec<DT, OP>(acc[u], load_vec(p + v));
           }
         }
         if constexpr (MODE == kRecvFold) {
@@ -239,7 +260,7 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase) {
 #pragma unroll
           for (int u = 0; u < kVecPerThread; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
-            if (v < nvec) acc[u] = op_vec<DT, OP>(p[v], acc[u]);
+            if (v < nvec) acc[u] = op_vec<DT, OP>(load_vec(p + v), acc[u]);
           }
         }
       }
@@ -249,28 +270,28 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase) {
 #pragma unroll
       for (int u = 0; u < kVecPerThread; ++u) {
         const uint64_t v = v0 + uint64_t(u) * kThreads;
-        if (v < nvec) q[v] = acc[u];
+        if (v < nvec) store_vec(q + v, acc[u]);
       }
     }
   }
 
   // head and tail elements (fewer than 16 bytes each), by the item's first tile
-  if (blockIdx.x == 0) {
+  if (tile == 0) {
     const uint64_t t = threadIdx.x;
     if (t < head) do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + t);
-    if (t >= 64 && t - 64 < count - body_end) do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + body_end + (t - 64));
+    if (t >= 32 && t - 32 < count - body_end) do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + body_end + (t - 32));
   }
 }
 
 // Element-wise kernel for buffers whose 16-byte phases differ.
 template <int DT, int OP, int MODE>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kElemThreads)
 step_elem(RankPtrs ptrs, const DevItem* __restrict__ items) {
   const DevItem* it = items + blockIdx.y;
   const uint64_t begin = it->begin, count = it->count;
   const int ns = static_cast<int>(it->nsrc), nd = static_cast<int>(it->ndst);
-  const uint64_t stride = uint64_t(gridDim.x) * kThreads;
-  for (uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x; i < count; i += stride)
+  const uint64_t stride = uint64_t(gridDim.x) * kElemThreads;
+  for (uint64_t i = uint64_t(blockIdx.x) * kElemThreads + threadIdx.x; i < count; i += stride)
     do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + i);
 }
 
@@ -279,9 +300,9 @@ step_elem(RankPtrs ptrs, const DevItem* __restrict__ items) {
 template <int DT, int OP>
 hipError_t launch_typed(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream) {
   constexpr uint32_t E = Width<DT>::bytes;
-  const dim3 block(kThreads);
   if (!s.aligned) {
-    uint64_t gx = (s.max_count + kThreads - 1) / kThreads;
+    const dim3 block(kElemThreads);
+    uint64_t gx = (s.max_count + kElemThreads - 1) / kElemThreads;
     if (gx > 2048) gx = 2048;
     if (gx < 1) gx = 1;
     const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
@@ -292,19 +313,21 @@ hipError_t launch_typed(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t s
     }
     return hipGetLastError();
   }
+  const dim3 block(kThreads);
   const uint64_t vecs = s.max_count * E / 16 + 1;
   const uint64_t gx = (vecs + kTileVecs - 1) / kTileVecs;
   const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
+  const uint32_t xcd = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? 1u : 0u;
   if (s.mode == kRecvFold && s.nsrc == 2 && s.ndst == 1) {
-    hipLaunchKernelGGL((step_vec<DT, OP, kRecvFold, 2, 1>), grid, block, 0, stream, ptrs, s.items, s.phase);
+    hipLaunchKernelGGL((step_vec<DT, OP, kRecvFold, 2, 1>), grid, block, 0, stream, ptrs, s.items, s.phase, xcd);
   } else if (s.mode == kCopy && s.nsrc == 1 && s.ndst == 1) {
-    hipLaunchKernelGGL((step_vec<DT, kSum, kCopy, 1, 1>), grid, block, 0, stream, ptrs, s.items, s.phase);
+    hipLaunchKernelGGL((step_vec<DT, kSum, kCopy, 1, 1>), grid, block, 0, stream, ptrs, s.items, s.phase, xcd);
   } else if (s.mode == kCopy) {
-    hipLaunchKernelGGL((step_vec<DT, kSum, kCopy, 1, 0>), grid, block, 0, stream, ptrs, s.items, s.phase);
+    hipLaunchKernelGGL((step_vec<DT, kSum, kCopy, 1, 0>), grid, block, 0, stream, ptrs, s.items, s.phase, xcd);
   } else if (s.mode == kFold) {
-    hipLaunchKernelGGL((step_vec<DT, OP, kFold, 0, 1>), grid, block, 0, stream, ptrs, s.items, s.phase);
+    hipLaunchKernelGGL((step_vec<DT, OP, kFold, 0, 1>), grid, block, 0, stream, ptrs, s.items, s.phase, xcd);
   } else {
-    hipLaunchKernelGGL((step_vec<DT, OP, kRecvFold, 0, 1>), grid, block, 0, stream, ptrs, s.items, s.phase);
+    hipLaunchKernelGGL((step_vec<DT, OP, kRecvFold, 0, 1>), grid, block, 0, stream, ptrs, s.items, s.phase, xcd);
   }
   return hipGetLastError();
 }
