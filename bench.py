@@ -29,6 +29,24 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
 
 
+def measured_traffic():
+    """HBM bytes per launch of the ring reduce step from the committed counter
+    summary, or None once the kernel source differs from the one measured."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "ring_rs_step_p8_fp32_64Mi_hbm_traffic.md")
+    src = b"".join(open(os.path.join(ROOT, "allreduce_reduction_amd", "csrc", f), "rb").read()
+                   for f in ("step_kernels.hip", "launch.hpp"))
+    digest = hashlib.sha256(src).hexdigest()[:16]
+    try:
+        kv = dict(line.strip().split(": ", 1) for line in open(path, encoding="utf-8")
+                  if line.strip().startswith(("traffic_bytes_per_launch:", "kernel_source_sha256_16:")))
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256_16") != digest:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,7 +152,8 @@ def main():
         "pct_hbm": round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2),
         "roofline": {"bound": "hbm", "kernel": "step_vec<fp32,sum,recv_fold,2,1> (ring reduce step)",
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK, 4),
+                     "traffic": measured_traffic() if (P, L, a.algo) == (8, 64 << 20, "ring") else None,
                      "bytes_per_launch": rs_bytes, "mean_launch_us": round(rs_ms * 1e3, 2)},
     }
     if ag_ms:

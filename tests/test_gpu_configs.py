@@ -1,0 +1,245 @@
+"""The five workloads at their full sizes, on the GPU, against the oracle.
+
+Small workloads are replayed whole by the oracle; large ones are checked on
+windows: every element within 64 of a segment / block / loop boundary plus
+random 64 Ki-element windows, replayed by the oracle with the full-size
+schedule (an element's result depends only on its own column and on the
+segment or block it lies in).  On the GPU every rank's buffer must equal
+rank 0's bit for bit.  Accuracy against the binary64 direct sum: norm-wise
+relative error <= 1e-5 (fp32) or 2^-7 (P-1) (fp16 / bf16), and the
+per-element bound of a (P-1)-addition sum.
+
+Workloads:
+  ring_p4   ring AllReduce, P=4, L=4096, fp32 integers in [-8, 8]
+  ring_p8   ring AllReduce, P=8, L=64 Mi fp32 N(0, 1e-3)  (the benchmark's workload)
+  rhd       RHD AllReduce, P in {8, 5}, bf16 N(0,1) sum and int32 U[-2^20, 2^20] max,
+            1 KiB .. 64 KiB per rank
+  sweep     ring and RHD AllReduce / reduce-scatter / all-gather, P=16, fp16 N(0, 0.01),
+            4 KiB .. 1 GiB per rank in powers of 4
+  pipe      pipeline AllReduce, 4 servers x 8 ranks, 32 MiB loops, bf16 N(0, 1e-2), 512 MiB per rank
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import allreduce_reduction_amd as hc
+import oracle
+import refops
+import synth
+from gpu_util import TORCH, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def upload_recipe(recipe, P, L):
+    """Generate each rank on the host (one at a time) and upload it."""
+    r = synth.RECIPES[recipe]
+    bufs = []
+    for k in range(P):
+        x = synth.generate(r["dtype"], L, r["dist"], r["p0"], r["p1"], stream=r["stream"], rank=k)
+        bufs.append(to_dev(x, r["dtype"]))
+        del x
+    return bufs
+
+
+def host_window(recipe, P, w0, w1):
+    return synth.rank_inputs(recipe, P, w1, first=w0, n=w1 - w0)
+
+
+def windows(boundaries, L, n_random=16, width=64, rand_width=65536, seed=0):
+    rng = np.random.default_rng(seed)
+    spans = [(max(0, b - width), min(L, b + width)) for b in boundaries]
+    for _ in range(n_random):
+        a = int(rng.integers(0, max(1, L - rand_width)))
+        spans.append((a, min(L, a + rand_width)))
+    spans = sorted(s for s in spans if s[1] > s[0])
+    merged = []
+    for a, b in spans:
+        if merged and a <= merged[-1][1]:
+            merged[-1] = (merged[-1][0], max(merged[-1][1], b))
+        else:
+            merged.append((a, b))
+    return merged
+
+
+def ranks_identical(bufs, dtype):
+    iv = {1: torch.int8, 2: torch.int16, 4: torch.int32}[torch.tensor([], dtype=TORCH[dtype]).element_size()]
+    b0 = bufs[0].view(iv)
+    return all(torch.equal(b.view(iv), b0) for b in bufs[1:])
+
+
+def check_windows(coll, algo, recipe, P, L, dev, spans, *, S=1, M=1, loop_bytes=0, op="sum",
+                  owner_only=False):
+    """Oracle replay of each window vs the GPU result; returns (num, den) of the norm-wise error."""
+    dtype = synth.RECIPES[recipe]["dtype"]
+    num = den = 0.0
+    for w0, w1 in spans:
+        xs = host_window(recipe, P, w0, w1)
+        want = [x.copy() for x in xs]
+        oracle.run(coll, algo, want, dtype, op, L=L, w0=w0, S=S, M=M, loop_bytes=loop_bytes)
+        ranks = range(P)
+        for r in ranks:
+            got = to_host(dev[r][w0:w1], dtype)
+            if owner_only:
+                # reduce-scatter: only the owned segment is specified
+                b, e = refops.seg_bounds(L, P, r)
+                lo, hi = max(b, w0), min(e, w1)
+                if lo < hi:
+                    refops.assert_same(dtype, got[lo - w0:hi - w0], want[r][lo - w0:hi - w0],
+                                       f"{algo} {coll} window [{w0},{w1}) rank {r}")
+            else:
+                refops.assert_same(dtype, got, want[r], f"{algo} {coll} window [{w0},{w1}) rank {r}")
+        if coll == "allreduce" and op == "sum" and dtype in refops.FLOATS:
+            y = to_host(dev[0][w0:w1], dtype)
+            ok = refops.sum_bound_ok(dtype, y, xs)
+            assert ok.all(), f"per-element bound fails in [{w0},{w1})"
+            exact = np.stack([refops.to_f64(dtype, x) for x in xs]).sum(axis=0)
+            num += float(np.sum((refops.to_f64(dtype, y) - exact) ** 2))
+            den += float(np.sum(exact ** 2))
+    return num, den
+
+
+def test_ring_p4_fp32_integers():
+    P, L = 4, 4096
+    xs = synth.rank_inputs("ring_p4_fp32_int", P, L)
+    dev = [to_dev(x, "fp32") for x in xs]
+    with hc.Comm(P, "ring") as c:
+        assert c.plan_info("allreduce", L, "fp32")["nsteps"] == 6
+        c.allreduce(dev, "fp32", "sum")
+        torch.cuda.synchronize()
+    want = [x.copy() for x in xs]
+    oracle.run("allreduce", "ring", want, "fp32", "sum")
+    exact = np.stack([x.astype(np.int64) for x in xs]).sum(axis=0).astype(np.float32)
+    for r in range(P):
+        got = to_host(dev[r], "fp32")
+        assert np.array_equal(got.view(np.uint32), want[r].view(np.uint32))
+        assert np.array_equal(got, exact)
+
+
+def test_ring_p8_fp32_64Mi():
+    P, L = 8, 64 << 20
+    say("case ring_p8 fp32 64Mi: upload")
+    dev = upload_recipe("ring_p8_fp32_grad", P, L)
+    with hc.Comm(P, "ring") as c:
+        say("case ring_p8 fp32 64Mi: allreduce")
+        c.allreduce(dev, "fp32", "sum")
+        torch.cuda.synchronize()
+    assert ranks_identical(dev, "fp32")
+    q = L // P
+    spans = windows([k * q for k in range(P + 1)], L, seed=2)
+    say(f"case ring_p8: {len(spans)} windows")
+    num, den = check_windows("allreduce", "ring", "ring_p8_fp32_grad", P, L, dev, spans)
+    assert np.sqrt(num / den) <= 1e-5
+    del dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("P", [8, 5])
+def test_rhd_small_messages(P):
+    for kib in (1, 2, 4, 8, 16, 32, 64):
+        for recipe, op in (("rhd_bf16_normal", "sum"), ("rhd_int32_uniform", "max")):
+            dtype = synth.RECIPES[recipe]["dtype"]
+            L = kib * 1024 // np.dtype(refops.STORAGE[dtype]).itemsize
+            say(f"case rhd P={P} {kib} KiB {dtype} {op}")
+            xs = synth.rank_inputs(recipe, P, L)
+            dev = [to_dev(x, dtype) for x in xs]
+            with hc.Comm(P, "rhd") as c:
+                assert c.plan_info("allreduce", L, dtype)["nsteps"] == 6
+                c.allreduce(dev, dtype, op)
+                torch.cuda.synchronize()
+            want = [x.copy() for x in xs]
+            oracle.run("allreduce", "rhd", want, dtype, op)
+            for r in range(P):
+                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"rank {r}")
+            if op == "max":
+                exact = np.stack(xs).max(axis=0)
+                assert np.array_equal(to_host(dev[0], dtype), exact)
+            else:
+                ok = refops.sum_bound_ok(dtype, want[0], xs)
+                assert ok.all()
+                exact = np.stack([refops.to_f64(dtype, x) for x in xs]).sum(axis=0)
+                rel = np.linalg.norm(refops.to_f64(dtype, want[0]) - exact) / np.linalg.norm(exact)
+                assert rel <= 2.0 ** -7 * (P - 1)
+
+
+SWEEP = [4096 * 4 ** i for i in range(10)]  # bytes per rank: 4 KiB .. 1 GiB
+
+
+@pytest.mark.parametrize("nbytes", SWEEP)
+def test_sweep_p16_fp16(nbytes):
+    P, dtype, recipe = 16, "fp16", "sweep_p16_fp16"
+    L = nbytes // 2
+    say(f"case sweep P=16 fp16 {nbytes} B/rank: upload")
+    pristine = upload_recipe(recipe, P, L)
+    dev = [torch.empty_like(t) for t in pristine]
+    full = nbytes <= (4 << 20)
+    if not full:
+        bounds = sorted(set([k * (-(-L // P)) for k in range(P + 1)]))
+        spans = windows(bounds, L, seed=nbytes % 1000)
+    for algo in ("ring", "rhd"):
+        with hc.Comm(P, algo) as c:
+            for coll in ("allreduce", "reduce_scatter", "all_gather"):
+                for d, p in zip(dev, pristine):
+                    d.copy_(p)
+                say(f"case sweep {algo} {coll} {nbytes} B/rank")
+                getattr(c, coll)(dev, dtype, "sum")
+                torch.cuda.synchronize()
+                if coll != "reduce_scatter":
+                    assert ranks_identical(dev, dtype)
+                if full:
+                    xs = synth.rank_inputs(recipe, P, L)
+                    want = [x.copy() for x in xs]
+                    oracle.run(coll, algo, want, dtype, "sum")
+                    for r in range(P):
+                        got = to_host(dev[r], dtype)
+                        if coll == "reduce_scatter":
+                            b, e = refops.seg_bounds(L, P, r)
+                            refops.assert_same(dtype, got[b:e], want[r][b:e], f"{algo} rs rank {r}")
+                        else:
+                            refops.assert_same(dtype, got, want[r], f"{algo} {coll} rank {r}")
+                    if coll == "allreduce":
+                        exact = np.stack([refops.to_f64(dtype, x) for x in xs]).sum(axis=0)
+                        rel = np.linalg.norm(refops.to_f64(dtype, want[0]) - exact) / np.linalg.norm(exact)
+                        assert rel <= 2.0 ** -7 * (P - 1)
+                        assert refops.sum_bound_ok(dtype, want[0], xs).all()
+                else:
+                    num, den = check_windows(coll, algo, recipe, P, L, dev, spans,
+                                             owner_only=(coll == "reduce_scatter"))
+                    if coll == "allreduce":
+                        assert np.sqrt(num / den) <= 2.0 ** -7 * (P - 1)
+    del dev, pristine
+    torch.cuda.empty_cache()
+
+
+def test_pipeline_4x8_bf16_512MiB():
+    S, M = 4, 8
+    P, dtype, recipe = S * M, "bf16", "pipe_4x8_bf16"
+    L = 256 << 20  # 512 MiB per rank
+    loop_bytes = 32 << 20
+    say("case pipeline 4x8 bf16 512MiB: upload")
+    dev = upload_recipe(recipe, P, L)
+    with hc.Comm(P, "pipeline", S, M, loop_bytes) as c:
+        assert c.plan_info("allreduce", L, dtype)["nsteps"] == 2 * S
+        say("case pipeline 4x8: allreduce")
+        c.allreduce(dev, dtype, "sum")
+        torch.cuda.synchronize()
+    assert ranks_identical(dev, dtype)
+    C = loop_bytes // 2
+    bounds = []
+    for lb in (0, C * 7, L - C):
+        q = -(-C // P)
+        bounds += [lb + k * q for k in range(P + 1)]
+    spans = windows(sorted(set(bounds)), L, n_random=12, rand_width=4096, seed=5)
+    say(f"case pipeline 4x8: {len(spans)} windows")
+    num, den = check_windows("allreduce", "pipeline", recipe, P, L, dev, spans, S=S, M=M,
+                             loop_bytes=loop_bytes)
+    assert np.sqrt(num / den) <= 2.0 ** -7 * (P - 1)
+    del dev
+    torch.cuda.empty_cache()
