@@ -14,6 +14,9 @@ Reported (one JSON line):
   cpu_baseline  the CPU oracle replaying the same AllReduce (single thread)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --suite    (one JSON line per other workload: RHD small
+                                   messages, the P=16 ring / RHD sweep, the 4x8
+                                   pipeline; not the headline line)
 """
 from __future__ import annotations
 
@@ -57,7 +60,112 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=4, help="oracle AllReduces timed for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--algo", default="ring", choices=["ring", "rhd"])
+    ap.add_argument("--suite", action="store_true", help="time the other workloads instead")
+    ap.add_argument("--max-sweep-bytes", type=int, default=1 << 30)
     return ap.parse_args()
+
+
+def time_calls(fn, reps, warmup):
+    """Median GPU time of one call (s), from HIP events on the current stream
+    around `reps` back-to-back calls, repeated 3 times."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        out.append(a.elapsed_time(b) / 1e3 / reps)
+    out.sort()
+    return out[1]
+
+
+def suite(a):
+    """Timing of the other workloads: RHD small messages (P = 8 and 5), the P=16
+    ring / RHD sweep (AllReduce, reduce-scatter, all-gather) and the 4 x 8
+    pipeline.  Inputs are restored from a pristine copy before every timed
+    group, so values stay finite; timing covers only the collective calls."""
+    import torch
+
+    import allreduce_reduction_amd as hc
+    import synth
+
+    def upload(recipe, P, L):
+        r = synth.RECIPES[recipe]
+        out = []
+        for k in range(P):
+            x = synth.generate(r["dtype"], L, r["dist"], r["p0"], r["p1"], stream=r["stream"], rank=k)
+            t = torch.from_numpy(x.view("int16") if r["dtype"] == "bf16" else x).cuda()
+            out.append(t.view(torch.bfloat16) if r["dtype"] == "bf16" else t)
+        return out
+
+    def emit(**kw):
+        print(json.dumps(kw), flush=True)
+
+    # RHD small messages: launch-bound; report us per AllReduce and per step
+    for P in (8, 5):
+        for recipe, op in (("rhd_bf16_normal", "sum"), ("rhd_int32_uniform", "max")):
+            dtype = synth.RECIPES[recipe]["dtype"]
+            e = 2 if dtype == "bf16" else 4
+            for kib in (1, 2, 4, 8, 16, 32, 64):
+                L = kib * 1024 // e
+                bufs = upload(recipe, P, L)
+                pristine = [b.clone() for b in bufs]
+                with hc.Comm(P, "rhd") as c:
+                    n = c.plan_info("allreduce", L, dtype)["nsteps"]
+                    for b, q in zip(bufs, pristine):
+                        b.copy_(q)
+                    t = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
+                emit(workload="rhd_small", algo="rhd", coll="allreduce", P=P, dtype=dtype, op=op,
+                     bytes_per_rank=L * e, us=round(t * 1e6, 2), steps=n, us_per_step=round(t * 1e6 / n, 2),
+                     busbw_GBps=round(L * e / t * 2 * (P - 1) / P / 1e9, 3))
+
+    # P=16 fp16 sweep, ring vs RHD, AR / RS / AG
+    P = 16
+    nbytes = 4096
+    while nbytes <= a.max_sweep_bytes:
+        L = nbytes // 2
+        bufs = upload("sweep_p16_fp16", P, L)
+        pristine = [b.clone() for b in bufs]
+        for algo in ("ring", "rhd"):
+            with hc.Comm(P, algo) as c:
+                for coll in ("allreduce", "reduce_scatter", "all_gather"):
+                    for b, q in zip(bufs, pristine):
+                        b.copy_(q)
+                    info = c.plan_info(coll, L, "fp16")
+                    reps = max(3, min(200, int(2e8 // max(info["hbm_bytes"], 1))))
+                    t = time_calls(lambda: getattr(c, coll)(bufs, "fp16", "sum"), reps, 2)
+                    factor = 2 * (P - 1) / P if coll == "allreduce" else (P - 1) / P
+                    emit(workload="sweep_p16_fp16", algo=algo, coll=coll, P=P, bytes_per_rank=nbytes,
+                         us=round(t * 1e6, 2), steps=info["nsteps"],
+                         busbw_GBps=round(nbytes / t * factor / 1e9, 3),
+                         pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2))
+        del bufs, pristine
+        torch.cuda.empty_cache()
+        nbytes *= 4
+
+    # pipeline 4 x 8, bf16, 512 MiB per rank, 32 MiB loops
+    S, M = 4, 8
+    P, L = S * M, 256 << 20
+    bufs = upload("pipe_4x8_bf16", P, L)
+    with hc.Comm(P, "pipeline", S, M, 32 << 20) as c:
+        info = c.plan_info("allreduce", L, "bf16")
+        t = time_calls(lambda: c.allreduce(bufs, "bf16", "sum"), 3, 1)
+        steps = []
+        for s in range(info["nsteps"]):
+            si = c.step_info("allreduce", L, "bf16", s)
+            ts = time_calls(lambda: c.run_steps("allreduce", bufs, s, s + 1, "bf16", "sum"), 3, 1)
+            steps.append(dict(step=s, us=round(ts * 1e6, 1), GBps=round(si["hbm_bytes"] / ts / 1e9, 1)))
+    emit(workload="pipe_4x8_bf16", algo="pipeline", coll="allreduce", P=P, S=S, M=M,
+         bytes_per_rank=L * 2, us=round(t * 1e6, 1), steps=info["nsteps"],
+         busbw_GBps=round(L * 2 / t * 2 * (P - 1) / P / 1e9, 3),
+         pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2), per_step=steps)
 
 
 def main():
@@ -70,6 +178,10 @@ def main():
         # values grow by P per AllReduce; 35 passes of x8 stay finite in fp32
         print("--steps above 35 would overflow the fp32 inputs; use at most 35", file=sys.stderr)
         sys.exit(2)
+
+    if a.suite:
+        suite(a)
+        return
 
     import numpy as np
     import torch
