@@ -25,7 +25,8 @@ MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
 # every symbol include/hbmcoll.h declares
 EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
            "hbmc_all_gather", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
-           "hbmc_plan_items", "hbmc_status_string")
+           "hbmc_plan_items", "hbmc_status_string", "hbmc_graph_create", "hbmc_graph_add",
+           "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy")
 
 
 class HbmcError(RuntimeError):
@@ -72,6 +73,16 @@ def load_library():
         L.hbmc_plan_step_info.argtypes = [vp, ci, sz, ci, ci, ctypes.POINTER(ci), u64p]
         L.hbmc_plan_items.restype = ci
         L.hbmc_plan_items.argtypes = [vp, ci, sz, ci, ctypes.POINTER(Item), sz, ctypes.POINTER(sz)]
+        L.hbmc_graph_create.restype = ci
+        L.hbmc_graph_create.argtypes = [ctypes.POINTER(vp)]
+        L.hbmc_graph_add.restype = ci
+        L.hbmc_graph_add.argtypes = [vp, vp, ci, ctypes.POINTER(vp), sz, ci, ci]
+        L.hbmc_graph_build.restype = ci
+        L.hbmc_graph_build.argtypes = [vp]
+        L.hbmc_graph_launch.restype = ci
+        L.hbmc_graph_launch.argtypes = [vp, vp]
+        L.hbmc_graph_destroy.restype = ci
+        L.hbmc_graph_destroy.argtypes = [vp]
         L.hbmc_status_string.restype = ctypes.c_char_p
         L.hbmc_status_string.argtypes = [ci]
         _lib = L
@@ -193,3 +204,38 @@ class Comm:
             out.append(dict(step=it.step, mode=MODE[it.mode], begin=it.begin, count=it.count,
                             src=ranks[:it.nsrc], dst=ranks[it.nsrc:]))
         return out
+
+
+class Graph:
+    """Graph mode: add collectives, build once, launch many times."""
+
+    def __init__(self):
+        self._h = ctypes.c_void_p()
+        self._keep = []  # buffer-pointer arrays stay alive with the graph
+        _check(load_library().hbmc_graph_create(ctypes.byref(self._h)), "hbmc_graph_create")
+
+    def add(self, comm: Comm, coll: str, bufs, dtype=None, op="sum", *, count=None):
+        arr, n, dt = _ptrs(bufs)
+        dtype = dtype or dt
+        count = n if count is None else count
+        self._keep.append((arr, list(bufs)))
+        _check(load_library().hbmc_graph_add(self._h, comm._h, COLL[coll], arr, count, DTYPE[dtype], OP[op]),
+               "hbmc_graph_add")
+
+    def build(self):
+        _check(load_library().hbmc_graph_build(self._h), "hbmc_graph_build")
+
+    def launch(self, stream=None):
+        _check(load_library().hbmc_graph_launch(self._h, _stream(stream)), "hbmc_graph_launch")
+
+    def close(self):
+        if self._h:
+            _check(load_library().hbmc_graph_destroy(self._h), "hbmc_graph_destroy")
+            self._h = ctypes.c_void_p()
+            self._keep = []
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -1,0 +1,169 @@
+// Communicator internals: schedule cache, device item tables, step launches.
+#include "comm.hpp"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstring>
+#include <new>
+
+namespace hbmc {
+
+uint32_t elem_bytes(int dtype) {
+  switch (dtype) {
+    case HBMC_FP32: return 4;
+    case HBMC_FP16: return 2;
+    case HBMC_BF16: return 2;
+    case HBMC_INT32: return 4;
+    case HBMC_INT8: return 1;
+    default: return 0;
+  }
+}
+
+namespace {
+
+hbmc_status_t from_build(BuildStatus b) {
+  switch (b) {
+    case kBuilt: return HBMC_OK;
+    case kUnsupported: return HBMC_ERR_UNSUPPORTED;
+    default: return HBMC_ERR_INVALID_ARG;
+  }
+}
+
+}  // namespace
+
+bool valid_coll(int c) { return c >= HBMC_COLL_ALLREDUCE && c <= HBMC_COLL_ALL_GATHER; }
+bool valid_op(int op) { return op >= HBMC_SUM && op <= HBMC_MIN; }
+
+hbmc_status_t get_plan(hbmc_comm* c, int coll, size_t count, int dtype, Plan** out) {
+  const uint32_t e = elem_bytes(dtype);
+  if (!c || e == 0 || !valid_coll(coll)) return HBMC_ERR_INVALID_ARG;
+  if (count > SIZE_MAX / e) return HBMC_ERR_INVALID_ARG;
+  auto key = std::make_tuple(coll, static_cast<uint64_t>(count), dtype);
+  auto it = c->plans.find(key);
+  if (it != c->plans.end()) {
+    *out = it->second.get();
+    return HBMC_OK;
+  }
+  std::unique_ptr<Plan> p(new (std::nothrow) Plan);
+  if (!p) return HBMC_ERR_NOMEM;
+  hbmc_status_t st = from_build(build_schedule(c->topo, static_cast<Coll>(coll), count, e, &p->sched));
+  if (st != HBMC_OK) return st;
+  size_t off = 0;
+  for (const Step& s : p->sched.steps) {
+    p->first_item.push_back(off);
+    off += s.items.size();
+  }
+  *out = p.get();
+  c->plans.emplace(key, std::move(p));
+  return HBMC_OK;
+}
+
+hbmc_status_t upload(Plan* p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HBMC_ERR_HIP;
+  if (p->dev) return p->device == dev ? HBMC_OK : HBMC_ERR_INVALID_ARG;
+  size_t n = 0;
+  for (const Step& s : p->sched.steps) n += s.items.size();
+  if (n == 0) {
+    p->device = dev;
+    return HBMC_OK;
+  }
+  std::vector<DevItem> host(n);
+  size_t k = 0;
+  for (const Step& s : p->sched.steps)
+    for (const Item& it : s.items) {
+      DevItem& d = host[k++];
+      std::memset(&d, 0, sizeof(d));
+      d.begin = it.begin;
+      d.count = it.count;
+      d.nsrc = static_cast<uint32_t>(it.nsrc);
+      d.ndst = static_cast<uint32_t>(it.ndst);
+      std::memcpy(d.rank, it.rank, sizeof(d.rank));
+    }
+  void* mem = nullptr;
+  if (hipMalloc(&mem, n * sizeof(DevItem)) != hipSuccess) return HBMC_ERR_NOMEM;
+  if (hipMemcpy(mem, host.data(), n * sizeof(DevItem), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(mem);
+    return HBMC_ERR_HIP;
+  }
+  p->dev = static_cast<DevItem*>(mem);
+  p->device = dev;
+  return HBMC_OK;
+}
+
+hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e) {
+  if (!bufs) return HBMC_ERR_INVALID_ARG;
+  const uint64_t bytes = uint64_t(count) * e;
+  for (int r = 0; r < P; ++r) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(bufs[r]);
+    if (!a || a % e) return HBMC_ERR_INVALID_ARG;
+    if (a + bytes < a) return HBMC_ERR_INVALID_ARG;
+    for (int q = 0; q < r; ++q) {
+      const uintptr_t b = reinterpret_cast<uintptr_t>(bufs[q]);
+      if (a < b + bytes && b < a + bytes) return HBMC_ERR_INVALID_ARG;  // aliased / overlapping
+    }
+  }
+  return HBMC_OK;
+}
+
+hbmc_status_t prepare(hbmc_comm* c, int coll, void* const bufs[], size_t count, int dtype, int op,
+                      int first, int last, bool whole, std::vector<StepLaunch>* steps, RankPtrs* ptrs) {
+  steps->clear();
+  if (!c || !valid_op(op) || !valid_coll(coll) || elem_bytes(dtype) == 0) return HBMC_ERR_INVALID_ARG;
+  const uint32_t e = elem_bytes(dtype);
+  if (count > SIZE_MAX / e) return HBMC_ERR_INVALID_ARG;
+  Plan* p = nullptr;
+  hbmc_status_t st = get_plan(c, coll, count, dtype, &p);
+  if (st != HBMC_OK) return st;
+  const int nsteps = static_cast<int>(p->sched.steps.size());
+  if (whole) {
+    first = 0;
+    last = nsteps;
+  } else if (first < 0 || last > nsteps || first >= last) {
+    return HBMC_ERR_INVALID_ARG;
+  }
+  if (count == 0 || c->topo.P == 1) return HBMC_OK;
+  st = check_bufs(c->topo.P, bufs, count, e);
+  if (st != HBMC_OK) return st;
+  st = upload(p);
+  if (st != HBMC_OK) return st;
+
+  std::memset(ptrs, 0, sizeof(*ptrs));
+  const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0]) & 15u);
+  bool aligned = true;
+  for (int r = 0; r < c->topo.P; ++r) {
+    ptrs->p[r] = static_cast<unsigned char*>(bufs[r]);
+    aligned = aligned && (reinterpret_cast<uintptr_t>(bufs[r]) & 15u) == phase;
+  }
+  for (int s = first; s < last; ++s) {
+    const Step& step = p->sched.steps[s];
+    if (step.items.empty()) continue;
+    StepLaunch L;
+    L.dtype = dtype;
+    L.op = op;
+    L.mode = step.mode;
+    L.nsrc = step.nsrc;
+    L.ndst = step.ndst;
+    L.items = p->dev + p->first_item[s];
+    L.nitems = static_cast<int>(step.items.size());
+    L.max_count = step.max_count;
+    L.aligned = aligned;
+    L.phase = phase;
+    L.xcd_split = c->xcd_split;
+    steps->push_back(L);
+  }
+  return HBMC_OK;
+}
+
+hbmc_status_t run(hbmc_comm* c, int coll, void* const bufs[], size_t count, int dtype, int op,
+                  int first, int last, bool whole, void* stream) {
+  std::vector<StepLaunch> steps;
+  RankPtrs ptrs;
+  hbmc_status_t st = prepare(c, coll, bufs, count, dtype, op, first, last, whole, &steps, &ptrs);
+  if (st != HBMC_OK) return st;
+  for (const StepLaunch& L : steps)
+    if (launch_step(L, ptrs, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
+  return HBMC_OK;
+}
+
+}  // namespace hbmc

@@ -34,6 +34,27 @@ struct StepLaunch {
   bool xcd_split;         // give each XCD one contiguous range of tiles
 };
 
+// One kernel launch of a step: kernel, shape and argument values, usable with
+// hipLaunchKernel or as a kernel graph node.
+struct KernelDesc {
+  const void* func = nullptr;
+  dim3 grid, block;
+  RankPtrs ptrs;
+  const DevItem* items = nullptr;
+  uint32_t phase = 0, xcd = 0;
+  int nargs = 0;   // 2 for the element-wise kernel, 4 for the vector kernel
+  void* argv[4];   // filled by bind(); valid while this object lives
+  void bind() {
+    argv[0] = &ptrs;
+    argv[1] = &items;
+    argv[2] = &phase;
+    argv[3] = &xcd;
+  }
+};
+
+// Choose the kernel and launch shape of one step.
+hipError_t describe_step(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* out);
+
 // Enqueue one step on `stream`; returns the launch's error state.
 hipError_t launch_step(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream);
 

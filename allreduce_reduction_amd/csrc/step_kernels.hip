@@ -308,81 +308,98 @@ step_elem(RankPtrs ptrs, const DevItem* __restrict__ items) {
 
 // ------------------------------------------------------------- dispatch
 
+template <typename F>
+const void* fn(F* f) {
+  return reinterpret_cast<const void*>(f);
+}
+
 template <int DT, int OP>
-hipError_t launch_typed(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream) {
+void describe_typed(const StepLaunch& s, KernelDesc* k) {
   constexpr uint32_t E = Width<DT>::bytes;
   if (!s.aligned) {
-    const dim3 block(kElemThreads);
     uint64_t gx = (s.max_count + kElemThreads - 1) / kElemThreads;
     if (gx > 2048) gx = 2048;
     if (gx < 1) gx = 1;
-    const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
+    k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
+    k->block = dim3(kElemThreads);
+    k->nargs = 2;
     switch (s.mode) {
-      case kCopy: hipLaunchKernelGGL((step_elem<DT, OP, kCopy>), grid, block, 0, stream, ptrs, s.items); break;
-      case kFold: hipLaunchKernelGGL((step_elem<DT, OP, kFold>), grid, block, 0, stream, ptrs, s.items); break;
-      default: hipLaunchKernelGGL((step_elem<DT, OP, kRecvFold>), grid, block, 0, stream, ptrs, s.items); break;
+      case kCopy: k->func = fn(step_elem<DT, OP, kCopy>); break;
+      case kFold: k->func = fn(step_elem<DT, OP, kFold>); break;
+      default: k->func = fn(step_elem<DT, OP, kRecvFold>); break;
     }
-    return hipGetLastError();
+    return;
   }
-  const dim3 block(kThreads);
   const uint64_t vecs = s.max_count * E / 16 + 1;
   const uint64_t gx = (vecs + kTileVecs - 1) / kTileVecs;
-  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
-  const uint32_t xcd = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? 1u : 0u;
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, ptrs, s.items, s.phase, xcd);
-  };
+  k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
+  k->block = dim3(kThreads);
+  k->nargs = 4;
+  k->xcd = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? 1u : 0u;
   // item shapes of the schedules get compile-time source counts: ring / RHD
   // (2 sources) and the pipeline with 1, 2, 4 or 8 ranks per server; any
   // other shape takes the runtime-count kernel
   if (s.mode == kRecvFold) {
     switch (s.nsrc) {
-      case 2: go(step_vec<DT, OP, kRecvFold, 2, 1>); break;
-      case 3: go(step_vec<DT, OP, kRecvFold, 3, 1>); break;
-      case 5: go(step_vec<DT, OP, kRecvFold, 5, 1>); break;
-      case 9: go(step_vec<DT, OP, kRecvFold, 9, 1>); break;
-      default: go(step_vec<DT, OP, kRecvFold, 0, 1>); break;
+      case 2: k->func = fn(step_vec<DT, OP, kRecvFold, 2, 1>); break;
+      case 3: k->func = fn(step_vec<DT, OP, kRecvFold, 3, 1>); break;
+      case 5: k->func = fn(step_vec<DT, OP, kRecvFold, 5, 1>); break;
+      case 9: k->func = fn(step_vec<DT, OP, kRecvFold, 9, 1>); break;
+      default: k->func = fn(step_vec<DT, OP, kRecvFold, 0, 1>); break;
     }
   } else if (s.mode == kFold) {
     switch (s.nsrc) {
-      case 2: go(step_vec<DT, OP, kFold, 2, 1>); break;
-      case 4: go(step_vec<DT, OP, kFold, 4, 1>); break;
-      case 8: go(step_vec<DT, OP, kFold, 8, 1>); break;
-      default: go(step_vec<DT, OP, kFold, 0, 1>); break;
+      case 2: k->func = fn(step_vec<DT, OP, kFold, 2, 1>); break;
+      case 4: k->func = fn(step_vec<DT, OP, kFold, 4, 1>); break;
+      case 8: k->func = fn(step_vec<DT, OP, kFold, 8, 1>); break;
+      default: k->func = fn(step_vec<DT, OP, kFold, 0, 1>); break;
     }
   } else {
     // several destinations: the runtime-count store loop measured faster
     // than an unrolled one (1 read, 8 writes: 5.8 vs 5.4 TB/s)
     if (s.ndst == 1)
-      go(step_vec<DT, kSum, kCopy, 1, 1>);
+      k->func = fn(step_vec<DT, kSum, kCopy, 1, 1>);
     else
-      go(step_vec<DT, kSum, kCopy, 1, 0>);
+      k->func = fn(step_vec<DT, kSum, kCopy, 1, 0>);
   }
-  return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_op(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream) {
+void describe_op(const StepLaunch& s, KernelDesc* k) {
   switch (s.op) {
-    case kSum: return launch_typed<DT, kSum>(s, ptrs, stream);
-    case kProd: return launch_typed<DT, kProd>(s, ptrs, stream);
-    case kMax: return launch_typed<DT, kMax>(s, ptrs, stream);
-    default: return launch_typed<DT, kMin>(s, ptrs, stream);
+    case kSum: describe_typed<DT, kSum>(s, k); break;
+    case kProd: describe_typed<DT, kProd>(s, k); break;
+    case kMax: describe_typed<DT, kMax>(s, k); break;
+    default: describe_typed<DT, kMin>(s, k); break;
   }
 }
 
 }  // namespace
 
+hipError_t describe_step(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
+  if (s.nitems <= 0) return hipErrorInvalidValue;
+  if (s.ndst > 1 && s.mode != kCopy) return hipErrorInvalidValue;  // no such schedule step
+  k->ptrs = ptrs;
+  k->items = s.items;
+  k->phase = s.phase;
+  switch (s.dtype) {
+    case kF32: describe_op<kF32>(s, k); break;
+    case kF16: describe_op<kF16>(s, k); break;
+    case kBF16: describe_op<kBF16>(s, k); break;
+    case kI32: describe_op<kI32>(s, k); break;
+    default: describe_op<kI8>(s, k); break;
+  }
+  k->bind();
+  return hipSuccess;
+}
+
 hipError_t launch_step(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t stream) {
   if (s.nitems <= 0) return hipSuccess;
-  if (s.ndst > 1 && s.mode != kCopy) return hipErrorInvalidValue;  // no such schedule step
-  switch (s.dtype) {
-    case kF32: return launch_op<kF32>(s, ptrs, stream);
-    case kF16: return launch_op<kF16>(s, ptrs, stream);
-    case kBF16: return launch_op<kBF16>(s, ptrs, stream);
-    case kI32: return launch_op<kI32>(s, ptrs, stream);
-    default: return launch_op<kI8>(s, ptrs, stream);
-  }
+  KernelDesc k;
+  const hipError_t e = describe_step(s, ptrs, &k);
+  if (e != hipSuccess) return e;
+  const hipError_t l = hipLaunchKernel(k.func, k.grid, k.block, k.argv, 0, stream);
+  return l != hipSuccess ? l : hipGetLastError();
 }
 
 }  // namespace hbmc

@@ -122,9 +122,23 @@ def suite(a):
                     for b, q in zip(bufs, pristine):
                         b.copy_(q)
                     t = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
+                    # graph mode: the same AllReduce as one graph launch, and a
+                    # graph of 10 AllReduces on these buffers (one launch)
+                    with hc.Graph() as g:
+                        g.add(c, "allreduce", bufs, dtype, op)
+                        g.build()
+                        tg = time_calls(lambda: g.launch(), 200, 20)
+                    with hc.Graph() as g10:
+                        for _ in range(10):
+                            g10.add(c, "allreduce", bufs, dtype, op)
+                        g10.build()
+                        tg10 = time_calls(lambda: g10.launch(), 50, 5) / 10
                 emit(workload="rhd_small", algo="rhd", coll="allreduce", P=P, dtype=dtype, op=op,
                      bytes_per_rank=L * e, us=round(t * 1e6, 2), steps=n, us_per_step=round(t * 1e6 / n, 2),
-                     busbw_GBps=round(L * e / t * 2 * (P - 1) / P / 1e9, 3))
+                     graph_us=round(tg * 1e6, 2), graph_us_per_step=round(tg * 1e6 / n, 2),
+                     graph10_us_per_allreduce=round(tg10 * 1e6, 2),
+                     busbw_GBps=round(L * e / t * 2 * (P - 1) / P / 1e9, 3),
+                     graph_busbw_GBps=round(L * e / tg * 2 * (P - 1) / P / 1e9, 3))
 
     # P=16 fp16 sweep, ring vs RHD, AR / RS / AG
     P = 16

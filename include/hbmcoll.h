@@ -151,6 +151,32 @@ typedef struct {
 hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, hbmc_dtype_t dtype,
                               hbmc_item_t* out, size_t cap, size_t* n_items);
 
+/*
+ * Graph mode ([RING-RHD] section "Ascend950的AIVAICPU通信引擎与图模式": a
+ * sequence of collectives is composed into a graph whose data dependencies
+ * are analysed at build time, then scheduled and launched as one unit).
+ *
+ * hbmc_graph_add appends a collective with its buffers fixed (same argument
+ * rules as the direct calls; the schedule is built and checked here).  At
+ * hbmc_graph_build every collective becomes a chain of kernel nodes, one per
+ * schedule step; a collective starts after every earlier one whose rank
+ * buffers overlap its own, and collectives on disjoint buffers may run
+ * concurrently.  Build uploads the schedules' device tables and instantiates
+ * the graph (it must not be called while the calling thread captures a
+ * stream); no node can be added after it.
+ * hbmc_graph_launch enqueues the whole graph on `stream` (asynchronous,
+ * stream-ordered).  The communicators and buffers must outlive the graph.
+ * Errors: HBMC_ERR_INVALID_ARG for adding after build, launching before
+ * build, or a bad argument; the direct calls' codes otherwise.
+ */
+typedef struct hbmc_graph* hbmc_graph_t;
+hbmc_status_t hbmc_graph_create(hbmc_graph_t* out);
+hbmc_status_t hbmc_graph_add(hbmc_graph_t graph, hbmc_comm_t comm, hbmc_coll_t coll, void* const bufs[],
+                             size_t count, hbmc_dtype_t dtype, hbmc_op_t op);
+hbmc_status_t hbmc_graph_build(hbmc_graph_t graph);
+hbmc_status_t hbmc_graph_launch(hbmc_graph_t graph, void* stream);
+hbmc_status_t hbmc_graph_destroy(hbmc_graph_t graph);
+
 /* Static text for a status code. */
 const char* hbmc_status_string(hbmc_status_t status);
 

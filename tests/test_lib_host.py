@@ -207,3 +207,24 @@ def test_algorithm_from_environment(monkeypatch):
         assert c.plan_info("allreduce", 64, "fp32")["nsteps"] == 4
     monkeypatch.setenv("HBMC_ALGO", "tree")
     assert lib.hbmc_comm_create(4, 3, 0, 0, 0, ctypes.byref(h)) == 1
+
+
+def test_graph_validation_without_device():
+    lib = hc.load_library()
+    assert lib.hbmc_graph_create(None) == 1
+    assert lib.hbmc_graph_launch(None, None) == 1
+    assert lib.hbmc_graph_build(None) == 1
+    assert lib.hbmc_graph_destroy(None) == 1
+    g = ctypes.c_void_p()
+    assert lib.hbmc_graph_create(ctypes.byref(g)) == 0
+    with hc.Comm(4, "ring") as c, hc.Comm(5, "rhd") as r5:
+        arr = (ctypes.c_void_p * 4)(0x10000, 0x20000, 0x30000, 0x40000)
+        alias = (ctypes.c_void_p * 4)(0x10000, 0x10000, 0x30000, 0x40000)
+        assert lib.hbmc_graph_add(g, c._h, 0, alias, 16, 0, 0) == 1          # aliased buffers
+        assert lib.hbmc_graph_add(g, c._h, 0, arr, 16, 0, 7) == 1            # bad op
+        assert lib.hbmc_graph_add(g, None, 0, arr, 16, 0, 0) == 1            # no communicator
+        five = (ctypes.c_void_p * 5)(0x10000, 0x20000, 0x30000, 0x40000, 0x50000)
+        assert lib.hbmc_graph_add(g, r5._h, 1, five, 16, 0, 0) == 2          # RHD RS, P=5
+        assert lib.hbmc_graph_add(g, c._h, 0, arr, 16, 0, 0) == 0            # host-only checks pass
+        assert lib.hbmc_graph_launch(g, None) == 1                          # not built yet
+    assert lib.hbmc_graph_destroy(g) == 0
