@@ -19,12 +19,12 @@ DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2, "int32": 3, "int8": 4}
 ESIZE = {"fp32": 4, "fp16": 2, "bf16": 2, "int32": 4, "int8": 1}
 OP = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3}
-COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
+COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
 
 # every symbol include/hbmcoll.h declares
 EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
-           "hbmc_all_gather", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
+           "hbmc_all_gather", "hbmc_reduce", "hbmc_broadcast", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
            "hbmc_plan_items", "hbmc_status_string", "hbmc_graph_create", "hbmc_graph_add",
            "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy")
 
@@ -65,18 +65,22 @@ def load_library():
             f = getattr(L, name)
             f.restype = ci
             f.argtypes = [vp, ctypes.POINTER(vp), sz, ci, ci, vp]
+        L.hbmc_reduce.restype = ci
+        L.hbmc_reduce.argtypes = [vp, ctypes.POINTER(vp), sz, ci, ci, ci, vp]
+        L.hbmc_broadcast.restype = ci
+        L.hbmc_broadcast.argtypes = [vp, ctypes.POINTER(vp), sz, ci, ci, vp]
         L.hbmc_run_steps.restype = ci
-        L.hbmc_run_steps.argtypes = [vp, ci, ctypes.POINTER(vp), sz, ci, ci, ci, ci, vp]
+        L.hbmc_run_steps.argtypes = [vp, ci, ci, ctypes.POINTER(vp), sz, ci, ci, ci, ci, vp]
         L.hbmc_plan_info.restype = ci
-        L.hbmc_plan_info.argtypes = [vp, ci, sz, ci, ctypes.POINTER(ci), u64p, u64p]
+        L.hbmc_plan_info.argtypes = [vp, ci, ci, sz, ci, ctypes.POINTER(ci), u64p, u64p]
         L.hbmc_plan_step_info.restype = ci
-        L.hbmc_plan_step_info.argtypes = [vp, ci, sz, ci, ci, ctypes.POINTER(ci), u64p]
+        L.hbmc_plan_step_info.argtypes = [vp, ci, ci, sz, ci, ci, ctypes.POINTER(ci), u64p]
         L.hbmc_plan_items.restype = ci
-        L.hbmc_plan_items.argtypes = [vp, ci, sz, ci, ctypes.POINTER(Item), sz, ctypes.POINTER(sz)]
+        L.hbmc_plan_items.argtypes = [vp, ci, ci, sz, ci, ctypes.POINTER(Item), sz, ctypes.POINTER(sz)]
         L.hbmc_graph_create.restype = ci
         L.hbmc_graph_create.argtypes = [ctypes.POINTER(vp)]
         L.hbmc_graph_add.restype = ci
-        L.hbmc_graph_add.argtypes = [vp, vp, ci, ctypes.POINTER(vp), sz, ci, ci]
+        L.hbmc_graph_add.argtypes = [vp, vp, ci, ci, ctypes.POINTER(vp), sz, ci, ci]
         L.hbmc_graph_build.restype = ci
         L.hbmc_graph_build.argtypes = [vp]
         L.hbmc_graph_launch.restype = ci
@@ -167,37 +171,51 @@ class Comm:
     def all_gather(self, bufs, dtype=None, op="sum", *, count=None, stream=None):
         self._coll("hbmc_all_gather", bufs, dtype, op, count, stream)
 
-    def run_steps(self, coll, bufs, first, last, dtype=None, op="sum", *, count=None, stream=None):
+    def reduce(self, bufs, dtype=None, op="sum", *, root=0, count=None, stream=None):
         arr, n, dt = _ptrs(bufs)
         dtype = dtype or dt
         count = n if count is None else count
-        _check(load_library().hbmc_run_steps(self._h, COLL[coll], arr, count, DTYPE[dtype], OP[op], first,
-                                             last, _stream(stream)), "hbmc_run_steps")
+        _check(load_library().hbmc_reduce(self._h, arr, count, DTYPE[dtype], OP[op], root, _stream(stream)),
+               "hbmc_reduce")
+
+    def broadcast(self, bufs, dtype=None, *, root=0, count=None, stream=None):
+        arr, n, dt = _ptrs(bufs)
+        dtype = dtype or dt
+        count = n if count is None else count
+        _check(load_library().hbmc_broadcast(self._h, arr, count, DTYPE[dtype], root, _stream(stream)),
+               "hbmc_broadcast")
+
+    def run_steps(self, coll, bufs, first, last, dtype=None, op="sum", *, root=0, count=None, stream=None):
+        arr, n, dt = _ptrs(bufs)
+        dtype = dtype or dt
+        count = n if count is None else count
+        _check(load_library().hbmc_run_steps(self._h, COLL[coll], root, arr, count, DTYPE[dtype], OP[op],
+                                             first, last, _stream(stream)), "hbmc_run_steps")
 
     # -- schedule facts (host only)
-    def plan_info(self, coll: str, count: int, dtype: str):
+    def plan_info(self, coll: str, count: int, dtype: str, root: int = 0):
         n = ctypes.c_int()
         b = ctypes.c_uint64()
         r = ctypes.c_uint64()
-        _check(load_library().hbmc_plan_info(self._h, COLL[coll], count, DTYPE[dtype], ctypes.byref(n),
+        _check(load_library().hbmc_plan_info(self._h, COLL[coll], root, count, DTYPE[dtype], ctypes.byref(n),
                                              ctypes.byref(b), ctypes.byref(r)), "hbmc_plan_info")
         return dict(nsteps=n.value, hbm_bytes=b.value, max_recv_bytes=r.value)
 
-    def step_info(self, coll: str, count: int, dtype: str, step: int):
+    def step_info(self, coll: str, count: int, dtype: str, step: int, root: int = 0):
         n = ctypes.c_int()
         b = ctypes.c_uint64()
-        _check(load_library().hbmc_plan_step_info(self._h, COLL[coll], count, DTYPE[dtype], step,
+        _check(load_library().hbmc_plan_step_info(self._h, COLL[coll], root, count, DTYPE[dtype], step,
                                                   ctypes.byref(n), ctypes.byref(b)), "hbmc_plan_step_info")
         return dict(nitems=n.value, hbm_bytes=b.value)
 
-    def plan_items(self, coll: str, count: int, dtype: str):
+    def plan_items(self, coll: str, count: int, dtype: str, root: int = 0):
         n = ctypes.c_size_t()
         L = load_library()
-        _check(L.hbmc_plan_items(self._h, COLL[coll], count, DTYPE[dtype], None, 0, ctypes.byref(n)),
+        _check(L.hbmc_plan_items(self._h, COLL[coll], root, count, DTYPE[dtype], None, 0, ctypes.byref(n)),
                "hbmc_plan_items")
         arr = (Item * max(n.value, 1))()
-        _check(L.hbmc_plan_items(self._h, COLL[coll], count, DTYPE[dtype], arr, n.value, ctypes.byref(n)),
-               "hbmc_plan_items")
+        _check(L.hbmc_plan_items(self._h, COLL[coll], root, count, DTYPE[dtype], arr, n.value,
+                                 ctypes.byref(n)), "hbmc_plan_items")
         out = []
         for it in arr[:n.value]:
             ranks = list(it.rank[:it.nsrc + it.ndst])
@@ -214,13 +232,13 @@ class Graph:
         self._keep = []  # buffer-pointer arrays stay alive with the graph
         _check(load_library().hbmc_graph_create(ctypes.byref(self._h)), "hbmc_graph_create")
 
-    def add(self, comm: Comm, coll: str, bufs, dtype=None, op="sum", *, count=None):
+    def add(self, comm: Comm, coll: str, bufs, dtype=None, op="sum", *, root=0, count=None):
         arr, n, dt = _ptrs(bufs)
         dtype = dtype or dt
         count = n if count is None else count
         self._keep.append((arr, list(bufs)))
-        _check(load_library().hbmc_graph_add(self._h, comm._h, COLL[coll], arr, count, DTYPE[dtype], OP[op]),
-               "hbmc_graph_add")
+        _check(load_library().hbmc_graph_add(self._h, comm._h, COLL[coll], root, arr, count, DTYPE[dtype],
+                                             OP[op]), "hbmc_graph_add")
 
     def build(self):
         _check(load_library().hbmc_graph_build(self._h), "hbmc_graph_build")

@@ -60,29 +60,40 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
 
 hbmc_status_t hbmc_allreduce(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
                              hbmc_op_t op, void* stream) {
-  return run(comm, HBMC_COLL_ALLREDUCE, bufs, count, dtype, op, 0, 0, true, stream);
+  return run(comm, HBMC_COLL_ALLREDUCE, 0, bufs, count, dtype, op, 0, 0, true, stream);
 }
 
 hbmc_status_t hbmc_reduce_scatter(hbmc_comm_t comm, void* const bufs[], size_t count,
                                   hbmc_dtype_t dtype, hbmc_op_t op, void* stream) {
-  return run(comm, HBMC_COLL_REDUCE_SCATTER, bufs, count, dtype, op, 0, 0, true, stream);
+  return run(comm, HBMC_COLL_REDUCE_SCATTER, 0, bufs, count, dtype, op, 0, 0, true, stream);
 }
 
 hbmc_status_t hbmc_all_gather(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
                               hbmc_op_t op, void* stream) {
-  return run(comm, HBMC_COLL_ALL_GATHER, bufs, count, dtype, op, 0, 0, true, stream);
+  return run(comm, HBMC_COLL_ALL_GATHER, 0, bufs, count, dtype, op, 0, 0, true, stream);
 }
 
-hbmc_status_t hbmc_run_steps(hbmc_comm_t comm, hbmc_coll_t coll, void* const bufs[], size_t count,
-                             hbmc_dtype_t dtype, hbmc_op_t op, int first_step, int last_step,
-                             void* stream) {
-  return run(comm, coll, bufs, count, dtype, op, first_step, last_step, false, stream);
+hbmc_status_t hbmc_reduce(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
+                          hbmc_op_t op, int root, void* stream) {
+  return run(comm, HBMC_COLL_REDUCE, root, bufs, count, dtype, op, 0, 0, true, stream);
 }
 
-hbmc_status_t hbmc_plan_info(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, hbmc_dtype_t dtype,
-                             int* nsteps, uint64_t* hbm_bytes, uint64_t* max_recv_bytes) {
+hbmc_status_t hbmc_broadcast(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
+                             int root, void* stream) {
+  return run(comm, HBMC_COLL_BROADCAST, root, bufs, count, dtype, HBMC_SUM, 0, 0, true, stream);
+}
+
+hbmc_status_t hbmc_run_steps(hbmc_comm_t comm, hbmc_coll_t coll, int root, void* const bufs[],
+                             size_t count, hbmc_dtype_t dtype, hbmc_op_t op, int first_step,
+                             int last_step, void* stream) {
+  return run(comm, coll, root, bufs, count, dtype, op, first_step, last_step, false, stream);
+}
+
+hbmc_status_t hbmc_plan_info(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
+                             hbmc_dtype_t dtype, int* nsteps, uint64_t* hbm_bytes,
+                             uint64_t* max_recv_bytes) {
   Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, count, dtype, &p);
+  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
   if (st != HBMC_OK) return st;
   if (nsteps) *nsteps = static_cast<int>(p->sched.steps.size());
   if (hbm_bytes) *hbm_bytes = p->sched.hbm_bytes;
@@ -90,10 +101,10 @@ hbmc_status_t hbmc_plan_info(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, h
   return HBMC_OK;
 }
 
-hbmc_status_t hbmc_plan_step_info(hbmc_comm_t comm, hbmc_coll_t coll, size_t count,
+hbmc_status_t hbmc_plan_step_info(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                                   hbmc_dtype_t dtype, int step, int* nitems, uint64_t* hbm_bytes) {
   Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, count, dtype, &p);
+  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
   if (st != HBMC_OK) return st;
   if (step < 0 || step >= static_cast<int>(p->sched.steps.size())) return HBMC_ERR_INVALID_ARG;
   const Step& s = p->sched.steps[step];
@@ -102,10 +113,10 @@ hbmc_status_t hbmc_plan_step_info(hbmc_comm_t comm, hbmc_coll_t coll, size_t cou
   return HBMC_OK;
 }
 
-hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, hbmc_dtype_t dtype,
-                              hbmc_item_t* out, size_t cap, size_t* n_items) {
+hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
+                              hbmc_dtype_t dtype, hbmc_item_t* out, size_t cap, size_t* n_items) {
   Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, count, dtype, &p);
+  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
   if (st != HBMC_OK) return st;
   size_t k = 0;
   for (size_t s = 0; s < p->sched.steps.size(); ++s) {
@@ -132,7 +143,7 @@ const char* hbmc_status_string(hbmc_status_t status) {
   switch (status) {
     case HBMC_OK: return "success";
     case HBMC_ERR_INVALID_ARG: return "invalid argument";
-    case HBMC_ERR_UNSUPPORTED: return "unsupported (RHD reduce_scatter/all_gather needs a power-of-two rank count)";
+    case HBMC_ERR_UNSUPPORTED: return "unsupported (Reduce and Broadcast exist for the RHD algorithm only)";
     case HBMC_ERR_HIP: return "HIP error";
     case HBMC_ERR_NOMEM: return "out of memory";
     default: return "unknown status";

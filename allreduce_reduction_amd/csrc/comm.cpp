@@ -31,14 +31,17 @@ hbmc_status_t from_build(BuildStatus b) {
 
 }  // namespace
 
-bool valid_coll(int c) { return c >= HBMC_COLL_ALLREDUCE && c <= HBMC_COLL_ALL_GATHER; }
+bool valid_coll(int c) { return c >= HBMC_COLL_ALLREDUCE && c <= HBMC_COLL_BROADCAST; }
 bool valid_op(int op) { return op >= HBMC_SUM && op <= HBMC_MIN; }
 
-hbmc_status_t get_plan(hbmc_comm* c, int coll, size_t count, int dtype, Plan** out) {
+hbmc_status_t get_plan(hbmc_comm* c, int coll, int root, size_t count, int dtype, Plan** out) {
   const uint32_t e = elem_bytes(dtype);
   if (!c || e == 0 || !valid_coll(coll)) return HBMC_ERR_INVALID_ARG;
   if (count > SIZE_MAX / e) return HBMC_ERR_INVALID_ARG;
-  auto key = std::make_tuple(coll, static_cast<uint64_t>(count), dtype);
+  const bool rooted = coll == HBMC_COLL_REDUCE || coll == HBMC_COLL_BROADCAST;
+  if (rooted && (root < 0 || root >= c->topo.P)) return HBMC_ERR_INVALID_ARG;
+  if (!rooted) root = 0;
+  auto key = std::make_tuple(coll, root, static_cast<uint64_t>(count), dtype);
   auto it = c->plans.find(key);
   if (it != c->plans.end()) {
     *out = it->second.get();
@@ -46,7 +49,7 @@ hbmc_status_t get_plan(hbmc_comm* c, int coll, size_t count, int dtype, Plan** o
   }
   std::unique_ptr<Plan> p(new (std::nothrow) Plan);
   if (!p) return HBMC_ERR_NOMEM;
-  hbmc_status_t st = from_build(build_schedule(c->topo, static_cast<Coll>(coll), count, e, &p->sched));
+  hbmc_status_t st = from_build(build_schedule(c->topo, static_cast<Coll>(coll), count, e, root, &p->sched));
   if (st != HBMC_OK) return st;
   size_t off = 0;
   for (const Step& s : p->sched.steps) {
@@ -106,14 +109,15 @@ hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e) {
   return HBMC_OK;
 }
 
-hbmc_status_t prepare(hbmc_comm* c, int coll, void* const bufs[], size_t count, int dtype, int op,
-                      int first, int last, bool whole, std::vector<StepLaunch>* steps, RankPtrs* ptrs) {
+hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
+                      int op, int first, int last, bool whole, std::vector<StepLaunch>* steps,
+                      RankPtrs* ptrs) {
   steps->clear();
   if (!c || !valid_op(op) || !valid_coll(coll) || elem_bytes(dtype) == 0) return HBMC_ERR_INVALID_ARG;
   const uint32_t e = elem_bytes(dtype);
   if (count > SIZE_MAX / e) return HBMC_ERR_INVALID_ARG;
   Plan* p = nullptr;
-  hbmc_status_t st = get_plan(c, coll, count, dtype, &p);
+  hbmc_status_t st = get_plan(c, coll, root, count, dtype, &p);
   if (st != HBMC_OK) return st;
   const int nsteps = static_cast<int>(p->sched.steps.size());
   if (whole) {
@@ -155,11 +159,11 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, void* const bufs[], size_t count, 
   return HBMC_OK;
 }
 
-hbmc_status_t run(hbmc_comm* c, int coll, void* const bufs[], size_t count, int dtype, int op,
-                  int first, int last, bool whole, void* stream) {
+hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
+                  int op, int first, int last, bool whole, void* stream) {
   std::vector<StepLaunch> steps;
   RankPtrs ptrs;
-  hbmc_status_t st = prepare(c, coll, bufs, count, dtype, op, first, last, whole, &steps, &ptrs);
+  hbmc_status_t st = prepare(c, coll, root, bufs, count, dtype, op, first, last, whole, &steps, &ptrs);
   if (st != HBMC_OK) return st;
   for (const StepLaunch& L : steps)
     if (launch_step(L, ptrs, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;

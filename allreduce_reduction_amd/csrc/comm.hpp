@@ -31,13 +31,14 @@ struct Plan {
 struct hbmc_comm {
   hbmc::Topology topo;
   bool xcd_split = false;
-  std::map<std::tuple<int, uint64_t, int>, std::unique_ptr<hbmc::Plan>> plans;
+  std::map<std::tuple<int, int, uint64_t, int>, std::unique_ptr<hbmc::Plan>> plans;  // (coll, root, count, dtype)
 };
 
 namespace hbmc {
 
-// Build (or fetch) the host schedule of (coll, count, dtype).
-hbmc_status_t get_plan(hbmc_comm* c, int coll, size_t count, int dtype, Plan** out);
+// Build (or fetch) the host schedule of (coll, root, count, dtype); the root
+// matters only for Reduce and Broadcast.
+hbmc_status_t get_plan(hbmc_comm* c, int coll, int root, size_t count, int dtype, Plan** out);
 // Copy the plan's item table to the current device (once per plan).
 hbmc_status_t upload(Plan* p);
 // Non-null, element-aligned, pairwise disjoint rank buffers of count elements.
@@ -45,11 +46,12 @@ hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e);
 // Validate a call and list the launches of its steps [first, last) (all of
 // them when `whole`); uploads the plan's device table.  No launches for
 // count == 0 or P == 1.
-hbmc_status_t prepare(hbmc_comm* c, int coll, void* const bufs[], size_t count, int dtype, int op,
-                      int first, int last, bool whole, std::vector<StepLaunch>* steps, RankPtrs* ptrs);
+hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
+                      int op, int first, int last, bool whole, std::vector<StepLaunch>* steps,
+                      RankPtrs* ptrs);
 // Validate and enqueue steps [first, last) of a collective (all of them when
 // `whole`) on `stream`, one kernel launch per non-empty step.
-hbmc_status_t run(hbmc_comm* c, int coll, void* const bufs[], size_t count, int dtype, int op,
-                  int first, int last, bool whole, void* stream);
+hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
+                  int op, int first, int last, bool whole, void* stream);
 
 }  // namespace hbmc

@@ -17,7 +17,7 @@ using namespace hbmc;
 struct hbmc_graph {
   struct Node {
     hbmc_comm* comm;
-    int coll;
+    int coll, root;
     std::vector<void*> bufs;
     size_t count;
     int dtype, op;
@@ -58,14 +58,14 @@ hbmc_status_t hbmc_graph_create(hbmc_graph_t* out) {
   return *out ? HBMC_OK : HBMC_ERR_NOMEM;
 }
 
-hbmc_status_t hbmc_graph_add(hbmc_graph_t g, hbmc_comm_t comm, hbmc_coll_t coll, void* const bufs[],
-                             size_t count, hbmc_dtype_t dtype, hbmc_op_t op) {
+hbmc_status_t hbmc_graph_add(hbmc_graph_t g, hbmc_comm_t comm, hbmc_coll_t coll, int root,
+                             void* const bufs[], size_t count, hbmc_dtype_t dtype, hbmc_op_t op) {
   if (!g || g->built || !comm || !valid_op(op) || !valid_coll(coll) || elem_bytes(dtype) == 0)
     return HBMC_ERR_INVALID_ARG;
   Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, count, dtype, &p);
+  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
   if (st != HBMC_OK) return st;
-  hbmc_graph::Node n{comm, coll, {}, count, dtype, op};
+  hbmc_graph::Node n{comm, coll, root, {}, count, dtype, op};
   if (count > 0 && comm->topo.P > 1) {
     st = check_bufs(comm->topo.P, bufs, count, elem_bytes(dtype));
     if (st != HBMC_OK) return st;
@@ -87,7 +87,7 @@ hbmc_status_t hbmc_graph_build(hbmc_graph_t g) {
       if (overlaps(n, g->nodes[j])) deps.push_back(last[j]);
     std::vector<StepLaunch> steps;
     RankPtrs ptrs;
-    st = prepare(n.comm, n.coll, n.bufs.data(), n.count, n.dtype, n.op, 0, 0, true, &steps, &ptrs);
+    st = prepare(n.comm, n.coll, n.root, n.bufs.data(), n.count, n.dtype, n.op, 0, 0, true, &steps, &ptrs);
     if (st != HBMC_OK) break;
     if (steps.empty()) {
       if (hipGraphAddEmptyNode(&last[i], g->graph, deps.data(), deps.size()) != hipSuccess) st = HBMC_ERR_HIP;

@@ -17,6 +17,17 @@
 // distances P/2 .. 1 (rank v keeps the aligned block containing segment v),
 // then 1 .. P/2 for the all-gather.
 //
+// Stand-alone RHD reduce-scatter / all-gather for P not a power of two
+// ([RHD] Table 1): Reduce (two-share pairs merge), a non-uniform halving over
+// the 2^k virtual ranks, Scatter (and the mirror image for all-gather).  The
+// P shares lie in order along the virtual ranks; virtual rank v carries two
+// shares when the k-bit reversal of v is below r, which bounds the exchange
+// of halving step i by ceil(P / 2^i) shares.  RHD Reduce / Broadcast with a
+// root: in part1 the rank of each pair with the root's parity takes part in
+// the 2^k block; Reduce = merge + order-preserving reduce-scatter over the
+// 2^k-way split + gather to the root; Broadcast = distance halving from the
+// root, then one copy to each part1 partner.
+//
 // Pipeline ([PIPE] "AllGather 算子的 Pipeline 时序编排", "Rank0 视角的传输任务编排",
 // Table 1): rank g = s*M + m; each loop (slice of at most loop_bytes) is split
 // into P blocks.  Reduce-scatter: one intra-server step in which (s,m) folds
@@ -171,6 +182,118 @@ void rhd_ordered(const Topology& t, Coll coll, uint64_t L, Builder& B) {
   }
 }
 
+// ---------------------------------------------------------------- RHD, P not 2^k
+struct ShareMap {
+  int k, pp, r;
+  std::vector<int> first;  // first share of virtual rank v, first[pp] == P
+  std::vector<bool> two;   // virtual rank v carries two shares
+};
+
+ShareMap share_map(int P) {
+  ShareMap m;
+  m.k = log2_floor(P);
+  m.pp = 1 << m.k;
+  m.r = P - m.pp;
+  m.first.assign(m.pp + 1, 0);
+  m.two.assign(m.pp, false);
+  for (int v = 0; v < m.pp; ++v) {
+    int rev = 0;
+    for (int b = 0; b < m.k; ++b) rev |= ((v >> b) & 1) << (m.k - 1 - b);
+    m.two[v] = rev < m.r;
+    m.first[v + 1] = m.first[v] + (m.two[v] ? 2 : 1);
+  }
+  return m;
+}
+
+void rhd_unordered_np2(const Topology& t, Coll coll, uint64_t L, Builder& B) {
+  const ShareMap m = share_map(t.P);
+  Split seg(L, t.P);
+  auto span = [&](int v0, int v1, uint64_t* lo, uint64_t* hi) {  // shares of virtual ranks [v0, v1)
+    *lo = seg.at(m.first[v0]);
+    *hi = seg.at(m.first[v1]);
+  };
+  uint64_t lo, hi;
+  if (coll == kReduceScatter) {
+    Step& merge = B.open(kRecvFold);
+    for (int v = 0; v < m.pp; ++v)
+      if (m.two[v]) Builder::add(merge, 0, L, {m.first[v] + 1, m.first[v]}, {m.first[v]});
+    for (int d = m.pp / 2; d >= 1; d /= 2) {
+      Step& st = B.open(kRecvFold);
+      for (int v = 0; v < m.pp; ++v) {
+        const int a = v & ~(d - 1);  // the aligned block of d virtual ranks that holds v
+        span(a, a + d, &lo, &hi);
+        Builder::add(st, lo, hi, {m.first[v ^ d], m.first[v]}, {m.first[v]});
+      }
+    }
+    Step& scatter = B.open(kCopy);
+    for (int v = 0; v < m.pp; ++v)
+      if (m.two[v]) {
+        const int g = m.first[v] + 1;
+        Builder::add(scatter, seg.at(g), seg.at(g + 1), {m.first[v]}, {g});
+      }
+  } else {
+    Step& gather = B.open(kCopy);
+    for (int v = 0; v < m.pp; ++v)
+      if (m.two[v]) {
+        const int g = m.first[v] + 1;
+        Builder::add(gather, seg.at(g), seg.at(g + 1), {g}, {m.first[v]});
+      }
+    for (int d = 1; d < m.pp; d *= 2) {
+      Step& st = B.open(kCopy);
+      for (int v = 0; v < m.pp; ++v) {
+        const int a = (v ^ d) & ~(d - 1);  // the partner's collected block
+        span(a, a + d, &lo, &hi);
+        Builder::add(st, lo, hi, {m.first[v ^ d]}, {m.first[v]});
+      }
+    }
+    Step& spread = B.open(kCopy);
+    for (int v = 0; v < m.pp; ++v)
+      if (m.two[v]) Builder::add(spread, 0, L, {m.first[v]}, {m.first[v] + 1});
+  }
+}
+
+// ---------------------------------------------------------------- RHD rooted
+void rhd_rooted(const Topology& t, Coll coll, uint64_t L, int root, Builder& B) {
+  const int k = log2_floor(t.P), pp = 1 << k, r = t.P - pp;
+  const int par = (root < 2 * r) ? (root & 1) : 0;  // part1 side that joins the block
+  auto real = [&](int v) { return v < r ? 2 * v + par : v + r; };
+  auto mate = [&](int i) { return 2 * i + 1 - par; };
+  const int vroot = root < 2 * r ? root / 2 : root - r;
+  Split seg(L, pp);
+  if (coll == kReduce) {
+    if (r > 0) {
+      Step& merge = B.open(kRecvFold);
+      for (int i = 0; i < r; ++i) Builder::add(merge, 0, L, {mate(i), real(i)}, {real(i)});
+    }
+    for (int d = pp / 2; d >= 1; d /= 2) {
+      Step& st = B.open(kRecvFold);
+      for (int v = 0; v < pp; ++v) {
+        const int a = v & ~(d - 1);
+        Builder::add(st, seg.at(a), seg.at(a + d), {real(v ^ d), real(v)}, {real(v)});
+      }
+    }
+    for (int d = 1; d < pp; d *= 2) {
+      Step& st = B.open(kCopy);
+      for (int v = 0; v < pp; ++v) {
+        const int rel = v ^ vroot;
+        if ((rel & d) == 0 || (rel & (d - 1)) != 0) continue;  // lowest set bit of rel must be d
+        const int a = v & ~(d - 1);
+        Builder::add(st, seg.at(a), seg.at(a + d), {real(v)}, {real(v ^ d)});
+      }
+    }
+  } else {
+    for (int d = pp / 2; d >= 1; d /= 2) {
+      Step& st = B.open(kCopy);
+      for (int v = 0; v < pp; ++v)
+        if (((v ^ vroot) % (2 * d)) == 0) Builder::add(st, 0, L, {real(v)}, {real(v ^ d)});
+    }
+    if (r > 0) {
+      Step& st = B.open(kCopy);
+      for (int i = 0; i < r; ++i) Builder::add(st, 0, L, {real(i)}, {mate(i)});
+    }
+  }
+}
+
 // ---------------------------------------------------------------- pipeline
 void pipeline(const Topology& t, Coll coll, uint64_t L, uint32_t esize, Builder& B,
               Schedule* sched) {
@@ -275,14 +398,17 @@ bool step_is_race_free(const Step& st) {
 
 }  // namespace
 
-BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint32_t esize,
+BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint32_t esize, int root,
                            Schedule* out) {
   *out = Schedule{};
   if (topo.P < 1 || topo.P > kMaxRanks || esize == 0) return kBadArg;
+  if (coll < kAllReduce || coll > kBroadcast) return kBadArg;
   if (topo.algo == kPipeline && (topo.S < 1 || topo.M < 1 || topo.S * topo.M != topo.P))
     return kBadArg;
+  const bool rooted = coll == kReduce || coll == kBroadcast;
+  if (rooted && (root < 0 || root >= topo.P)) return kBadArg;
+  if (rooted && topo.algo != kRhd) return kUnsupported;
   const bool pow2 = (topo.P & (topo.P - 1)) == 0;
-  if (topo.algo == kRhd && coll != kAllReduce && !pow2) return kUnsupported;
   if (topo.P == 1) return kBuilt;
 
   Builder B(out);
@@ -291,8 +417,12 @@ BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint
     case kRhd:
       if (coll == kAllReduce)
         rhd_allreduce(topo, count, B);
-      else
+      else if (rooted)
+        rhd_rooted(topo, coll, count, root, B);
+      else if (pow2)
         rhd_ordered(topo, coll, count, B);
+      else
+        rhd_unordered_np2(topo, coll, count, B);
       break;
     case kPipeline: pipeline(topo, coll, count, esize, B, out); break;
     default: return kBadArg;

@@ -12,7 +12,7 @@ constexpr int kMaxRanks = 64;
 
 enum Mode : int32_t { kCopy = 0, kFold = 1, kRecvFold = 2 };
 enum Algo : int32_t { kRing = 0, kRhd = 1, kPipeline = 2 };
-enum Coll : int32_t { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
+enum Coll : int32_t { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2, kReduce = 3, kBroadcast = 4 };
 
 // One unit of work: every destination's range [begin, begin+count) receives
 // the combination (per Mode) of the sources' same range.
@@ -45,11 +45,13 @@ struct Schedule {
 
 enum BuildStatus { kBuilt = 0, kBadArg = 1, kUnsupported = 2 };
 
-// Build the schedule of `coll` over `count` elements of `esize` bytes.
+// Build the schedule of `coll` over `count` elements of `esize` bytes
+// (`root`: the root rank of Reduce / Broadcast, ignored otherwise).
 // Also verifies that no two items of a step touch overlapping ranges of one
 // rank where either writes (so a step's items may run concurrently in place);
-// a violation is reported as kBadArg.
-BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint32_t esize,
+// a violation is reported as kBadArg.  Reduce and Broadcast exist for RHD only
+// (kUnsupported otherwise).
+BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint32_t esize, int root,
                            Schedule* out);
 
 }  // namespace hbmc

@@ -43,7 +43,7 @@ typedef enum {
   HBMC_OK = 0,
   HBMC_ERR_INVALID_ARG = 1, /* null / aliased / misaligned buffers, bad P, count*e overflow,
                                S*M != P, enum out of range, step range out of bounds      */
-  HBMC_ERR_UNSUPPORTED = 2, /* RHD reduce_scatter / all_gather with P not a power of two   */
+  HBMC_ERR_UNSUPPORTED = 2, /* Reduce / Broadcast with an algorithm other than RHD          */
   HBMC_ERR_HIP = 3,         /* a HIP call or kernel launch failed                          */
   HBMC_ERR_NOMEM = 4        /* host or device allocation failed                            */
 } hbmc_status_t;
@@ -66,7 +66,13 @@ typedef enum { HBMC_SUM = 0, HBMC_PROD = 1, HBMC_MAX = 2, HBMC_MIN = 3 } hbmc_op
  * pages' HCCL_ALGO selects an algorithm ([RHD] "RHD 在 HCCL 中的定位与启用方式"). */
 typedef enum { HBMC_ALGO_RING = 0, HBMC_ALGO_RHD = 1, HBMC_ALGO_PIPELINE = 2, HBMC_ALGO_ENV = 3 } hbmc_algo_t;
 
-typedef enum { HBMC_COLL_ALLREDUCE = 0, HBMC_COLL_REDUCE_SCATTER = 1, HBMC_COLL_ALL_GATHER = 2 } hbmc_coll_t;
+typedef enum {
+  HBMC_COLL_ALLREDUCE = 0,
+  HBMC_COLL_REDUCE_SCATTER = 1,
+  HBMC_COLL_ALL_GATHER = 2,
+  HBMC_COLL_REDUCE = 3,    /* to a root; RHD only */
+  HBMC_COLL_BROADCAST = 4  /* from a root; RHD only */
+} hbmc_coll_t;
 
 /*
  * Create a communicator of `nranks` logical ranks (1..64) using `algo`.
@@ -96,7 +102,9 @@ hbmc_status_t hbmc_allreduce(hbmc_comm_t comm, void* const bufs[], size_t count,
  * (segment k = [min(k q, count), min((k+1) q, count)), q = ceil(count / P),
  * [TOPO] "AllReduce算法实现"); for the pipeline each loop is split that way.
  * On completion bufs[r] holds Y on segment r (each loop's block r for the
- * pipeline); its other segments are unspecified.
+ * pipeline); its other segments are unspecified.  RHD with P not a power of
+ * two runs the three-part schedule of [RHD] Table 1 (Reduce, non-uniform
+ * reduce-scatter over 2^floor(log2 P) virtual ranks, Scatter).
  */
 hbmc_status_t hbmc_reduce_scatter(hbmc_comm_t comm, void* const bufs[], size_t count,
                                   hbmc_dtype_t dtype, hbmc_op_t op, void* stream);
@@ -110,15 +118,36 @@ hbmc_status_t hbmc_all_gather(hbmc_comm_t comm, void* const bufs[], size_t count
                               hbmc_op_t op, void* stream);
 
 /*
+ * Reduce to `root` (0 <= root < P), RHD communicators only ([RHD] Table 1:
+ * Reduce = ReduceScatter + Gather; for P not a power of two the pairs of
+ * part1 first merge into the rank with the root's parity).  On completion
+ * bufs[root] holds Y; the other buffers are unspecified.
+ * HBMC_ERR_UNSUPPORTED for ring and pipeline communicators.
+ */
+hbmc_status_t hbmc_reduce(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
+                          hbmc_op_t op, int root, void* stream);
+
+/*
+ * Broadcast from `root`, RHD communicators only ([RHD] Table 1: the root's
+ * parity picks the part1 ranks that join the 2^k block, distance halving
+ * inside the block, then one more send to the remaining ranks).  On
+ * completion every buffer holds bufs[root]'s contents.
+ * HBMC_ERR_UNSUPPORTED for ring and pipeline communicators.
+ */
+hbmc_status_t hbmc_broadcast(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
+                             int root, void* stream);
+
+/*
  * Run only schedule steps [first_step, last_step) of a collective (every
  * loop's steps with those indices for the pipeline).  Running [0, k) and then
  * [k, nsteps) equals the whole collective.  For step-by-step checking and
- * per-step timing.  Returns HBMC_ERR_INVALID_ARG for an empty or
- * out-of-range step interval.
+ * per-step timing.  `root` is used by Reduce and Broadcast and ignored
+ * otherwise (also in the plan and graph calls below).  Returns
+ * HBMC_ERR_INVALID_ARG for an empty or out-of-range step interval.
  */
-hbmc_status_t hbmc_run_steps(hbmc_comm_t comm, hbmc_coll_t coll, void* const bufs[], size_t count,
-                             hbmc_dtype_t dtype, hbmc_op_t op, int first_step, int last_step,
-                             void* stream);
+hbmc_status_t hbmc_run_steps(hbmc_comm_t comm, hbmc_coll_t coll, int root, void* const bufs[],
+                             size_t count, hbmc_dtype_t dtype, hbmc_op_t op, int first_step,
+                             int last_step, void* stream);
 
 /*
  * Schedule facts, computed on the host without touching the device:
@@ -127,11 +156,12 @@ hbmc_status_t hbmc_run_steps(hbmc_comm_t comm, hbmc_coll_t coll, void* const buf
  * once), and the largest number of bytes any rank receives from other ranks.
  * Any out-pointer may be NULL.
  */
-hbmc_status_t hbmc_plan_info(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, hbmc_dtype_t dtype,
-                             int* nsteps, uint64_t* hbm_bytes, uint64_t* max_recv_bytes);
+hbmc_status_t hbmc_plan_info(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
+                             hbmc_dtype_t dtype, int* nsteps, uint64_t* hbm_bytes,
+                             uint64_t* max_recv_bytes);
 
 /* The same for one step: its work items and algorithmic HBM bytes. */
-hbmc_status_t hbmc_plan_step_info(hbmc_comm_t comm, hbmc_coll_t coll, size_t count,
+hbmc_status_t hbmc_plan_step_info(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                                   hbmc_dtype_t dtype, int step, int* nitems, uint64_t* hbm_bytes);
 
 /* One work item of a step: every destination rank's range
@@ -148,8 +178,8 @@ typedef struct {
 
 /* Copy out every work item of a collective's schedule (host only).  Writes
  * at most `cap` items and sets *n_items to the total. */
-hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, hbmc_dtype_t dtype,
-                              hbmc_item_t* out, size_t cap, size_t* n_items);
+hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
+                              hbmc_dtype_t dtype, hbmc_item_t* out, size_t cap, size_t* n_items);
 
 /*
  * Graph mode ([RING-RHD] section "Ascend950的AIVAICPU通信引擎与图模式": a
@@ -171,8 +201,8 @@ hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, size_t count, 
  */
 typedef struct hbmc_graph* hbmc_graph_t;
 hbmc_status_t hbmc_graph_create(hbmc_graph_t* out);
-hbmc_status_t hbmc_graph_add(hbmc_graph_t graph, hbmc_comm_t comm, hbmc_coll_t coll, void* const bufs[],
-                             size_t count, hbmc_dtype_t dtype, hbmc_op_t op);
+hbmc_status_t hbmc_graph_add(hbmc_graph_t graph, hbmc_comm_t comm, hbmc_coll_t coll, int root,
+                             void* const bufs[], size_t count, hbmc_dtype_t dtype, hbmc_op_t op);
 hbmc_status_t hbmc_graph_build(hbmc_graph_t graph);
 hbmc_status_t hbmc_graph_launch(hbmc_graph_t graph, void* stream);
 hbmc_status_t hbmc_graph_destroy(hbmc_graph_t graph);

@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2, "int32": 3, "int8": 4}
 OP = {"sum": 0, "prod": 1, "max": 2, "min": 3}
 ALGO = {"ring": 0, "rhd": 1, "pipeline": 2}
-COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2}
+COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 KIND = {0: "copy", 1: "reduce", 2: "fold", 3: "fold_recv"}
 NP_STORAGE = {"fp32": np.float32, "fp16": np.float16, "bf16": np.uint16,
               "int32": np.int32, "int8": np.int8}
@@ -67,7 +67,7 @@ def lib():
         L.orc_num_steps.restype = ctypes.c_long
         L.orc_num_steps.argtypes = [ci, ci, ci, ci, ci, sz, ci, sz]
         L.orc_collective.restype = ci
-        L.orc_collective.argtypes = [ci, ci, ci, ci, ci, sz, ctypes.POINTER(vp), sz, sz, sz, ci, ci,
+        L.orc_collective.argtypes = [ci, ci, ci, ci, ci, sz, ci, ctypes.POINTER(vp), sz, sz, sz, ci, ci,
                                      ctypes.c_long, ctypes.c_long, ctypes.POINTER(TraceRec), sz,
                                      ctypes.POINTER(sz)]
         _lib = L
@@ -124,8 +124,8 @@ def num_steps(coll: str, algo: str, P: int, S: int = 1, M: int = 1) -> int:
 
 
 def run(coll: str, algo: str, bufs: list[np.ndarray], dtype: str, op: str, *, L: int | None = None,
-        w0: int = 0, S: int = 1, M: int = 1, loop_bytes: int = 0, first_step: int = 0,
-        last_step: int = -1, trace: bool = False, trace_cap: int = 1 << 16):
+        w0: int = 0, S: int = 1, M: int = 1, loop_bytes: int = 0, root: int = 0,
+        first_step: int = 0, last_step: int = -1, trace: bool = False, trace_cap: int = 1 << 16):
     """Replay a collective in place on ``bufs`` (numpy storage arrays, one per rank).
 
     ``bufs[r]`` holds elements ``w0 .. w0+len-1`` of a vector of ``L`` elements
@@ -140,7 +140,7 @@ def run(coll: str, algo: str, bufs: list[np.ndarray], dtype: str, op: str, *, L:
     ptrs = (ctypes.c_void_p * max(P, 1))(*[b.ctypes.data for b in bufs])
     recs = (TraceRec * trace_cap)() if trace else None
     tlen = ctypes.c_size_t(0)
-    rc = lib().orc_collective(COLL[coll], ALGO[algo], P, S, M, loop_bytes, ptrs, L, w0, w0 + n,
+    rc = lib().orc_collective(COLL[coll], ALGO[algo], P, S, M, loop_bytes, root, ptrs, L, w0, w0 + n,
                               DTYPE[dtype], OP[op], first_step, last_step, recs,
                               trace_cap if trace else 0, ctypes.byref(tlen))
     _check(rc)

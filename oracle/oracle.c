@@ -677,6 +677,222 @@ static void rhd_all_gather(run_t* R, size_t L) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* RHD with P not a power of two, stand-alone ([RHD] "耗时计算", Table 1).
+ * Reduce-scatter: (1) Reduce: each two-share pair merges into one rank;
+ * (2) a non-uniform reduce-scatter over the 2^k virtual ranks, distance
+ * halving, in which some virtual ranks hold two shares; (3) Scatter: the
+ * merged rank hands the second share to its partner.  The two-share virtual
+ * ranks are those whose k-bit reversal is below r, which makes the largest
+ * exchange of halving step i equal to ceil(p / 2^i) shares, the table's n_i.
+ * Shares (segments of the P-way split) lie in order along the virtual ranks,
+ * so rank g ends owning segment g.  All-gather is the mirror image: Gather of
+ * the second share, distance doubling, and a final copy of everything to the
+ * partner. */
+
+static int bitrev(int v, int k) {
+  int out = 0;
+  for (int i = 0; i < k; ++i)
+    if ((v >> i) & 1) out |= 1 << (k - 1 - i);
+  return out;
+}
+
+typedef struct {
+  int k, pp, r;
+  int first[65]; /* first share (= real rank) of virtual rank v; first[pp] = P */
+  int two[64];   /* virtual rank v holds two shares */
+} shares_t;
+
+static void share_layout(int P, shares_t* S) {
+  S->k = floor_log2(P);
+  S->pp = 1 << S->k;
+  S->r = P - S->pp;
+  int s = 0;
+  for (int v = 0; v < S->pp; ++v) {
+    S->two[v] = bitrev(v, S->k) < S->r;
+    S->first[v] = s;
+    s += S->two[v] ? 2 : 1;
+  }
+  S->first[S->pp] = s;
+}
+
+static void rhd_reduce_scatter_np2(run_t* R, size_t L) {
+  int P = R->P;
+  shares_t S;
+  share_layout(P, &S);
+  /* (1) Reduce: share first+1 is folded into the rank owning share first */
+  step_begin(R);
+  for (int v = 0; v < S.pp; ++v)
+    if (S.two[v]) {
+      int odd = S.first[v] + 1;
+      add_action(R, ORC_REDUCE, S.first[v], &odd, 1, 0, L);
+    }
+  step_end(R);
+  /* (2) non-uniform halving over virtual ranks; v keeps the half holding v */
+  int lo[64], hi[64];
+  for (int v = 0; v < S.pp; ++v) {
+    lo[v] = 0;
+    hi[v] = S.pp;
+  }
+  for (int d = S.pp / 2; d >= 1; d /= 2) {
+    step_begin(R);
+    int nlo[64], nhi[64];
+    for (int v = 0; v < S.pp; ++v) {
+      int u = v ^ d, mid = (lo[v] + hi[v]) / 2;
+      nlo[v] = v < mid ? lo[v] : mid;
+      nhi[v] = v < mid ? mid : hi[v];
+      size_t b = seg_begin(L, (size_t)P, (size_t)S.first[nlo[v]]);
+      size_t e = seg_begin(L, (size_t)P, (size_t)S.first[nhi[v]]);
+      int src = S.first[u];
+      add_action(R, ORC_REDUCE, S.first[v], &src, 1, b, e - b);
+    }
+    for (int v = 0; v < S.pp; ++v) {
+      lo[v] = nlo[v];
+      hi[v] = nhi[v];
+    }
+    step_end(R);
+  }
+  /* (3) Scatter: the second share goes to its own rank */
+  step_begin(R);
+  for (int v = 0; v < S.pp; ++v)
+    if (S.two[v]) {
+      int g = S.first[v] + 1, src = S.first[v];
+      size_t b = seg_begin(L, (size_t)P, (size_t)g), e = seg_begin(L, (size_t)P, (size_t)g + 1);
+      add_action(R, ORC_COPY, g, &src, 1, b, e - b);
+    }
+  step_end(R);
+}
+
+static void rhd_all_gather_np2(run_t* R, size_t L) {
+  int P = R->P;
+  shares_t S;
+  share_layout(P, &S);
+  /* (1) Gather: the partner's share comes to the merged rank */
+  step_begin(R);
+  for (int v = 0; v < S.pp; ++v)
+    if (S.two[v]) {
+      int g = S.first[v] + 1;
+      size_t b = seg_begin(L, (size_t)P, (size_t)g), e = seg_begin(L, (size_t)P, (size_t)g + 1);
+      add_action(R, ORC_COPY, S.first[v], &g, 1, b, e - b);
+    }
+  step_end(R);
+  /* (2) distance doubling over virtual ranks */
+  int lo[64], hi[64];
+  for (int v = 0; v < S.pp; ++v) {
+    lo[v] = v;
+    hi[v] = v + 1;
+  }
+  for (int d = 1; d < S.pp; d *= 2) {
+    step_begin(R);
+    int nlo[64], nhi[64];
+    for (int v = 0; v < S.pp; ++v) {
+      int u = v ^ d;
+      size_t b = seg_begin(L, (size_t)P, (size_t)S.first[lo[u]]);
+      size_t e = seg_begin(L, (size_t)P, (size_t)S.first[hi[u]]);
+      int src = S.first[u];
+      add_action(R, ORC_COPY, S.first[v], &src, 1, b, e - b);
+      nlo[v] = lo[v] < lo[u] ? lo[v] : lo[u];
+      nhi[v] = hi[v] > hi[u] ? hi[v] : hi[u];
+    }
+    for (int v = 0; v < S.pp; ++v) {
+      lo[v] = nlo[v];
+      hi[v] = nhi[v];
+    }
+    step_end(R);
+  }
+  /* (3) the merged rank copies everything to its partner */
+  step_begin(R);
+  for (int v = 0; v < S.pp; ++v)
+    if (S.two[v]) {
+      int src = S.first[v];
+      add_action(R, ORC_COPY, S.first[v] + 1, &src, 1, 0, L);
+    }
+  step_end(R);
+}
+
+/* ------------------------------------------------------------------------ */
+/* RHD Reduce and Broadcast with a root ([RHD] Table 1).  For P not a power
+ * of two the ranks 0..2r-1 pair up (2i, 2i+1); in each pair the rank with the
+ * root's parity (even when the root is outside part1) takes part in the 2^k
+ * block.  Reduce = merge of part1 + order-preserving reduce-scatter over the
+ * 2^k-way split (distance halving) + gather to the root (distance doubling,
+ * each rank sending the block it has collected).  Broadcast = distance
+ * halving from the root over the block, then one send to each part1 partner. */
+
+typedef struct {
+  int k, pp, r, odd, vroot;
+} rooted_t;
+
+static rooted_t rooted(int P, int root) {
+  rooted_t t;
+  t.k = floor_log2(P);
+  t.pp = 1 << t.k;
+  t.r = P - t.pp;
+  t.odd = (root < 2 * t.r) && (root & 1);
+  t.vroot = root < 2 * t.r ? root / 2 : root - t.r;
+  return t;
+}
+static int rooted_real(const rooted_t* t, int v) { return v < t->r ? 2 * v + t->odd : v + t->r; }
+static int rooted_partner(const rooted_t* t, int i) { return 2 * i + 1 - t->odd; }
+
+static void rhd_reduce(run_t* R, size_t L, int root) {
+  rooted_t t = rooted(R->P, root);
+  if (t.r > 0) {
+    step_begin(R);
+    for (int i = 0; i < t.r; ++i) {
+      int from = rooted_partner(&t, i);
+      add_action(R, ORC_REDUCE, rooted_real(&t, i), &from, 1, 0, L);
+    }
+    step_end(R);
+  }
+  /* reduce-scatter: virtual rank v ends with segment v of the pp-way split */
+  for (int d = t.pp / 2; d >= 1; d /= 2) {
+    step_begin(R);
+    for (int v = 0; v < t.pp; ++v) {
+      int a = v & ~(d - 1); /* aligned block of d segments holding v */
+      size_t b = seg_begin(L, (size_t)t.pp, (size_t)a), e = seg_begin(L, (size_t)t.pp, (size_t)(a + d));
+      int src = rooted_real(&t, v ^ d);
+      add_action(R, ORC_REDUCE, rooted_real(&t, v), &src, 1, b, e - b);
+    }
+    step_end(R);
+  }
+  /* gather to the root: at distance d the rank whose offset from the root
+   * has lowest set bit d sends its collected block of d segments */
+  for (int d = 1; d < t.pp; d *= 2) {
+    step_begin(R);
+    for (int v = 0; v < t.pp; ++v) {
+      int rel = v ^ t.vroot;
+      if ((rel & d) && !(rel & (d - 1))) {
+        int a = v & ~(d - 1), src = rooted_real(&t, v);
+        size_t b = seg_begin(L, (size_t)t.pp, (size_t)a), e = seg_begin(L, (size_t)t.pp, (size_t)(a + d));
+        add_action(R, ORC_COPY, rooted_real(&t, v ^ d), &src, 1, b, e - b);
+      }
+    }
+    step_end(R);
+  }
+}
+
+static void rhd_broadcast(run_t* R, size_t L, int root) {
+  rooted_t t = rooted(R->P, root);
+  for (int d = t.pp / 2; d >= 1; d /= 2) {
+    step_begin(R);
+    for (int v = 0; v < t.pp; ++v)
+      if (((v ^ t.vroot) & (2 * d - 1)) == 0) {
+        int src = rooted_real(&t, v);
+        add_action(R, ORC_COPY, rooted_real(&t, v ^ d), &src, 1, 0, L);
+      }
+    step_end(R);
+  }
+  if (t.r > 0) {
+    step_begin(R);
+    for (int i = 0; i < t.r; ++i) {
+      int src = rooted_real(&t, i);
+      add_action(R, ORC_COPY, rooted_partner(&t, i), &src, 1, 0, L);
+    }
+    step_end(R);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* two-level pipeline ([PIPE] "AllGather 算子的 Pipeline 时序编排", Table 1)  */
 
 typedef struct {
@@ -762,27 +978,32 @@ long orc_num_steps(int coll, int algo, int P, int S, int M, size_t L, int dtype,
   (void)loop_bytes;
   (void)M;
   if (P <= 1) return 0;
-  long half;
-  switch (algo) {
-    case ORC_RING: half = P - 1; break;
-    case ORC_RHD: half = floor_log2(P); break;
-    default: half = S; break;
+  const int pow2 = (P & (P - 1)) == 0, k = floor_log2(P);
+  if (algo == ORC_RHD) {
+    switch (coll) {
+      case ORC_ALLREDUCE: return 2 * k + (pow2 ? 0 : 2);
+      case ORC_REDUCE_SCATTER:
+      case ORC_ALL_GATHER: return k + (pow2 ? 0 : 2);
+      case ORC_ROOT_REDUCE: return 2 * k + (pow2 ? 0 : 1);
+      default: return k + (pow2 ? 0 : 1);
+    }
   }
-  if (coll != ORC_ALLREDUCE) return half;
-  long extra = (algo == ORC_RHD && (P & (P - 1))) ? 2 : 0;
-  return 2 * half + extra;
+  long half = algo == ORC_RING ? P - 1 : S;
+  return coll == ORC_ALLREDUCE ? 2 * half : half;
 }
 
-int orc_collective(int coll, int algo, int P, int S, int M, size_t loop_bytes, void* const* bufs,
-                   size_t L, size_t w0, size_t w1, int dtype, int op, long first_step,
-                   long last_step, orc_trace_t* trace, size_t trace_cap, size_t* trace_len) {
+int orc_collective(int coll, int algo, int P, int S, int M, size_t loop_bytes, int root,
+                   void* const* bufs, size_t L, size_t w0, size_t w1, int dtype, int op,
+                   long first_step, long last_step, orc_trace_t* trace, size_t trace_cap,
+                   size_t* trace_len) {
   if (trace_len) *trace_len = 0;
   if (P < 1 || P > 64 || esize(dtype) == 0 || op < ORC_SUM || op > ORC_MIN) return ORC_EINVAL;
-  if (coll < ORC_ALLREDUCE || coll > ORC_ALL_GATHER || algo < ORC_RING || algo > ORC_PIPELINE)
+  if (coll < ORC_ALLREDUCE || coll > ORC_BROADCAST || algo < ORC_RING || algo > ORC_PIPELINE)
     return ORC_EINVAL;
   if (w0 > w1 || w1 > L || (w1 > w0 && !bufs)) return ORC_EINVAL;
   if (algo == ORC_PIPELINE && (S < 1 || M < 1 || S * M != P || M + 1 > MAX_SRC)) return ORC_EINVAL;
-  if (algo == ORC_RHD && coll != ORC_ALLREDUCE && (P & (P - 1))) return ORC_EUNSUPPORTED;
+  if ((coll == ORC_ROOT_REDUCE || coll == ORC_BROADCAST) && (root < 0 || root >= P)) return ORC_EINVAL;
+  if ((coll == ORC_ROOT_REDUCE || coll == ORC_BROADCAST) && algo != ORC_RHD) return ORC_EUNSUPPORTED;
   if (w1 > w0)
     for (int r = 0; r < P; ++r)
       if (!bufs[r]) return ORC_EINVAL;
@@ -807,12 +1028,14 @@ int orc_collective(int coll, int algo, int P, int S, int M, size_t loop_bytes, v
       if (coll != ORC_ALL_GATHER) ring_reduce_scatter(&R, L);
       if (coll != ORC_REDUCE_SCATTER) ring_all_gather(&R, L);
     } else if (algo == ORC_RHD) {
-      if (coll == ORC_ALLREDUCE)
-        rhd_allreduce(&R, L);
-      else if (coll == ORC_REDUCE_SCATTER)
-        rhd_reduce_scatter(&R, L);
-      else
-        rhd_all_gather(&R, L);
+      const int pow2 = (P & (P - 1)) == 0;
+      switch (coll) {
+        case ORC_ALLREDUCE: rhd_allreduce(&R, L); break;
+        case ORC_REDUCE_SCATTER: pow2 ? rhd_reduce_scatter(&R, L) : rhd_reduce_scatter_np2(&R, L); break;
+        case ORC_ALL_GATHER: pow2 ? rhd_all_gather(&R, L) : rhd_all_gather_np2(&R, L); break;
+        case ORC_ROOT_REDUCE: rhd_reduce(&R, L, root); break;
+        default: rhd_broadcast(&R, L, root); break;
+      }
     } else {
       size_t C = loop_elems(loop_bytes, dtype);
       for (size_t lb = 0; lb < L && !R.err; lb += C) {

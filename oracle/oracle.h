@@ -36,7 +36,7 @@ extern "C" {
 enum { ORC_FP32 = 0, ORC_FP16 = 1, ORC_BF16 = 2, ORC_INT32 = 3, ORC_INT8 = 4 };
 enum { ORC_SUM = 0, ORC_PROD = 1, ORC_MAX = 2, ORC_MIN = 3 };
 enum { ORC_RING = 0, ORC_RHD = 1, ORC_PIPELINE = 2 };
-enum { ORC_ALLREDUCE = 0, ORC_REDUCE_SCATTER = 1, ORC_ALL_GATHER = 2 };
+enum { ORC_ALLREDUCE = 0, ORC_REDUCE_SCATTER = 1, ORC_ALL_GATHER = 2, ORC_ROOT_REDUCE = 3, ORC_BROADCAST = 4 };
 
 /* action kinds of one step, as recorded in a trace */
 enum {
@@ -85,11 +85,13 @@ long orc_num_steps(int coll, int algo, int P, int S, int M, size_t L, int dtype,
  *   [first_step, last_step) run (pass 0, -1 for all); the trace, if given,
  *   receives up to trace_cap records and *trace_len the number produced.
  *   S, M describe the pipeline's servers and ranks per server (S*M == P);
- *   loop_bytes is the pipeline's per-loop slice (0 selects 32 MiB).
+ *   loop_bytes is the pipeline's per-loop slice (0 selects 32 MiB); root is
+ *   the root rank of Reduce and Broadcast (RHD only; others ignore it).
  */
-int orc_collective(int coll, int algo, int P, int S, int M, size_t loop_bytes, void* const* bufs,
-                   size_t L, size_t w0, size_t w1, int dtype, int op, long first_step,
-                   long last_step, orc_trace_t* trace, size_t trace_cap, size_t* trace_len);
+int orc_collective(int coll, int algo, int P, int S, int M, size_t loop_bytes, int root,
+                   void* const* bufs, size_t L, size_t w0, size_t w1, int dtype, int op,
+                   long first_step, long last_step, orc_trace_t* trace, size_t trace_cap,
+                   size_t* trace_len);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,12 @@ combines a received partial with a local block.
       balanced binary tree over v in natural order (pairs (2w, 2w+1) first)
   RHD order-preserving reduce-scatter, P = 2^k:
       tree pairing v with v + P/2 first, then v + P/4, ...
+  RHD stand-alone reduce-scatter, P not a power of two (shares in order
+  along 2^k virtual ranks, two-share ranks where the k-bit reversal of v
+  is below r): leaves X'_v = X_{s+1} op X_s for a two-share rank with
+  first share s, else X_s; tree pairing v with v + 2^k/2 first, ...
+  RHD Reduce to a root: part1 pairs (2i, 2i+1) keep on the root's
+  parity side: X'_v = X_partner op X_keeper; the same halving tree.
   pipeline (S servers x M ranks), block (s, m) of each loop:
       I_sigma = ((X_(sigma,0) op X_(sigma,1)) op ...) op X_(sigma,M-1)
       result  = ((I_{s+1} op I_{s+2}) op ...) op I_s
@@ -65,6 +71,56 @@ def rhd_reduce_scatter_value(dtype, op, xs):
         vals = [combine(dtype, op, vals[w + d], vals[w]) for w in range(d)]
         d //= 2
     return vals[0]
+
+
+def _bitrev(v, k):
+    return int(format(v, f"0{k}b")[::-1], 2) if k else 0
+
+
+def np2_share_layout(P):
+    """(k, first share of each virtual rank + end, two-share flags)."""
+    k = P.bit_length() - 1
+    pp = 1 << k
+    r = P - pp
+    two = [_bitrev(v, k) < r for v in range(pp)]
+    first, s = [], 0
+    for v in range(pp):
+        first.append(s)
+        s += 2 if two[v] else 1
+    return k, first + [s], two
+
+
+def _halving_tree(dtype, op, leaves):
+    vals = [x.copy() for x in leaves]
+    d = len(vals) // 2
+    while d >= 1:
+        vals = [combine(dtype, op, vals[w + d], vals[w]) for w in range(d)]
+        d //= 2
+    return vals[0]
+
+
+def rhd_reduce_scatter_np2_value(dtype, op, xs):
+    P = len(xs)
+    k, first, two = np2_share_layout(P)
+    leaves = [combine(dtype, op, xs[first[v] + 1], xs[first[v]]) if two[v] else xs[first[v]].copy()
+              for v in range(1 << k)]
+    return _halving_tree(dtype, op, leaves)
+
+
+def rhd_reduce_value(dtype, op, xs, root):
+    P = len(xs)
+    k = P.bit_length() - 1
+    pp = 1 << k
+    r = P - pp
+    odd = 1 if (root < 2 * r and root % 2) else 0
+    leaves = []
+    for v in range(pp):
+        if v < r:
+            keeper, partner = 2 * v + odd, 2 * v + 1 - odd
+            leaves.append(combine(dtype, op, xs[partner], xs[keeper]))
+        else:
+            leaves.append(xs[v + r].copy())
+    return _halving_tree(dtype, op, leaves)
 
 
 def pipeline_allreduce(dtype, op, xs, S, M, loop_elems):

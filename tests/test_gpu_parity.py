@@ -77,12 +77,36 @@ LS = [0, 1, 5, 1000, 3 * 4096 + 7, 50_001]
 @pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
 def test_parity(algo, coll, dtype):
     rng = np.random.default_rng(zlib.crc32(f"{algo}/{coll}/{dtype}".encode()))
-    Ps = [2, 3, 5, 8] if not (algo == "rhd" and coll != "allreduce") else [2, 4, 8]
+    Ps = [2, 3, 5, 8] if not (algo == "rhd" and coll != "allreduce") else [2, 4, 5, 6, 8]
     for op in OPS:
         for P in Ps:
             L = int(rng.choice(LS))
             check_case(algo, coll, dtype, op, P, L, seed=int(rng.integers(1 << 30)),
                        loop_bytes=(8192 if algo == "pipeline" else 0))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("coll", ["reduce", "broadcast"])
+def test_parity_rooted(coll, dtype):
+    """RHD Reduce / Broadcast from every root (the root's buffer for Reduce,
+    every buffer for Broadcast, bit for bit against the oracle)."""
+    for P in (2, 3, 5, 6, 8, 13):
+        L = 4096 * 2 + 37 * P
+        with hc.Comm(P, "rhd") as comm:
+            for root in range(P):
+                op = "max" if dtype in ("int8",) else "sum"
+                say(f"case rooted coll={coll} dtype={dtype} op={op} P={P} root={root} L={L}")
+                xs = make_inputs(dtype, op, P, L, seed=root)
+                dev = [to_dev(x, dtype) for x in xs]
+                if coll == "reduce":
+                    comm.reduce(dev, dtype, op, root=root)
+                else:
+                    comm.broadcast(dev, dtype, root=root)
+                torch.cuda.synchronize()
+                want = [x.copy() for x in xs]
+                oracle.run(coll, "rhd", want, dtype, op, root=root)
+                for r in ([root] if coll == "reduce" else range(P)):
+                    refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{coll} P={P} root={root} r={r}")
 
 
 @pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
@@ -133,6 +157,7 @@ def test_unaligned_buffers(dtype, phases):
 
 @pytest.mark.parametrize("algo,coll,P", [("ring", "allreduce", 8), ("rhd", "allreduce", 5),
                                          ("rhd", "allreduce", 8), ("rhd", "reduce_scatter", 8),
+                                         ("rhd", "reduce_scatter", 6), ("rhd", "all_gather", 7),
                                          ("pipeline", "allreduce", 8), ("ring", "all_gather", 6)])
 def test_step_by_step(algo, coll, P):
     """Every rank's whole buffer after every step equals the oracle's replay state."""

@@ -125,17 +125,34 @@ def simulate(items, nsteps, xs, dtype, op, *, sequential=False):
     return bufs
 
 
-CASES = [("ring", P, {}) for P in (2, 3, 5, 8)] + [("rhd", P, {}) for P in (2, 3, 5, 6, 8, 12)] + \
+CASES = [("ring", P, {}) for P in (2, 3, 5, 8)] + [("rhd", P, {}) for P in (2, 3, 5, 6, 7, 8, 11, 12, 13)] + \
         [("pipeline", 8, dict(S=2, M=4)), ("pipeline", 6, dict(S=3, M=2)), ("pipeline", 4, dict(S=4, M=1)),
          ("pipeline", 4, dict(S=1, M=4))]
+
+
+@pytest.mark.parametrize("P", [2, 3, 5, 6, 7, 8, 12, 13])
+@pytest.mark.parametrize("coll", ["reduce", "broadcast"])
+def test_library_rooted_schedule_matches_oracle(P, coll):
+    dtype = "bf16"
+    with hc.Comm(P, "rhd") as comm:
+        for root in range(P):
+            for L in (1, P + 1, 77):
+                xs = synth.rank_inputs("rhd_bf16_normal", P, L, seed=L + root)
+                items = comm.plan_items(coll, L, dtype, root=root)
+                nsteps = comm.plan_info(coll, L, dtype, root=root)["nsteps"]
+                assert nsteps == oracle.num_steps(coll, "rhd", P)
+                got = simulate(items, nsteps, xs, dtype, "sum")
+                want = [x.copy() for x in xs]
+                oracle.run(coll, "rhd", want, dtype, "sum", root=root)
+                ranks = [root] if coll == "reduce" else range(P)
+                for r in ranks:
+                    refops.assert_same(dtype, got[r], want[r], f"{coll} P={P} root={root} L={L} r={r}")
 
 
 @pytest.mark.parametrize("algo,P,kw", CASES)
 @pytest.mark.parametrize("coll", ["allreduce", "reduce_scatter", "all_gather"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_library_schedule_matches_oracle(algo, P, kw, coll, dtype):
-    if algo == "rhd" and coll != "allreduce" and P & (P - 1):
-        return
     loop_bytes = 96 * refops.np.dtype(refops.STORAGE[dtype]).itemsize if algo == "pipeline" else 0
     args = (P, algo, kw.get("S", 0), kw.get("M", 0), loop_bytes) if algo == "pipeline" else (P, algo)
     with hc.Comm(*args) as comm:
@@ -165,9 +182,10 @@ def test_validation_status_codes():
     assert lib.hbmc_comm_create(8, 0, 0, 0, 0, None) == 1
     assert lib.hbmc_comm_destroy(None) == 1
     with hc.Comm(5, "rhd") as c:
+        assert c.plan_info("reduce_scatter", 100, "fp32")["nsteps"] == 4
         with pytest.raises(hc.HbmcError) as e:
-            c.plan_info("reduce_scatter", 100, "fp32")
-        assert e.value.code == 2
+            c.plan_info("reduce", 100, "fp32", root=5)
+        assert e.value.code == 1
         with pytest.raises(hc.HbmcError) as e:
             c.plan_info("allreduce", 2 ** 63, "fp32")            # count * 4 overflows
         assert e.value.code == 1
@@ -185,9 +203,11 @@ def test_validation_status_codes():
         nulls = (ctypes.c_void_p * 4)(0x10000, None, 0x30000, 0x40000)
         assert lib.hbmc_allreduce(c._h, nulls, 16, 0, 0, None) == 1
         assert lib.hbmc_allreduce(c._h, arr, 0, 0, 0, None) == 0             # count 0: nothing to do
-        assert lib.hbmc_run_steps(c._h, 0, arr, 16, 0, 0, 3, 3, None) == 1    # empty step range
-        assert lib.hbmc_run_steps(c._h, 0, arr, 16, 0, 0, 0, 7, None) == 1    # past the last step
-        assert lib.hbmc_run_steps(c._h, 5, arr, 16, 0, 0, 0, 1, None) == 1    # bad collective
+        assert lib.hbmc_run_steps(c._h, 0, 0, arr, 16, 0, 0, 3, 3, None) == 1    # empty step range
+        assert lib.hbmc_run_steps(c._h, 0, 0, arr, 16, 0, 0, 0, 7, None) == 1    # past the last step
+        assert lib.hbmc_run_steps(c._h, 9, 0, arr, 16, 0, 0, 0, 1, None) == 1    # bad collective
+        assert lib.hbmc_reduce(c._h, arr, 16, 0, 0, 0, None) == 2               # ring: no Reduce
+        assert lib.hbmc_broadcast(c._h, arr, 16, 0, 0, None) == 2               # ring: no Broadcast
     with hc.Comm(1, "ring") as c:
         one = (ctypes.c_void_p * 1)(0x10000)
         assert lib.hbmc_allreduce(c._h, one, 16, 0, 0, None) == 0            # one rank: nothing to do
@@ -220,11 +240,13 @@ def test_graph_validation_without_device():
     with hc.Comm(4, "ring") as c, hc.Comm(5, "rhd") as r5:
         arr = (ctypes.c_void_p * 4)(0x10000, 0x20000, 0x30000, 0x40000)
         alias = (ctypes.c_void_p * 4)(0x10000, 0x10000, 0x30000, 0x40000)
-        assert lib.hbmc_graph_add(g, c._h, 0, alias, 16, 0, 0) == 1          # aliased buffers
-        assert lib.hbmc_graph_add(g, c._h, 0, arr, 16, 0, 7) == 1            # bad op
-        assert lib.hbmc_graph_add(g, None, 0, arr, 16, 0, 0) == 1            # no communicator
+        assert lib.hbmc_graph_add(g, c._h, 0, 0, alias, 16, 0, 0) == 1       # aliased buffers
+        assert lib.hbmc_graph_add(g, c._h, 0, 0, arr, 16, 0, 7) == 1         # bad op
+        assert lib.hbmc_graph_add(g, None, 0, 0, arr, 16, 0, 0) == 1         # no communicator
         five = (ctypes.c_void_p * 5)(0x10000, 0x20000, 0x30000, 0x40000, 0x50000)
-        assert lib.hbmc_graph_add(g, r5._h, 1, five, 16, 0, 0) == 2          # RHD RS, P=5
-        assert lib.hbmc_graph_add(g, c._h, 0, arr, 16, 0, 0) == 0            # host-only checks pass
+        assert lib.hbmc_graph_add(g, r5._h, 3, 5, five, 16, 0, 0) == 1       # root out of range
+        assert lib.hbmc_graph_add(g, c._h, 3, 0, arr, 16, 0, 0) == 2         # ring Reduce
+        assert lib.hbmc_graph_add(g, r5._h, 1, 0, five, 16, 0, 0) == 0       # RHD RS, P=5
+        assert lib.hbmc_graph_add(g, c._h, 0, 0, arr, 16, 0, 0) == 0         # host-only checks pass
         assert lib.hbmc_graph_launch(g, None) == 1                          # not built yet
     assert lib.hbmc_graph_destroy(g) == 0

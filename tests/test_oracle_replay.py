@@ -302,9 +302,13 @@ def test_window_and_step_range_replay(algo, coll):
             refops.assert_same(dtype, part[r], full[r], f"cut at {cut}")
 
 
-def test_rhd_non_power_of_two_standalone_is_unsupported():
-    xs = inputs("fp32", 5, 10)
-    for coll in ("reduce_scatter", "all_gather"):
+def test_rooted_collectives_need_rhd_and_a_valid_root():
+    xs = inputs("fp32", 6, 10)
+    for algo in ("ring", "pipeline"):
         with pytest.raises(oracle.OracleError) as e:
-            replay(coll, "rhd", xs, "fp32", "sum")
+            oracle.run("reduce", algo, [x.copy() for x in xs], "fp32", "sum", S=2, M=3)
         assert e.value.code == oracle.EUNSUPPORTED
+    for root in (-1, 6):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.run("broadcast", "rhd", [x.copy() for x in xs], "fp32", "sum", root=root)
+        assert e.value.code == oracle.EINVAL
