@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2, "int32": 3, "int8": 4}
 OP = {"sum": 0, "prod": 1, "max": 2, "min": 3}
-ALGO = {"ring": 0, "rhd": 1, "pipeline": 2}
+ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "flat": 3, "tree": 4, "hier": 5}
 COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 KIND = {0: "copy", 1: "reduce", 2: "fold", 3: "fold_recv"}
 NP_STORAGE = {"fp32": np.float32, "fp16": np.float16, "bf16": np.uint16,

@@ -33,6 +33,12 @@
  *    after the last ring step one more intra-server pass.  Reduce-scatter is
  *    the time reverse: one intra-server step, then S-1 ring steps that each
  *    fold the server's M contributions into the received partial.
+ *  - Flat, tree and hierarchical AllReduce ([TOPO] "AllReduce算法实现": Flat
+ *    below a size threshold has every device talk directly to the root; Tree
+ *    reduces from the leaves of a K-ary tree to the root and broadcasts back
+ *    down, 2 log_K N rounds; [PIPE] "与其它分级算法的关系": the non-pipelined
+ *    hierarchical AllReduce is an intra-server reduce-scatter, an
+ *    inter-server AllReduce and an intra-server all-gather).
  *  - Element ops: sum / prod / max / min; binary16 and bfloat16 are widened
  *    to binary32, combined, and rounded back to nearest even after every
  *    operation; integers wrap ([RING-RHD], section "Ascend950的AIVAICPU通信
@@ -963,6 +969,102 @@ static void pipe_all_gather(run_t* R, const pipe_t* pl) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Flat, tree and hierarchical AllReduce                                      */
+
+/* Flat: rank 0 receives every rank's vector and reduces them in rank order,
+ * then sends the result to every rank. */
+static void flat_allreduce(run_t* R, size_t L) {
+  int P = R->P, all[64];
+  for (int r = 0; r < P; ++r) all[r] = r;
+  step_begin(R);
+  add_action(R, ORC_FOLD, 0, all, P, 0, L);
+  step_end(R);
+  step_begin(R);
+  for (int r = 1; r < P; ++r) {
+    int root = 0;
+    add_action(R, ORC_COPY, r, &root, 1, 0, L);
+  }
+  step_end(R);
+}
+
+/* Tree: K-ary tree in heap order (parent of i is (i-1)/K).  Reduce rounds go
+ * from the deepest level of parents up to the root, each parent folding its
+ * own vector and its children's (in rank order); broadcast rounds go back
+ * down, each parent copying the result to its children. */
+static int tree_depth(int i, int K) {
+  int d = 0;
+  while (i > 0) {
+    i = (i - 1) / K;
+    ++d;
+  }
+  return d;
+}
+
+static void tree_allreduce(run_t* R, size_t L, int K) {
+  int P = R->P, maxd = tree_depth(P - 1, K);
+  for (int lvl = maxd - 1; lvl >= 0; --lvl) {
+    step_begin(R);
+    for (int p = 0; p < P; ++p) {
+      if (tree_depth(p, K) != lvl || K * p + 1 >= P) continue;
+      int src[MAX_SRC], n = 0;
+      src[n++] = p;
+      for (int c = K * p + 1; c <= K * p + K && c < P; ++c) src[n++] = c;
+      add_action(R, ORC_FOLD, p, src, n, 0, L);
+    }
+    step_end(R);
+  }
+  for (int lvl = 0; lvl < maxd; ++lvl) {
+    step_begin(R);
+    for (int p = 0; p < P; ++p) {
+      if (tree_depth(p, K) != lvl) continue;
+      for (int c = K * p + 1; c <= K * p + K && c < P; ++c) add_action(R, ORC_COPY, c, &p, 1, 0, L);
+    }
+    step_end(R);
+  }
+}
+
+/* Hierarchical (not pipelined), S servers x M ranks, rank g = s*M + m:
+ * (1) intra-server reduce-scatter by full mesh: (s,m) folds block m (M-way
+ *     ceiling split) of its server's M vectors, in local-rank order;
+ * (2) inter-server ring AllReduce of block m among (0,m) .. (S-1,m), with the
+ *     ring's S-way ceiling split of the block and its step rules;
+ * (3) intra-server all-gather by full mesh: (s,m) sends block m to its peers. */
+static void hier_allreduce(run_t* R, size_t L, int S, int M) {
+  int src[MAX_SRC];
+  step_begin(R);
+  for (int s = 0; s < S; ++s)
+    for (int m = 0; m < M; ++m) {
+      for (int l = 0; l < M; ++l) src[l] = s * M + l;
+      size_t b = seg_begin(L, (size_t)M, (size_t)m), e = seg_begin(L, (size_t)M, (size_t)m + 1);
+      add_action(R, ORC_FOLD, s * M + m, src, M, b, e - b);
+    }
+  step_end(R);
+  for (int phase = 0; phase < 2; ++phase)
+    for (int t = 0; t < S - 1; ++t) {
+      step_begin(R);
+      for (int m = 0; m < M; ++m) {
+        size_t b0 = seg_begin(L, (size_t)M, (size_t)m), n = seg_begin(L, (size_t)M, (size_t)m + 1) - b0;
+        for (int i = 0; i < S; ++i) { /* server i sends to server i+1 */
+          int c = phase == 0 ? imod((long)i - 1 - t, S) : imod((long)i - t, S);
+          size_t b = b0 + seg_begin(n, (size_t)S, (size_t)c), e = b0 + seg_begin(n, (size_t)S, (size_t)c + 1);
+          int from = i * M + m, to = ((i + 1) % S) * M + m;
+          add_action(R, phase == 0 ? ORC_REDUCE : ORC_COPY, to, &from, 1, b, e - b);
+        }
+      }
+      step_end(R);
+    }
+  step_begin(R);
+  for (int s = 0; s < S; ++s)
+    for (int m = 0; m < M; ++m) {
+      int g = s * M + m;
+      size_t b = seg_begin(L, (size_t)M, (size_t)m), e = seg_begin(L, (size_t)M, (size_t)m + 1);
+      for (int l = 0; l < M; ++l)
+        if (l != m) add_action(R, ORC_COPY, s * M + l, &g, 1, b, e - b);
+    }
+  step_end(R);
+}
+
+/* ------------------------------------------------------------------------ */
 /* entry points                                                               */
 
 static size_t loop_elems(size_t loop_bytes, int dtype) {
@@ -988,6 +1090,13 @@ long orc_num_steps(int coll, int algo, int P, int S, int M, size_t L, int dtype,
       default: return k + (pow2 ? 0 : 1);
     }
   }
+  if (algo == ORC_FLAT) return 2;
+  if (algo == ORC_TREE) {
+    int d = 0;
+    for (int i = P - 1; i > 0; i = (i - 1) / (M < 2 ? 2 : M)) ++d;
+    return 2 * d;
+  }
+  if (algo == ORC_HIER) return 2 * S;
   long half = algo == ORC_RING ? P - 1 : S;
   return coll == ORC_ALLREDUCE ? 2 * half : half;
 }
@@ -998,10 +1107,13 @@ int orc_collective(int coll, int algo, int P, int S, int M, size_t loop_bytes, i
                    size_t* trace_len) {
   if (trace_len) *trace_len = 0;
   if (P < 1 || P > 64 || esize(dtype) == 0 || op < ORC_SUM || op > ORC_MIN) return ORC_EINVAL;
-  if (coll < ORC_ALLREDUCE || coll > ORC_BROADCAST || algo < ORC_RING || algo > ORC_PIPELINE)
+  if (coll < ORC_ALLREDUCE || coll > ORC_BROADCAST || algo < ORC_RING || algo > ORC_HIER)
     return ORC_EINVAL;
   if (w0 > w1 || w1 > L || (w1 > w0 && !bufs)) return ORC_EINVAL;
-  if (algo == ORC_PIPELINE && (S < 1 || M < 1 || S * M != P || M + 1 > MAX_SRC)) return ORC_EINVAL;
+  if ((algo == ORC_PIPELINE || algo == ORC_HIER) && (S < 1 || M < 1 || S * M != P || M + 1 > MAX_SRC))
+    return ORC_EINVAL;
+  if (algo == ORC_TREE && (M < 2 || M + 1 > MAX_SRC)) return ORC_EINVAL;
+  if (algo >= ORC_FLAT && coll != ORC_ALLREDUCE) return ORC_EUNSUPPORTED;
   if ((coll == ORC_ROOT_REDUCE || coll == ORC_BROADCAST) && (root < 0 || root >= P)) return ORC_EINVAL;
   if ((coll == ORC_ROOT_REDUCE || coll == ORC_BROADCAST) && algo != ORC_RHD) return ORC_EUNSUPPORTED;
   if (w1 > w0)
@@ -1036,6 +1148,12 @@ int orc_collective(int coll, int algo, int P, int S, int M, size_t loop_bytes, i
         case ORC_ROOT_REDUCE: rhd_reduce(&R, L, root); break;
         default: rhd_broadcast(&R, L, root); break;
       }
+    } else if (algo == ORC_FLAT) {
+      flat_allreduce(&R, L);
+    } else if (algo == ORC_TREE) {
+      tree_allreduce(&R, L, M);
+    } else if (algo == ORC_HIER) {
+      hier_allreduce(&R, L, S, M);
     } else {
       size_t C = loop_elems(loop_bytes, dtype);
       for (size_t lb = 0; lb < L && !R.err; lb += C) {

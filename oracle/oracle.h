@@ -35,7 +35,7 @@ extern "C" {
 /* element types, reduce ops, algorithms, collectives (numeric codes) */
 enum { ORC_FP32 = 0, ORC_FP16 = 1, ORC_BF16 = 2, ORC_INT32 = 3, ORC_INT8 = 4 };
 enum { ORC_SUM = 0, ORC_PROD = 1, ORC_MAX = 2, ORC_MIN = 3 };
-enum { ORC_RING = 0, ORC_RHD = 1, ORC_PIPELINE = 2 };
+enum { ORC_RING = 0, ORC_RHD = 1, ORC_PIPELINE = 2, ORC_FLAT = 3, ORC_TREE = 4, ORC_HIER = 5 };
 enum { ORC_ALLREDUCE = 0, ORC_REDUCE_SCATTER = 1, ORC_ALL_GATHER = 2, ORC_ROOT_REDUCE = 3, ORC_BROADCAST = 4 };
 
 /* action kinds of one step, as recorded in a trace */
@@ -84,7 +84,8 @@ long orc_num_steps(int coll, int algo, int P, int S, int M, size_t L, int dtype,
  *   (w0 = 0, w1 = L replays everything); only steps with index in
  *   [first_step, last_step) run (pass 0, -1 for all); the trace, if given,
  *   receives up to trace_cap records and *trace_len the number produced.
- *   S, M describe the pipeline's servers and ranks per server (S*M == P);
+ *   S, M describe the pipeline's (and the hierarchical AllReduce's) servers
+ *   and ranks per server (S*M == P); for the tree M is the arity K (>= 2);
  *   loop_bytes is the pipeline's per-loop slice (0 selects 32 MiB); root is
  *   the root rank of Reduce and Broadcast (RHD only; others ignore it).
  */

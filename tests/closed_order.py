@@ -17,6 +17,12 @@ combines a received partial with a local block.
   first share s, else X_s; tree pairing v with v + 2^k/2 first, ...
   RHD Reduce to a root: part1 pairs (2i, 2i+1) keep on the root's
   parity side: X'_v = X_partner op X_keeper; the same halving tree.
+  Flat AllReduce: left fold in rank order X_0 op X_1 op ... op X_{P-1}.
+  K-ary tree AllReduce (heap order): value(p) = fold of X_p, value(c_1),
+  ..., value(c_K) over its children in rank order; the root's value.
+  hierarchical AllReduce (S x M): element in block m (M-way split), and in
+  sub-segment c of that block's S-way split: I_sigma = fold over l of
+  X_(sigma,l); result ((I_{c+1} op I_{c+2}) op ...) op I_c.
   pipeline (S servers x M ranks), block (s, m) of each loop:
       I_sigma = ((X_(sigma,0) op X_(sigma,1)) op ...) op X_(sigma,M-1)
       result  = ((I_{s+1} op I_{s+2}) op ...) op I_s
@@ -154,3 +160,40 @@ def left_fold(dtype, op, xs):
     for x in xs[1:]:
         acc = combine(dtype, op, acc, x)
     return acc
+
+
+def tree_allreduce(dtype, op, xs, K):
+    P = len(xs)
+
+    def value(p):
+        acc = xs[p].copy()
+        for c in range(K * p + 1, min(K * p + K, P - 1) + 1):
+            acc = combine(dtype, op, acc, value(c))
+        return acc
+
+    return value(0)
+
+
+def hier_allreduce(dtype, op, xs, S, M):
+    L = xs[0].size
+    out = np.empty(L, STORAGE[dtype])
+    for m in range(M):
+        b0, e0 = seg_bounds(L, M, m)
+        n = e0 - b0
+        for c in range(S):
+            b, e = seg_bounds(n, S, c)
+            b, e = b + b0, e + b0
+            if b == e:
+                continue
+
+            def intra(sigma):
+                acc = xs[sigma * M][b:e].copy()
+                for l in range(1, M):
+                    acc = combine(dtype, op, acc, xs[sigma * M + l][b:e])
+                return acc
+
+            acc = intra((c + 1) % S)
+            for i in range(2, S + 1):
+                acc = combine(dtype, op, acc, intra((c + i) % S))
+            out[b:e] = acc
+    return out
