@@ -27,18 +27,32 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
     if (v == "ring") a = HBMC_ALGO_RING;
     else if (v == "rhd" || v == "H-D_R") a = HBMC_ALGO_RHD;
     else if (v == "pipeline") a = HBMC_ALGO_PIPELINE;
+    else if (v == "flat") a = HBMC_ALGO_FLAT;
+    else if (v == "tree") a = HBMC_ALGO_TREE;
+    else if (v == "hier") a = HBMC_ALGO_HIER;
     else return HBMC_ERR_INVALID_ARG;
   }
-  if (a < HBMC_ALGO_RING || a > HBMC_ALGO_PIPELINE) return HBMC_ERR_INVALID_ARG;
   Topology t;
   t.P = nranks;
-  t.algo = static_cast<Algo>(a);
-  if (a == HBMC_ALGO_PIPELINE) {
-    if (servers < 1 || ranks_per_server < 1 || servers * ranks_per_server != nranks)
-      return HBMC_ERR_INVALID_ARG;
-    t.S = servers;
-    t.M = ranks_per_server;
-    t.loop_bytes = loop_bytes;
+  switch (a) {
+    case HBMC_ALGO_RING: t.algo = kRing; break;
+    case HBMC_ALGO_RHD: t.algo = kRhd; break;
+    case HBMC_ALGO_FLAT: t.algo = kFlat; break;
+    case HBMC_ALGO_TREE:
+      t.algo = kTree;
+      t.K = ranks_per_server == 0 ? 2 : ranks_per_server;
+      if (t.K < 2 || t.K > kMaxRanks) return HBMC_ERR_INVALID_ARG;
+      break;
+    case HBMC_ALGO_PIPELINE:
+    case HBMC_ALGO_HIER:
+      t.algo = a == HBMC_ALGO_PIPELINE ? kPipeline : kHier;
+      if (servers < 1 || ranks_per_server < 1 || servers * ranks_per_server != nranks)
+        return HBMC_ERR_INVALID_ARG;
+      t.S = servers;
+      t.M = ranks_per_server;
+      t.loop_bytes = loop_bytes;
+      break;
+    default: return HBMC_ERR_INVALID_ARG;
   }
   hbmc_comm* c = new (std::nothrow) hbmc_comm;
   if (!c) return HBMC_ERR_NOMEM;
@@ -143,7 +157,7 @@ const char* hbmc_status_string(hbmc_status_t status) {
   switch (status) {
     case HBMC_OK: return "success";
     case HBMC_ERR_INVALID_ARG: return "invalid argument";
-    case HBMC_ERR_UNSUPPORTED: return "unsupported (Reduce and Broadcast exist for the RHD algorithm only)";
+    case HBMC_ERR_UNSUPPORTED: return "unsupported collective for this algorithm (Reduce / Broadcast: RHD only; Flat, tree, hierarchical: AllReduce only)";
     case HBMC_ERR_HIP: return "HIP error";
     case HBMC_ERR_NOMEM: return "out of memory";
     default: return "unknown status";

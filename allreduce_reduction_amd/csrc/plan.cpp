@@ -28,6 +28,15 @@
 // 2^k-way split + gather to the root; Broadcast = distance halving from the
 // root, then one copy to each part1 partner.
 //
+// Flat, tree and hierarchical AllReduce ([TOPO] "AllReduce算法实现"; [PIPE]
+// "与其它分级算法的关系"): Flat folds all P vectors at rank 0 in rank order and
+// copies the result to every rank (one read, P-1 writes); the tree reduces a
+// heap-ordered K-ary tree level by level (each parent folds itself and its
+// children in rank order) and copies back down; the hierarchical AllReduce is
+// an intra-server full-mesh reduce-scatter of block m onto (s,m), a ring
+// AllReduce of block m over the servers, and an intra-server copy of block m
+// from (s,m) to its peers.
+//
 // Pipeline ([PIPE] "AllGather 算子的 Pipeline 时序编排", "Rank0 视角的传输任务编排",
 // Table 1): rank g = s*M + m; each loop (slice of at most loop_bytes) is split
 // into P blocks.  Reduce-scatter: one intra-server step in which (s,m) folds
@@ -367,6 +376,84 @@ void pipeline(const Topology& t, Coll coll, uint64_t L, uint32_t esize, Builder&
   }
 }
 
+// ---------------------------------------------------------------- flat / tree / hier
+void flat(const Topology& t, uint64_t L, Builder& B) {
+  std::vector<int> all, rest;
+  for (int r = 0; r < t.P; ++r) {
+    all.push_back(r);
+    if (r) rest.push_back(r);
+  }
+  Step& red = B.open(kFold);
+  Builder::add(red, 0, L, all, {0});
+  Step& out = B.open(kCopy);
+  Builder::add(out, 0, L, {0}, rest);
+}
+
+void tree(const Topology& t, uint64_t L, Builder& B) {
+  const int P = t.P, K = t.K;
+  std::vector<int> level(P, 0);
+  for (int i = 1; i < P; ++i) level[i] = level[(i - 1) / K] + 1;
+  const int height = level[P - 1];
+  auto children = [&](int p) {
+    std::vector<int> c;
+    for (int q = K * p + 1; q <= K * p + K && q < P; ++q) c.push_back(q);
+    return c;
+  };
+  for (int lvl = height - 1; lvl >= 0; --lvl) {
+    Step& st = B.open(kFold);
+    for (int p = 0; p < P; ++p) {
+      if (level[p] != lvl) continue;
+      std::vector<int> src{p}, c = children(p);
+      if (c.empty()) continue;
+      src.insert(src.end(), c.begin(), c.end());
+      Builder::add(st, 0, L, src, {p});
+    }
+  }
+  for (int lvl = 0; lvl < height; ++lvl) {
+    Step& st = B.open(kCopy);
+    for (int p = 0; p < P; ++p)
+      if (level[p] == lvl) Builder::add(st, 0, L, {p}, children(p));
+  }
+}
+
+void hier(const Topology& t, uint64_t L, Builder& B) {
+  const int S = t.S, M = t.M;
+  auto g = [M](int s, int m) { return s * M + m; };
+  Split blk(L, M);
+  Step& rs = B.open(kFold);
+  for (int s = 0; s < S; ++s)
+    for (int m = 0; m < M; ++m) {
+      if (M == 1) continue;  // a fold of one block onto itself is no work
+      std::vector<int> src;
+      for (int l = 0; l < M; ++l) src.push_back(g(s, l));
+      Builder::add(rs, blk.at(m), blk.at(m + 1), src, {g(s, m)});
+    }
+  for (int phase = 0; phase < 2; ++phase)
+    for (int step = 0; step < S - 1; ++step) {
+      Step& st = B.open(phase == 0 ? kRecvFold : kCopy);
+      for (int m = 0; m < M; ++m) {
+        const uint64_t b0 = blk.at(m);
+        Split sub(blk.at(m + 1) - b0, S);
+        for (int s = 0; s < S; ++s) {  // receiver (s, m)
+          const int c = phase == 0 ? wrap(s - step - 2, S) : wrap(s - 1 - step, S);
+          const int from = g(wrap(s - 1, S), m);
+          if (phase == 0)
+            Builder::add(st, b0 + sub.at(c), b0 + sub.at(c + 1), {from, g(s, m)}, {g(s, m)});
+          else
+            Builder::add(st, b0 + sub.at(c), b0 + sub.at(c + 1), {from}, {g(s, m)});
+        }
+      }
+    }
+  Step& ag = B.open(kCopy);
+  for (int s = 0; s < S; ++s)
+    for (int m = 0; m < M; ++m) {
+      std::vector<int> peers;
+      for (int l = 0; l < M; ++l)
+        if (l != m) peers.push_back(g(s, l));
+      Builder::add(ag, blk.at(m), blk.at(m + 1), {g(s, m)}, peers);
+    }
+}
+
 // ---------------------------------------------------------------- checks
 // No two items of a step may touch overlapping ranges of one rank where
 // either writes; within an item a destination may only be read on its own
@@ -403,9 +490,13 @@ BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint
   *out = Schedule{};
   if (topo.P < 1 || topo.P > kMaxRanks || esize == 0) return kBadArg;
   if (coll < kAllReduce || coll > kBroadcast) return kBadArg;
-  if (topo.algo == kPipeline && (topo.S < 1 || topo.M < 1 || topo.S * topo.M != topo.P))
+  if ((topo.algo == kPipeline || topo.algo == kHier) &&
+      (topo.S < 1 || topo.M < 1 || topo.S * topo.M != topo.P))
     return kBadArg;
+  if (topo.algo == kTree && (topo.K < 2 || topo.K > kMaxRanks)) return kBadArg;
   const bool rooted = coll == kReduce || coll == kBroadcast;
+  if ((topo.algo == kFlat || topo.algo == kTree || topo.algo == kHier) && coll != kAllReduce)
+    return kUnsupported;
   if (rooted && (root < 0 || root >= topo.P)) return kBadArg;
   if (rooted && topo.algo != kRhd) return kUnsupported;
   const bool pow2 = (topo.P & (topo.P - 1)) == 0;
@@ -425,19 +516,22 @@ BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint
         rhd_unordered_np2(topo, coll, count, B);
       break;
     case kPipeline: pipeline(topo, coll, count, esize, B, out); break;
+    case kFlat: flat(topo, count, B); break;
+    case kTree: tree(topo, count, B); break;
+    case kHier: hier(topo, count, B); break;
     default: return kBadArg;
   }
 
   std::vector<uint64_t> recv(topo.P, 0);
   for (Step& st : out->steps) {
-    bool first = true;
+    bool first = true, mixed = false;
     for (const Item& it : st.items) {
       if (first) {
         st.nsrc = it.nsrc;
         st.ndst = it.ndst;
         first = false;
       } else if (it.nsrc != st.nsrc || it.ndst != st.ndst) {
-        return kBadArg;  // the launcher relies on one item shape per step
+        mixed = true;  // items of different shapes: the kernel reads each item's counts
       }
       st.hbm_bytes += uint64_t(it.nsrc + it.ndst) * it.count * esize;
       st.max_count = std::max(st.max_count, it.count);
@@ -447,6 +541,7 @@ BuildStatus build_schedule(const Topology& topo, Coll coll, uint64_t count, uint
         recv[it.rank[d]] += uint64_t(others) * it.count * esize;
       }
     }
+    if (mixed) st.nsrc = st.ndst = 0;
     if (!step_is_race_free(st)) return kBadArg;
     out->hbm_bytes += st.hbm_bytes;
   }

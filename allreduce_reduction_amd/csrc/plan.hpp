@@ -11,7 +11,7 @@ namespace hbmc {
 constexpr int kMaxRanks = 64;
 
 enum Mode : int32_t { kCopy = 0, kFold = 1, kRecvFold = 2 };
-enum Algo : int32_t { kRing = 0, kRhd = 1, kPipeline = 2 };
+enum Algo : int32_t { kRing = 0, kRhd = 1, kPipeline = 2, kFlat = 4, kTree = 5, kHier = 6 };
 enum Coll : int32_t { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2, kReduce = 3, kBroadcast = 4 };
 
 // One unit of work: every destination's range [begin, begin+count) receives
@@ -24,7 +24,7 @@ struct Item {
 
 struct Step {
   Mode mode = kCopy;
-  int32_t nsrc = 0, ndst = 0;  // identical for every item of the step
+  int32_t nsrc = 0, ndst = 0;  // shared by every item of the step; 0 when items differ
   std::vector<Item> items;     // items with count == 0 are dropped
   uint64_t hbm_bytes = 0;      // (nsrc + ndst) * count * esize summed over items
   uint64_t max_count = 0;
@@ -33,7 +33,8 @@ struct Step {
 struct Topology {
   int P = 1;
   Algo algo = kRing;
-  int S = 1, M = 1;          // pipeline servers x ranks per server
+  int S = 1, M = 1;          // pipeline / hierarchical servers x ranks per server
+  int K = 2;                 // tree arity
   uint64_t loop_bytes = 0;   // pipeline slice; 0 -> 32 MiB
 };
 

@@ -43,7 +43,9 @@ typedef enum {
   HBMC_OK = 0,
   HBMC_ERR_INVALID_ARG = 1, /* null / aliased / misaligned buffers, bad P, count*e overflow,
                                S*M != P, enum out of range, step range out of bounds      */
-  HBMC_ERR_UNSUPPORTED = 2, /* Reduce / Broadcast with an algorithm other than RHD          */
+  HBMC_ERR_UNSUPPORTED = 2, /* collective not offered by the algorithm: Reduce / Broadcast
+                               other than RHD; anything but AllReduce for Flat, tree,
+                               hierarchical                                               */
   HBMC_ERR_HIP = 3,         /* a HIP call or kernel launch failed                          */
   HBMC_ERR_NOMEM = 4        /* host or device allocation failed                            */
 } hbmc_status_t;
@@ -61,10 +63,25 @@ typedef enum { HBMC_SUM = 0, HBMC_PROD = 1, HBMC_MAX = 2, HBMC_MIN = 3 } hbmc_op
  * RHD: [RHD] "算法描述" and Table 1 (non-power-of-two P merges the first 2r
  * ranks into r, r = P - 2^floor(log2 P), and restores them at the end).
  * PIPELINE: [PIPE] -- S servers x M ranks, inter-server ring, intra-server
- * full mesh, sliced into loops.  ENV: take the algorithm from the environment
- * variable HBMC_ALGO ("ring", "rhd" or "H-D_R", "pipeline"), the way the
- * pages' HCCL_ALGO selects an algorithm ([RHD] "RHD 在 HCCL 中的定位与启用方式"). */
-typedef enum { HBMC_ALGO_RING = 0, HBMC_ALGO_RHD = 1, HBMC_ALGO_PIPELINE = 2, HBMC_ALGO_ENV = 3 } hbmc_algo_t;
+ * full mesh, sliced into loops.  FLAT: every rank talks directly to rank 0,
+ * which reduces and sends the result back ([TOPO] "AllReduce算法实现").
+ * TREE: K-ary tree in heap order, reduce up then broadcast down, 2 x height
+ * steps ([TOPO] "AllReduce算法实现").  HIER: S servers x M ranks,
+ * intra-server reduce-scatter, inter-server ring AllReduce, intra-server
+ * all-gather, not pipelined ([PIPE] "与其它分级算法的关系").  FLAT, TREE and
+ * HIER offer AllReduce only.  ENV: take the algorithm from the environment
+ * variable HBMC_ALGO ("ring", "rhd" or "H-D_R", "pipeline", "flat", "tree",
+ * "hier"), the way the pages' HCCL_ALGO selects an algorithm ([RHD] "RHD 在
+ * HCCL 中的定位与启用方式"). */
+typedef enum {
+  HBMC_ALGO_RING = 0,
+  HBMC_ALGO_RHD = 1,
+  HBMC_ALGO_PIPELINE = 2,
+  HBMC_ALGO_ENV = 3,
+  HBMC_ALGO_FLAT = 4,
+  HBMC_ALGO_TREE = 5,
+  HBMC_ALGO_HIER = 6
+} hbmc_algo_t;
 
 typedef enum {
   HBMC_COLL_ALLREDUCE = 0,
@@ -76,11 +93,13 @@ typedef enum {
 
 /*
  * Create a communicator of `nranks` logical ranks (1..64) using `algo`.
- * For HBMC_ALGO_PIPELINE, servers * ranks_per_server must equal nranks and
- * loop_bytes is the per-loop slice ([PIPE] "源码中的流水执行印证": the
- * executor slices the data into loops bounded by its buffer limits); 0 selects
- * 32 MiB.  Other algorithms ignore servers, ranks_per_server and loop_bytes.
- * Touches no device state.  *out receives the handle.
+ * For HBMC_ALGO_PIPELINE and HBMC_ALGO_HIER, servers * ranks_per_server must
+ * equal nranks; for the pipeline loop_bytes is the per-loop slice ([PIPE]
+ * "源码中的流水执行印证": the executor slices the data into loops bounded by
+ * its buffer limits), 0 selecting 32 MiB.  For HBMC_ALGO_TREE,
+ * ranks_per_server is the arity K (2..64; 0 selects 2).  Other algorithms
+ * ignore servers, ranks_per_server and loop_bytes.  Touches no device state.
+ * *out receives the handle.
  */
 hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_per_server,
                                size_t loop_bytes, hbmc_comm_t* out);

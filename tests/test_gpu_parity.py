@@ -85,6 +85,30 @@ def test_parity(algo, coll, dtype):
                        loop_bytes=(8192 if algo == "pipeline" else 0))
 
 
+VARIANT_COMMS = [("flat", P, (P, "flat"), {}) for P in (2, 5, 8, 16)] + \
+    [("tree", P, (P, "tree", 0, K), dict(M=K)) for P, K in ((7, 2), (13, 3), (16, 4), (32, 2))] + \
+    [("hier", S * M, (S * M, "hier", S, M), dict(S=S, M=M)) for S, M in ((2, 4), (4, 8), (3, 2), (4, 1))]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_parity_variants(dtype):
+    """Flat, tree and hierarchical AllReduce against the oracle, every op."""
+    rng = np.random.default_rng(zlib.crc32(dtype.encode()))
+    for algo, P, args, kw in VARIANT_COMMS:
+        with hc.Comm(*args) as comm:
+            for op in OPS:
+                L = int(rng.choice(LS))
+                say(f"case variant algo={algo} {kw} dtype={dtype} op={op} P={P} L={L}")
+                xs = make_inputs(dtype, op, P, L, seed=L + P)
+                dev = [to_dev(x, dtype) for x in xs]
+                comm.allreduce(dev, dtype, op)
+                torch.cuda.synchronize()
+                want = [x.copy() for x in xs]
+                oracle.run("allreduce", algo, want, dtype, op, **kw)
+                for r in range(P):
+                    refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{algo} {kw} rank {r}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("coll", ["reduce", "broadcast"])
 def test_parity_rooted(coll, dtype):

@@ -126,6 +126,8 @@ def simulate(items, nsteps, xs, dtype, op, *, sequential=False):
 
 
 CASES = [("ring", P, {}) for P in (2, 3, 5, 8)] + [("rhd", P, {}) for P in (2, 3, 5, 6, 7, 8, 11, 12, 13)] + \
+        [("flat", P, {}) for P in (2, 5, 8)] + [("tree", P, dict(K=K)) for P in (3, 8, 13) for K in (2, 3)] + \
+        [("hier", 8, dict(S=2, M=4)), ("hier", 6, dict(S=3, M=2)), ("hier", 4, dict(S=4, M=1))] + \
         [("pipeline", 8, dict(S=2, M=4)), ("pipeline", 6, dict(S=3, M=2)), ("pipeline", 4, dict(S=4, M=1)),
          ("pipeline", 4, dict(S=1, M=4))]
 
@@ -153,8 +155,15 @@ def test_library_rooted_schedule_matches_oracle(P, coll):
 @pytest.mark.parametrize("coll", ["allreduce", "reduce_scatter", "all_gather"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_library_schedule_matches_oracle(algo, P, kw, coll, dtype):
+    if algo in ("flat", "tree", "hier") and coll != "allreduce":
+        return
     loop_bytes = 96 * refops.np.dtype(refops.STORAGE[dtype]).itemsize if algo == "pipeline" else 0
-    args = (P, algo, kw.get("S", 0), kw.get("M", 0), loop_bytes) if algo == "pipeline" else (P, algo)
+    if algo in ("pipeline", "hier"):
+        args = (P, algo, kw["S"], kw["M"], loop_bytes)
+    elif algo == "tree":
+        args = (P, algo, 0, kw["K"])
+    else:
+        args = (P, algo)
     with hc.Comm(*args) as comm:
         for L in (1, P - 1, P + 1, 37, 300):
             if L <= 0:
@@ -165,7 +174,7 @@ def test_library_schedule_matches_oracle(algo, P, kw, coll, dtype):
             got = simulate(items, nsteps, xs, dtype, "sum")
             seq = simulate(items, nsteps, xs, dtype, "sum", sequential=True)
             want = [x.copy() for x in xs]
-            oracle.run(coll, algo, want, dtype, "sum", S=kw.get("S", 1), M=kw.get("M", 1),
+            oracle.run(coll, algo, want, dtype, "sum", S=kw.get("S", 1), M=kw.get("M", kw.get("K", 1)),
                        loop_bytes=loop_bytes)
             for r in range(P):
                 refops.assert_same(dtype, got[r], want[r], f"{algo} {coll} P={P} L={L} r={r}")
@@ -179,6 +188,8 @@ def test_validation_status_codes():
     assert lib.hbmc_comm_create(65, 0, 0, 0, 0, ctypes.byref(h)) == 1
     assert lib.hbmc_comm_create(8, 7, 0, 0, 0, ctypes.byref(h)) == 1
     assert lib.hbmc_comm_create(8, 2, 3, 3, 0, ctypes.byref(h)) == 1       # S*M != P
+    assert lib.hbmc_comm_create(8, 6, 3, 3, 0, ctypes.byref(h)) == 1       # hierarchical S*M != P
+    assert lib.hbmc_comm_create(8, 5, 0, 1, 0, ctypes.byref(h)) == 1       # tree arity 1
     assert lib.hbmc_comm_create(8, 0, 0, 0, 0, None) == 1
     assert lib.hbmc_comm_destroy(None) == 1
     with hc.Comm(5, "rhd") as c:
@@ -208,6 +219,8 @@ def test_validation_status_codes():
         assert lib.hbmc_run_steps(c._h, 9, 0, arr, 16, 0, 0, 0, 1, None) == 1    # bad collective
         assert lib.hbmc_reduce(c._h, arr, 16, 0, 0, 0, None) == 2               # ring: no Reduce
         assert lib.hbmc_broadcast(c._h, arr, 16, 0, 0, None) == 2               # ring: no Broadcast
+    with hc.Comm(4, "flat") as c:
+        assert lib.hbmc_reduce_scatter(c._h, arr, 16, 0, 0, None) == 2          # Flat: AllReduce only
     with hc.Comm(1, "ring") as c:
         one = (ctypes.c_void_p * 1)(0x10000)
         assert lib.hbmc_allreduce(c._h, one, 16, 0, 0, None) == 0            # one rank: nothing to do
@@ -225,7 +238,10 @@ def test_algorithm_from_environment(monkeypatch):
     monkeypatch.setenv("HBMC_ALGO", "pipeline")
     with hc.Comm(4, "env", 2, 2) as c:
         assert c.plan_info("allreduce", 64, "fp32")["nsteps"] == 4
-    monkeypatch.setenv("HBMC_ALGO", "tree")
+    monkeypatch.setenv("HBMC_ALGO", "flat")
+    with hc.Comm(4, "env") as c:
+        assert c.plan_info("allreduce", 64, "fp32")["nsteps"] == 2
+    monkeypatch.setenv("HBMC_ALGO", "mesh")
     assert lib.hbmc_comm_create(4, 3, 0, 0, 0, ctypes.byref(h)) == 1
 
 
