@@ -18,7 +18,8 @@ STATUS = {0: "HBMC_OK", 1: "HBMC_ERR_INVALID_ARG", 2: "HBMC_ERR_UNSUPPORTED", 3:
 DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2, "int32": 3, "int8": 4}
 ESIZE = {"fp32": 4, "fp16": 2, "bf16": 2, "int32": 4, "int8": 1}
 OP = {"sum": 0, "prod": 1, "max": 2, "min": 3}
-ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3, "flat": 4, "tree": 5, "hier": 6}
+ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3, "flat": 4, "tree": 5, "hier": 6, "auto": 7}
+ALGO_NAME = {v: k for k, v in ALGO.items()}
 COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
 
@@ -26,7 +27,8 @@ MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
 EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
            "hbmc_all_gather", "hbmc_reduce", "hbmc_broadcast", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
            "hbmc_plan_items", "hbmc_status_string", "hbmc_graph_create", "hbmc_graph_add",
-           "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy")
+           "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy", "hbmc_comm_set_cost_model",
+           "hbmc_auto_choice")
 
 
 class HbmcError(RuntimeError):
@@ -87,6 +89,10 @@ def load_library():
         L.hbmc_graph_launch.argtypes = [vp, vp]
         L.hbmc_graph_destroy.restype = ci
         L.hbmc_graph_destroy.argtypes = [vp]
+        L.hbmc_comm_set_cost_model.restype = ci
+        L.hbmc_comm_set_cost_model.argtypes = [vp, ctypes.c_double, ctypes.c_double]
+        L.hbmc_auto_choice.restype = ci
+        L.hbmc_auto_choice.argtypes = [vp, ci, ci, sz, ci, ctypes.POINTER(ci)]
         L.hbmc_status_string.restype = ctypes.c_char_p
         L.hbmc_status_string.argtypes = [ci]
         _lib = L
@@ -191,6 +197,16 @@ class Comm:
         count = n if count is None else count
         _check(load_library().hbmc_run_steps(self._h, COLL[coll], root, arr, count, DTYPE[dtype], OP[op],
                                              first, last, _stream(stream)), "hbmc_run_steps")
+
+    # -- AUTO selection (host only)
+    def set_cost_model(self, alpha_us: float, beta_gbps: float):
+        _check(load_library().hbmc_comm_set_cost_model(self._h, alpha_us, beta_gbps), "hbmc_comm_set_cost_model")
+
+    def auto_choice(self, coll: str, count: int, dtype: str, root: int = 0) -> str:
+        a = ctypes.c_int()
+        _check(load_library().hbmc_auto_choice(self._h, COLL[coll], root, count, DTYPE[dtype], ctypes.byref(a)),
+               "hbmc_auto_choice")
+        return ALGO_NAME[a.value]
 
     # -- schedule facts (host only)
     def plan_info(self, coll: str, count: int, dtype: str, root: int = 0):

@@ -30,10 +30,12 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
     else if (v == "flat") a = HBMC_ALGO_FLAT;
     else if (v == "tree") a = HBMC_ALGO_TREE;
     else if (v == "hier") a = HBMC_ALGO_HIER;
+    else if (v == "auto") a = HBMC_ALGO_AUTO;
     else return HBMC_ERR_INVALID_ARG;
   }
   Topology t;
   t.P = nranks;
+  std::vector<Topology> topos;
   switch (a) {
     case HBMC_ALGO_RING: t.algo = kRing; break;
     case HBMC_ALGO_RHD: t.algo = kRhd; break;
@@ -52,14 +54,63 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
       t.M = ranks_per_server;
       t.loop_bytes = loop_bytes;
       break;
+    case HBMC_ALGO_AUTO: {
+      // candidates: ring, RHD, Flat, binary tree; with a server shape also
+      // the pipeline and the hierarchical AllReduce
+      for (Algo al : {kRing, kRhd, kFlat, kTree}) {
+        Topology c = t;
+        c.algo = al;
+        topos.push_back(c);
+      }
+      if (servers > 0 || ranks_per_server > 0) {
+        if (servers < 1 || ranks_per_server < 1 || servers * ranks_per_server != nranks)
+          return HBMC_ERR_INVALID_ARG;
+        for (Algo al : {kPipeline, kHier}) {
+          Topology c = t;
+          c.algo = al;
+          c.S = servers;
+          c.M = ranks_per_server;
+          c.loop_bytes = loop_bytes;
+          topos.push_back(c);
+        }
+      }
+      break;
+    }
     default: return HBMC_ERR_INVALID_ARG;
   }
+  if (topos.empty()) topos.push_back(t);
   hbmc_comm* c = new (std::nothrow) hbmc_comm;
   if (!c) return HBMC_ERR_NOMEM;
-  c->topo = t;
+  c->topos = topos;
+  c->auto_select = a == HBMC_ALGO_AUTO;
   const char* xs = std::getenv("HBMC_XCD_SPLIT");
   c->xcd_split = xs && xs[0] == '1';
   *out = c;
+  return HBMC_OK;
+}
+
+hbmc_status_t hbmc_comm_set_cost_model(hbmc_comm_t comm, double alpha_us, double beta_gbps) {
+  if (!comm || !(alpha_us >= 0.0) || !(beta_gbps > 0.0)) return HBMC_ERR_INVALID_ARG;
+  comm->alpha_us = alpha_us;
+  comm->beta_gbps = beta_gbps;
+  comm->chosen.clear();
+  return HBMC_OK;
+}
+
+hbmc_status_t hbmc_auto_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
+                               hbmc_dtype_t dtype, hbmc_algo_t* algo) {
+  if (!algo) return HBMC_ERR_INVALID_ARG;
+  int ti = 0;
+  hbmc_status_t st = choose_topology(comm, coll, root, count, dtype, &ti);
+  if (st != HBMC_OK) return st;
+  switch (comm->topos[ti].algo) {
+    case kRing: *algo = HBMC_ALGO_RING; break;
+    case kRhd: *algo = HBMC_ALGO_RHD; break;
+    case kPipeline: *algo = HBMC_ALGO_PIPELINE; break;
+    case kFlat: *algo = HBMC_ALGO_FLAT; break;
+    case kTree: *algo = HBMC_ALGO_TREE; break;
+    default: *algo = HBMC_ALGO_HIER; break;
+  }
   return HBMC_OK;
 }
 

@@ -34,14 +34,11 @@ hbmc_status_t from_build(BuildStatus b) {
 bool valid_coll(int c) { return c >= HBMC_COLL_ALLREDUCE && c <= HBMC_COLL_BROADCAST; }
 bool valid_op(int op) { return op >= HBMC_SUM && op <= HBMC_MIN; }
 
-hbmc_status_t get_plan(hbmc_comm* c, int coll, int root, size_t count, int dtype, Plan** out) {
+namespace {
+
+hbmc_status_t plan_for(hbmc_comm* c, int ti, int coll, int root, size_t count, int dtype, Plan** out) {
   const uint32_t e = elem_bytes(dtype);
-  if (!c || e == 0 || !valid_coll(coll)) return HBMC_ERR_INVALID_ARG;
-  if (count > SIZE_MAX / e) return HBMC_ERR_INVALID_ARG;
-  const bool rooted = coll == HBMC_COLL_REDUCE || coll == HBMC_COLL_BROADCAST;
-  if (rooted && (root < 0 || root >= c->topo.P)) return HBMC_ERR_INVALID_ARG;
-  if (!rooted) root = 0;
-  auto key = std::make_tuple(coll, root, static_cast<uint64_t>(count), dtype);
+  auto key = std::make_tuple(ti, coll, root, static_cast<uint64_t>(count), dtype);
   auto it = c->plans.find(key);
   if (it != c->plans.end()) {
     *out = it->second.get();
@@ -49,7 +46,8 @@ hbmc_status_t get_plan(hbmc_comm* c, int coll, int root, size_t count, int dtype
   }
   std::unique_ptr<Plan> p(new (std::nothrow) Plan);
   if (!p) return HBMC_ERR_NOMEM;
-  hbmc_status_t st = from_build(build_schedule(c->topo, static_cast<Coll>(coll), count, e, root, &p->sched));
+  hbmc_status_t st =
+      from_build(build_schedule(c->topos[ti], static_cast<Coll>(coll), count, e, root, &p->sched));
   if (st != HBMC_OK) return st;
   size_t off = 0;
   for (const Step& s : p->sched.steps) {
@@ -59,6 +57,67 @@ hbmc_status_t get_plan(hbmc_comm* c, int coll, int root, size_t count, int dtype
   *out = p.get();
   c->plans.emplace(key, std::move(p));
   return HBMC_OK;
+}
+
+hbmc_status_t normalise(hbmc_comm* c, int coll, int* root, size_t count, int dtype) {
+  const uint32_t e = elem_bytes(dtype);
+  if (!c || e == 0 || !valid_coll(coll) || c->topos.empty()) return HBMC_ERR_INVALID_ARG;
+  if (count > SIZE_MAX / e) return HBMC_ERR_INVALID_ARG;
+  const bool rooted = coll == HBMC_COLL_REDUCE || coll == HBMC_COLL_BROADCAST;
+  if (rooted && (*root < 0 || *root >= c->topos[0].P)) return HBMC_ERR_INVALID_ARG;
+  if (!rooted) *root = 0;
+  return HBMC_OK;
+}
+
+}  // namespace
+
+hbmc_status_t choose_topology(hbmc_comm* c, int coll, int root, size_t count, int dtype, int* index) {
+  hbmc_status_t st = normalise(c, coll, &root, count, dtype);
+  if (st != HBMC_OK) return st;
+  if (!c->auto_select) {
+    *index = 0;
+    return HBMC_OK;
+  }
+  auto key = std::make_tuple(coll, root, static_cast<uint64_t>(count), dtype);
+  auto it = c->chosen.find(key);
+  if (it != c->chosen.end()) {
+    *index = it->second;
+    return HBMC_OK;
+  }
+  int best = -1;
+  double best_t = 0;
+  size_t best_steps = 0;
+  hbmc_status_t first_err = HBMC_ERR_UNSUPPORTED;
+  for (int ti = 0; ti < static_cast<int>(c->topos.size()); ++ti) {
+    Plan* p = nullptr;
+    st = plan_for(c, ti, coll, root, count, dtype, &p);
+    if (st == HBMC_ERR_UNSUPPORTED) continue;
+    if (st != HBMC_OK) {
+      first_err = st;
+      continue;
+    }
+    size_t launches = 0;
+    for (const Step& s : p->sched.steps) launches += s.items.empty() ? 0 : 1;
+    const double t = double(launches) * c->alpha_us + double(p->sched.hbm_bytes) / (c->beta_gbps * 1e3);
+    if (best < 0 || t < best_t || (t == best_t && launches < best_steps)) {
+      best = ti;
+      best_t = t;
+      best_steps = launches;
+    }
+  }
+  if (best < 0) return first_err;
+  c->chosen.emplace(key, best);
+  *index = best;
+  return HBMC_OK;
+}
+
+hbmc_status_t get_plan(hbmc_comm* c, int coll, int root, size_t count, int dtype, Plan** out) {
+  hbmc_status_t st = normalise(c, coll, &root, count, dtype);
+  if (st != HBMC_OK) return st;
+  int ti = 0;
+  st = choose_topology(c, coll, root, count, dtype, &ti);
+  if (st != HBMC_OK) return st;
+  return plan_for(c, ti, coll, root, count, dtype, out);
 }
 
 hbmc_status_t upload(Plan* p) {
@@ -126,8 +185,9 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
   } else if (first < 0 || last > nsteps || first >= last) {
     return HBMC_ERR_INVALID_ARG;
   }
-  if (count == 0 || c->topo.P == 1) return HBMC_OK;
-  st = check_bufs(c->topo.P, bufs, count, e);
+  const int P = c->topos[0].P;
+  if (count == 0 || P == 1) return HBMC_OK;
+  st = check_bufs(P, bufs, count, e);
   if (st != HBMC_OK) return st;
   st = upload(p);
   if (st != HBMC_OK) return st;
@@ -135,7 +195,7 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
   std::memset(ptrs, 0, sizeof(*ptrs));
   const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0]) & 15u);
   bool aligned = true;
-  for (int r = 0; r < c->topo.P; ++r) {
+  for (int r = 0; r < P; ++r) {
     ptrs->p[r] = static_cast<unsigned char*>(bufs[r]);
     aligned = aligned && (reinterpret_cast<uintptr_t>(bufs[r]) & 15u) == phase;
   }

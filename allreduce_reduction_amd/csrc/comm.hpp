@@ -29,16 +29,27 @@ struct Plan {
 }  // namespace hbmc
 
 struct hbmc_comm {
-  hbmc::Topology topo;
+  // One topology, or for AUTO the candidates the cost model chooses among.
+  std::vector<hbmc::Topology> topos;
+  bool auto_select = false;
+  double alpha_us = 4.4;      // launch-to-launch cost of one step, measured eager on MI355X
+  double beta_gbps = 6400.0;  // sustained HBM rate of the step kernels, measured
   bool xcd_split = false;
-  std::map<std::tuple<int, int, uint64_t, int>, std::unique_ptr<hbmc::Plan>> plans;  // (coll, root, count, dtype)
+  // (topology index, coll, root, count, dtype) -> plan
+  std::map<std::tuple<int, int, int, uint64_t, int>, std::unique_ptr<hbmc::Plan>> plans;
+  // AUTO: (coll, root, count, dtype) -> chosen topology index
+  std::map<std::tuple<int, int, uint64_t, int>, int> chosen;
 };
 
 namespace hbmc {
 
 // Build (or fetch) the host schedule of (coll, root, count, dtype); the root
-// matters only for Reduce and Broadcast.
+// matters only for Reduce and Broadcast.  For AUTO communicators this picks
+// the candidate with the least modelled time first (see choose_topology).
 hbmc_status_t get_plan(hbmc_comm* c, int coll, int root, size_t count, int dtype, Plan** out);
+// AUTO: index into c->topos of the candidate with the least modelled time
+// steps * alpha + hbm_bytes / beta (ties: fewer steps, then lower index).
+hbmc_status_t choose_topology(hbmc_comm* c, int coll, int root, size_t count, int dtype, int* index);
 // Copy the plan's item table to the current device (once per plan).
 hbmc_status_t upload(Plan* p);
 // Non-null, element-aligned, pairwise disjoint rank buffers of count elements.

@@ -66,10 +66,10 @@ hbmc_status_t hbmc_graph_add(hbmc_graph_t g, hbmc_comm_t comm, hbmc_coll_t coll,
   hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
   if (st != HBMC_OK) return st;
   hbmc_graph::Node n{comm, coll, root, {}, count, dtype, op};
-  if (count > 0 && comm->topo.P > 1) {
-    st = check_bufs(comm->topo.P, bufs, count, elem_bytes(dtype));
+  if (count > 0 && comm->topos[0].P > 1) {
+    st = check_bufs(comm->topos[0].P, bufs, count, elem_bytes(dtype));
     if (st != HBMC_OK) return st;
-    n.bufs.assign(bufs, bufs + comm->topo.P);
+    n.bufs.assign(bufs, bufs + comm->topos[0].P);
   }
   g->nodes.push_back(std::move(n));
   return HBMC_OK;

@@ -164,6 +164,29 @@ def suite(a):
         torch.cuda.empty_cache()
         nbytes *= 4
 
+    # AllReduce algorithms side by side, and the AUTO communicator's choice
+    for P in (8, 16):
+        nbytes = 4096
+        while nbytes <= min(a.max_sweep_bytes, 256 << 20):
+            L = nbytes // 2
+            bufs = upload("sweep_p16_fp16", P, L)
+            pristine = [b.clone() for b in bufs]
+            row = {}
+            for algo, args in (("ring", (P, "ring")), ("rhd", (P, "rhd")), ("flat", (P, "flat")),
+                               ("tree", (P, "tree", 0, 2)), ("auto", (P, "auto"))):
+                with hc.Comm(*args) as c:
+                    for b, q in zip(bufs, pristine):
+                        b.copy_(q)
+                    info = c.plan_info("allreduce", L, "fp16")
+                    reps = max(3, min(200, int(2e8 // max(info["hbm_bytes"], 1))))
+                    row[algo] = round(time_calls(lambda: c.allreduce(bufs, "fp16", "sum"), reps, 2) * 1e6, 2)
+                    if algo == "auto":
+                        row["auto_choice"] = c.auto_choice("allreduce", L, "fp16")
+            emit(workload="allreduce_algorithms", P=P, dtype="fp16", bytes_per_rank=nbytes, us=row)
+            del bufs, pristine
+            torch.cuda.empty_cache()
+            nbytes *= 16
+
     # pipeline 4 x 8, bf16, 512 MiB per rank, 32 MiB loops
     S, M = 4, 8
     P, L = S * M, 256 << 20

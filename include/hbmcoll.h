@@ -69,10 +69,11 @@ typedef enum { HBMC_SUM = 0, HBMC_PROD = 1, HBMC_MAX = 2, HBMC_MIN = 3 } hbmc_op
  * steps ([TOPO] "AllReduce算法实现").  HIER: S servers x M ranks,
  * intra-server reduce-scatter, inter-server ring AllReduce, intra-server
  * all-gather, not pipelined ([PIPE] "与其它分级算法的关系").  FLAT, TREE and
- * HIER offer AllReduce only.  ENV: take the algorithm from the environment
- * variable HBMC_ALGO ("ring", "rhd" or "H-D_R", "pipeline", "flat", "tree",
- * "hier"), the way the pages' HCCL_ALGO selects an algorithm ([RHD] "RHD 在
- * HCCL 中的定位与启用方式"). */
+ * HIER offer AllReduce only.  AUTO: per call, the candidate schedule with
+ * the least modelled time (see hbmc_comm_set_cost_model).  ENV: take the
+ * algorithm from the environment variable HBMC_ALGO ("ring", "rhd" or
+ * "H-D_R", "pipeline", "flat", "tree", "hier", "auto"), the way the pages'
+ * HCCL_ALGO selects an algorithm ([RHD] "RHD 在 HCCL 中的定位与启用方式"). */
 typedef enum {
   HBMC_ALGO_RING = 0,
   HBMC_ALGO_RHD = 1,
@@ -80,7 +81,8 @@ typedef enum {
   HBMC_ALGO_ENV = 3,
   HBMC_ALGO_FLAT = 4,
   HBMC_ALGO_TREE = 5,
-  HBMC_ALGO_HIER = 6
+  HBMC_ALGO_HIER = 6,
+  HBMC_ALGO_AUTO = 7
 } hbmc_algo_t;
 
 typedef enum {
@@ -107,6 +109,25 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
 /* Free the communicator and its device tables.  The caller must have
  * synchronised every stream that still runs one of its collectives. */
 hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
+
+/*
+ * AUTO selection ([RHD] "RHD 在 HCCL 中的定位与启用方式": the algorithm is
+ * chosen adaptively from product, data size and rank count; [RHD] "耗时计算"
+ * and [TOPO] "AllReduce算法实现": alpha-beta cost models).  An AUTO
+ * communicator's candidates are ring, RHD, Flat and a binary tree, plus the
+ * pipeline and the hierarchical AllReduce when created with a server shape
+ * (servers * ranks_per_server == nranks; 0, 0 for none).  For each
+ * (collective, root, count, dtype) it builds every candidate's schedule and
+ * keeps the one minimising launches * alpha + algorithmic HBM bytes / beta
+ * (ties: fewer launches), caching the choice.  Defaults are this library's
+ * measurements on MI355X: alpha = 4.4 us per step launch, beta = 6400 GB/s.
+ * hbmc_comm_set_cost_model replaces alpha (us, >= 0) and beta (GB/s, > 0)
+ * and forgets earlier choices; hbmc_auto_choice reports the algorithm a call
+ * would use (for any communicator: its own algorithm).  Host only.
+ */
+hbmc_status_t hbmc_comm_set_cost_model(hbmc_comm_t comm, double alpha_us, double beta_gbps);
+hbmc_status_t hbmc_auto_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
+                               hbmc_dtype_t dtype, hbmc_algo_t* algo);
 
 /*
  * AllReduce, Y[j] = op over ranks i of X_i[j] ([RING-RHD] "AllReduce的数学抽象与问题定义").

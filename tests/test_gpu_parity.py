@@ -109,6 +109,34 @@ def test_parity_variants(dtype):
                     refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{algo} {kw} rank {r}")
 
 
+@pytest.mark.parametrize("P,S,M", [(8, 0, 0), (6, 0, 0), (8, 2, 4)])
+def test_parity_auto(P, S, M):
+    """An AUTO communicator runs the schedule it reports, bit for bit."""
+    dtype = "bf16"
+    with hc.Comm(P, "auto", S, M) as comm:
+        for coll in ("allreduce", "reduce_scatter", "all_gather", "reduce", "broadcast"):
+            for L in (100, 3 * 4096 + 1, 200_003):
+                algo = comm.auto_choice(coll, L, dtype, root=1)
+                say(f"case auto P={P} coll={coll} L={L} -> {algo}")
+                xs = make_inputs(dtype, "sum", P, L, seed=L)
+                dev = [to_dev(x, dtype) for x in xs]
+                if coll in ("reduce", "broadcast"):
+                    getattr(comm, coll)(dev, dtype, **({"op": "sum"} if coll == "reduce" else {}), root=1)
+                else:
+                    getattr(comm, coll)(dev, dtype, "sum")
+                torch.cuda.synchronize()
+                want = [x.copy() for x in xs]
+                kw = dict(S=S, M=M) if algo in ("pipeline", "hier") else (dict(M=2) if algo == "tree" else {})
+                oracle.run(coll, algo, want, dtype, "sum", root=1, **kw)
+                ranks = [1] if coll == "reduce" else range(P)
+                for r in ranks:
+                    if coll == "reduce_scatter":
+                        b, e = refops.seg_bounds(L, P, r) if algo != "pipeline" else (0, 0)
+                        refops.assert_same(dtype, to_host(dev[r], dtype)[b:e], want[r][b:e], f"{coll} rank {r}")
+                    else:
+                        refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{coll} {algo} rank {r}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("coll", ["reduce", "broadcast"])
 def test_parity_rooted(coll, dtype):

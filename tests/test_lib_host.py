@@ -186,7 +186,7 @@ def test_validation_status_codes():
     h = ctypes.c_void_p()
     assert lib.hbmc_comm_create(0, 0, 0, 0, 0, ctypes.byref(h)) == 1
     assert lib.hbmc_comm_create(65, 0, 0, 0, 0, ctypes.byref(h)) == 1
-    assert lib.hbmc_comm_create(8, 7, 0, 0, 0, ctypes.byref(h)) == 1
+    assert lib.hbmc_comm_create(8, 9, 0, 0, 0, ctypes.byref(h)) == 1
     assert lib.hbmc_comm_create(8, 2, 3, 3, 0, ctypes.byref(h)) == 1       # S*M != P
     assert lib.hbmc_comm_create(8, 6, 3, 3, 0, ctypes.byref(h)) == 1       # hierarchical S*M != P
     assert lib.hbmc_comm_create(8, 5, 0, 1, 0, ctypes.byref(h)) == 1       # tree arity 1
@@ -266,3 +266,62 @@ def test_graph_validation_without_device():
         assert lib.hbmc_graph_add(g, c._h, 0, 0, arr, 16, 0, 0) == 0         # host-only checks pass
         assert lib.hbmc_graph_launch(g, None) == 1                          # not built yet
     assert lib.hbmc_graph_destroy(g) == 0
+
+
+def _model_time(comm, coll, count, dtype, alpha, beta, root=0):
+    info = comm.plan_info(coll, count, dtype, root=root)
+    items = comm.plan_items(coll, count, dtype, root=root)
+    launches = len({it["step"] for it in items})
+    return launches * alpha + info["hbm_bytes"] / (beta * 1e3), launches
+
+
+def _explicit(algo, P, S=0, M=0):
+    if algo in ("pipeline", "hier"):
+        return hc.Comm(P, algo, S, M)
+    if algo == "tree":
+        return hc.Comm(P, "tree", 0, 2)
+    return hc.Comm(P, algo)
+
+
+@pytest.mark.parametrize("P,S,M", [(8, 0, 0), (5, 0, 0), (16, 0, 0), (8, 2, 4), (32, 4, 8)])
+@pytest.mark.parametrize("alpha,beta", [(4.4, 6400.0), (0.0, 1.0), (1e6, 6400.0), (2.0, 100.0)])
+def test_auto_picks_the_least_modelled_time(P, S, M, alpha, beta):
+    """The AUTO choice equals the argmin of launches*alpha + bytes/beta computed
+    here from explicitly created communicators of every candidate."""
+    cands = ["ring", "rhd", "flat", "tree"] + (["pipeline", "hier"] if S else [])
+    with hc.Comm(P, "auto", S, M) as auto:
+        auto.set_cost_model(alpha, beta)
+        for coll in ("allreduce", "reduce_scatter", "all_gather", "reduce", "broadcast"):
+            for count in (64, 4096 * P, 1 << 22):
+                best = None
+                for algo in cands:
+                    with _explicit(algo, P, S, M) as c:
+                        try:
+                            t, n = _model_time(c, coll, count, "fp32", alpha, beta)
+                        except hc.HbmcError as e:
+                            assert e.code == 2
+                            continue
+                    if best is None or (t, n) < (best[0], best[1]):
+                        best = (t, n, algo)
+                assert auto.auto_choice(coll, count, "fp32") == best[2], (coll, count)
+                # the AUTO communicator's plan is that candidate's plan
+                with _explicit(best[2], P, S, M) as c:
+                    assert auto.plan_items(coll, count, "fp32") == c.plan_items(coll, count, "fp32")
+
+
+def test_auto_defaults_on_one_gpu():
+    """With the measured defaults Flat wins AllReduce (2 launches, (2P+1) D bytes,
+    against 5 D (P-1) for ring / RHD) and RHD wins the stand-alone collectives."""
+    with hc.Comm(8, "auto") as a:
+        assert a.auto_choice("allreduce", 1 << 20, "bf16") == "flat"
+        assert a.auto_choice("reduce_scatter", 1 << 20, "bf16") == "rhd"
+        assert a.auto_choice("all_gather", 1 << 20, "bf16") == "rhd"
+        assert a.auto_choice("reduce", 1 << 20, "bf16", root=3) == "rhd"
+    with hc.Comm(8, "ring") as r:
+        assert r.auto_choice("allreduce", 1 << 20, "bf16") == "ring"
+    lib = hc.load_library()
+    with hc.Comm(8, "auto") as a:
+        assert lib.hbmc_comm_set_cost_model(a._h, -1.0, 1.0) == 1
+        assert lib.hbmc_comm_set_cost_model(a._h, 1.0, 0.0) == 1
+    h = ctypes.c_void_p()
+    assert lib.hbmc_comm_create(8, 7, 3, 3, 0, ctypes.byref(h)) == 1  # bad server shape
