@@ -12,6 +12,8 @@ Reported (one JSON line):
              (3 bytes per segment byte, 8 segments) / its mean duration from
              HIP events recorded between the steps on the launch stream
   cpu_baseline  the CPU oracle replaying the same AllReduce (single thread)
+  auto_allreduce_same_workload  not the headline: the AUTO communicator's
+             AllReduce of the same buffers (its cost model picks Flat)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --suite    (one JSON line per other workload: RHD small
@@ -57,7 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--P", type=int, default=8)
     ap.add_argument("--elems", type=int, default=64 << 20, help="elements per rank")
-    ap.add_argument("--cpu-reps", type=int, default=4, help="oracle AllReduces timed for cpu_baseline")
+    ap.add_argument("--cpu-reps", type=int, default=10, help="oracle AllReduces timed for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--algo", default="ring", choices=["ring", "rhd"])
     ap.add_argument("--suite", action="store_true", help="time the other workloads instead")
@@ -239,6 +241,7 @@ def main():
         synth.fill_ptr(host.data_ptr(), dtype, L, recipe["dist"], recipe["p0"], recipe["p1"],
                        seed=0, stream=recipe["stream"], rank=r)
         bufs.append(host.to(dev, non_blocking=False).clone())
+    pristine = [b.clone() for b in bufs]
     torch.cuda.synchronize()
 
     comm = hc.Comm(P, a.algo)
@@ -310,6 +313,30 @@ def main():
         out["copy_step"] = {"kernel": "step_vec<fp32,copy,1,1> (ring all-gather step)",
                             "mean_launch_us": round(ag_ms * 1e3, 2),
                             "achieved_GBps": round(ag_bytes / (ag_ms / 1e3) / 1e9, 1)}
+
+    # not the headline: the same workload on an AUTO communicator (the cost model
+    # picks Flat on one GPU), inputs restored first, same number of calls
+    for b, q in zip(bufs, pristine):
+        b.copy_(q)
+    with hc.Comm(P, "auto") as auto:
+        choice = auto.auto_choice("allreduce", L, dtype)
+        for _ in range(a.warmup):
+            auto.allreduce(bufs, dtype, "sum")
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            auto.allreduce(bufs, dtype, "sum")
+        e1.record(stream)
+        e1.synchronize()
+        ta = e0.elapsed_time(e1) / 1e3 / K
+        ainfo = auto.plan_info("allreduce", L, dtype)
+    out["auto_allreduce_same_workload"] = {
+        "note": "not the headline value: AUTO communicator on this workload",
+        "algo": choice, "ms": round(ta * 1e3, 4), "busbw_GBps": round(D / ta * 2 * (P - 1) / P / 1e9, 3),
+        "pct_hbm": round(100 * ainfo["hbm_bytes"] / ta / HBM_PEAK, 2), "kernel_launches": ainfo["nsteps"]}
+    del pristine
 
     if not a.no_cpu:
         import oracle
