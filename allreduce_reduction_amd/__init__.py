@@ -25,7 +25,7 @@ MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
 
 # every symbol include/hbmcoll.h declares
 EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
-           "hbmc_all_gather", "hbmc_reduce", "hbmc_broadcast", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
+           "hbmc_all_gather", "hbmc_reduce", "hbmc_broadcast", "hbmc_collective_oop", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
            "hbmc_plan_items", "hbmc_status_string", "hbmc_graph_create", "hbmc_graph_add",
            "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy", "hbmc_comm_set_cost_model",
            "hbmc_auto_choice")
@@ -71,6 +71,8 @@ def load_library():
         L.hbmc_reduce.argtypes = [vp, ctypes.POINTER(vp), sz, ci, ci, ci, vp]
         L.hbmc_broadcast.restype = ci
         L.hbmc_broadcast.argtypes = [vp, ctypes.POINTER(vp), sz, ci, ci, vp]
+        L.hbmc_collective_oop.restype = ci
+        L.hbmc_collective_oop.argtypes = [vp, ci, ci, ctypes.POINTER(vp), ctypes.POINTER(vp), sz, ci, ci, vp]
         L.hbmc_run_steps.restype = ci
         L.hbmc_run_steps.argtypes = [vp, ci, ci, ctypes.POINTER(vp), sz, ci, ci, ci, ci, vp]
         L.hbmc_plan_info.restype = ci
@@ -190,6 +192,17 @@ class Comm:
         count = n if count is None else count
         _check(load_library().hbmc_broadcast(self._h, arr, count, DTYPE[dtype], root, _stream(stream)),
                "hbmc_broadcast")
+
+    def out_of_place(self, coll, send, recv, dtype=None, op="sum", *, root=0, count=None, stream=None):
+        """Collective from `send` into `recv` (LocalCopy first where they differ)."""
+        sarr, n, dt = _ptrs(send)
+        rarr, n2, dt2 = _ptrs(recv)
+        if n is not None and (n != n2 or dt != dt2):
+            raise ValueError("send and recv must match in size and dtype")
+        dtype = dtype or dt
+        count = n if count is None else count
+        _check(load_library().hbmc_collective_oop(self._h, COLL[coll], root, sarr, rarr, count, DTYPE[dtype],
+                                                  OP[op], _stream(stream)), "hbmc_collective_oop")
 
     def run_steps(self, coll, bufs, first, last, dtype=None, op="sum", *, root=0, count=None, stream=None):
         arr, n, dt = _ptrs(bufs)

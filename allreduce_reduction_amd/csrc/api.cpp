@@ -148,6 +148,12 @@ hbmc_status_t hbmc_broadcast(hbmc_comm_t comm, void* const bufs[], size_t count,
   return run(comm, HBMC_COLL_BROADCAST, root, bufs, count, dtype, HBMC_SUM, 0, 0, true, stream);
 }
 
+hbmc_status_t hbmc_collective_oop(hbmc_comm_t comm, hbmc_coll_t coll, int root, const void* const send[],
+                                  void* const recv[], size_t count, hbmc_dtype_t dtype, hbmc_op_t op,
+                                  void* stream) {
+  return run_out_of_place(comm, coll, root, send, recv, count, dtype, op, stream);
+}
+
 hbmc_status_t hbmc_run_steps(hbmc_comm_t comm, hbmc_coll_t coll, int root, void* const bufs[],
                              size_t count, hbmc_dtype_t dtype, hbmc_op_t op, int first_step,
                              int last_step, void* stream) {

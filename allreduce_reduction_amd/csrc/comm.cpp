@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstring>
 #include <new>
 
@@ -225,6 +226,109 @@ hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t c
   RankPtrs ptrs;
   hbmc_status_t st = prepare(c, coll, root, bufs, count, dtype, op, first, last, whole, &steps, &ptrs);
   if (st != HBMC_OK) return st;
+  for (const StepLaunch& L : steps)
+    if (launch_step(L, ptrs, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
+  return HBMC_OK;
+}
+
+namespace {
+
+constexpr int kCopyChunk = kDevRanks / 2;  // ranks per LocalCopy launch: sources then destinations
+
+// Plan of the LocalCopy: one copy step whose item j moves table slot j
+// (a send buffer) to slot kCopyChunk + j (its recv buffer), whole vector.
+hbmc_status_t local_copy_plan(hbmc_comm* c, size_t count, int dtype, Plan** out) {
+  auto key = std::make_tuple(-1, -1, 0, static_cast<uint64_t>(count), dtype);
+  auto it = c->plans.find(key);
+  if (it == c->plans.end()) {
+    std::unique_ptr<Plan> p(new (std::nothrow) Plan);
+    if (!p) return HBMC_ERR_NOMEM;
+    Step st;
+    st.mode = kCopy;
+    st.nsrc = st.ndst = 1;
+    for (int j = 0; j < kCopyChunk; ++j) {
+      Item item;
+      item.begin = 0;
+      item.count = count;
+      item.nsrc = item.ndst = 1;
+      item.rank[0] = static_cast<uint8_t>(j);
+      item.rank[1] = static_cast<uint8_t>(kCopyChunk + j);
+      st.items.push_back(item);
+    }
+    st.max_count = count;
+    st.hbm_bytes = uint64_t(2) * count * elem_bytes(dtype) * kCopyChunk;
+    p->sched.steps.push_back(st);
+    p->first_item.push_back(0);
+    it = c->plans.emplace(key, std::move(p)).first;
+  }
+  *out = it->second.get();
+  return upload(*out);
+}
+
+}  // namespace
+
+hbmc_status_t run_out_of_place(hbmc_comm* c, int coll, int root, const void* const send[],
+                               void* const recv[], size_t count, int dtype, int op, void* stream) {
+  // every host-side check before any device work
+  if (!c || c->topos.empty() || !valid_op(op) || !valid_coll(coll) || elem_bytes(dtype) == 0)
+    return HBMC_ERR_INVALID_ARG;
+  const int P = c->topos[0].P;
+  const uint32_t e = elem_bytes(dtype);
+  if (count > SIZE_MAX / e) return HBMC_ERR_INVALID_ARG;
+  Plan* plan = nullptr;
+  hbmc_status_t st = get_plan(c, coll, root, count, dtype, &plan);
+  if (st != HBMC_OK) return st;
+  if (count == 0) return HBMC_OK;
+  if (!send) return HBMC_ERR_INVALID_ARG;
+  st = check_bufs(P, recv, count, e);
+  if (st != HBMC_OK) return st;
+  const uint64_t bytes = uint64_t(count) * e;
+  std::vector<int> moved;
+  for (int r = 0; r < P; ++r) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(send[r]);
+    if (!a || a % e || a + bytes < a) return HBMC_ERR_INVALID_ARG;
+    if (send[r] == recv[r]) continue;
+    for (int q = 0; q < P; ++q) {
+      const uintptr_t b = reinterpret_cast<uintptr_t>(recv[q]);
+      if (a < b + bytes && b < a + bytes) return HBMC_ERR_INVALID_ARG;  // input overlaps an output
+    }
+    moved.push_back(r);
+  }
+  std::vector<StepLaunch> steps;
+  RankPtrs ptrs;
+  st = prepare(c, coll, root, recv, count, dtype, op, 0, 0, true, &steps, &ptrs);
+  if (st != HBMC_OK) return st;
+  if (!moved.empty()) {
+    Plan* lc = nullptr;
+    st = local_copy_plan(c, count, dtype, &lc);
+    if (st != HBMC_OK) return st;
+    for (size_t base = 0; base < moved.size(); base += kCopyChunk) {
+      const int n = static_cast<int>(std::min<size_t>(kCopyChunk, moved.size() - base));
+      RankPtrs cp;
+      std::memset(&cp, 0, sizeof(cp));
+      const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(send[moved[base]]) & 15u);
+      bool aligned = true;
+      for (int j = 0; j < n; ++j) {
+        const int r = moved[base + j];
+        cp.p[j] = static_cast<unsigned char*>(const_cast<void*>(send[r]));
+        cp.p[kCopyChunk + j] = static_cast<unsigned char*>(recv[r]);
+        aligned = aligned && (reinterpret_cast<uintptr_t>(send[r]) & 15u) == phase &&
+                  (reinterpret_cast<uintptr_t>(recv[r]) & 15u) == phase;
+      }
+      StepLaunch L;
+      L.dtype = dtype;
+      L.op = op;
+      L.mode = kCopy;
+      L.nsrc = L.ndst = 1;
+      L.items = lc->dev;
+      L.nitems = n;
+      L.max_count = count;
+      L.aligned = aligned;
+      L.phase = phase;
+      L.xcd_split = false;
+      if (launch_step(L, cp, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
+    }
+  }
   for (const StepLaunch& L : steps)
     if (launch_step(L, ptrs, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
   return HBMC_OK;

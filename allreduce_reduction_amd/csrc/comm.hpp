@@ -64,5 +64,9 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
 // `whole`) on `stream`, one kernel launch per non-empty step.
 hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
                   int op, int first, int last, bool whole, void* stream);
+// Out-of-place: LocalCopy of send into recv where they differ (one copy
+// launch per 32 ranks), then the collective in place on recv.
+hbmc_status_t run_out_of_place(hbmc_comm* c, int coll, int root, const void* const send[],
+                               void* const recv[], size_t count, int dtype, int op, void* stream);
 
 }  // namespace hbmc

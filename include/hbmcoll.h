@@ -178,6 +178,21 @@ hbmc_status_t hbmc_broadcast(hbmc_comm_t comm, void* const bufs[], size_t count,
                              int root, void* stream);
 
 /*
+ * Out-of-place form of every collective ([PIPE] "Rank0 视角的传输任务编排":
+ * LocalCopy moves data from input to output memory only when the two differ
+ * and is skipped in place).  send[r] holds rank r's input (count elements,
+ * read only); on completion recv[r] holds what the in-place call would leave
+ * in bufs[r].  Ranks with send[r] != recv[r] are first copied by one
+ * LocalCopy launch per 32 such ranks, then the collective runs in place on
+ * recv.  send[r] must equal recv[r] or overlap no recv buffer (else
+ * HBMC_ERR_INVALID_ARG); send buffers are left unchanged.  `root` is used by
+ * Reduce and Broadcast.  Asynchronous and stream-ordered like the others.
+ */
+hbmc_status_t hbmc_collective_oop(hbmc_comm_t comm, hbmc_coll_t coll, int root, const void* const send[],
+                                  void* const recv[], size_t count, hbmc_dtype_t dtype, hbmc_op_t op,
+                                  void* stream);
+
+/*
  * Run only schedule steps [first_step, last_step) of a collective (every
  * loop's steps with those indices for the pipeline).  Running [0, k) and then
  * [k, nsteps) equals the whole collective.  For step-by-step checking and

