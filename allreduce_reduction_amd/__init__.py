@@ -28,7 +28,7 @@ EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_redu
            "hbmc_all_gather", "hbmc_reduce", "hbmc_broadcast", "hbmc_collective_oop", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
            "hbmc_plan_items", "hbmc_status_string", "hbmc_graph_create", "hbmc_graph_add",
            "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy", "hbmc_comm_set_cost_model",
-           "hbmc_auto_choice")
+           "hbmc_auto_choice", "hbmc_comm_set_fused_limit")
 
 
 class HbmcError(RuntimeError):
@@ -91,6 +91,8 @@ def load_library():
         L.hbmc_graph_launch.argtypes = [vp, vp]
         L.hbmc_graph_destroy.restype = ci
         L.hbmc_graph_destroy.argtypes = [vp]
+        L.hbmc_comm_set_fused_limit.restype = ci
+        L.hbmc_comm_set_fused_limit.argtypes = [vp, ctypes.c_uint64]
         L.hbmc_comm_set_cost_model.restype = ci
         L.hbmc_comm_set_cost_model.argtypes = [vp, ctypes.c_double, ctypes.c_double]
         L.hbmc_auto_choice.restype = ci
@@ -210,6 +212,10 @@ class Comm:
         count = n if count is None else count
         _check(load_library().hbmc_run_steps(self._h, COLL[coll], root, arr, count, DTYPE[dtype], OP[op],
                                              first, last, _stream(stream)), "hbmc_run_steps")
+
+    def set_fused_limit(self, max_bytes: int):
+        """Run calls moving at most max_bytes as one single-workgroup launch."""
+        _check(load_library().hbmc_comm_set_fused_limit(self._h, max_bytes), "hbmc_comm_set_fused_limit")
 
     # -- AUTO selection (host only)
     def set_cost_model(self, alpha_us: float, beta_gbps: float):

@@ -83,9 +83,16 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
   if (!c) return HBMC_ERR_NOMEM;
   c->topos = topos;
   c->auto_select = a == HBMC_ALGO_AUTO;
+  if (const char* fl = std::getenv("HBMC_FUSED_LIMIT")) c->fused_limit = std::strtoull(fl, nullptr, 10);
   const char* xs = std::getenv("HBMC_XCD_SPLIT");
   c->xcd_split = xs && xs[0] == '1';
   *out = c;
+  return HBMC_OK;
+}
+
+hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes) {
+  if (!comm) return HBMC_ERR_INVALID_ARG;
+  comm->fused_limit = max_bytes;
   return HBMC_OK;
 }
 

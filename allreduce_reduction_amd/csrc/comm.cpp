@@ -143,13 +143,24 @@ hbmc_status_t upload(Plan* p) {
       d.ndst = static_cast<uint32_t>(it.ndst);
       std::memcpy(d.rank, it.rank, sizeof(d.rank));
     }
+  std::vector<FusedStep> fs(p->sched.steps.size());
+  for (size_t s = 0; s < fs.size(); ++s) {
+    fs[s].first_item = static_cast<uint32_t>(p->first_item[s]);
+    fs[s].nitems = static_cast<uint32_t>(p->sched.steps[s].items.size());
+    fs[s].mode = static_cast<uint32_t>(p->sched.steps[s].mode);
+    fs[s].pad = 0;
+  }
+  const size_t item_bytes = n * sizeof(DevItem), step_bytes = fs.size() * sizeof(FusedStep);
   void* mem = nullptr;
-  if (hipMalloc(&mem, n * sizeof(DevItem)) != hipSuccess) return HBMC_ERR_NOMEM;
-  if (hipMemcpy(mem, host.data(), n * sizeof(DevItem), hipMemcpyHostToDevice) != hipSuccess) {
+  if (hipMalloc(&mem, item_bytes + step_bytes) != hipSuccess) return HBMC_ERR_NOMEM;
+  if (hipMemcpy(mem, host.data(), item_bytes, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(static_cast<char*>(mem) + item_bytes, fs.data(), step_bytes, hipMemcpyHostToDevice) !=
+          hipSuccess) {
     (void)hipFree(mem);
     return HBMC_ERR_HIP;
   }
   p->dev = static_cast<DevItem*>(mem);
+  p->dev_steps = reinterpret_cast<FusedStep*>(static_cast<char*>(mem) + item_bytes);
   p->device = dev;
   return HBMC_OK;
 }
@@ -170,9 +181,8 @@ hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e) {
 }
 
 hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
-                      int op, int first, int last, bool whole, std::vector<StepLaunch>* steps,
-                      RankPtrs* ptrs) {
-  steps->clear();
+                      int op, int first, int last, bool whole, std::vector<KernelDesc>* launches) {
+  launches->clear();
   if (!c || !valid_op(op) || !valid_coll(coll) || elem_bytes(dtype) == 0) return HBMC_ERR_INVALID_ARG;
   const uint32_t e = elem_bytes(dtype);
   if (count > SIZE_MAX / e) return HBMC_ERR_INVALID_ARG;
@@ -193,12 +203,26 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
   st = upload(p);
   if (st != HBMC_OK) return st;
 
-  std::memset(ptrs, 0, sizeof(*ptrs));
+  RankPtrs ptrs;
+  std::memset(&ptrs, 0, sizeof(ptrs));
   const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0]) & 15u);
   bool aligned = true;
   for (int r = 0; r < P; ++r) {
-    ptrs->p[r] = static_cast<unsigned char*>(bufs[r]);
+    ptrs.p[r] = static_cast<unsigned char*>(bufs[r]);
     aligned = aligned && (reinterpret_cast<uintptr_t>(bufs[r]) & 15u) == phase;
+  }
+  // small enough: the whole step range as one single-workgroup launch
+  uint64_t bytes = 0;
+  bool fits = aligned && c->fused_limit > 0;
+  for (int s = first; s < last && fits; ++s) {
+    bytes += p->sched.steps[s].hbm_bytes;
+    fits = p->sched.steps[s].items.size() <= kFusedMaxItems && bytes <= c->fused_limit;
+  }
+  if (fits && bytes > 0) {
+    KernelDesc k;
+    describe_fused(dtype, op, ptrs, p->dev, p->dev_steps + first, static_cast<uint32_t>(last - first), phase, &k);
+    launches->push_back(k);
+    return HBMC_OK;
   }
   for (int s = first; s < last; ++s) {
     const Step& step = p->sched.steps[s];
@@ -215,20 +239,26 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     L.aligned = aligned;
     L.phase = phase;
     L.xcd_split = c->xcd_split;
-    steps->push_back(L);
+    KernelDesc k;
+    if (describe_step(L, ptrs, &k) != hipSuccess) return HBMC_ERR_HIP;
+    launches->push_back(k);
   }
   return HBMC_OK;
 }
 
+hbmc_status_t launch(KernelDesc& k, void* stream) {
+  k.bind();
+  const hipError_t e = hipLaunchKernel(k.func, k.grid, k.block, k.argv, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return HBMC_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? HBMC_OK : HBMC_ERR_HIP;
+}
+
 hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
                   int op, int first, int last, bool whole, void* stream) {
-  std::vector<StepLaunch> steps;
-  RankPtrs ptrs;
-  hbmc_status_t st = prepare(c, coll, root, bufs, count, dtype, op, first, last, whole, &steps, &ptrs);
-  if (st != HBMC_OK) return st;
-  for (const StepLaunch& L : steps)
-    if (launch_step(L, ptrs, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
-  return HBMC_OK;
+  std::vector<KernelDesc> launches;
+  hbmc_status_t st = prepare(c, coll, root, bufs, count, dtype, op, first, last, whole, &launches);
+  for (size_t i = 0; st == HBMC_OK && i < launches.size(); ++i) st = launch(launches[i], stream);
+  return st;
 }
 
 namespace {
@@ -294,9 +324,8 @@ hbmc_status_t run_out_of_place(hbmc_comm* c, int coll, int root, const void* con
     }
     moved.push_back(r);
   }
-  std::vector<StepLaunch> steps;
-  RankPtrs ptrs;
-  st = prepare(c, coll, root, recv, count, dtype, op, 0, 0, true, &steps, &ptrs);
+  std::vector<KernelDesc> launches;
+  st = prepare(c, coll, root, recv, count, dtype, op, 0, 0, true, &launches);
   if (st != HBMC_OK) return st;
   if (!moved.empty()) {
     Plan* lc = nullptr;
@@ -329,9 +358,8 @@ hbmc_status_t run_out_of_place(hbmc_comm* c, int coll, int root, const void* con
       if (launch_step(L, cp, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
     }
   }
-  for (const StepLaunch& L : steps)
-    if (launch_step(L, ptrs, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
-  return HBMC_OK;
+  for (size_t i = 0; st == HBMC_OK && i < launches.size(); ++i) st = launch(launches[i], stream);
+  return st;
 }
 
 }  // namespace hbmc

@@ -22,7 +22,8 @@ bool valid_op(int op);
 struct Plan {
   Schedule sched;
   std::vector<size_t> first_item;  // offset of each step's items in the device table
-  DevItem* dev = nullptr;
+  DevItem* dev = nullptr;          // all items, step after step
+  FusedStep* dev_steps = nullptr;  // one entry per step, for the single-workgroup kernel
   int device = -1;
 };
 
@@ -34,6 +35,7 @@ struct hbmc_comm {
   bool auto_select = false;
   double alpha_us = 4.4;      // launch-to-launch cost of one step, measured eager on MI355X
   double beta_gbps = 6400.0;  // sustained HBM rate of the step kernels, measured
+  uint64_t fused_limit = 0;   // run whole step ranges moving <= this many bytes as one launch
   bool xcd_split = false;
   // (topology index, coll, root, count, dtype) -> plan
   std::map<std::tuple<int, int, int, uint64_t, int>, std::unique_ptr<hbmc::Plan>> plans;
@@ -54,12 +56,15 @@ hbmc_status_t choose_topology(hbmc_comm* c, int coll, int root, size_t count, in
 hbmc_status_t upload(Plan* p);
 // Non-null, element-aligned, pairwise disjoint rank buffers of count elements.
 hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e);
-// Validate a call and list the launches of its steps [first, last) (all of
-// them when `whole`); uploads the plan's device table.  No launches for
-// count == 0 or P == 1.
+// Validate a call and describe the launches of its steps [first, last) (all
+// of them when `whole`): one step kernel per non-empty step, or a single
+// workgroup kernel for the whole range when it moves no more than the
+// communicator's fused limit.  Uploads the plan's device tables.  No
+// launches for count == 0 or P == 1.
 hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
-                      int op, int first, int last, bool whole, std::vector<StepLaunch>* steps,
-                      RankPtrs* ptrs);
+                      int op, int first, int last, bool whole, std::vector<KernelDesc>* launches);
+// Enqueue one described launch on `stream`.
+hbmc_status_t launch(KernelDesc& k, void* stream);
 // Validate and enqueue steps [first, last) of a collective (all of them when
 // `whole`) on `stream`, one kernel launch per non-empty step.
 hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,

@@ -85,20 +85,15 @@ hbmc_status_t hbmc_graph_build(hbmc_graph_t g) {
     std::vector<hipGraphNode_t> deps;
     for (size_t j = 0; j < i; ++j)
       if (overlaps(n, g->nodes[j])) deps.push_back(last[j]);
-    std::vector<StepLaunch> steps;
-    RankPtrs ptrs;
-    st = prepare(n.comm, n.coll, n.root, n.bufs.data(), n.count, n.dtype, n.op, 0, 0, true, &steps, &ptrs);
+    std::vector<KernelDesc> launches;
+    st = prepare(n.comm, n.coll, n.root, n.bufs.data(), n.count, n.dtype, n.op, 0, 0, true, &launches);
     if (st != HBMC_OK) break;
-    if (steps.empty()) {
+    if (launches.empty()) {
       if (hipGraphAddEmptyNode(&last[i], g->graph, deps.data(), deps.size()) != hipSuccess) st = HBMC_ERR_HIP;
       continue;
     }
-    for (const StepLaunch& L : steps) {
-      KernelDesc k;
-      if (describe_step(L, ptrs, &k) != hipSuccess) {
-        st = HBMC_ERR_HIP;
-        break;
-      }
+    for (KernelDesc& k : launches) {
+      k.bind();
       hipKernelNodeParams prm{};
       prm.func = const_cast<void*>(k.func);
       prm.gridDim = k.grid;
@@ -111,7 +106,7 @@ hbmc_status_t hbmc_graph_build(hbmc_graph_t g) {
         st = HBMC_ERR_HIP;
         break;
       }
-      deps.assign(1, node);  // the next step waits for this one
+      deps.assign(1, node);  // the next launch waits for this one
       last[i] = node;
     }
   }

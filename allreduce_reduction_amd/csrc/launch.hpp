@@ -34,23 +34,42 @@ struct StepLaunch {
   bool xcd_split;         // give each XCD one contiguous range of tiles
 };
 
-// One kernel launch of a step: kernel, shape and argument values, usable with
+// A step of the single-workgroup plan kernel (device table).
+constexpr uint32_t kFusedMaxItems = 256;
+struct FusedStep {
+  uint32_t first_item, nitems, mode, pad;
+};
+
+// One kernel launch: kernel, shape and argument values, usable with
 // hipLaunchKernel or as a kernel graph node.
 struct KernelDesc {
+  enum Kind { kVector = 0, kElement = 1, kFused = 2 };
+  Kind kind = kVector;
   const void* func = nullptr;
   dim3 grid, block;
   RankPtrs ptrs;
   const DevItem* items = nullptr;
+  const FusedStep* steps = nullptr;  // plan kernel only
+  uint32_t nsteps = 0;               // plan kernel only
   uint32_t phase = 0, xcd = 0;
-  int nargs = 0;   // 2 for the element-wise kernel, 4 for the vector kernel
-  void* argv[4];   // filled by bind(); valid while this object lives
+  void* argv[5];  // filled by bind(); valid while this object lives
   void bind() {
     argv[0] = &ptrs;
     argv[1] = &items;
-    argv[2] = &phase;
-    argv[3] = &xcd;
+    if (kind == kFused) {
+      argv[2] = &steps;
+      argv[3] = &nsteps;
+      argv[4] = &phase;
+    } else {
+      argv[2] = &phase;
+      argv[3] = &xcd;
+    }
   }
 };
+
+// The single-workgroup kernel running `nsteps` steps of a plan.
+void describe_fused(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const FusedStep* steps,
+                    uint32_t nsteps, uint32_t phase, KernelDesc* k);
 
 // Choose the kernel and launch shape of one step.
 hipError_t describe_step(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* out);

@@ -21,166 +21,19 @@
 // +0 and give the canonical quiet NaN when either operand is NaN.
 #include <hip/hip_runtime.h>
 
+#include "elemops.hpp"
 #include "launch.hpp"
 #include "plan.hpp"
 
 namespace hbmc {
 namespace {
 
+using namespace dev;
+
 constexpr int kThreads = 64;        // vector kernel: one wave per workgroup
 constexpr int kVecPerThread = 1;    // 16-byte vectors per lane per operand
 constexpr uint64_t kTileVecs = uint64_t(kThreads) * kVecPerThread;
 constexpr int kElemThreads = 256;   // element-wise kernel
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-enum { kF32 = 0, kF16 = 1, kBF16 = 2, kI32 = 3, kI8 = 4 };
-enum { kSum = 0, kProd = 1, kMax = 2, kMin = 3 };
-
-template <int DT>
-struct Width {
-  static constexpr uint32_t bytes = (DT == kF32 || DT == kI32) ? 4 : (DT == kI8 ? 1 : 2);
-};
-
-// ------------------------------------------------------------- element ops
-
-__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
-__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
-
-// Monotone map of an IEEE bit pattern (sign bit `sb`) to an unsigned key:
-// negative values reversed below positive ones, so -0 sorts under +0.
-template <uint32_t SB, uint32_t MASK>
-__device__ __forceinline__ uint32_t order_key(uint32_t u) {
-  return (u & SB) ? (~u & MASK) : (u | SB);
-}
-
-template <int OP>
-__device__ __forceinline__ uint32_t op_f32(uint32_t a, uint32_t b) {
-  if constexpr (OP == kSum) {
-    return f2u(u2f(a) + u2f(b));
-  } else if constexpr (OP == kProd) {
-    return f2u(u2f(a) * u2f(b));
-  } else {
-    const bool nan = ((a & 0x7fffffffu) > 0x7f800000u) | ((b & 0x7fffffffu) > 0x7f800000u);
-    const uint32_t ka = order_key<0x80000000u, 0xffffffffu>(a);
-    const uint32_t kb = order_key<0x80000000u, 0xffffffffu>(b);
-    const uint32_t r = (OP == kMax) ? (ka >= kb ? a : b) : (ka <= kb ? a : b);
-    return nan ? 0x7fc00000u : r;
-  }
-}
-
-__device__ __forceinline__ float widen_f16(uint32_t h) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
-}
-__device__ __forceinline__ uint32_t narrow_f16(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // v_cvt_f16_f32, nearest even
-}
-__device__ __forceinline__ float widen_bf16(uint32_t h) { return u2f(h << 16); }
-__device__ __forceinline__ uint32_t narrow_bf16(float f) {
-  const uint32_t u = f2u(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet the NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                  // nearest even
-}
-
-// One 16-bit lane (value in the low half of the word).
-template <int DT, int OP>
-__device__ __forceinline__ uint32_t op_h16(uint32_t a, uint32_t b) {
-  if constexpr (OP == kSum || OP == kProd) {
-    const float x = DT == kF16 ? widen_f16(a) : widen_bf16(a);
-    const float y = DT == kF16 ? widen_f16(b) : widen_bf16(b);
-    const float z = OP == kSum ? x + y : x * y;
-    return DT == kF16 ? narrow_f16(z) : narrow_bf16(z);
-  } else {
-    constexpr uint32_t inf = DT == kF16 ? 0x7c00u : 0x7f80u;
-    constexpr uint32_t qnan = DT == kF16 ? 0x7e00u : 0x7fc0u;
-    const bool nan = ((a & 0x7fffu) > inf) | ((b & 0x7fffu) > inf);
-    const uint32_t ka = order_key<0x8000u, 0xffffu>(a);
-    const uint32_t kb = order_key<0x8000u, 0xffffu>(b);
-    const uint32_t r = (OP == kMax) ? (ka >= kb ? a : b) : (ka <= kb ? a : b);
-    return nan ? qnan : r;
-  }
-}
-
-template <int OP>
-__device__ __forceinline__ int op_int(int x, int y) {
-  if constexpr (OP == kSum) return static_cast<int>(static_cast<uint32_t>(x) + static_cast<uint32_t>(y));
-  if constexpr (OP == kProd) return static_cast<int>(static_cast<uint32_t>(x) * static_cast<uint32_t>(y));
-  if constexpr (OP == kMax) return x >= y ? x : y;
-  return x <= y ? x : y;
-}
-
-// The op on one 32-bit word of packed elements.
-template <int DT, int OP>
-__device__ __forceinline__ uint32_t op_word(uint32_t a, uint32_t b) {
-  if constexpr (DT == kF32) {
-    return op_f32<OP>(a, b);
-  } else if constexpr (DT == kF16 || DT == kBF16) {
-    return op_h16<DT, OP>(a & 0xffffu, b & 0xffffu) | (op_h16<DT, OP>(a >> 16, b >> 16) << 16);
-  } else if constexpr (DT == kI32) {
-    return static_cast<uint32_t>(op_int<OP>(static_cast<int>(a), static_cast<int>(b)));
-  } else {
-    uint32_t r = 0;
-#pragma unroll
-    for (int k = 0; k < 32; k += 8) {
-      const int x = static_cast<int8_t>(a >> k), y = static_cast<int8_t>(b >> k);
-      r |= (static_cast<uint32_t>(op_int<OP>(x, y)) & 0xffu) << k;
-    }
-    return r;
-  }
-}
-
-template <int DT, int OP>
-__device__ __forceinline__ u32x4 op_vec(u32x4 a, u32x4 b) {
-  u32x4 r;
-  r.x = op_word<DT, OP>(a.x, b.x);
-  r.y = op_word<DT, OP>(a.y, b.y);
-  r.z = op_word<DT, OP>(a.z, b.z);
-  r.w = op_word<DT, OP>(a.w, b.w);
-  return r;
-}
-
-__device__ __forceinline__ u32x4 load_vec(const u32x4* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void store_vec(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
-
-template <uint32_t E>
-__device__ __forceinline__ uint32_t load_elem(const unsigned char* p) {
-  if constexpr (E == 4) return *reinterpret_cast<const uint32_t*>(p);
-  if constexpr (E == 2) return *reinterpret_cast<const uint16_t*>(p);
-  return *p;
-}
-template <uint32_t E>
-__device__ __forceinline__ void store_elem(unsigned char* p, uint32_t v) {
-  if constexpr (E == 4) *reinterpret_cast<uint32_t*>(p) = v;
-  else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(v);
-  else *p = static_cast<unsigned char>(v);
-}
-
-// Combination of an item's sources at one element (byte offset `off`).
-template <int DT, int OP, int MODE>
-__device__ __forceinline__ uint32_t combine_elem(const RankPtrs& ptrs, const DevItem* it, int ns,
-                                                 uint64_t off) {
-  constexpr uint32_t E = Width<DT>::bytes;
-  if constexpr (MODE == kCopy) {
-    return load_elem<E>(ptrs.p[it->rank[0]] + off);
-  } else if constexpr (MODE == kFold) {
-    uint32_t acc = load_elem<E>(ptrs.p[it->rank[0]] + off);
-    for (int s = 1; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(ptrs.p[it->rank[s]] + off));
-    return acc;
-  } else {
-    uint32_t acc = load_elem<E>(ptrs.p[it->rank[1]] + off);
-    for (int s = 2; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(ptrs.p[it->rank[s]] + off));
-    return op_word<DT, OP>(load_elem<E>(ptrs.p[it->rank[0]] + off), acc);
-  }
-}
-
-template <int DT, int OP, int MODE>
-__device__ __forceinline__ void do_elem(const RankPtrs& ptrs, const DevItem* it, int ns, int nd,
-                                        uint64_t elem) {
-  constexpr uint32_t E = Width<DT>::bytes;
-  const uint64_t off = elem * E;
-  const uint32_t v = combine_elem<DT, OP, MODE>(ptrs, it, ns, off);
-  for (int d = 0; d < nd; ++d) store_elem<E>(ptrs.p[it->rank[ns + d]] + off, v);
-}
 
 // ------------------------------------------------------------- kernels
 
@@ -322,7 +175,7 @@ void describe_typed(const StepLaunch& s, KernelDesc* k) {
     if (gx < 1) gx = 1;
     k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
     k->block = dim3(kElemThreads);
-    k->nargs = 2;
+    k->kind = KernelDesc::kElement;
     switch (s.mode) {
       case kCopy: k->func = fn(step_elem<DT, OP, kCopy>); break;
       case kFold: k->func = fn(step_elem<DT, OP, kFold>); break;
@@ -334,7 +187,7 @@ void describe_typed(const StepLaunch& s, KernelDesc* k) {
   const uint64_t gx = (vecs + kTileVecs - 1) / kTileVecs;
   k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
   k->block = dim3(kThreads);
-  k->nargs = 4;
+  k->kind = KernelDesc::kVector;
   k->xcd = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? 1u : 0u;
   // item shapes of the schedules get compile-time source counts: ring / RHD
   // (2 sources) and the pipeline with 1, 2, 4 or 8 ranks per server; any

@@ -166,6 +166,21 @@ def suite(a):
         torch.cuda.empty_cache()
         nbytes *= 4
 
+    # small messages: one launch per step versus the single-workgroup plan kernel
+    for P in (8, 16):
+        for algo in ("ring", "rhd", "flat"):
+            for kib in (1, 4, 16, 64, 256, 1024):
+                L = kib * 1024 // 2
+                bufs = upload("rhd_bf16_normal", P, L)
+                with hc.Comm(P, algo) as c:
+                    info = c.plan_info("allreduce", L, "bf16")
+                    te = time_calls(lambda: c.allreduce(bufs, "bf16", "max"), 200, 20)
+                    c.set_fused_limit(1 << 40)
+                    tf = time_calls(lambda: c.allreduce(bufs, "bf16", "max"), 200, 20)
+                emit(workload="small_fused", algo=algo, P=P, dtype="bf16", op="max", bytes_per_rank=L * 2,
+                     hbm_bytes=info["hbm_bytes"], steps=info["nsteps"], eager_us=round(te * 1e6, 2),
+                     fused_us=round(tf * 1e6, 2))
+
     # AllReduce algorithms side by side, and the AUTO communicator's choice
     for P in (8, 16):
         nbytes = 4096

@@ -111,6 +111,19 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
 hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
 
 /*
+ * Fewer launches for small collectives ([RHD] "耗时计算": every step pays a
+ * fixed alpha).  A call whose steps move at most `max_bytes` algorithmic HBM
+ * bytes in total, whose buffers share one 16-byte phase and whose steps have
+ * at most 256 work items each, runs all its steps in one launch of a single
+ * 1024-thread workgroup, with a workgroup barrier between consecutive steps
+ * (same items, element ops and order; bit-identical results).  0 (the
+ * default, unless the environment variable HBMC_FUSED_LIMIT gives a byte
+ * count) keeps one launch per step.  Also used by hbmc_run_steps and graph
+ * mode.  Host only.
+ */
+hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes);
+
+/*
  * AUTO selection ([RHD] "RHD 在 HCCL 中的定位与启用方式": the algorithm is
  * chosen adaptively from product, data size and rank count; [RHD] "耗时计算"
  * and [TOPO] "AllReduce算法实现": alpha-beta cost models).  An AUTO

@@ -293,3 +293,65 @@ def test_out_of_place(algo, P):
                         refops.assert_same(dtype, got, want[r], f"{coll} rank {r}")
                     if r > 0:
                         assert np.array_equal(to_host(send[r], dtype).view(np.uint16), xs[r].view(np.uint16))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_parity_fused_single_workgroup(dtype):
+    """Whole schedules run as one single-workgroup launch give the oracle's bits."""
+    rng = np.random.default_rng(zlib.crc32(("fused" + dtype).encode()))
+    cases = [("ring", 5, (5, "ring"), {}), ("rhd", 8, (8, "rhd"), {}), ("rhd", 6, (6, "rhd"), {}),
+             ("pipeline", 8, (8, "pipeline", 2, 4, 4096), dict(S=2, M=4, loop_bytes=4096)),
+             ("flat", 7, (7, "flat"), {}), ("tree", 13, (13, "tree", 0, 3), dict(M=3)),
+             ("hier", 6, (6, "hier", 3, 2), dict(S=3, M=2))]
+    for algo, P, args, kw in cases:
+        with hc.Comm(*args) as comm:
+            comm.set_fused_limit(1 << 40)
+            colls = ["allreduce"] if algo in ("flat", "tree", "hier") else ["allreduce", "reduce_scatter", "all_gather"]
+            if algo == "rhd":
+                colls += ["reduce", "broadcast"]
+            for coll in colls:
+                op = str(rng.choice(OPS))
+                L = int(rng.choice([1, 5, 1000, 3 * 4096 + 7]))
+                say(f"case fused algo={algo} coll={coll} dtype={dtype} op={op} P={P} L={L}")
+                xs = make_inputs(dtype, op, P, L, seed=L + P)
+                dev = [to_dev(x, dtype) for x in xs]
+                if coll == "reduce":
+                    comm.reduce(dev, dtype, op, root=P - 1)
+                elif coll == "broadcast":
+                    comm.broadcast(dev, dtype, root=P - 1)
+                else:
+                    getattr(comm, coll)(dev, dtype, op)
+                torch.cuda.synchronize()
+                want = [x.copy() for x in xs]
+                oracle.run(coll, algo, want, dtype, op, root=P - 1, **kw)
+                for r in ([P - 1] if coll == "reduce" else range(P)):
+                    refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"fused {algo} {coll} rank {r}")
+
+
+def test_fused_step_ranges_and_graph():
+    """run_steps over sub-ranges and graph nodes also take the single-workgroup path."""
+    P, L, dtype = 8, 5000, "bf16"
+    xs = make_inputs(dtype, "sum", P, L, seed=3)
+    with hc.Comm(P, "ring") as comm:
+        comm.set_fused_limit(1 << 40)
+        n = comm.plan_info("allreduce", L, dtype)["nsteps"]
+        dev = [to_dev(x, dtype) for x in xs]
+        want = [x.copy() for x in xs]
+        for a, b in ((0, 3), (3, 4), (4, n)):
+            comm.run_steps("allreduce", dev, a, b, dtype, "sum")
+            torch.cuda.synchronize()
+            oracle.run("allreduce", "ring", want, dtype, "sum", first_step=a, last_step=b)
+            for r in range(P):
+                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"steps [{a},{b}) rank {r}")
+        gb = [to_dev(x, dtype) for x in xs]
+        with hc.Graph() as g:
+            g.add(comm, "allreduce", gb, dtype, "sum")
+            g.build()
+            for rep in range(3):
+                for t, x in zip(gb, xs):
+                    t.copy_(to_dev(x, dtype))
+                torch.cuda.synchronize()
+                g.launch()
+                torch.cuda.synchronize()
+                for r in range(P):
+                    refops.assert_same(dtype, to_host(gb[r], dtype), want[r], f"graph replay {rep} rank {r}")
