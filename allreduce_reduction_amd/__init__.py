@@ -28,7 +28,8 @@ EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_redu
            "hbmc_all_gather", "hbmc_reduce", "hbmc_broadcast", "hbmc_collective_oop", "hbmc_run_steps", "hbmc_plan_info", "hbmc_plan_step_info",
            "hbmc_plan_items", "hbmc_status_string", "hbmc_graph_create", "hbmc_graph_add",
            "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy", "hbmc_comm_set_cost_model",
-           "hbmc_auto_choice", "hbmc_comm_set_fused_limit")
+           "hbmc_auto_choice", "hbmc_comm_set_fused_limit",
+           "hbmc_comm_set_columns", "hbmc_plan_chunks")
 
 
 class HbmcError(RuntimeError):
@@ -46,6 +47,12 @@ class Item(ctypes.Structure):
     _fields_ = [("step", ctypes.c_int32), ("mode", ctypes.c_int32), ("nsrc", ctypes.c_int32),
                 ("ndst", ctypes.c_int32), ("begin", ctypes.c_uint64), ("count", ctypes.c_uint64),
                 ("rank", ctypes.c_uint8 * 128)]
+
+
+class Chunk(ctypes.Structure):
+    _fields_ = [("begin", ctypes.c_uint64), ("count", ctypes.c_uint32), ("item", ctypes.c_uint32),
+                ("step", ctypes.c_uint32), ("dep_lo", ctypes.c_uint32), ("dep_hi", ctypes.c_uint32),
+                ("pad", ctypes.c_uint32)]
 
 
 _lib = None
@@ -81,6 +88,9 @@ def load_library():
         L.hbmc_plan_step_info.argtypes = [vp, ci, ci, sz, ci, ci, ctypes.POINTER(ci), u64p]
         L.hbmc_plan_items.restype = ci
         L.hbmc_plan_items.argtypes = [vp, ci, ci, sz, ci, ctypes.POINTER(Item), sz, ctypes.POINTER(sz)]
+        L.hbmc_plan_chunks.restype = ci
+        L.hbmc_plan_chunks.argtypes = [vp, ci, ci, sz, ci, ctypes.c_uint64, ctypes.POINTER(Chunk), sz,
+                                       ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_uint32), sz, ctypes.POINTER(sz)]
         L.hbmc_graph_create.restype = ci
         L.hbmc_graph_create.argtypes = [ctypes.POINTER(vp)]
         L.hbmc_graph_add.restype = ci
@@ -93,6 +103,8 @@ def load_library():
         L.hbmc_graph_destroy.argtypes = [vp]
         L.hbmc_comm_set_fused_limit.restype = ci
         L.hbmc_comm_set_fused_limit.argtypes = [vp, ctypes.c_uint64]
+        L.hbmc_comm_set_columns.restype = ci
+        L.hbmc_comm_set_columns.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint64]
         L.hbmc_comm_set_cost_model.restype = ci
         L.hbmc_comm_set_cost_model.argtypes = [vp, ctypes.c_double, ctypes.c_double]
         L.hbmc_auto_choice.restype = ci
@@ -217,6 +229,12 @@ class Comm:
         """Run calls moving at most max_bytes as one single-workgroup launch."""
         _check(load_library().hbmc_comm_set_fused_limit(self._h, max_bytes), "hbmc_comm_set_fused_limit")
 
+    def set_columns(self, max_total_bytes: int, column_bytes: int = 0):
+        """Run multi-step calls over at most max_total_bytes (P * count * e) as one
+        column-kernel launch (0: off); column_bytes 0 picks the column length."""
+        _check(load_library().hbmc_comm_set_columns(self._h, max_total_bytes, column_bytes),
+               "hbmc_comm_set_columns")
+
     # -- AUTO selection (host only)
     def set_cost_model(self, alpha_us: float, beta_gbps: float):
         _check(load_library().hbmc_comm_set_cost_model(self._h, alpha_us, beta_gbps), "hbmc_comm_set_cost_model")
@@ -257,6 +275,19 @@ class Comm:
             out.append(dict(step=it.step, mode=MODE[it.mode], begin=it.begin, count=it.count,
                             src=ranks[:it.nsrc], dst=ranks[it.nsrc:]))
         return out
+
+    def plan_chunks(self, coll: str, count: int, dtype: str, chunk_bytes: int, root: int = 0):
+        """Column-kernel chunks (dicts: begin, count, item, step, deps) of a collective (host only)."""
+        L = load_library()
+        n, nd = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(L.hbmc_plan_chunks(self._h, COLL[coll], root, count, DTYPE[dtype], chunk_bytes, None, 0,
+                                  ctypes.byref(n), None, 0, ctypes.byref(nd)), "hbmc_plan_chunks")
+        arr = (Chunk * max(n.value, 1))()
+        deps = (ctypes.c_uint32 * max(nd.value, 1))()
+        _check(L.hbmc_plan_chunks(self._h, COLL[coll], root, count, DTYPE[dtype], chunk_bytes, arr, n.value,
+                                  ctypes.byref(n), deps, nd.value, ctypes.byref(nd)), "hbmc_plan_chunks")
+        return [dict(begin=c.begin, count=c.count, item=c.item, step=c.step, deps=list(deps[c.dep_lo:c.dep_hi]))
+                for c in arr[:n.value]]
 
 
 class Graph:

@@ -84,6 +84,7 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
   c->topos = topos;
   c->auto_select = a == HBMC_ALGO_AUTO;
   if (const char* fl = std::getenv("HBMC_FUSED_LIMIT")) c->fused_limit = std::strtoull(fl, nullptr, 10);
+  if (const char* cl = std::getenv("HBMC_COLUMNS_LIMIT")) c->columns_limit = std::strtoull(cl, nullptr, 10);
   const char* xs = std::getenv("HBMC_XCD_SPLIT");
   c->xcd_split = xs && xs[0] == '1';
   *out = c;
@@ -93,6 +94,14 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
 hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes) {
   if (!comm) return HBMC_ERR_INVALID_ARG;
   comm->fused_limit = max_bytes;
+  return HBMC_OK;
+}
+
+hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, uint64_t column_bytes) {
+  if (!comm) return HBMC_ERR_INVALID_ARG;
+  if (column_bytes != 0 && (column_bytes < 16 || column_bytes > (uint64_t(1) << 31))) return HBMC_ERR_INVALID_ARG;
+  comm->columns_limit = max_total_bytes;
+  comm->column_bytes = column_bytes;
   return HBMC_OK;
 }
 
@@ -124,8 +133,10 @@ hbmc_status_t hbmc_auto_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
 hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
   if (!comm) return HBMC_ERR_INVALID_ARG;
   hbmc_status_t st = HBMC_OK;
-  for (auto& kv : comm->plans)
+  for (auto& kv : comm->plans) {
     if (kv.second->dev && hipFree(kv.second->dev) != hipSuccess) st = HBMC_ERR_HIP;
+    if (kv.second->cols_mem && hipFree(kv.second->cols_mem) != hipSuccess) st = HBMC_ERR_HIP;
+  }
   delete comm;
   return st;
 }
@@ -214,6 +225,26 @@ hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, int root, size
     }
   }
   if (n_items) *n_items = k;
+  return HBMC_OK;
+}
+
+hbmc_status_t hbmc_plan_chunks(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
+                               hbmc_dtype_t dtype, uint64_t chunk_bytes, hbmc_chunk_t* chunks, size_t cap,
+                               size_t* n_chunks, uint32_t* deps, size_t dcap, size_t* n_deps) {
+  if (chunk_bytes < 16 || chunk_bytes > (uint64_t(1) << 31)) return HBMC_ERR_INVALID_ARG;
+  Plan* p = nullptr;
+  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+  if (st != HBMC_OK) return st;
+  ColumnTable f;
+  if (!build_columns(p->sched, comm->topos[0].P, column_elems(chunk_bytes, count, elem_bytes(dtype), 1), &f))
+    return HBMC_ERR_INVALID_ARG;
+  for (size_t i = 0; chunks && i < f.chunks.size() && i < cap; ++i) {
+    const ColumnChunk& c = f.chunks[i];
+    chunks[i] = hbmc_chunk_t{c.begin, c.count, c.item, c.step, c.dep_lo, c.dep_hi, 0};
+  }
+  for (size_t i = 0; deps && i < f.deps.size() && i < dcap; ++i) deps[i] = f.deps[i];
+  if (n_chunks) *n_chunks = f.chunks.size();
+  if (n_deps) *n_deps = f.deps.size();
   return HBMC_OK;
 }
 

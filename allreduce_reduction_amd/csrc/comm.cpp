@@ -165,6 +165,55 @@ hbmc_status_t upload(Plan* p) {
   return HBMC_OK;
 }
 
+uint64_t column_elems(uint64_t column_bytes, uint64_t count, uint32_t e, uint32_t compute_units) {
+  if (column_bytes > 0) return std::max<uint64_t>(16, column_bytes / 16 * 16) / e;
+  const uint64_t cols = uint64_t(compute_units) * 4;
+  uint64_t b = (count * e + cols - 1) / cols;
+  b = std::max<uint64_t>(1024, (b + 1023) / 1024 * 1024);
+  return b / e;
+}
+
+hbmc_status_t upload_columns(Plan* p, int P, uint64_t chunk_elems) {
+  if (p->cols_mem && p->cols.chunk_elems == chunk_elems) return HBMC_OK;
+  if (p->cols_mem) {
+    if (hipDeviceSynchronize() != hipSuccess || hipFree(p->cols_mem) != hipSuccess) return HBMC_ERR_HIP;
+    p->cols_mem = nullptr;
+  }
+  ColumnTable& f = p->cols;
+  if (!build_columns(p->sched, P, chunk_elems, &f)) return HBMC_ERR_INVALID_ARG;
+  const size_t n = f.chunks.size();
+  std::vector<DevChunk> host(n);
+  for (size_t i = 0; i < n; ++i) {
+    const ColumnChunk& c = f.chunks[i];
+    host[i].begin = c.begin;
+    host[i].count = c.count;
+    host[i].item = c.item;
+    host[i].mode = static_cast<uint32_t>(p->sched.steps[c.step].mode);
+    host[i].step = c.step;
+    host[i].pad0 = host[i].pad1 = 0;
+  }
+  auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+  const size_t b_chunks = up(n * sizeof(DevChunk) + 16);
+  const size_t b_list = up(f.col_list.size() * sizeof(uint32_t) + 4);
+  const size_t b_off = up(f.col_off.size() * sizeof(uint32_t) + 4);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, b_chunks + b_list + b_off) != hipSuccess) return HBMC_ERR_NOMEM;
+  char* base = static_cast<char*>(mem);
+  if ((n && hipMemcpy(base, host.data(), n * sizeof(DevChunk), hipMemcpyHostToDevice) != hipSuccess) ||
+      (!f.col_list.empty() && hipMemcpy(base + b_chunks, f.col_list.data(), f.col_list.size() * sizeof(uint32_t),
+                                        hipMemcpyHostToDevice) != hipSuccess) ||
+      (!f.col_off.empty() && hipMemcpy(base + b_chunks + b_list, f.col_off.data(),
+                                       f.col_off.size() * sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess)) {
+    (void)hipFree(mem);
+    return HBMC_ERR_HIP;
+  }
+  p->cols_mem = mem;
+  p->dev_chunks = reinterpret_cast<DevChunk*>(base);
+  p->dev_col_list = reinterpret_cast<uint32_t*>(base + b_chunks);
+  p->dev_col_off = reinterpret_cast<uint32_t*>(base + b_chunks + b_list);
+  return HBMC_OK;
+}
+
 hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e) {
   if (!bufs) return HBMC_ERR_INVALID_ARG;
   const uint64_t bytes = uint64_t(count) * e;
@@ -179,6 +228,23 @@ hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e) {
   }
   return HBMC_OK;
 }
+
+namespace {
+
+uint32_t compute_units() {
+  static uint32_t cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = static_cast<uint32_t>(cus);
+  }
+  return cached[dev];
+}
+
+}  // namespace
 
 hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
                       int op, int first, int last, bool whole, std::vector<KernelDesc>* launches) {
@@ -221,6 +287,22 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
   if (fits && bytes > 0) {
     KernelDesc k;
     describe_fused(dtype, op, ptrs, p->dev, p->dev_steps + first, static_cast<uint32_t>(last - first), phase, &k);
+    launches->push_back(k);
+    return HBMC_OK;
+  }
+  // several steps over a small working set: one column-kernel launch
+  int busy = 0;
+  for (int s = first; s < last; ++s) busy += p->sched.steps[s].items.empty() ? 0 : 1;
+  if (aligned && busy > 1 && c->columns_limit > 0 && uint64_t(count) * e <= c->columns_limit / uint64_t(P)) {
+    const uint32_t cus = compute_units();
+    st = upload_columns(p, P, column_elems(c->column_bytes, count, e, cus));
+    if (st != HBMC_OK) return st;
+    const ColumnTable& f = p->cols;
+    const uint32_t ncols = static_cast<uint32_t>(f.col_off.size() - 1);
+    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(ncols, cus * 8));
+    KernelDesc k;
+    describe_columns(dtype, op, ptrs, p->dev, p->dev_chunks, p->dev_col_list, p->dev_col_off, ncols,
+                     f.step_first[first], f.step_first[last], phase, grid, &k);
     launches->push_back(k);
     return HBMC_OK;
   }

@@ -8,6 +8,7 @@
 #include <tuple>
 #include <vector>
 
+#include "columns.hpp"
 #include "hbmcoll.h"
 #include "launch.hpp"
 #include "plan.hpp"
@@ -25,6 +26,12 @@ struct Plan {
   DevItem* dev = nullptr;          // all items, step after step
   FusedStep* dev_steps = nullptr;  // one entry per step, for the single-workgroup kernel
   int device = -1;
+  // column kernel tables (one allocation), built on first use
+  ColumnTable cols;
+  void* cols_mem = nullptr;
+  DevChunk* dev_chunks = nullptr;
+  uint32_t* dev_col_list = nullptr;
+  uint32_t* dev_col_off = nullptr;
 };
 
 }  // namespace hbmc
@@ -36,6 +43,8 @@ struct hbmc_comm {
   double alpha_us = 4.4;      // launch-to-launch cost of one step, measured eager on MI355X
   double beta_gbps = 6400.0;  // sustained HBM rate of the step kernels, measured
   uint64_t fused_limit = 0;   // run whole step ranges moving <= this many bytes as one launch
+  uint64_t columns_limit = 0;  // column kernel for calls whose P * count * e is at most this; 0: off
+  uint64_t column_bytes = 0;   // column length in bytes; 0: chosen per call
   bool xcd_split = false;
   // (topology index, coll, root, count, dtype) -> plan
   std::map<std::tuple<int, int, int, uint64_t, int>, std::unique_ptr<hbmc::Plan>> plans;
@@ -57,16 +66,27 @@ hbmc_status_t upload(Plan* p);
 // Non-null, element-aligned, pairwise disjoint rank buffers of count elements.
 hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e);
 // Validate a call and describe the launches of its steps [first, last) (all
-// of them when `whole`): one step kernel per non-empty step, or a single
-// workgroup kernel for the whole range when it moves no more than the
-// communicator's fused limit.  Uploads the plan's device tables.  No
-// launches for count == 0 or P == 1.
+// of them when `whole`): a single-workgroup kernel for the whole range when
+// it moves no more than the communicator's fused limit; else one column
+// kernel launch when the rank buffers' total size is within the
+// communicator's column limit and the range has two or more busy steps; else
+// one step kernel per non-empty step.  Both one-launch forms need buffers of
+// one 16-byte phase.  Uploads the plan's device tables.  No launches for
+// count == 0 or P == 1.
 hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
                       int op, int first, int last, bool whole, std::vector<KernelDesc>* launches);
+// Column length in elements for `column_bytes` (a multiple of 16 bytes, at
+// least 16) or, for 0, for a call of `count` elements: about four columns per
+// compute unit, no shorter than 1 KiB (one 16-byte vector per lane of a wave).
+uint64_t column_elems(uint64_t column_bytes, uint64_t count, uint32_t e, uint32_t compute_units);
+// Build and upload the plan's column tables for a column length of
+// `chunk_elems` (rebuilt when it changes; the old tables are freed after a
+// device synchronisation).
+hbmc_status_t upload_columns(Plan* p, int P, uint64_t chunk_elems);
 // Enqueue one described launch on `stream`.
 hbmc_status_t launch(KernelDesc& k, void* stream);
 // Validate and enqueue steps [first, last) of a collective (all of them when
-// `whole`) on `stream`, one kernel launch per non-empty step.
+// `whole`) on `stream`, with the launches prepare() describes.
 hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
                   int op, int first, int last, bool whole, void* stream);
 // Out-of-place: LocalCopy of send into recv where they differ (one copy

@@ -40,10 +40,17 @@ struct FusedStep {
   uint32_t first_item, nitems, mode, pad;
 };
 
+// A chunk of the column kernel (device table): elements [begin,
+// begin+count) of item `item` in step `step`.
+struct alignas(16) DevChunk {
+  uint64_t begin;
+  uint32_t count, item, mode, step, pad0, pad1;
+};
+
 // One kernel launch: kernel, shape and argument values, usable with
 // hipLaunchKernel or as a kernel graph node.
 struct KernelDesc {
-  enum Kind { kVector = 0, kElement = 1, kFused = 2 };
+  enum Kind { kVector = 0, kElement = 1, kFused = 2, kColumns = 3 };
   Kind kind = kVector;
   const void* func = nullptr;
   dim3 grid, block;
@@ -52,7 +59,12 @@ struct KernelDesc {
   const FusedStep* steps = nullptr;  // plan kernel only
   uint32_t nsteps = 0;               // plan kernel only
   uint32_t phase = 0, xcd = 0;
-  void* argv[5];  // filled by bind(); valid while this object lives
+  // column kernel only
+  const DevChunk* chunks = nullptr;
+  const uint32_t* col_list = nullptr;
+  const uint32_t* col_off = nullptr;
+  uint32_t ncols = 0, c_lo = 0, c_hi = 0;
+  void* argv[9];  // filled by bind(); valid while this object lives
   void bind() {
     argv[0] = &ptrs;
     argv[1] = &items;
@@ -60,12 +72,26 @@ struct KernelDesc {
       argv[2] = &steps;
       argv[3] = &nsteps;
       argv[4] = &phase;
+    } else if (kind == kColumns) {
+      argv[2] = &chunks;
+      argv[3] = &col_list;
+      argv[4] = &col_off;
+      argv[5] = &ncols;
+      argv[6] = &c_lo;
+      argv[7] = &c_hi;
+      argv[8] = &phase;
     } else {
       argv[2] = &phase;
       argv[3] = &xcd;
     }
   }
 };
+
+// The column kernel over chunks [c_lo, c_hi) of a plan: `grid` one-wave
+// workgroups, workgroup w running columns w, w + grid, ...
+void describe_columns(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const DevChunk* chunks,
+                      const uint32_t* col_list, const uint32_t* col_off, uint32_t ncols, uint32_t c_lo,
+                      uint32_t c_hi, uint32_t phase, uint32_t grid, KernelDesc* k);
 
 // The single-workgroup kernel running `nsteps` steps of a plan.
 void describe_fused(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const FusedStep* steps,

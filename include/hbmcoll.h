@@ -124,6 +124,26 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
 hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes);
 
 /*
+ * One launch per call for small working sets ([RHD] "耗时计算": every step
+ * pays a fixed alpha; [RING-RHD] "Ring AllReduce带宽最优的环形流水线": the
+ * ring pipelines segments so no link waits for a whole step).  A call of two
+ * or more non-empty steps whose rank buffers share one 16-byte phase, whose
+ * total size P * count * e is at most max_total_bytes, and that the fused
+ * limit does not take, runs as ONE launch of the column kernel: elements are
+ * split into columns of column_bytes per rank buffer (0: chosen per call,
+ * about four columns per compute unit and at least 1 KiB; otherwise rounded
+ * down to a multiple of 16, at least 16, at most 2 GiB), and one wave runs
+ * a column's share of every step in schedule order.  Steps combine operands
+ * at equal offsets, so columns are independent and no wave waits for
+ * another.  Same items, element ops and order: bit-identical results.  Meant
+ * for working sets the caches hold; 0 (the default unless the environment
+ * variable HBMC_COLUMNS_LIMIT gives a byte count) keeps one launch per step.
+ * Also used by hbmc_run_steps, out-of-place calls and graph mode.  The column
+ * tables are allocated per plan on first use.  Host only.
+ */
+hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, uint64_t column_bytes);
+
+/*
  * AUTO selection ([RHD] "RHD 在 HCCL 中的定位与启用方式": the algorithm is
  * chosen adaptively from product, data size and rank count; [RHD] "耗时计算"
  * and [TOPO] "AllReduce算法实现": alpha-beta cost models).  An AUTO
@@ -248,6 +268,22 @@ typedef struct {
  * at most `cap` items and sets *n_items to the total. */
 hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                               hbmc_dtype_t dtype, hbmc_item_t* out, size_t cap, size_t* n_items);
+
+/* One chunk of the column kernel: elements [begin, begin+count) of work item
+ * `item` (index in hbmc_plan_items order) of step `step`; it must follow the
+ * chunks deps[dep_lo..dep_hi) (all of earlier steps, all in its column). */
+typedef struct {
+  uint64_t begin;
+  uint32_t count, item, step, dep_lo, dep_hi, pad;
+} hbmc_chunk_t;
+
+/* The column kernel's chunk table for columns of chunk_bytes (rounded as
+ * hbmc_comm_set_columns does; at least 16), host only: writes at most `cap`
+ * chunks and `dcap` dependency indices, and sets *n_chunks / *n_deps to the
+ * totals. */
+hbmc_status_t hbmc_plan_chunks(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
+                               hbmc_dtype_t dtype, uint64_t chunk_bytes, hbmc_chunk_t* chunks, size_t cap,
+                               size_t* n_chunks, uint32_t* deps, size_t dcap, size_t* n_deps);
 
 /*
  * Graph mode ([RING-RHD] section "Ascend950的AIVAICPU通信引擎与图模式": a

@@ -1,0 +1,133 @@
+"""The column kernel (one launch per call; one wave runs each column of
+elements through every step) against the CPU oracle, bit for bit.
+
+Columns far narrower than the items (down to one 16-byte vector) make every
+item span many columns and every column cross item and segment boundaries;
+sizes leave ragged tails and empty segments; the buffers share a non-zero
+16-byte phase in some cases; the automatic column length is used too.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import allreduce_reduction_amd as hc
+import oracle
+import refops
+from gpu_util import strided_buffers, to_dev, to_host
+from test_gpu_parity import OPS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["fp32", "fp16", "bf16", "int32", "int8"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+CASES = [  # (algo, P, comm args, oracle keywords, collectives)
+    ("ring", 5, (5, "ring"), {}, ["allreduce", "reduce_scatter", "all_gather"]),
+    ("ring", 8, (8, "ring"), {}, ["allreduce"]),
+    ("rhd", 8, (8, "rhd"), {}, ["allreduce", "reduce_scatter", "all_gather", "reduce", "broadcast"]),
+    ("rhd", 7, (7, "rhd"), {}, ["allreduce", "reduce_scatter", "all_gather", "reduce", "broadcast"]),
+    ("pipeline", 8, (8, "pipeline", 2, 4, 4096), dict(S=2, M=4, loop_bytes=4096),
+     ["allreduce", "reduce_scatter", "all_gather"]),
+    ("flat", 6, (6, "flat"), {}, ["allreduce"]),
+    ("tree", 11, (11, "tree", 0, 3), dict(M=3), ["allreduce"]),
+    ("hier", 6, (6, "hier", 3, 2), dict(S=3, M=2), ["allreduce"]),
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}{c[1]}" for c in CASES])
+def test_columns_parity(case, dtype):
+    algo, P, args, kw, colls = case
+    rng = np.random.default_rng(zlib.crc32(f"columns/{algo}/{P}/{dtype}".encode()))
+    with hc.Comm(*args) as comm:
+        for coll in colls:
+            op = str(rng.choice(OPS))
+            L = int(rng.choice([7, 1000, 3 * 4096 + 5, 40_003]))
+            chunk = int(rng.choice([0, 16, 48, 1024, 4096]))
+            comm.set_columns(1 << 40, chunk)
+            root = int(rng.integers(0, P))
+            say(f"case columns algo={algo} P={P} coll={coll} dtype={dtype} op={op} L={L} chunk={chunk} root={root}")
+            xs = make_inputs(dtype, op, P, L, seed=L + P)
+            if rng.random() < 0.5:
+                dev = [to_dev(x, dtype) for x in xs]
+            else:
+                ph = int(rng.integers(1, 4))
+                dev, _keep = strided_buffers(xs, dtype, [ph] * P)
+            if coll == "reduce":
+                comm.reduce(dev, dtype, op, root=root)
+            elif coll == "broadcast":
+                comm.broadcast(dev, dtype, root=root)
+            else:
+                getattr(comm, coll)(dev, dtype, op)
+            torch.cuda.synchronize()
+            want = [x.copy() for x in xs]
+            oracle.run(coll, algo, want, dtype, op, root=root, **kw)
+            for r in ([root] if coll == "reduce" else range(P)):
+                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"columns {algo} {coll} rank {r}")
+
+
+def test_columns_step_ranges_and_repeats():
+    """Sub-ranges of steps, repeated launches of one plan, column lengths
+    changed between calls and per-step calls interleaved on one communicator."""
+    P, L, dtype = 6, 30_001, "int32"
+    xs = make_inputs(dtype, "sum", P, L, seed=9)
+    with hc.Comm(P, "ring") as comm:
+        comm.set_columns(1 << 40, 512)
+        n = comm.plan_info("allreduce", L, dtype)["nsteps"]
+        dev = [to_dev(x, dtype) for x in xs]
+        want = [x.copy() for x in xs]
+        for a, b in ((0, 1), (1, 4), (4, n)):
+            say(f"case columns steps [{a},{b})")
+            comm.run_steps("allreduce", dev, a, b, dtype, "sum")
+            oracle.run("allreduce", "ring", want, dtype, "sum", first_step=a, last_step=b)
+            torch.cuda.synchronize()
+            for r in range(P):
+                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"steps [{a},{b}) rank {r}")
+        for rep in range(6):
+            say(f"case columns repeat {rep}")
+            if rep % 2:
+                comm.set_columns(0)
+            else:
+                comm.set_columns(1 << 40, 512 if rep < 4 else 2048)
+            comm.allreduce(dev, dtype, "sum")
+            oracle.run("allreduce", "ring", want, dtype, "sum")
+            torch.cuda.synchronize()
+            for r in range(P):
+                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"repeat {rep} rank {r}")
+
+
+def test_columns_out_of_place_and_graph():
+    P, L, dtype = 5, 9999, "bf16"
+    xs = make_inputs(dtype, "max", P, L, seed=4)
+    with hc.Comm(P, "rhd") as comm:
+        comm.set_columns(1 << 40, 1024)
+        send = [to_dev(x, dtype) for x in xs]
+        recv = [torch.empty_like(t) for t in send]
+        comm.out_of_place("allreduce", send, recv, dtype, "max")
+        torch.cuda.synchronize()
+        want = [x.copy() for x in xs]
+        oracle.run("allreduce", "rhd", want, dtype, "max")
+        for r in range(P):
+            refops.assert_same(dtype, to_host(recv[r], dtype), want[r], f"oop rank {r}")
+            refops.assert_same(dtype, to_host(send[r], dtype), xs[r], f"send untouched rank {r}")
+        # graph node of the same call, replayed with eager work between replays
+        gb = [to_dev(x, dtype) for x in xs]
+        with hc.Graph() as g:
+            g.add(comm, "allreduce", gb, dtype, "max")
+            g.build()
+            for rep in range(3):
+                for t, x in zip(gb, xs):
+                    t.copy_(to_dev(x, dtype))
+                torch.cuda.synchronize()
+                g.launch()
+                torch.cuda.synchronize()
+                for r in range(P):
+                    refops.assert_same(dtype, to_host(gb[r], dtype), want[r], f"graph replay {rep} rank {r}")

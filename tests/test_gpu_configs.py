@@ -123,11 +123,14 @@ def test_ring_p4_fp32_integers():
         assert np.array_equal(got, exact)
 
 
-def test_ring_p8_fp32_64Mi():
+@pytest.mark.parametrize("columns", [False, True])
+def test_ring_p8_fp32_64Mi(columns):
     P, L = 8, 64 << 20
-    say("case ring_p8 fp32 64Mi: upload")
+    say(f"case ring_p8 fp32 64Mi columns={columns}: upload")
     dev = upload_recipe("ring_p8_fp32_grad", P, L)
     with hc.Comm(P, "ring") as c:
+        if columns:
+            c.set_columns(1 << 40)
         say("case ring_p8 fp32 64Mi: allreduce")
         c.allreduce(dev, "fp32", "sum")
         torch.cuda.synchronize()
