@@ -22,6 +22,7 @@ ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3, "flat": 4, "tree": 5, "hie
 ALGO_NAME = {v: k for k, v in ALGO.items()}
 COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
+EXEC = {"auto": 0, "steps": 1, "fused": 2, "columns": 3}
 
 # every symbol include/hbmcoll.h declares
 EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
@@ -29,7 +30,8 @@ EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_redu
            "hbmc_plan_items", "hbmc_status_string", "hbmc_graph_create", "hbmc_graph_add",
            "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy", "hbmc_comm_set_cost_model",
            "hbmc_auto_choice", "hbmc_comm_set_fused_limit",
-           "hbmc_comm_set_columns", "hbmc_plan_chunks")
+           "hbmc_comm_set_columns", "hbmc_plan_chunks",
+           "hbmc_comm_set_exec_mode", "hbmc_exec_choice")
 
 
 class HbmcError(RuntimeError):
@@ -105,6 +107,10 @@ def load_library():
         L.hbmc_comm_set_fused_limit.argtypes = [vp, ctypes.c_uint64]
         L.hbmc_comm_set_columns.restype = ci
         L.hbmc_comm_set_columns.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint64]
+        L.hbmc_comm_set_exec_mode.restype = ci
+        L.hbmc_comm_set_exec_mode.argtypes = [vp, ci]
+        L.hbmc_exec_choice.restype = ci
+        L.hbmc_exec_choice.argtypes = [vp, ci, ci, sz, ci, ci, ci, ctypes.POINTER(ci)]
         L.hbmc_comm_set_cost_model.restype = ci
         L.hbmc_comm_set_cost_model.argtypes = [vp, ctypes.c_double, ctypes.c_double]
         L.hbmc_auto_choice.restype = ci
@@ -225,13 +231,24 @@ class Comm:
         _check(load_library().hbmc_run_steps(self._h, COLL[coll], root, arr, count, DTYPE[dtype], OP[op],
                                              first, last, _stream(stream)), "hbmc_run_steps")
 
+    def set_exec_mode(self, mode: str):
+        """Launch form of every call: "auto" (default), "steps", "fused" or "columns"."""
+        _check(load_library().hbmc_comm_set_exec_mode(self._h, EXEC[mode]), "hbmc_comm_set_exec_mode")
+
+    def exec_choice(self, coll: str, count: int, dtype: str, root: int = 0, first: int = 0, last: int = 0) -> str:
+        """Launch form a call (or steps [first, last)) would take, host only."""
+        m = ctypes.c_int()
+        _check(load_library().hbmc_exec_choice(self._h, COLL[coll], root, count, DTYPE[dtype], first, last,
+                                               ctypes.byref(m)), "hbmc_exec_choice")
+        return {v: k for k, v in EXEC.items()}[m.value]
+
     def set_fused_limit(self, max_bytes: int):
-        """Run calls moving at most max_bytes as one single-workgroup launch."""
+        """Single-workgroup form eligible for calls moving at most max_bytes."""
         _check(load_library().hbmc_comm_set_fused_limit(self._h, max_bytes), "hbmc_comm_set_fused_limit")
 
     def set_columns(self, max_total_bytes: int, column_bytes: int = 0):
-        """Run multi-step calls over at most max_total_bytes (P * count * e) as one
-        column-kernel launch (0: off); column_bytes 0 picks the column length."""
+        """Column form eligible for calls over at most max_total_bytes (P * count * e);
+        column_bytes 0 picks the column length."""
         _check(load_library().hbmc_comm_set_columns(self._h, max_total_bytes, column_bytes),
                "hbmc_comm_set_columns")
 

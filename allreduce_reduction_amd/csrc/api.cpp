@@ -85,6 +85,13 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
   c->auto_select = a == HBMC_ALGO_AUTO;
   if (const char* fl = std::getenv("HBMC_FUSED_LIMIT")) c->fused_limit = std::strtoull(fl, nullptr, 10);
   if (const char* cl = std::getenv("HBMC_COLUMNS_LIMIT")) c->columns_limit = std::strtoull(cl, nullptr, 10);
+  if (const char* ex = std::getenv("HBMC_EXEC")) {
+    const std::string v(ex);
+    if (v == "steps") c->exec_mode = kExecSteps;
+    else if (v == "fused") c->exec_mode = kExecFused;
+    else if (v == "columns") c->exec_mode = kExecColumns;
+    else if (v == "auto") c->exec_mode = kExecAuto;
+  }
   const char* xs = std::getenv("HBMC_XCD_SPLIT");
   c->xcd_split = xs && xs[0] == '1';
   *out = c;
@@ -102,6 +109,30 @@ hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, 
   if (column_bytes != 0 && (column_bytes < 16 || column_bytes > (uint64_t(1) << 31))) return HBMC_ERR_INVALID_ARG;
   comm->columns_limit = max_total_bytes;
   comm->column_bytes = column_bytes;
+  return HBMC_OK;
+}
+
+hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode) {
+  if (!comm || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_COLUMNS) return HBMC_ERR_INVALID_ARG;
+  comm->exec_mode = static_cast<int>(mode);
+  return HBMC_OK;
+}
+
+hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
+                               int first_step, int last_step, hbmc_exec_t* mode) {
+  if (!mode) return HBMC_ERR_INVALID_ARG;
+  Plan* p = nullptr;
+  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+  if (st != HBMC_OK) return st;
+  const int nsteps = static_cast<int>(p->sched.steps.size());
+  if (first_step == 0 && last_step == 0) last_step = nsteps;
+  if (first_step < 0 || last_step > nsteps || first_step > last_step) return HBMC_ERR_INVALID_ARG;
+  *mode = HBMC_EXEC_STEPS;
+  if (count == 0 || comm->topos[0].P == 1 || first_step == last_step) return HBMC_OK;
+  int m = kExecSteps;
+  st = choose_exec(comm, p, first_step, last_step, count, elem_bytes(dtype), true, &m);
+  if (st != HBMC_OK) return st;
+  *mode = static_cast<hbmc_exec_t>(m);
   return HBMC_OK;
 }
 
@@ -236,7 +267,7 @@ hbmc_status_t hbmc_plan_chunks(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
   hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
   if (st != HBMC_OK) return st;
   ColumnTable f;
-  if (!build_columns(p->sched, comm->topos[0].P, column_elems(chunk_bytes, count, elem_bytes(dtype), 1), &f))
+  if (!build_columns(p->sched, comm->topos[0].P, column_elems(chunk_bytes, count, elem_bytes(dtype), 1), true, &f))
     return HBMC_ERR_INVALID_ARG;
   for (size_t i = 0; chunks && i < f.chunks.size() && i < cap; ++i) {
     const ColumnChunk& c = f.chunks[i];

@@ -32,14 +32,15 @@ void split(History& h, uint64_t x) {
 
 }  // namespace
 
-bool build_columns(const Schedule& sched, int P, uint64_t chunk_elems, ColumnTable* out) {
+bool build_columns(const Schedule& sched, int P, uint64_t chunk_elems, bool with_deps, ColumnTable* out) {
   if (chunk_elems == 0 || P < 1 || P > kMaxRanks) return false;
   out->chunks.clear();
   out->deps.clear();
   out->step_first.clear();
   out->chunk_elems = chunk_elems;
-  std::vector<History> hist(P);
-  for (int r = 0; r < P; ++r) hist[r].emplace(0, Seg{UINT64_MAX, -1, {}});
+  out->with_deps = with_deps;
+  std::vector<History> hist(with_deps ? P : 0);
+  for (size_t r = 0; r < hist.size(); ++r) hist[r].emplace(0, Seg{UINT64_MAX, -1, {}});
 
   uint64_t item_index = 0;
   std::vector<uint32_t> d;
@@ -58,7 +59,7 @@ bool build_columns(const Schedule& sched, int P, uint64_t chunk_elems, ColumnTab
         ch.item = static_cast<uint32_t>(item_index);
         ch.step = static_cast<uint32_t>(s);
         d.clear();
-        for (int k = 0; k < it.nsrc + it.ndst; ++k) {
+        for (int k = 0; with_deps && k < it.nsrc + it.ndst; ++k) {
           const bool write = k >= it.nsrc;
           History& h = hist[it.rank[k]];
           auto seg = h.upper_bound(b);
@@ -83,7 +84,7 @@ bool build_columns(const Schedule& sched, int P, uint64_t chunk_elems, ColumnTab
       ++item_index;
     }
     // record the step's accesses
-    for (size_t c = step_lo; c < out->chunks.size(); ++c) {
+    for (size_t c = step_lo; with_deps && c < out->chunks.size(); ++c) {
       const ColumnChunk& ch = out->chunks[c];
       const Item& it = step.items[ch.item - (item_index - step.items.size())];
       const uint64_t b = ch.begin, e = ch.begin + ch.count;
@@ -115,6 +116,9 @@ bool build_columns(const Schedule& sched, int P, uint64_t chunk_elems, ColumnTab
   for (const ColumnChunk& ch : out->chunks) ++out->col_off[ch.begin / chunk_elems + 1];
   for (uint64_t g = 0; g < ncols; ++g) out->col_off[g + 1] += out->col_off[g];
   out->col_list.assign(out->chunks.size(), 0);
+  out->max_per_col = 0;
+  for (uint64_t g = 0; g < ncols; ++g)
+    out->max_per_col = std::max<uint64_t>(out->max_per_col, out->col_off[g + 1] - out->col_off[g]);
   std::vector<uint32_t> fill(out->col_off.begin(), out->col_off.end() - 1);
   for (size_t c = 0; c < out->chunks.size(); ++c)
     out->col_list[fill[out->chunks[c].begin / chunk_elems]++] = static_cast<uint32_t>(c);

@@ -30,7 +30,9 @@ struct ColumnTable {
   std::vector<uint32_t> step_first;    // chunks of step s: [step_first[s], step_first[s+1])
   std::vector<uint32_t> col_list;      // column g's chunk indices, ascending: col_list[col_off[g] .. col_off[g+1])
   std::vector<uint32_t> col_off;
+  uint64_t max_per_col = 0;            // chunks of the longest column (run one after another by one wave)
   uint64_t chunk_elems = 0;
+  bool with_deps = false;
 };
 
 // Cut every item of `sched` at the multiples of `chunk_elems`, and derive each chunk's
@@ -43,6 +45,8 @@ struct ColumnTable {
 // conflict).  Also builds the per-column chunk lists.  Returns false for a bad
 // argument, a table beyond 2^32 entries, or a dependency across columns
 // (impossible for element-aligned items).
-bool build_columns(const Schedule& sched, int P, uint64_t chunk_elems, ColumnTable* out);
+// Without `with_deps` the dependency lists stay empty (the kernel does not
+// need them: a column runs in index order).
+bool build_columns(const Schedule& sched, int P, uint64_t chunk_elems, bool with_deps, ColumnTable* out);
 
 }  // namespace hbmc

@@ -173,14 +173,22 @@ uint64_t column_elems(uint64_t column_bytes, uint64_t count, uint32_t e, uint32_
   return b / e;
 }
 
-hbmc_status_t upload_columns(Plan* p, int P, uint64_t chunk_elems) {
-  if (p->cols_mem && p->cols.chunk_elems == chunk_elems) return HBMC_OK;
-  if (p->cols_mem) {
-    if (hipDeviceSynchronize() != hipSuccess || hipFree(p->cols_mem) != hipSuccess) return HBMC_ERR_HIP;
-    p->cols_mem = nullptr;
+hbmc_status_t column_table(Plan* p, int P, uint64_t chunk_elems, const ColumnTable** out) {
+  if (p->cols.chunk_elems != chunk_elems || p->cols.col_off.empty()) {
+    if (p->cols_mem) {
+      // the device copy belongs to the old length
+      if (hipDeviceSynchronize() != hipSuccess || hipFree(p->cols_mem) != hipSuccess) return HBMC_ERR_HIP;
+      p->cols_mem = nullptr;
+    }
+    if (!build_columns(p->sched, P, chunk_elems, false, &p->cols)) return HBMC_ERR_INVALID_ARG;
   }
-  ColumnTable& f = p->cols;
-  if (!build_columns(p->sched, P, chunk_elems, &f)) return HBMC_ERR_INVALID_ARG;
+  *out = &p->cols;
+  return HBMC_OK;
+}
+
+hbmc_status_t upload_columns(Plan* p) {
+  if (p->cols_mem) return HBMC_OK;
+  const ColumnTable& f = p->cols;
   const size_t n = f.chunks.size();
   std::vector<DevChunk> host(n);
   for (size_t i = 0; i < n; ++i) {
@@ -246,6 +254,57 @@ uint32_t compute_units() {
 
 }  // namespace
 
+hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t count, uint32_t e, bool aligned,
+                          int* mode) {
+  const int P = c->topos[0].P;
+  const ExecModel& m = c->model;
+  uint64_t bytes = 0;
+  int busy = 0, busy_all = 0;
+  bool items_ok = true;
+  double t_steps = 0.0;
+  for (size_t s = 0; s < p->sched.steps.size(); ++s) busy_all += p->sched.steps[s].items.empty() ? 0 : 1;
+  for (int s = first; s < last; ++s) {
+    const Step& st = p->sched.steps[s];
+    if (st.items.empty()) continue;
+    ++busy;
+    bytes += st.hbm_bytes;
+    items_ok = items_ok && st.items.size() <= kFusedMaxItems;
+    t_steps += std::max(m.launch_us, m.step_us + double(st.hbm_bytes) / (m.hbm_gbps * 1e3));
+  }
+  const bool fused_ok = aligned && busy > 0 && items_ok && bytes <= c->fused_limit;
+  const bool cols_ok = aligned && busy > 1 && count * e <= c->columns_limit / uint64_t(P);
+  *mode = kExecSteps;
+  if (c->exec_mode == kExecFused) {
+    if (fused_ok) *mode = kExecFused;
+    return HBMC_OK;
+  }
+  if (c->exec_mode == kExecColumns) {
+    if (cols_ok) *mode = kExecColumns;
+    return HBMC_OK;
+  }
+  if (c->exec_mode != kExecAuto) return HBMC_OK;
+  double best = t_steps;
+  if (fused_ok) {
+    const double t = m.fused_us + busy * m.fused_step_us + double(bytes) / (m.fused_gbps * 1e3);
+    if (t < best) {
+      best = t;
+      *mode = kExecFused;
+    }
+  }
+  if (cols_ok) {
+    const ColumnTable* f = nullptr;
+    hbmc_status_t st = column_table(p, P, column_elems(c->column_bytes, count, e, compute_units()), &f);
+    if (st != HBMC_OK) return st;
+    const double hops = double(f->max_per_col) * busy / std::max(1, busy_all);
+    const double t = m.col_us + hops * m.col_hop_us + double(bytes) / (m.col_gbps * 1e3);
+    if (t < best) {
+      best = t;
+      *mode = kExecColumns;
+    }
+  }
+  return HBMC_OK;
+}
+
 hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,
                       int op, int first, int last, bool whole, std::vector<KernelDesc>* launches) {
   launches->clear();
@@ -277,32 +336,28 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     ptrs.p[r] = static_cast<unsigned char*>(bufs[r]);
     aligned = aligned && (reinterpret_cast<uintptr_t>(bufs[r]) & 15u) == phase;
   }
-  // small enough: the whole step range as one single-workgroup launch
-  uint64_t bytes = 0;
-  bool fits = aligned && c->fused_limit > 0;
-  for (int s = first; s < last && fits; ++s) {
-    bytes += p->sched.steps[s].hbm_bytes;
-    fits = p->sched.steps[s].items.size() <= kFusedMaxItems && bytes <= c->fused_limit;
-  }
-  if (fits && bytes > 0) {
+  int mode = kExecSteps;
+  st = choose_exec(c, p, first, last, count, e, aligned, &mode);
+  if (st != HBMC_OK) return st;
+  if (mode == kExecFused) {
+    // the whole step range as one single-workgroup launch
     KernelDesc k;
     describe_fused(dtype, op, ptrs, p->dev, p->dev_steps + first, static_cast<uint32_t>(last - first), phase, &k);
     launches->push_back(k);
     return HBMC_OK;
   }
-  // several steps over a small working set: one column-kernel launch
-  int busy = 0;
-  for (int s = first; s < last; ++s) busy += p->sched.steps[s].items.empty() ? 0 : 1;
-  if (aligned && busy > 1 && c->columns_limit > 0 && uint64_t(count) * e <= c->columns_limit / uint64_t(P)) {
+  if (mode == kExecColumns) {
+    // the whole step range as one column-kernel launch
     const uint32_t cus = compute_units();
-    st = upload_columns(p, P, column_elems(c->column_bytes, count, e, cus));
+    const ColumnTable* f = nullptr;
+    st = column_table(p, P, column_elems(c->column_bytes, count, e, cus), &f);
+    if (st == HBMC_OK) st = upload_columns(p);
     if (st != HBMC_OK) return st;
-    const ColumnTable& f = p->cols;
-    const uint32_t ncols = static_cast<uint32_t>(f.col_off.size() - 1);
+    const uint32_t ncols = static_cast<uint32_t>(f->col_off.size() - 1);
     const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(ncols, cus * 8));
     KernelDesc k;
     describe_columns(dtype, op, ptrs, p->dev, p->dev_chunks, p->dev_col_list, p->dev_col_off, ncols,
-                     f.step_first[first], f.step_first[last], phase, grid, &k);
+                     f->step_first[first], f->step_first[last], phase, grid, &k);
     launches->push_back(k);
     return HBMC_OK;
   }

@@ -15,6 +15,24 @@
 
 namespace hbmc {
 
+// How a call's steps are launched.
+enum ExecMode : int { kExecAuto = 0, kExecSteps = 1, kExecFused = 2, kExecColumns = 3 };
+
+// Modelled time (us) of a range of steps in each launch form, fitted to
+// measurements on MI355X (one launch per step, the single-workgroup kernel,
+// the column kernel; see choose_exec).
+struct ExecModel {
+  double launch_us = 4.2;       // host-side cost of one step launch (bounds eager small steps)
+  double step_us = 3.0;         // fixed GPU cost of one step kernel
+  double hbm_gbps = 6400.0;     // step kernels' streaming rate
+  double fused_us = 2.0;        // single-workgroup kernel: launch
+  double fused_step_us = 1.6;   //   per step (workgroup barrier, loads, stores)
+  double fused_gbps = 33.0;     //   one compute unit's streaming rate
+  double col_us = 4.0;          // column kernel: launch
+  double col_hop_us = 0.85;     //   per chunk of the longest column (run one after another)
+  double col_gbps = 6000.0;     //   streaming rate
+};
+
 uint32_t elem_bytes(int dtype);
 bool valid_coll(int c);
 bool valid_op(int op);
@@ -26,7 +44,8 @@ struct Plan {
   DevItem* dev = nullptr;          // all items, step after step
   FusedStep* dev_steps = nullptr;  // one entry per step, for the single-workgroup kernel
   int device = -1;
-  // column kernel tables (one allocation), built on first use
+  // column kernel tables (one allocation), built on first use; the host table
+  // also serves the launch-form choice
   ColumnTable cols;
   void* cols_mem = nullptr;
   DevChunk* dev_chunks = nullptr;
@@ -42,8 +61,13 @@ struct hbmc_comm {
   bool auto_select = false;
   double alpha_us = 4.4;      // launch-to-launch cost of one step, measured eager on MI355X
   double beta_gbps = 6400.0;  // sustained HBM rate of the step kernels, measured
-  uint64_t fused_limit = 0;   // run whole step ranges moving <= this many bytes as one launch
-  uint64_t columns_limit = 0;  // column kernel for calls whose P * count * e is at most this; 0: off
+  int exec_mode = hbmc::kExecAuto;
+  hbmc::ExecModel model;
+  // eligibility: the single-workgroup kernel for step ranges moving at most
+  // fused_limit algorithmic bytes, the column kernel for calls whose rank
+  // buffers total at most columns_limit bytes (working sets the caches hold)
+  uint64_t fused_limit = uint64_t(64) << 20;
+  uint64_t columns_limit = uint64_t(64) << 20;
   uint64_t column_bytes = 0;   // column length in bytes; 0: chosen per call
   bool xcd_split = false;
   // (topology index, coll, root, count, dtype) -> plan
@@ -79,10 +103,26 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
 // least 16) or, for 0, for a call of `count` elements: about four columns per
 // compute unit, no shorter than 1 KiB (one 16-byte vector per lane of a wave).
 uint64_t column_elems(uint64_t column_bytes, uint64_t count, uint32_t e, uint32_t compute_units);
-// Build and upload the plan's column tables for a column length of
-// `chunk_elems` (rebuilt when it changes; the old tables are freed after a
-// device synchronisation).
-hbmc_status_t upload_columns(Plan* p, int P, uint64_t chunk_elems);
+// The plan's host column table for a column length of `chunk_elems` (built
+// once per length, without dependency lists).
+hbmc_status_t column_table(Plan* p, int P, uint64_t chunk_elems, const ColumnTable** out);
+// Upload the plan's column table to the current device (again after the
+// column length changed; the old tables are freed after a device
+// synchronisation).
+hbmc_status_t upload_columns(Plan* p);
+// Launch form of steps [first, last) of plan `p` (count elements of e bytes,
+// buffers of one 16-byte phase when `aligned`): the communicator's mode when
+// not AUTO and the form is eligible; for AUTO the eligible form of least
+// modelled time, where, for B algorithmic bytes in S non-empty steps,
+//   steps:   sum over steps of max(launch_us, step_us + B_s / hbm)
+//   fused:   fused_us + S * fused_step_us + B / fused_gbps
+//   columns: col_us + H * col_hop_us + B / col_gbps, H the chunks of the
+//            longest column, scaled to the range's share of the busy steps
+// (ties: steps, then fused).  Fused needs <= 256 items per step and B within
+// the fused limit; columns need two or more busy steps and P * count * e
+// within the column limit; both need `aligned`.  Steps otherwise.
+hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t count, uint32_t e, bool aligned,
+                          int* mode);
 // Enqueue one described launch on `stream`.
 hbmc_status_t launch(KernelDesc& k, void* stream);
 // Validate and enqueue steps [first, last) of a collective (all of them when

@@ -8,17 +8,21 @@ AllReduce.
 Reported (one JSON line):
   value      busbw = algbw * 2(P-1)/P, algbw = D / t, D = bytes per rank
   pct_hbm    algorithmic HBM bytes of the AllReduce (5 D (P-1)) / t / 8 TB/s
+  value / ms_per_step  from K whole AllReduces (hbmc_allreduce), HIP events
+             around each call on the launch stream, median
   roofline   the ring reduce-scatter step kernel: algorithmic bytes per launch
              (3 bytes per segment byte, 8 segments) / its mean duration from
-             HIP events recorded between the steps on the launch stream
+             a second pass of K AllReduces issued step by step with HIP events
+             recorded between the steps on the launch stream
   cpu_baseline  the CPU oracle replaying the same AllReduce (single thread)
   auto_allreduce_same_workload  not the headline: the AUTO communicator's
              AllReduce of the same buffers (its cost model picks Flat)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --suite    (one JSON line per other workload: RHD small
-                                   messages, the P=16 ring / RHD sweep, the 4x8
-                                   pipeline; not the headline line)
+                                   messages, launch forms across sizes, the P=16
+                                   ring / RHD sweep, the 4x8 pipeline; not the
+                                   headline line)
 """
 from __future__ import annotations
 
@@ -40,7 +44,7 @@ def measured_traffic():
     import hashlib
     path = os.path.join(ROOT, "profiles", "ring_rs_step_p8_fp32_64Mi_hbm_traffic.md")
     src = b"".join(open(os.path.join(ROOT, "allreduce_reduction_amd", "csrc", f), "rb").read()
-                   for f in ("step_kernels.hip", "launch.hpp"))
+                   for f in ("step_kernels.hip", "elemops.hpp"))
     digest = hashlib.sha256(src).hexdigest()[:16]
     try:
         kv = dict(line.strip().split(": ", 1) for line in open(path, encoding="utf-8")
@@ -123,7 +127,11 @@ def suite(a):
                     n = c.plan_info("allreduce", L, dtype)["nsteps"]
                     for b, q in zip(bufs, pristine):
                         b.copy_(q)
+                    form = c.exec_choice("allreduce", L, dtype)
                     t = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
+                    c.set_exec_mode("steps")
+                    t_steps = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
+                    c.set_exec_mode("auto")
                     # graph mode: the same AllReduce as one graph launch, and a
                     # graph of 10 AllReduces on these buffers (one launch)
                     with hc.Graph() as g:
@@ -136,7 +144,9 @@ def suite(a):
                         g10.build()
                         tg10 = time_calls(lambda: g10.launch(), 50, 5) / 10
                 emit(workload="rhd_small", algo="rhd", coll="allreduce", P=P, dtype=dtype, op=op,
-                     bytes_per_rank=L * e, us=round(t * 1e6, 2), steps=n, us_per_step=round(t * 1e6 / n, 2),
+                     bytes_per_rank=L * e, launch_form=form, us=round(t * 1e6, 2), steps=n,
+                     us_per_step=round(t * 1e6 / n, 2), one_launch_per_step_us=round(t_steps * 1e6, 2),
+                     one_launch_per_step_us_per_step=round(t_steps * 1e6 / n, 2),
                      graph_us=round(tg * 1e6, 2), graph_us_per_step=round(tg * 1e6 / n, 2),
                      graph10_us_per_allreduce=round(tg10 * 1e6, 2),
                      busbw_GBps=round(L * e / t * 2 * (P - 1) / P / 1e9, 3),
@@ -159,27 +169,37 @@ def suite(a):
                     t = time_calls(lambda: getattr(c, coll)(bufs, "fp16", "sum"), reps, 2)
                     factor = 2 * (P - 1) / P if coll == "allreduce" else (P - 1) / P
                     emit(workload="sweep_p16_fp16", algo=algo, coll=coll, P=P, bytes_per_rank=nbytes,
-                         us=round(t * 1e6, 2), steps=info["nsteps"],
+                         launch_form=c.exec_choice(coll, L, "fp16"), us=round(t * 1e6, 2), steps=info["nsteps"],
                          busbw_GBps=round(nbytes / t * factor / 1e9, 3),
                          pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2))
         del bufs, pristine
         torch.cuda.empty_cache()
         nbytes *= 4
 
-    # small messages: one launch per step versus the single-workgroup plan kernel
+    # launch forms across sizes: one launch per step, the single-workgroup
+    # kernel, the column kernel, and the form the communicator picks
     for P in (8, 16):
-        for algo in ("ring", "rhd", "flat"):
-            for kib in (1, 4, 16, 64, 256, 1024):
-                L = kib * 1024 // 2
-                bufs = upload("rhd_bf16_normal", P, L)
+        for algo in ("ring", "rhd"):
+            kib = 1
+            while kib <= min(16384, a.max_sweep_bytes >> 10):
+                L = kib * 512
+                bufs = upload("sweep_p16_fp16", P, L)
+                row = {}
                 with hc.Comm(P, algo) as c:
-                    info = c.plan_info("allreduce", L, "bf16")
-                    te = time_calls(lambda: c.allreduce(bufs, "bf16", "max"), 200, 20)
-                    c.set_fused_limit(1 << 40)
-                    tf = time_calls(lambda: c.allreduce(bufs, "bf16", "max"), 200, 20)
-                emit(workload="small_fused", algo=algo, P=P, dtype="bf16", op="max", bytes_per_rank=L * 2,
-                     hbm_bytes=info["hbm_bytes"], steps=info["nsteps"], eager_us=round(te * 1e6, 2),
-                     fused_us=round(tf * 1e6, 2))
+                    info = c.plan_info("allreduce", L, "fp16")
+                    reps = max(5, min(200, int(1e8 // info["hbm_bytes"])))
+                    auto_form = c.exec_choice("allreduce", L, "fp16")
+                    for form in ("steps", "fused", "columns", "auto"):
+                        c.set_exec_mode(form)
+                        if form != "auto" and c.exec_choice("allreduce", L, "fp16") != form:
+                            continue
+                        if form == "fused" and kib > 64:
+                            continue  # one compute unit: far slower, skip the long runs
+                        row[form] = round(time_calls(lambda: c.allreduce(bufs, "fp16", "max"), reps, 3) * 1e6, 2)
+                emit(workload="launch_forms", algo=algo, P=P, dtype="fp16", op="max", bytes_per_rank=kib << 10,
+                     hbm_bytes=info["hbm_bytes"], steps=info["nsteps"], auto_form=auto_form, us=row)
+                del bufs
+                kib *= 4
 
     # AllReduce algorithms side by side, and the AUTO communicator's choice
     for P in (8, 16):
@@ -272,24 +292,38 @@ def main():
         comm.allreduce(bufs, dtype, "sum")
     torch.cuda.synchronize()
 
-    # timed region: K AllReduces, each issued step by step with events between
-    # the steps (same launches as hbmc_allreduce, plus event markers)
+    # timed region: K whole AllReduces (hbmc_allreduce: one step kernel launch
+    # per step on this 2 GiB working set), HIP events only around each call
     K = a.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)] for _ in range(K)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        for s in range(nsteps):
-            ev[k][s].record(stream)
-            comm.run_steps("allreduce", bufs, s, s + 1, dtype, "sum")
-        ev[k][nsteps].record(stream)
+        ev[k][0].record(stream)
+        comm.allreduce(bufs, dtype, "sum")
+        ev[k][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
     wall = (t1 - t0) / K
-    gpu_ms = [ev[k][0].elapsed_time(ev[k][nsteps]) for k in range(K)]
+    gpu_ms = [b.elapsed_time(e) for b, e in ev]
     t = float(np.median(gpu_ms)) / 1e3
-    step_ms = np.array([[ev[k][s].elapsed_time(ev[k][s + 1]) for s in range(nsteps)] for k in range(K)])
+
+    # roofline pass: K more AllReduces issued step by step (the same kernels)
+    # with an event between consecutive steps, for each kernel's duration; an
+    # event between two kernels adds about 1.5 us of its own, so the headline
+    # value comes from the pass above
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)] for _ in range(K)]
+    for b, q in zip(bufs, pristine):
+        b.copy_(q)
+    torch.cuda.synchronize()
+    for k in range(K):
+        for s in range(nsteps):
+            sev[k][s].record(stream)
+            comm.run_steps("allreduce", bufs, s, s + 1, dtype, "sum")
+        sev[k][nsteps].record(stream)
+    torch.cuda.synchronize()
+    stepwise_ms = float(np.median([sev[k][0].elapsed_time(sev[k][nsteps]) for k in range(K)]))
+    step_ms = np.array([[sev[k][s].elapsed_time(sev[k][s + 1]) for s in range(nsteps)] for k in range(K)])
     rs_ms = float(step_ms[:, rs_steps].mean())
     ag_steps = [s for s in range(nsteps) if s not in rs_steps]
     ag_ms = float(step_ms[:, ag_steps].mean()) if ag_steps and a.algo == "ring" else None
@@ -307,6 +341,7 @@ def main():
         "warmup": a.warmup,
         "ms_per_step": round(t * 1e3, 4),
         "wall_ms_per_step": round(wall * 1e3, 4),
+        "stepwise_events_ms_per_allreduce": round(stepwise_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -111,37 +111,49 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
 hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
 
 /*
- * Fewer launches for small collectives ([RHD] "耗时计算": every step pays a
- * fixed alpha).  A call whose steps move at most `max_bytes` algorithmic HBM
- * bytes in total, whose buffers share one 16-byte phase and whose steps have
- * at most 256 work items each, runs all its steps in one launch of a single
- * 1024-thread workgroup, with a workgroup barrier between consecutive steps
- * (same items, element ops and order; bit-identical results).  0 (the
- * default, unless the environment variable HBMC_FUSED_LIMIT gives a byte
- * count) keeps one launch per step.  Also used by hbmc_run_steps and graph
- * mode.  Host only.
+ * Launch forms.  Every form runs the same items with the same element ops in
+ * the same order (bit-identical results); they differ in how the steps are
+ * launched, which decides the fixed per-step cost ([RHD] "耗时计算": every
+ * step pays alpha; [RING-RHD] "Ascend950的AIVAICPU通信引擎与图模式": short
+ * messages pay mostly control overhead, which fewer launches remove):
+ *  - HBMC_EXEC_STEPS: one kernel launch per non-empty step (stream order
+ *    separates the steps);
+ *  - HBMC_EXEC_FUSED: all steps of the call in one launch of a single
+ *    1024-thread workgroup, a workgroup barrier between steps;
+ *  - HBMC_EXEC_COLUMNS: all steps in one launch of the column kernel.  Steps
+ *    combine operands at equal element offsets, so the elements of all rank
+ *    buffers split into independent columns (column_bytes per rank buffer;
+ *    0 chooses about four columns per compute unit, at least 1 KiB) and one
+ *    wave runs a column's share of every step in schedule order, without
+ *    waiting for other waves ([RING-RHD] "Ring AllReduce带宽最优的环形流水线":
+ *    the ring pipelines segments so no one waits for a whole step);
+ *  - HBMC_EXEC_AUTO (default, or the environment variable HBMC_EXEC = auto,
+ *    steps, fused or columns): per call the eligible form of least modelled
+ *    time, with constants measured on MI355X: steps sum over the steps
+ *    max(4.2 us, 3 us + bytes / 6.4 TB/s); fused 2 us + 1.6 us per step +
+ *    bytes / 33 GB/s; columns 4 us + 0.85 us per chunk of the longest column
+ *    + bytes / 6 TB/s (bytes: the algorithmic HBM bytes of the steps).
+ * A forced form falls back to STEPS where it is not eligible.  Eligibility:
+ * both one-launch forms need rank buffers of one 16-byte phase; FUSED needs
+ * at most 256 items per step and at most `max_bytes` algorithmic bytes in
+ * the call's steps (hbmc_comm_set_fused_limit; default 64 MiB, or the
+ * environment variable HBMC_FUSED_LIMIT); COLUMNS needs two or more non-empty
+ * steps and P * count * e (the rank buffers' total size) of at most
+ * `max_total_bytes` (hbmc_comm_set_columns; default 64 MiB, or
+ * HBMC_COLUMNS_LIMIT): working sets the caches hold, so that larger calls
+ * keep the per-step HBM traffic the schedule defines.  The forms apply to
+ * every call, hbmc_run_steps ranges and graph nodes.  Host only.
  */
+typedef enum { HBMC_EXEC_AUTO = 0, HBMC_EXEC_STEPS = 1, HBMC_EXEC_FUSED = 2, HBMC_EXEC_COLUMNS = 3 } hbmc_exec_t;
+hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode);
 hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes);
-
-/*
- * One launch per call for small working sets ([RHD] "耗时计算": every step
- * pays a fixed alpha; [RING-RHD] "Ring AllReduce带宽最优的环形流水线": the
- * ring pipelines segments so no link waits for a whole step).  A call of two
- * or more non-empty steps whose rank buffers share one 16-byte phase, whose
- * total size P * count * e is at most max_total_bytes, and that the fused
- * limit does not take, runs as ONE launch of the column kernel: elements are
- * split into columns of column_bytes per rank buffer (0: chosen per call,
- * about four columns per compute unit and at least 1 KiB; otherwise rounded
- * down to a multiple of 16, at least 16, at most 2 GiB), and one wave runs
- * a column's share of every step in schedule order.  Steps combine operands
- * at equal offsets, so columns are independent and no wave waits for
- * another.  Same items, element ops and order: bit-identical results.  Meant
- * for working sets the caches hold; 0 (the default unless the environment
- * variable HBMC_COLUMNS_LIMIT gives a byte count) keeps one launch per step.
- * Also used by hbmc_run_steps, out-of-place calls and graph mode.  The column
- * tables are allocated per plan on first use.  Host only.
- */
+/* column_bytes: 0, or 16 .. 2^31 (rounded down to a multiple of 16). */
 hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, uint64_t column_bytes);
+/* The launch form steps [first_step, last_step) of a call would take (0, 0:
+ * all steps), for rank buffers of one 16-byte phase (host only; builds the
+ * plan and, for AUTO, its host column table). */
+hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
+                               int first_step, int last_step, hbmc_exec_t* mode);
 
 /*
  * AUTO selection ([RHD] "RHD 在 HCCL 中的定位与启用方式": the algorithm is

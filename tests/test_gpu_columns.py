@@ -48,6 +48,7 @@ def test_columns_parity(case, dtype):
     algo, P, args, kw, colls = case
     rng = np.random.default_rng(zlib.crc32(f"columns/{algo}/{P}/{dtype}".encode()))
     with hc.Comm(*args) as comm:
+        comm.set_exec_mode("columns")
         for coll in colls:
             op = str(rng.choice(OPS))
             L = int(rng.choice([7, 1000, 3 * 4096 + 5, 40_003]))
@@ -81,6 +82,7 @@ def test_columns_step_ranges_and_repeats():
     xs = make_inputs(dtype, "sum", P, L, seed=9)
     with hc.Comm(P, "ring") as comm:
         comm.set_columns(1 << 40, 512)
+        comm.set_exec_mode("columns")
         n = comm.plan_info("allreduce", L, dtype)["nsteps"]
         dev = [to_dev(x, dtype) for x in xs]
         want = [x.copy() for x in xs]
@@ -109,6 +111,7 @@ def test_columns_out_of_place_and_graph():
     xs = make_inputs(dtype, "max", P, L, seed=4)
     with hc.Comm(P, "rhd") as comm:
         comm.set_columns(1 << 40, 1024)
+        comm.set_exec_mode("columns")
         send = [to_dev(x, dtype) for x in xs]
         recv = [torch.empty_like(t) for t in send]
         comm.out_of_place("allreduce", send, recv, dtype, "max")

@@ -131,6 +131,7 @@ def test_ring_p8_fp32_64Mi(columns):
     with hc.Comm(P, "ring") as c:
         if columns:
             c.set_columns(1 << 40)
+            c.set_exec_mode("columns")
         say("case ring_p8 fp32 64Mi: allreduce")
         c.allreduce(dev, "fp32", "sum")
         torch.cuda.synchronize()
@@ -144,8 +145,9 @@ def test_ring_p8_fp32_64Mi(columns):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("exec_mode", ["steps", "auto"])
 @pytest.mark.parametrize("P", [8, 5])
-def test_rhd_small_messages(P):
+def test_rhd_small_messages(P, exec_mode):
     for kib in (1, 2, 4, 8, 16, 32, 64):
         for recipe, op in (("rhd_bf16_normal", "sum"), ("rhd_int32_uniform", "max")):
             dtype = synth.RECIPES[recipe]["dtype"]
@@ -154,6 +156,7 @@ def test_rhd_small_messages(P):
             xs = synth.rank_inputs(recipe, P, L)
             dev = [to_dev(x, dtype) for x in xs]
             with hc.Comm(P, "rhd") as c:
+                c.set_exec_mode(exec_mode)
                 assert c.plan_info("allreduce", L, dtype)["nsteps"] == 6
                 c.allreduce(dev, dtype, op)
                 torch.cuda.synchronize()

@@ -52,10 +52,11 @@ def comm_for(algo, P, loop_bytes=0):
     return hc.Comm(P, algo), 1, 1
 
 
-def check_case(algo, coll, dtype, op, P, L, seed, loop_bytes=0):
-    say(f"case algo={algo} coll={coll} dtype={dtype} op={op} P={P} L={L} seed={seed}")
+def check_case(algo, coll, dtype, op, P, L, seed, loop_bytes=0, exec_mode="auto"):
+    say(f"case algo={algo} coll={coll} dtype={dtype} op={op} P={P} L={L} seed={seed} exec={exec_mode}")
     comm, S, M = comm_for(algo, P, loop_bytes)
     with comm:
+        comm.set_exec_mode(exec_mode)
         xs = make_inputs(dtype, op, P, L, seed)
         dev = [to_dev(x, dtype) for x in xs]
         getattr(comm, coll)(dev, dtype, op)
@@ -72,17 +73,21 @@ def check_case(algo, coll, dtype, op, P, L, seed, loop_bytes=0):
 LS = [0, 1, 5, 1000, 3 * 4096 + 7, 50_001]
 
 
+@pytest.mark.parametrize("exec_mode", ["steps", "auto"])
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("coll", ["allreduce", "reduce_scatter", "all_gather"])
 @pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
-def test_parity(algo, coll, dtype):
+def test_parity(algo, coll, dtype, exec_mode):
+    """Every case once with one launch per step and once with the launch form
+    the communicator picks by default (single workgroup, column kernel or
+    steps, by size)."""
     rng = np.random.default_rng(zlib.crc32(f"{algo}/{coll}/{dtype}".encode()))
     Ps = [2, 3, 5, 8] if not (algo == "rhd" and coll != "allreduce") else [2, 4, 5, 6, 8]
     for op in OPS:
         for P in Ps:
             L = int(rng.choice(LS))
             check_case(algo, coll, dtype, op, P, L, seed=int(rng.integers(1 << 30)),
-                       loop_bytes=(8192 if algo == "pipeline" else 0))
+                       loop_bytes=(8192 if algo == "pipeline" else 0), exec_mode=exec_mode)
 
 
 VARIANT_COMMS = [("flat", P, (P, "flat"), {}) for P in (2, 5, 8, 16)] + \
@@ -306,6 +311,7 @@ def test_parity_fused_single_workgroup(dtype):
     for algo, P, args, kw in cases:
         with hc.Comm(*args) as comm:
             comm.set_fused_limit(1 << 40)
+            comm.set_exec_mode("fused")
             colls = ["allreduce"] if algo in ("flat", "tree", "hier") else ["allreduce", "reduce_scatter", "all_gather"]
             if algo == "rhd":
                 colls += ["reduce", "broadcast"]
@@ -334,6 +340,7 @@ def test_fused_step_ranges_and_graph():
     xs = make_inputs(dtype, "sum", P, L, seed=3)
     with hc.Comm(P, "ring") as comm:
         comm.set_fused_limit(1 << 40)
+        comm.set_exec_mode("fused")
         n = comm.plan_info("allreduce", L, dtype)["nsteps"]
         dev = [to_dev(x, dtype) for x in xs]
         want = [x.copy() for x in xs]

@@ -1,0 +1,74 @@
+"""Host checks of the launch-form choice (no GPU).
+
+Every launch form runs the same items in the same order (the GPU tests pin
+each form to the oracle); here the choice itself: AUTO picks the form of
+least modelled time among the eligible ones -- the single-workgroup kernel
+for the smallest calls, the column kernel for mid sizes, one launch per step
+once the working set outgrows the column limit -- forced forms fall back to
+one launch per step where not eligible, and the limits gate eligibility.
+"""
+import pytest
+
+import allreduce_reduction_amd as hc
+
+
+def test_auto_regimes_ring_p8_fp16():
+    with hc.Comm(8, "ring") as c:
+        assert c.exec_choice("allreduce", 512, "fp16") == "fused"          # 1 KiB per rank
+        assert c.exec_choice("allreduce", 32 << 10, "fp16") == "columns"   # 64 KiB per rank
+        assert c.exec_choice("allreduce", 2 << 20, "fp16") == "columns"    # 4 MiB per rank (32 MiB total)
+        assert c.exec_choice("allreduce", 8 << 20, "fp16") == "steps"      # 16 MiB per rank: over the limit
+        assert c.exec_choice("allreduce", 64 << 20, "fp32") == "steps"     # the 256 MiB per rank workload
+
+
+def test_auto_prefers_steps_where_launches_are_few_and_bytes_many():
+    # RHD at P=16 has 8 steps: at 1 MiB per rank eight launches beat the
+    # column kernel's 30-chunk columns
+    with hc.Comm(16, "rhd") as c:
+        assert c.exec_choice("allreduce", 512 << 10, "fp16") == "steps"
+        assert c.exec_choice("allreduce", 8 << 10, "fp16") == "columns"
+
+
+def test_forced_forms_and_fallbacks():
+    with hc.Comm(8, "ring") as c:
+        c.set_exec_mode("steps")
+        assert c.exec_choice("allreduce", 512, "fp16") == "steps"
+        c.set_exec_mode("fused")
+        assert c.exec_choice("allreduce", 32 << 10, "fp16") == "fused"
+        c.set_fused_limit(1000)
+        assert c.exec_choice("allreduce", 32 << 10, "fp16") == "steps"      # over the fused limit
+        c.set_exec_mode("columns")
+        assert c.exec_choice("allreduce", 512, "fp16") == "columns"
+        assert c.exec_choice("allreduce", 8 << 20, "fp16") == "steps"      # over the column limit
+        # a single busy step is never worth a column launch
+        assert c.exec_choice("allreduce", 512, "fp16", first=0, last=1) == "steps"
+        c.set_columns(0)
+        assert c.exec_choice("allreduce", 512, "fp16") == "steps"
+        c.set_exec_mode("auto")
+        assert c.exec_choice("allreduce", 512, "fp16") == "steps"          # neither one-launch form eligible
+        c.set_fused_limit(64 << 20)
+        c.set_columns(64 << 20)
+        assert c.exec_choice("allreduce", 512, "fp16") == "fused"
+
+
+def test_fused_needs_at_most_256_items_per_step():
+    # a 2 x 2 pipeline with 1 KiB loops over 256 KiB has 256 loops of 4 blocks: > 256 items per step
+    with hc.Comm(4, "pipeline", 2, 2, 1024) as c:
+        L = 64 << 10
+        assert max(c.step_info("allreduce", L, "fp32", s)["nitems"]
+                   for s in range(c.plan_info("allreduce", L, "fp32")["nsteps"])) > 256
+        c.set_exec_mode("fused")
+        assert c.exec_choice("allreduce", L, "fp32") == "steps"
+
+
+def test_exec_choice_edges_and_validation():
+    with hc.Comm(8, "ring") as c:
+        assert c.exec_choice("allreduce", 0, "fp32") == "steps"
+        with pytest.raises(hc.HbmcError):
+            c.exec_choice("allreduce", 100, "fp32", first=3, last=99)
+        with pytest.raises(KeyError):
+            c.set_exec_mode("bogus")
+        lib = hc.load_library()
+        assert lib.hbmc_comm_set_exec_mode(c._h, 4) == 1
+    with hc.Comm(1, "ring") as c:
+        assert c.exec_choice("allreduce", 100, "fp32") == "steps"
