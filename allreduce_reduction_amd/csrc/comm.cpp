@@ -376,6 +376,8 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     L.aligned = aligned;
     L.phase = phase;
     L.xcd_split = c->xcd_split;
+    L.write_bytes = 0;
+    for (const Item& it : step.items) L.write_bytes += it.count * uint64_t(it.ndst) * elem_bytes(dtype);
     KernelDesc k;
     if (describe_step(L, ptrs, &k) != hipSuccess) return HBMC_ERR_HIP;
     launches->push_back(k);
@@ -492,6 +494,7 @@ hbmc_status_t run_out_of_place(hbmc_comm* c, int coll, int root, const void* con
       L.aligned = aligned;
       L.phase = phase;
       L.xcd_split = false;
+      L.write_bytes = uint64_t(n) * count * elem_bytes(dtype);
       if (launch_step(L, cp, static_cast<hipStream_t>(stream)) != hipSuccess) return HBMC_ERR_HIP;
     }
   }

@@ -119,8 +119,12 @@ __device__ __forceinline__ u32x4 op_vec(u32x4 a, u32x4 b) {
   return r;
 }
 
+// 16-byte vector access.  Loads carry the nontemporal hint.  Stores are plain
+// write-back stores, or nontemporal ones (`store_vec_nt`) where the step
+// kernel is told that a step writes more than the memory-side cache holds.
 __device__ __forceinline__ u32x4 load_vec(const u32x4* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void store_vec(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_vec(u32x4* p, u32x4 v) { *p = v; }
+__device__ __forceinline__ void store_vec_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
 template <uint32_t E>
 __device__ __forceinline__ uint32_t load_elem(const unsigned char* p) {

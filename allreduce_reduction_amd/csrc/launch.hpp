@@ -32,7 +32,18 @@ struct StepLaunch {
   bool aligned;           // every rank buffer has the same 16-byte phase
   uint32_t phase;         // that phase, bytes
   bool xcd_split;         // give each XCD one contiguous range of tiles
+  uint64_t write_bytes;   // bytes the step writes, all items and destinations
 };
+
+// Step kernel flags.
+constexpr uint32_t kFlagXcdSplit = 1u;
+
+// A step that writes more than the memory-side cache holds (MI355X: 256 MiB
+// Infinity Cache) gets the step kernel whose stores carry the nontemporal
+// hint; plain stores measured 2-10% slower there.  At or below it, plain
+// stores measured 2-4% faster (each step there reads blocks the previous
+// step wrote).
+constexpr uint64_t kCacheBytes = uint64_t(256) << 20;
 
 // A step of the single-workgroup plan kernel (device table).
 constexpr uint32_t kFusedMaxItems = 256;
@@ -58,7 +69,8 @@ struct KernelDesc {
   const DevItem* items = nullptr;
   const FusedStep* steps = nullptr;  // plan kernel only
   uint32_t nsteps = 0;               // plan kernel only
-  uint32_t phase = 0, xcd = 0;
+  uint32_t phase = 0;
+  uint32_t flags = 0;  // step kernel: kFlagXcdSplit
   // column kernel only
   const DevChunk* chunks = nullptr;
   const uint32_t* col_list = nullptr;
@@ -82,7 +94,7 @@ struct KernelDesc {
       argv[8] = &phase;
     } else {
       argv[2] = &phase;
-      argv[3] = &xcd;
+      argv[3] = &flags;
     }
   }
 };

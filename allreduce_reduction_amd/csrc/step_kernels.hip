@@ -10,11 +10,12 @@
 //
 // Data path: every operand of an item sits at the same element offset, and
 // when all rank buffers share one 16-byte phase the item's body is moved as
-// 16-byte vectors (global_load/store_dwordx4 with the nontemporal hint): one
-// wave per workgroup and one vector per lane per operand, i.e. 1 KiB tiles of
-// every operand per workgroup, which measured fastest for streams far larger
-// than the caches; the few head / tail elements are done one by one.  Buffers
-// with different phases take an element-wise kernel.
+// 16-byte vectors (global_load_dwordx4 with the nontemporal hint, plain
+// global_store_dwordx4): one wave per workgroup and one vector per lane per
+// operand, i.e. 1 KiB tiles of every operand per workgroup, which measured
+// fastest for streams far larger than the caches; the few head / tail
+// elements are done one by one.  Buffers with different phases take an
+// element-wise kernel.
 //
 // Element ops: fp16 / bf16 lanes are widened to fp32, combined and rounded
 // back to nearest even per operation; integers wrap; max / min order -0 below
@@ -52,12 +53,14 @@ __device__ __forceinline__ void wg_tile(bool xcd_split, uint32_t* item, uint32_t
   *tile = lin % gridDim.x;
 }
 
-template <int DT, int OP, int MODE, int NS, int ND>
+// NT: stores with the nontemporal hint (a compile-time choice: the compiler
+// merges the two stores of a run-time branch into one plain store).
+template <int DT, int OP, int MODE, int NS, int ND, bool NT>
 __global__ void __launch_bounds__(kThreads)
-step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint32_t xcd_split) {
+step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint32_t flags) {
   constexpr uint32_t E = Width<DT>::bytes;
   uint32_t item, tile;
-  wg_tile(xcd_split != 0, &item, &tile);
+  wg_tile((flags & kFlagXcdSplit) != 0, &item, &tile);
   const DevItem* it = items + item;
   const uint64_t begin = it->begin, count = it->count;
   const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
@@ -134,7 +137,10 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint3
 #pragma unroll
       for (int u = 0; u < kVecPerThread; ++u) {
         const uint64_t v = v0 + uint64_t(u) * kThreads;
-        if (v < nvec) store_vec(q + v, acc[u]);
+        if (v < nvec) {
+          if constexpr (NT) store_vec_nt(q + v, acc[u]);
+          else store_vec(q + v, acc[u]);
+        }
       }
     }
   }
@@ -166,6 +172,34 @@ const void* fn(F* f) {
   return reinterpret_cast<const void*>(f);
 }
 
+// The vector kernel for one step shape.  Item shapes of the schedules get
+// compile-time source counts: ring / RHD (2 sources) and the pipeline with 1,
+// 2, 4 or 8 ranks per server; any other shape takes the runtime-count kernel.
+template <int DT, int OP, bool NT>
+const void* vector_kernel(const StepLaunch& s) {
+  if (s.mode == kRecvFold) {
+    switch (s.nsrc) {
+      case 2: return fn(step_vec<DT, OP, kRecvFold, 2, 1, NT>);
+      case 3: return fn(step_vec<DT, OP, kRecvFold, 3, 1, NT>);
+      case 5: return fn(step_vec<DT, OP, kRecvFold, 5, 1, NT>);
+      case 9: return fn(step_vec<DT, OP, kRecvFold, 9, 1, NT>);
+      default: return fn(step_vec<DT, OP, kRecvFold, 0, 1, NT>);
+    }
+  }
+  if (s.mode == kFold) {
+    switch (s.nsrc) {
+      case 2: return fn(step_vec<DT, OP, kFold, 2, 1, NT>);
+      case 4: return fn(step_vec<DT, OP, kFold, 4, 1, NT>);
+      case 8: return fn(step_vec<DT, OP, kFold, 8, 1, NT>);
+      default: return fn(step_vec<DT, OP, kFold, 0, 1, NT>);
+    }
+  }
+  // several destinations: the runtime-count store loop measured faster than
+  // an unrolled one (1 read, 8 writes: 5.8 vs 5.4 TB/s)
+  if (s.ndst == 1) return fn(step_vec<DT, kSum, kCopy, 1, 1, NT>);
+  return fn(step_vec<DT, kSum, kCopy, 1, 0, NT>);
+}
+
 template <int DT, int OP>
 void describe_typed(const StepLaunch& s, KernelDesc* k) {
   constexpr uint32_t E = Width<DT>::bytes;
@@ -188,33 +222,8 @@ void describe_typed(const StepLaunch& s, KernelDesc* k) {
   k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
   k->block = dim3(kThreads);
   k->kind = KernelDesc::kVector;
-  k->xcd = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? 1u : 0u;
-  // item shapes of the schedules get compile-time source counts: ring / RHD
-  // (2 sources) and the pipeline with 1, 2, 4 or 8 ranks per server; any
-  // other shape takes the runtime-count kernel
-  if (s.mode == kRecvFold) {
-    switch (s.nsrc) {
-      case 2: k->func = fn(step_vec<DT, OP, kRecvFold, 2, 1>); break;
-      case 3: k->func = fn(step_vec<DT, OP, kRecvFold, 3, 1>); break;
-      case 5: k->func = fn(step_vec<DT, OP, kRecvFold, 5, 1>); break;
-      case 9: k->func = fn(step_vec<DT, OP, kRecvFold, 9, 1>); break;
-      default: k->func = fn(step_vec<DT, OP, kRecvFold, 0, 1>); break;
-    }
-  } else if (s.mode == kFold) {
-    switch (s.nsrc) {
-      case 2: k->func = fn(step_vec<DT, OP, kFold, 2, 1>); break;
-      case 4: k->func = fn(step_vec<DT, OP, kFold, 4, 1>); break;
-      case 8: k->func = fn(step_vec<DT, OP, kFold, 8, 1>); break;
-      default: k->func = fn(step_vec<DT, OP, kFold, 0, 1>); break;
-    }
-  } else {
-    // several destinations: the runtime-count store loop measured faster
-    // than an unrolled one (1 read, 8 writes: 5.8 vs 5.4 TB/s)
-    if (s.ndst == 1)
-      k->func = fn(step_vec<DT, kSum, kCopy, 1, 1>);
-    else
-      k->func = fn(step_vec<DT, kSum, kCopy, 1, 0>);
-  }
+  k->flags = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? kFlagXcdSplit : 0u;
+  k->func = s.write_bytes > kCacheBytes ? vector_kernel<DT, OP, true>(s) : vector_kernel<DT, OP, false>(s);
 }
 
 template <int DT>

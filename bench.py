@@ -11,9 +11,11 @@ Reported (one JSON line):
   value / ms_per_step  from K whole AllReduces (hbmc_allreduce), HIP events
              around each call on the launch stream, median
   roofline   the ring reduce-scatter step kernel: algorithmic bytes per launch
-             (3 bytes per segment byte, 8 segments) / its mean duration from
-             a second pass of K AllReduces issued step by step with HIP events
-             recorded between the steps on the launch stream
+             (3 bytes per segment byte, 8 segments) / its mean launch duration
+             from a pass of K AllReduces issued phase by phase, HIP events on
+             the launch stream around the P-1 back-to-back reduce-scatter
+             launches (copy_step: the same for the all-gather launches); a
+             pass with an event between every two steps is reported beside it
   cpu_baseline  the CPU oracle replaying the same AllReduce (single thread)
   auto_allreduce_same_workload  not the headline: the AUTO communicator's
              AllReduce of the same buffers (its cost model picks Flat)
@@ -308,7 +310,7 @@ def main():
     gpu_ms = [b.elapsed_time(e) for b, e in ev]
     t = float(np.median(gpu_ms)) / 1e3
 
-    # roofline pass: K more AllReduces issued step by step (the same kernels)
+    # stepwise pass: K more AllReduces issued step by step (the same kernels)
     # with an event between consecutive steps, for each kernel's duration; an
     # event between two kernels adds about 1.5 us of its own, so the headline
     # value comes from the pass above
@@ -327,6 +329,27 @@ def main():
     rs_ms = float(step_ms[:, rs_steps].mean())
     ag_steps = [s for s in range(nsteps) if s not in rs_steps]
     ag_ms = float(step_ms[:, ag_steps].mean()) if ag_steps and a.algo == "ring" else None
+    stepwise_rs_ms, stepwise_ag_ms = rs_ms, ag_ms
+
+    # phase pass (ring): K more AllReduces, each issued as its P-1 reduce-scatter
+    # steps and then its P-1 all-gather steps, with HIP events only at the phase
+    # boundaries, so each phase is P-1 back-to-back launches of one kernel and
+    # its mean launch duration carries no event cost
+    if a.algo == "ring":
+        h = nsteps // 2
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for b, q in zip(bufs, pristine):
+            b.copy_(q)
+        torch.cuda.synchronize()
+        for k in range(K):
+            pev[k][0].record(stream)
+            comm.run_steps("allreduce", bufs, 0, h, dtype, "sum")
+            pev[k][1].record(stream)
+            comm.run_steps("allreduce", bufs, h, nsteps, dtype, "sum")
+            pev[k][2].record(stream)
+        torch.cuda.synchronize()
+        rs_ms = float(np.mean([pev[k][0].elapsed_time(pev[k][1]) for k in range(K)])) / h
+        ag_ms = float(np.mean([pev[k][1].elapsed_time(pev[k][2]) for k in range(K)])) / (nsteps - h)
 
     algbw = D / t
     busbw = algbw * 2 * (P - 1) / P
@@ -356,13 +379,19 @@ def main():
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4),
                      "traffic": measured_traffic() if (P, L, a.algo) == (8, 64 << 20, "ring") else None,
-                     "bytes_per_launch": rs_bytes, "mean_launch_us": round(rs_ms * 1e3, 2)},
+                     "bytes_per_launch": rs_bytes, "mean_launch_us": round(rs_ms * 1e3, 2),
+                     "timing": ("HIP events around the P-1 back-to-back reduce-scatter launches of each of "
+                                "K AllReduces, mean per launch" if a.algo == "ring" else
+                                "HIP events between consecutive step launches, mean per launch"),
+                     "stepwise_events_mean_launch_us": round(stepwise_rs_ms * 1e3, 2)},
     }
     if ag_ms:
         ag_bytes = comm.step_info("allreduce", L, dtype, ag_steps[0])["hbm_bytes"]
         out["copy_step"] = {"kernel": "step_vec<fp32,copy,1,1> (ring all-gather step)",
                             "mean_launch_us": round(ag_ms * 1e3, 2),
-                            "achieved_GBps": round(ag_bytes / (ag_ms / 1e3) / 1e9, 1)}
+                            "achieved_GBps": round(ag_bytes / (ag_ms / 1e3) / 1e9, 1),
+                            "frac": round(ag_bytes / (ag_ms / 1e3) / HBM_PEAK, 4),
+                            "stepwise_events_mean_launch_us": round(stepwise_ag_ms * 1e3, 2)}
 
     # not the headline: the same workload on an AUTO communicator (the cost model
     # picks Flat on one GPU), inputs restored first, same number of calls
