@@ -90,6 +90,7 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
     if (v == "steps") c->exec_mode = kExecSteps;
     else if (v == "fused") c->exec_mode = kExecFused;
     else if (v == "columns") c->exec_mode = kExecColumns;
+    else if (v == "lds") c->exec_mode = kExecLds;
     else if (v == "auto") c->exec_mode = kExecAuto;
   }
   const char* xs = std::getenv("HBMC_XCD_SPLIT");
@@ -113,7 +114,7 @@ hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, 
 }
 
 hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode) {
-  if (!comm || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_COLUMNS) return HBMC_ERR_INVALID_ARG;
+  if (!comm || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_LDS) return HBMC_ERR_INVALID_ARG;
   comm->exec_mode = static_cast<int>(mode);
   return HBMC_OK;
 }
@@ -167,6 +168,7 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
   for (auto& kv : comm->plans) {
     if (kv.second->dev && hipFree(kv.second->dev) != hipSuccess) st = HBMC_ERR_HIP;
     if (kv.second->cols_mem && hipFree(kv.second->cols_mem) != hipSuccess) st = HBMC_ERR_HIP;
+    if (kv.second->lds_mem && hipFree(kv.second->lds_mem) != hipSuccess) st = HBMC_ERR_HIP;
   }
   delete comm;
   return st;

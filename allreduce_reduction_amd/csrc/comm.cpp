@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <new>
 
@@ -222,6 +223,48 @@ hbmc_status_t upload_columns(Plan* p) {
   return HBMC_OK;
 }
 
+hbmc_status_t upload_lds_tables(Plan* p, int P, uint32_t e) {
+  if (p->lds_mem) return HBMC_OK;
+  if (p->lds_cols.chunk_elems != p->lds_col || p->lds_cols.col_off.empty())
+    if (!build_columns(p->sched, P, p->lds_col, false, &p->lds_cols)) return HBMC_ERR_INVALID_ARG;
+  const ColumnTable& f = p->lds_cols;
+  const size_t n = f.col_list.size();
+  const size_t ncols = f.col_off.size() - 1;
+  std::vector<DevColChunk> host(n + 1);
+  std::memset(host.data(), 0, host.size() * sizeof(DevColChunk));
+  for (size_t g = 0; g < ncols; ++g) {
+    const uint64_t col_begin = uint64_t(g) * f.chunk_elems;
+    for (uint32_t k = f.col_off[g]; k < f.col_off[g + 1]; ++k) {
+      const ColumnChunk& c = f.chunks[f.col_list[k]];
+      const Step& st = p->sched.steps[c.step];
+      const Item& it = st.items[c.item - p->first_item[c.step]];
+      DevColChunk& d = host[k];
+      d.lo = static_cast<uint32_t>((c.begin - col_begin) * e);
+      d.hi = d.lo + c.count * e;
+      d.step = c.step;
+      d.shape = static_cast<uint32_t>(st.mode) | (static_cast<uint32_t>(it.nsrc) << 8) |
+                (static_cast<uint32_t>(it.ndst) << 16);
+      d.dst_mask = 0;
+      for (int q = 0; q < it.nsrc + it.ndst; ++q) d.rank[q] = it.rank[q];
+      for (int q = it.nsrc; q < it.nsrc + it.ndst; ++q) d.dst_mask |= uint64_t(1) << it.rank[q];
+    }
+  }
+  const size_t b_image = (host.size() * sizeof(DevColChunk) + 255) & ~size_t(255);
+  const size_t b_off = f.col_off.size() * sizeof(uint32_t);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, b_image + b_off) != hipSuccess) return HBMC_ERR_NOMEM;
+  char* base = static_cast<char*>(mem);
+  if (hipMemcpy(base, host.data(), host.size() * sizeof(DevColChunk), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(base + b_image, f.col_off.data(), b_off, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(mem);
+    return HBMC_ERR_HIP;
+  }
+  p->lds_mem = mem;
+  p->dev_image = reinterpret_cast<DevColChunk*>(base);
+  p->dev_lds_col_off = reinterpret_cast<uint32_t*>(base + b_image);
+  return HBMC_OK;
+}
+
 hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e) {
   if (!bufs) return HBMC_ERR_INVALID_ARG;
   const uint64_t bytes = uint64_t(count) * e;
@@ -252,7 +295,114 @@ uint32_t compute_units() {
   return cached[dev];
 }
 
+// Dynamic LDS one workgroup may use, and LDS per compute unit, of the current
+// device.
+void lds_limits(uint64_t* per_block, uint64_t* per_cu) {
+  static uint64_t blk[64] = {}, cu[64] = {};
+  int dev = 0;
+  *per_block = 64 << 10;
+  *per_cu = 64 << 10;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  if (blk[dev] == 0) {
+    int b = 0, m = 0;
+    if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || b <= 0)
+      b = 64 << 10;
+    if (hipDeviceGetAttribute(&m, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || m < b)
+      m = b;
+    blk[dev] = static_cast<uint64_t>(b);
+    cu[dev] = static_cast<uint64_t>(m);
+  }
+  *per_block = blk[dev];
+  *per_cu = cu[dev];
+}
+
+// Workgroups of the LDS-resident column kernel: one per column, at most as
+// many as the compute units hold at once.
+uint32_t lds_grid(uint32_t ncols, uint64_t shared_bytes) {
+  uint64_t per_block = 0, per_cu = 0;
+  lds_limits(&per_block, &per_cu);
+  const uint64_t per = std::max<uint64_t>(1, std::min<uint64_t>(8, per_cu / std::max<uint64_t>(1, shared_bytes)));
+  return static_cast<uint32_t>(std::max<uint64_t>(1, std::min<uint64_t>(ncols, compute_units() * per)));
+}
+
+// Chunks of the longest column for a column length of `col` elements: each
+// item adds one chunk to every column it meets.
+uint64_t longest_column(const Schedule& s, uint64_t count, uint64_t col) {
+  const uint64_t ncols = (count + col - 1) / col;
+  std::vector<int64_t> diff(ncols + 1, 0);
+  for (const Step& st : s.steps)
+    for (const Item& it : st.items) {
+      if (it.count == 0) continue;
+      diff[it.begin / col] += 1;
+      diff[(it.begin + it.count - 1) / col + 1] -= 1;
+    }
+  int64_t run = 0, best = 0;
+  for (uint64_t g = 0; g < ncols; ++g) {
+    run += diff[g];
+    best = std::max(best, run);
+  }
+  return static_cast<uint64_t>(best);
+}
+
+// Modelled time of the LDS-resident form with columns of `col` elements
+// whose longest column has `longest` chunks (`share`: the fraction of the
+// schedule's busy steps the launch runs): the columns a workgroup runs one
+// after another, times the chunks of a column, times the 16-byte positions
+// each lane takes per chunk; plus loading and storing every rank buffer.
+double lds_time(const ExecModel& m, int P, uint64_t count, uint32_t e, uint64_t col, uint64_t longest,
+                double share) {
+  const uint64_t ncols = (count + col - 1) / col;
+  const uint32_t grid = lds_grid(static_cast<uint32_t>(std::min<uint64_t>(ncols, UINT32_MAX)),
+                                 lds_bytes(P, col, e, longest));
+  const double rounds = std::ceil(double(ncols) / grid);
+  const uint64_t positions = std::max<uint64_t>(1, col * e / 16);
+  const uint64_t lanes = lds_threads(col, e);
+  const double per_lane = std::ceil(double(positions) / lanes);
+  return m.lds_us + rounds * double(longest) * share * per_lane * m.lds_chunk_us +
+         2.0 * double(P) * double(count) * e / (m.lds_gbps * 1e3);
+}
+
 }  // namespace
+
+hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t e) {
+  if (p->lds_key == c->column_bytes) return HBMC_OK;
+  if (p->lds_mem) {
+    // the device tables belong to the old length
+    if (hipDeviceSynchronize() != hipSuccess || hipFree(p->lds_mem) != hipSuccess) return HBMC_ERR_HIP;
+    p->lds_mem = nullptr;
+  }
+  uint64_t per_block = 0, per_cu = 0;
+  lds_limits(&per_block, &per_cu);
+  p->lds_col = 0;
+  p->lds_longest = 0;
+  auto fits = [&](uint64_t col, uint64_t longest) { return lds_bytes(P, col, e, longest) <= per_block; };
+  if (c->column_bytes > 0) {
+    const uint64_t col = column_elems(c->column_bytes, count, e, compute_units());
+    const uint64_t longest = longest_column(p->sched, count, col);
+    if (fits(col, longest)) {
+      p->lds_col = col;
+      p->lds_longest = longest;
+    }
+  } else {
+    // 16-byte multiples from the longest that can fit down to 16 bytes
+    double best = 0.0;
+    uint64_t top = 16;
+    while (top * 2 <= uint64_t(count) * e && top * 2 * P <= per_block) top *= 2;
+    for (uint64_t bytes = top; bytes >= 16; bytes /= 2) {
+      const uint64_t col = bytes / e;
+      const uint64_t longest = longest_column(p->sched, count, col);
+      if (!fits(col, longest)) continue;
+      const double t = lds_time(c->model, P, count, e, col, longest, 1.0);
+      if (p->lds_col == 0 || t < best * 0.98) {
+        best = t;
+        p->lds_col = col;
+        p->lds_longest = longest;
+      }
+    }
+  }
+  p->lds_key = c->column_bytes;
+  return HBMC_OK;
+}
 
 hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t count, uint32_t e, bool aligned,
                           int* mode) {
@@ -273,6 +423,13 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
   }
   const bool fused_ok = aligned && busy > 0 && items_ok && bytes <= c->fused_limit;
   const bool cols_ok = aligned && busy > 1 && count * e <= c->columns_limit / uint64_t(P);
+  // the LDS-resident form: when some column length fits one workgroup's LDS
+  bool lds_ok = false;
+  if (cols_ok && (c->exec_mode == kExecLds || c->exec_mode == kExecAuto)) {
+    hbmc_status_t st = lds_layout(c, p, P, count, e);
+    if (st != HBMC_OK) return st;
+    lds_ok = p->lds_col > 0;
+  }
   *mode = kExecSteps;
   if (c->exec_mode == kExecFused) {
     if (fused_ok) *mode = kExecFused;
@@ -280,6 +437,10 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
   }
   if (c->exec_mode == kExecColumns) {
     if (cols_ok) *mode = kExecColumns;
+    return HBMC_OK;
+  }
+  if (c->exec_mode == kExecLds) {
+    if (lds_ok) *mode = kExecLds;
     return HBMC_OK;
   }
   if (c->exec_mode != kExecAuto) return HBMC_OK;
@@ -300,6 +461,13 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     if (t < best) {
       best = t;
       *mode = kExecColumns;
+    }
+  }
+  if (lds_ok) {
+    const double t = lds_time(m, P, count, e, p->lds_col, p->lds_longest, double(busy) / std::max(1, busy_all));
+    if (t < best) {
+      best = t;
+      *mode = kExecLds;
     }
   }
   return HBMC_OK;
@@ -361,6 +529,24 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     launches->push_back(k);
     return HBMC_OK;
   }
+  if (mode == kExecLds) {
+    // the whole step range as one LDS-resident column-kernel launch
+    st = upload_lds_tables(p, P, e);
+    if (st != HBMC_OK) return st;
+    const ColumnTable& f = p->lds_cols;
+    const uint32_t ncols = static_cast<uint32_t>(f.col_off.size() - 1);
+    const uint64_t shared = lds_bytes(P, p->lds_col, e, f.max_per_col);
+    KernelDesc k;
+    describe_columns_lds(dtype, op, ptrs, p->dev_image, p->dev_lds_col_off, ncols, static_cast<uint32_t>(first),
+                         static_cast<uint32_t>(last), phase, p->lds_col, count, static_cast<uint32_t>(P),
+                         f.max_per_col, lds_grid(ncols, shared), &k);
+    if (shared > (64u << 10) &&
+        hipFuncSetAttribute(k.func, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shared)) !=
+            hipSuccess)
+      return HBMC_ERR_HIP;
+    launches->push_back(k);
+    return HBMC_OK;
+  }
   for (int s = first; s < last; ++s) {
     const Step& step = p->sched.steps[s];
     if (step.items.empty()) continue;
@@ -387,7 +573,8 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
 
 hbmc_status_t launch(KernelDesc& k, void* stream) {
   k.bind();
-  const hipError_t e = hipLaunchKernel(k.func, k.grid, k.block, k.argv, 0, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      hipLaunchKernel(k.func, k.grid, k.block, k.argv, k.shared_bytes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return HBMC_ERR_HIP;
   return hipGetLastError() == hipSuccess ? HBMC_OK : HBMC_ERR_HIP;
 }

@@ -16,7 +16,7 @@
 namespace hbmc {
 
 // How a call's steps are launched.
-enum ExecMode : int { kExecAuto = 0, kExecSteps = 1, kExecFused = 2, kExecColumns = 3 };
+enum ExecMode : int { kExecAuto = 0, kExecSteps = 1, kExecFused = 2, kExecColumns = 3, kExecLds = 4 };
 
 // Modelled time (us) of a range of steps in each launch form, fitted to
 // measurements on MI355X (one launch per step, the single-workgroup kernel,
@@ -31,6 +31,9 @@ struct ExecModel {
   double col_us = 4.0;          // column kernel: launch
   double col_hop_us = 0.85;     //   per chunk of the longest column (run one after another)
   double col_gbps = 6000.0;     //   streaming rate
+  double lds_us = 4.0;          // LDS-resident column kernel: launch, load and store round trips
+  double lds_chunk_us = 0.56;   //   per chunk of the longest column (one wave's pass over it)
+  double lds_gbps = 5000.0;     //   loading and storing every rank buffer once
 };
 
 uint32_t elem_bytes(int dtype);
@@ -51,6 +54,17 @@ struct Plan {
   DevChunk* dev_chunks = nullptr;
   uint32_t* dev_col_list = nullptr;
   uint32_t* dev_col_off = nullptr;
+  // the LDS-resident column kernel: its column length, chosen per plan for
+  // the communicator's column_bytes setting `lds_key`; the chunks of its
+  // longest column; its own column table and, built on first launch, the
+  // device chunk records and column offsets (one allocation)
+  uint64_t lds_key = UINT64_MAX;
+  uint64_t lds_col = 0;  // 0: no column length fits one workgroup's LDS
+  uint64_t lds_longest = 0;
+  ColumnTable lds_cols;
+  void* lds_mem = nullptr;
+  DevColChunk* dev_image = nullptr;
+  uint32_t* dev_lds_col_off = nullptr;
 };
 
 }  // namespace hbmc
@@ -110,6 +124,16 @@ hbmc_status_t column_table(Plan* p, int P, uint64_t chunk_elems, const ColumnTab
 // column length changed; the old tables are freed after a device
 // synchronisation).
 hbmc_status_t upload_columns(Plan* p);
+// Column length of the LDS-resident column kernel for plan p (P ranks, count
+// elements of e bytes), cached in the plan: the communicator's column_bytes
+// when set; otherwise, of the lengths 16 B, 32 B, ... that fit one
+// workgroup's LDS, the one of least modelled time (ties: the longer).
+// Sets p->lds_col (0 when none fits) and p->lds_longest.
+hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t e);
+// Build and upload the LDS-resident kernel's tables for p->lds_col: column
+// g's chunks in order at [col_off[g], col_off[g+1]), each with its byte range
+// relative to the column, step, shape, rank numbers and destination mask.
+hbmc_status_t upload_lds_tables(Plan* p, int P, uint32_t e);
 // Launch form of steps [first, last) of plan `p` (count elements of e bytes,
 // buffers of one 16-byte phase when `aligned`): the communicator's mode when
 // not AUTO and the form is eligible; for AUTO the eligible form of least

@@ -98,7 +98,7 @@ hbmc_status_t hbmc_graph_build(hbmc_graph_t g) {
       prm.func = const_cast<void*>(k.func);
       prm.gridDim = k.grid;
       prm.blockDim = k.block;
-      prm.sharedMemBytes = 0;
+      prm.sharedMemBytes = k.shared_bytes;
       prm.kernelParams = k.argv;
       prm.extra = nullptr;
       hipGraphNode_t node = nullptr;

@@ -58,10 +58,22 @@ struct alignas(16) DevChunk {
   uint32_t count, item, mode, step, pad0, pad1;
 };
 
+// A chunk as the LDS-resident column kernel reads it (device table, one run
+// per column, in the column's schedule order; copied into LDS as is): bytes
+// [lo, hi) of the column, relative to its first element.
+struct alignas(16) DevColChunk {
+  uint32_t lo, hi, step;
+  uint32_t shape;                  // mode | nsrc << 8 | ndst << 16
+  uint64_t dst_mask;               // bit r set when rank r is a destination
+  uint32_t pad0, pad1;
+  uint8_t rank[2 * kDevRanks];     // sources, then destinations
+};
+static_assert(sizeof(DevColChunk) == 160, "column chunk record");
+
 // One kernel launch: kernel, shape and argument values, usable with
 // hipLaunchKernel or as a kernel graph node.
 struct KernelDesc {
-  enum Kind { kVector = 0, kElement = 1, kFused = 2, kColumns = 3 };
+  enum Kind { kVector = 0, kElement = 1, kFused = 2, kColumns = 3, kColumnsLds = 4 };
   Kind kind = kVector;
   const void* func = nullptr;
   dim3 grid, block;
@@ -76,7 +88,12 @@ struct KernelDesc {
   const uint32_t* col_list = nullptr;
   const uint32_t* col_off = nullptr;
   uint32_t ncols = 0, c_lo = 0, c_hi = 0;
-  void* argv[9];  // filled by bind(); valid while this object lives
+  // LDS-resident column kernel only
+  const DevColChunk* image = nullptr;
+  uint64_t col_elems = 0, count = 0;
+  uint32_t nranks = 0, slot_bytes = 0, s_lo = 0, s_hi = 0;
+  uint32_t shared_bytes = 0;  // dynamic LDS per workgroup
+  void* argv[12];  // filled by bind(); valid while this object lives
   void bind() {
     argv[0] = &ptrs;
     argv[1] = &items;
@@ -92,6 +109,18 @@ struct KernelDesc {
       argv[6] = &c_lo;
       argv[7] = &c_hi;
       argv[8] = &phase;
+    } else if (kind == kColumnsLds) {
+      argv[0] = &ptrs;
+      argv[1] = &image;
+      argv[2] = &col_off;
+      argv[3] = &ncols;
+      argv[4] = &s_lo;
+      argv[5] = &s_hi;
+      argv[6] = &phase;
+      argv[7] = &col_elems;
+      argv[8] = &count;
+      argv[9] = &nranks;
+      argv[10] = &slot_bytes;
     } else {
       argv[2] = &phase;
       argv[3] = &flags;
@@ -104,6 +133,23 @@ struct KernelDesc {
 void describe_columns(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const DevChunk* chunks,
                       const uint32_t* col_list, const uint32_t* col_off, uint32_t ncols, uint32_t c_lo,
                       uint32_t c_hi, uint32_t phase, uint32_t grid, KernelDesc* k);
+
+// The dynamic LDS a workgroup of the LDS-resident column kernel needs:
+// nranks column slots, then one record per entry of the longest column's
+// chunk list.
+uint32_t lds_slot_bytes(uint64_t col_elems, uint32_t e);
+// Lanes per workgroup: about one per 16-byte position of a column (64, 128
+// or 256).
+uint32_t lds_threads(uint64_t col_elems, uint32_t e);
+uint64_t lds_bytes(int nranks, uint64_t col_elems, uint32_t e, uint64_t max_chunks_per_col);
+
+// The LDS-resident column kernel over steps [s_lo, s_hi) of a plan: `grid`
+// workgroups, workgroup w running columns w, w + grid, ... of `col_elems`
+// elements (the last one cut at `count`); column g's chunk records are
+// image[col_off[g] .. col_off[g+1]).
+void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColChunk* image, const uint32_t* col_off,
+                          uint32_t ncols, uint32_t s_lo, uint32_t s_hi, uint32_t phase, uint64_t col_elems,
+                          uint64_t count, uint32_t nranks, uint64_t max_chunks_per_col, uint32_t grid, KernelDesc* k);
 
 // The single-workgroup kernel running `nsteps` steps of a plan.
 void describe_fused(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const FusedStep* steps,

@@ -191,7 +191,7 @@ def suite(a):
                     info = c.plan_info("allreduce", L, "fp16")
                     reps = max(5, min(200, int(1e8 // info["hbm_bytes"])))
                     auto_form = c.exec_choice("allreduce", L, "fp16")
-                    for form in ("steps", "fused", "columns", "auto"):
+                    for form in ("steps", "fused", "columns", "lds", "auto"):
                         c.set_exec_mode(form)
                         if form != "auto" and c.exec_choice("allreduce", L, "fp16") != form:
                             continue

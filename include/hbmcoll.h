@@ -127,12 +127,22 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    wave runs a column's share of every step in schedule order, without
  *    waiting for other waves ([RING-RHD] "Ring AllReduce带宽最优的环形流水线":
  *    the ring pipelines segments so no one waits for a whole step);
+ *  - HBMC_EXEC_LDS: all steps in one launch of the LDS-resident column
+ *    kernel: one workgroup per column loads the column of every rank buffer
+ *    into LDS once, runs every step on the LDS copies and writes back the
+ *    rank buffers the steps wrote.  Each lane owns fixed 16-byte positions
+ *    of the column for the whole launch, so steps need no barrier.  The
+ *    column length is column_bytes when set, else chosen per call shape by
+ *    the model below among 16 B, 32 B, ... lengths that fit LDS;
  *  - HBMC_EXEC_AUTO (default, or the environment variable HBMC_EXEC = auto,
- *    steps, fused or columns): per call the eligible form of least modelled
- *    time, with constants measured on MI355X: steps sum over the steps
- *    max(4.2 us, 3 us + bytes / 6.4 TB/s); fused 2 us + 1.6 us per step +
- *    bytes / 33 GB/s; columns 4 us + 0.85 us per chunk of the longest column
- *    + bytes / 6 TB/s (bytes: the algorithmic HBM bytes of the steps).
+ *    steps, fused, columns or lds): per call the eligible form of least
+ *    modelled time, with constants measured on MI355X: steps sum over the
+ *    steps max(4.2 us, 3 us + bytes / 6.4 TB/s); fused 2 us + 1.6 us per
+ *    step + bytes / 33 GB/s; columns 4 us + 0.85 us per chunk of the longest
+ *    column + bytes / 6 TB/s (bytes: the algorithmic HBM bytes of the
+ *    steps); lds 4 us + R * H * N * 0.56 us + 2 P count e / 5 TB/s, with R
+ *    the columns each workgroup runs one after another, H the chunks of the
+ *    longest column and N the 16-byte positions per lane.
  * A forced form falls back to STEPS where it is not eligible.  Eligibility:
  * both one-launch forms need rank buffers of one 16-byte phase; FUSED needs
  * at most 256 items per step and at most `max_bytes` algorithmic bytes in
@@ -141,10 +151,14 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  * steps and P * count * e (the rank buffers' total size) of at most
  * `max_total_bytes` (hbmc_comm_set_columns; default 64 MiB, or
  * HBMC_COLUMNS_LIMIT): working sets the caches hold, so that larger calls
- * keep the per-step HBM traffic the schedule defines.  The forms apply to
+ * keep the per-step HBM traffic the schedule defines; LDS needs what COLUMNS
+ * needs, and a column of every rank buffer plus 160 bytes per chunk of the
+ * longest column within one workgroup's LDS.  The forms apply to
  * every call, hbmc_run_steps ranges and graph nodes.  Host only.
  */
-typedef enum { HBMC_EXEC_AUTO = 0, HBMC_EXEC_STEPS = 1, HBMC_EXEC_FUSED = 2, HBMC_EXEC_COLUMNS = 3 } hbmc_exec_t;
+typedef enum {
+  HBMC_EXEC_AUTO = 0, HBMC_EXEC_STEPS = 1, HBMC_EXEC_FUSED = 2, HBMC_EXEC_COLUMNS = 3, HBMC_EXEC_LDS = 4
+} hbmc_exec_t;
 hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode);
 hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes);
 /* column_bytes: 0, or 16 .. 2^31 (rounded down to a multiple of 16). */

@@ -1,5 +1,6 @@
-"""The column kernel (one launch per call; one wave runs each column of
-elements through every step) against the CPU oracle, bit for bit.
+"""The column kernels (one launch per call; one wave, or with the columns
+resident in LDS one workgroup, runs each column of elements through every
+step) against the CPU oracle, bit for bit.
 
 Columns far narrower than the items (down to one 16-byte vector) make every
 item span many columns and every column cross item and segment boundaries;
@@ -22,6 +23,7 @@ from test_gpu_parity import OPS, make_inputs
 pytestmark = pytest.mark.gpu
 
 DTYPES = ["fp32", "fp16", "bf16", "int32", "int8"]
+MODES = ["columns", "lds"]
 
 
 def say(*a):
@@ -42,20 +44,22 @@ CASES = [  # (algo, P, comm args, oracle keywords, collectives)
 ]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}{c[1]}" for c in CASES])
-def test_columns_parity(case, dtype):
+def test_columns_parity(case, dtype, mode):
     algo, P, args, kw, colls = case
     rng = np.random.default_rng(zlib.crc32(f"columns/{algo}/{P}/{dtype}".encode()))
     with hc.Comm(*args) as comm:
-        comm.set_exec_mode("columns")
+        comm.set_exec_mode(mode)
         for coll in colls:
             op = str(rng.choice(OPS))
             L = int(rng.choice([7, 1000, 3 * 4096 + 5, 40_003]))
             chunk = int(rng.choice([0, 16, 48, 1024, 4096]))
             comm.set_columns(1 << 40, chunk)
             root = int(rng.integers(0, P))
-            say(f"case columns algo={algo} P={P} coll={coll} dtype={dtype} op={op} L={L} chunk={chunk} root={root}")
+            say(f"case {mode} algo={algo} P={P} coll={coll} dtype={dtype} op={op} L={L} chunk={chunk} root={root}")
+            assert comm.exec_choice(coll, L, dtype, root=root) == mode
             xs = make_inputs(dtype, op, P, L, seed=L + P)
             if rng.random() < 0.5:
                 dev = [to_dev(x, dtype) for x in xs]
@@ -72,29 +76,30 @@ def test_columns_parity(case, dtype):
             want = [x.copy() for x in xs]
             oracle.run(coll, algo, want, dtype, op, root=root, **kw)
             for r in ([root] if coll == "reduce" else range(P)):
-                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"columns {algo} {coll} rank {r}")
+                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{mode} {algo} {coll} rank {r}")
 
 
-def test_columns_step_ranges_and_repeats():
+@pytest.mark.parametrize("mode", MODES)
+def test_columns_step_ranges_and_repeats(mode):
     """Sub-ranges of steps, repeated launches of one plan, column lengths
     changed between calls and per-step calls interleaved on one communicator."""
     P, L, dtype = 6, 30_001, "int32"
     xs = make_inputs(dtype, "sum", P, L, seed=9)
     with hc.Comm(P, "ring") as comm:
         comm.set_columns(1 << 40, 512)
-        comm.set_exec_mode("columns")
+        comm.set_exec_mode(mode)
         n = comm.plan_info("allreduce", L, dtype)["nsteps"]
         dev = [to_dev(x, dtype) for x in xs]
         want = [x.copy() for x in xs]
         for a, b in ((0, 1), (1, 4), (4, n)):
-            say(f"case columns steps [{a},{b})")
+            say(f"case {mode} steps [{a},{b})")
             comm.run_steps("allreduce", dev, a, b, dtype, "sum")
             oracle.run("allreduce", "ring", want, dtype, "sum", first_step=a, last_step=b)
             torch.cuda.synchronize()
             for r in range(P):
                 refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"steps [{a},{b}) rank {r}")
         for rep in range(6):
-            say(f"case columns repeat {rep}")
+            say(f"case {mode} repeat {rep}")
             if rep % 2:
                 comm.set_columns(0)
             else:
@@ -106,12 +111,13 @@ def test_columns_step_ranges_and_repeats():
                 refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"repeat {rep} rank {r}")
 
 
-def test_columns_out_of_place_and_graph():
+@pytest.mark.parametrize("mode", MODES)
+def test_columns_out_of_place_and_graph(mode):
     P, L, dtype = 5, 9999, "bf16"
     xs = make_inputs(dtype, "max", P, L, seed=4)
     with hc.Comm(P, "rhd") as comm:
         comm.set_columns(1 << 40, 1024)
-        comm.set_exec_mode("columns")
+        comm.set_exec_mode(mode)
         send = [to_dev(x, dtype) for x in xs]
         recv = [torch.empty_like(t) for t in send]
         comm.out_of_place("allreduce", send, recv, dtype, "max")
