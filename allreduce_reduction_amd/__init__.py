@@ -126,36 +126,58 @@ def _check(rc: int, what: str) -> None:
         raise HbmcError(rc, what)
 
 
+_TORCH_DTYPES = None
+
+
+def _torch_dtypes():
+    global _TORCH_DTYPES
+    if _TORCH_DTYPES is None:
+        import torch
+        _TORCH_DTYPES = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16",
+                         torch.int32: "int32", torch.int8: "int8"}
+    return _TORCH_DTYPES
+
+
 def _torch_dtype_name(t) -> str:
-    import torch
-    m = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16", torch.int32: "int32",
-         torch.int8: "int8"}
-    if t.dtype not in m:
+    name = _torch_dtypes().get(t.dtype)
+    if name is None:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
-    return m[t.dtype]
+    return name
 
 
 def _ptrs(bufs):
     """(void*[P], count, dtype) from a list of device tensors or raw addresses."""
     P = len(bufs)
-    arr = (ctypes.c_void_p * max(P, 1))()
     if P and hasattr(bufs[0], "data_ptr"):
-        n = bufs[0].numel()
-        dt = _torch_dtype_name(bufs[0])
-        for i, b in enumerate(bufs):
-            if not b.is_cuda or not b.is_contiguous() or b.numel() != n or _torch_dtype_name(b) != dt:
+        b0 = bufs[0]
+        dt = _torch_dtype_name(b0)
+        t0, n = b0.dtype, b0.numel()
+        addrs = []
+        for b in bufs:
+            if b.dtype != t0 or not b.is_cuda or not b.is_contiguous() or b.numel() != n:
                 raise ValueError("buffers must be contiguous device tensors of one dtype and size")
-            arr[i] = b.data_ptr()
-        return arr, n, dt
+            addrs.append(b.data_ptr())
+        return (ctypes.c_void_p * P)(*addrs), n, dt
+    arr = (ctypes.c_void_p * max(P, 1))()
     for i, b in enumerate(bufs):
         arr[i] = int(b)
     return arr, None, None
 
 
+_RAW_STREAM = None
+
+
 def _stream(stream) -> int:
+    """The stream handle: the given torch stream or raw handle, else the
+    current device's current torch stream."""
+    global _RAW_STREAM
     if stream is None:
         import torch
-        return torch.cuda.current_stream().cuda_stream
+        if _RAW_STREAM is None:
+            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            _RAW_STREAM = (lambda: raw(torch.cuda.current_device())) if raw else \
+                (lambda: torch.cuda.current_stream().cuda_stream)
+        return _RAW_STREAM()
     return int(getattr(stream, "cuda_stream", stream))
 
 
