@@ -140,3 +140,25 @@ def test_columns_out_of_place_and_graph(mode):
                 torch.cuda.synchronize()
                 for r in range(P):
                     refops.assert_same(dtype, to_host(gb[r], dtype), want[r], f"graph replay {rep} rank {r}")
+
+
+@pytest.mark.parametrize("mode", MODES + ["auto"])
+@pytest.mark.parametrize("algo", ["ring", "rhd", "flat"])
+def test_max_ranks(algo, mode):
+    """64 ranks, the most a communicator takes: chunk records whose rank lists
+    run past 16 entries (Flat folds 64 sources into one destination and
+    copies one source to 63), empty segments (L < P) and ragged tails."""
+    P = 64
+    with hc.Comm(P, algo) as comm:
+        comm.set_exec_mode(mode)
+        for L, dtype, op in ((40, "int32", "sum"), (1000, "bf16", "max"), (6000 + 5, "fp16", "sum")):
+            say(f"case {mode} max ranks algo={algo} L={L} dtype={dtype} op={op} "
+                f"form={comm.exec_choice('allreduce', L, dtype)}")
+            xs = make_inputs(dtype, op, P, L, seed=L)
+            dev = [to_dev(x, dtype) for x in xs]
+            comm.allreduce(dev, dtype, op)
+            torch.cuda.synchronize()
+            want = [x.copy() for x in xs]
+            oracle.run("allreduce", algo, want, dtype, op)
+            for r in range(P):
+                refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{mode} {algo} P=64 rank {r}")
