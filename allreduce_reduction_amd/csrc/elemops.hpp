@@ -58,8 +58,9 @@ __device__ __forceinline__ uint32_t narrow_f16(float f) {
 __device__ __forceinline__ float widen_bf16(uint32_t h) { return u2f(h << 16); }
 __device__ __forceinline__ uint32_t narrow_bf16(float f) {
   const uint32_t u = f2u(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet the NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;                  // nearest even
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // nearest even
+  const uint32_t qnan = (u >> 16) | 0x40u;                      // the NaN, quieted
+  return (u & 0x7fffffffu) > 0x7f800000u ? qnan : rne;          // a select, no branch
 }
 
 // One 16-bit lane (value in the low half of the word).
