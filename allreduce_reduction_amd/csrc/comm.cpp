@@ -245,8 +245,28 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint32_t e) {
       d.shape = static_cast<uint32_t>(st.mode) | (static_cast<uint32_t>(it.nsrc) << 8) |
                 (static_cast<uint32_t>(it.ndst) << 16);
       d.dst_mask = 0;
+      d.batch = 1;
       for (int q = 0; q < it.nsrc + it.ndst; ++q) d.rank[q] = it.rank[q];
       for (int q = it.nsrc; q < it.nsrc + it.ndst; ++q) d.dst_mask |= uint64_t(1) << it.rank[q];
+    }
+    // runs of same-step, same-range records of the reduce (2 sources, 1
+    // destination) or copy (1, 1) shape, cut into batches of 8, 4 or 2
+    auto batchable = [&](const DevColChunk& a, const DevColChunk& b) {
+      const uint32_t sh = a.shape;
+      const bool shape_ok = sh == (uint32_t(kRecvFold) | (2u << 8) | (1u << 16)) ||
+                            sh == (uint32_t(kCopy) | (1u << 8) | (1u << 16));
+      return shape_ok && b.shape == sh && a.step == b.step && a.lo == b.lo && a.hi == b.hi;
+    };
+    for (uint32_t k = f.col_off[g]; k < f.col_off[g + 1];) {
+      uint32_t run = 1;
+      while (k + run < f.col_off[g + 1] && batchable(host[k], host[k + run])) ++run;
+      while (run > 0) {
+        const uint32_t b = run >= 8 ? 8 : (run >= 4 ? 4 : (run >= 2 ? 2 : 1));
+        host[k].batch = b;
+        for (uint32_t q = 1; q < b; ++q) host[k + q].batch = 0;
+        k += b;
+        run -= b;
+      }
     }
   }
   const size_t b_image = (host.size() * sizeof(DevColChunk) + 255) & ~size_t(255);
@@ -344,21 +364,68 @@ uint64_t longest_column(const Schedule& s, uint64_t count, uint64_t col) {
   return static_cast<uint64_t>(best);
 }
 
-// Modelled time of the LDS-resident form with columns of `col` elements
-// whose longest column has `longest` chunks (`share`: the fraction of the
-// schedule's busy steps the launch runs): the columns a workgroup runs one
-// after another, times the chunks of a column, times the 16-byte positions
-// each lane takes per chunk; plus loading and storing every rank buffer.
-double lds_time(const ExecModel& m, int P, uint64_t count, uint32_t e, uint64_t col, uint64_t longest,
-                double share) {
+// Serial chunk passes of the busiest column for a column length of `col`
+// elements, in units of one chunk's pass: per step, the chunks that cover a
+// whole column go in batches of 8, 4, 2 or 1 (the kernel's runs of
+// same-range chunks, assuming one shape per step), a batch of n costing
+// 1 + 0.75 (n - 1) passes (fitted on MI355X: a batch's loads overlap, its
+// element ops mostly do not); every chunk that covers part of a column goes
+// alone.  Beyond
+// 2^24 column-steps it falls back to counting every chunk.
+double longest_passes(const Schedule& s, uint64_t count, uint64_t col) {
+  const uint64_t ncols = (count + col - 1) / col;
+  if (ncols * s.steps.size() > (uint64_t(1) << 24)) return double(longest_column(s, count, col));
+  std::vector<double> passes(ncols, 0.0);
+  std::vector<int64_t> full(ncols + 1), part(ncols + 1);
+  for (const Step& st : s.steps) {
+    std::fill(full.begin(), full.end(), 0);
+    std::fill(part.begin(), part.end(), 0);
+    for (const Item& it : st.items) {
+      if (it.count == 0) continue;
+      const uint64_t b = it.begin, e = it.begin + it.count;
+      const uint64_t g0 = b / col, g1 = (e - 1) / col;  // columns met
+      // columns covered whole: [f0, f1) (the last column ends at count)
+      const uint64_t f0 = (b + col - 1) / col, f1 = e == count ? ncols : e / col;
+      if (f0 < f1) {
+        full[f0] += 1;
+        full[f1] -= 1;
+      }
+      const bool cut_first = g0 < f0, cut_last = g1 >= f1;
+      if (cut_first) part[g0] += 1;
+      if (cut_last && !(cut_first && g1 == g0)) part[g1] += 1;
+    }
+    int64_t run = 0;
+    for (uint64_t g = 0; g < ncols; ++g) {
+      run += full[g];
+      uint64_t n = static_cast<uint64_t>(run);
+      double t = double(part[g]);
+      for (uint64_t b : {8u, 4u, 2u, 1u})
+        for (; n >= b; n -= b) t += 1.0 + 0.75 * double(b - 1);
+      passes[g] += t;
+    }
+  }
+  double best = 0.0;
+  for (double v : passes) best = std::max(best, v);
+  return best;
+}
+
+// Modelled time of the LDS-resident form with columns of `col` elements,
+// `chunks` chunks in the longest column's list (its LDS records) and
+// `longest` serial chunk passes in the busiest column (`share`: the
+// fraction of the schedule's busy steps the launch runs): the columns a
+// workgroup runs one after another, times those passes, times the 16-byte
+// positions each lane takes per chunk; plus loading and storing every rank
+// buffer.
+double lds_time(const ExecModel& m, int P, uint64_t count, uint32_t e, uint64_t col, uint64_t chunks,
+                double longest, double share) {
   const uint64_t ncols = (count + col - 1) / col;
   const uint32_t grid = lds_grid(static_cast<uint32_t>(std::min<uint64_t>(ncols, UINT32_MAX)),
-                                 lds_bytes(P, col, e, longest));
+                                 lds_bytes(P, col, e, chunks));
   const double rounds = std::ceil(double(ncols) / grid);
   const uint64_t positions = std::max<uint64_t>(1, col * e / 16);
   const uint64_t lanes = lds_threads(col, e);
   const double per_lane = std::ceil(double(positions) / lanes);
-  return m.lds_us + rounds * double(longest) * share * per_lane * m.lds_chunk_us +
+  return m.lds_us + rounds * longest * share * per_lane * m.lds_chunk_us +
          2.0 * double(P) * double(count) * e / (m.lds_gbps * 1e3);
 }
 
@@ -374,14 +441,16 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
   uint64_t per_block = 0, per_cu = 0;
   lds_limits(&per_block, &per_cu);
   p->lds_col = 0;
-  p->lds_longest = 0;
+  p->lds_chunks = 0;
+  p->lds_longest = 0.0;
   auto fits = [&](uint64_t col, uint64_t longest) { return lds_bytes(P, col, e, longest) <= per_block; };
   if (c->column_bytes > 0) {
     const uint64_t col = column_elems(c->column_bytes, count, e, compute_units());
-    const uint64_t longest = longest_column(p->sched, count, col);
-    if (fits(col, longest)) {
+    const uint64_t chunks = longest_column(p->sched, count, col);
+    if (fits(col, chunks)) {
       p->lds_col = col;
-      p->lds_longest = longest;
+      p->lds_chunks = chunks;
+      p->lds_longest = longest_passes(p->sched, count, col);
     }
   } else {
     // 16-byte multiples from the longest that can fit down to 16 bytes
@@ -390,13 +459,15 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
     while (top * 2 <= uint64_t(count) * e && top * 2 * P <= per_block) top *= 2;
     for (uint64_t bytes = top; bytes >= 16; bytes /= 2) {
       const uint64_t col = bytes / e;
-      const uint64_t longest = longest_column(p->sched, count, col);
-      if (!fits(col, longest)) continue;
-      const double t = lds_time(c->model, P, count, e, col, longest, 1.0);
+      const uint64_t chunks = longest_column(p->sched, count, col);
+      if (!fits(col, chunks)) continue;
+      const double passes = longest_passes(p->sched, count, col);
+      const double t = lds_time(c->model, P, count, e, col, chunks, passes, 1.0);
       if (p->lds_col == 0 || t < best * 0.98) {
         best = t;
         p->lds_col = col;
-        p->lds_longest = longest;
+        p->lds_chunks = chunks;
+        p->lds_longest = passes;
       }
     }
   }
@@ -464,7 +535,8 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     }
   }
   if (lds_ok) {
-    const double t = lds_time(m, P, count, e, p->lds_col, p->lds_longest, double(busy) / std::max(1, busy_all));
+    const double t = lds_time(m, P, count, e, p->lds_col, p->lds_chunks, p->lds_longest,
+                              double(busy) / std::max(1, busy_all));
     if (t < best) {
       best = t;
       *mode = kExecLds;

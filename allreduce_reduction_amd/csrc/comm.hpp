@@ -60,7 +60,8 @@ struct Plan {
   // device chunk records and column offsets (one allocation)
   uint64_t lds_key = UINT64_MAX;
   uint64_t lds_col = 0;  // 0: no column length fits one workgroup's LDS
-  uint64_t lds_longest = 0;
+  uint64_t lds_chunks = 0;   // chunks of the longest column (its LDS records)
+  double lds_longest = 0.0;  // serial chunk passes of the busiest column (for the cost model)
   ColumnTable lds_cols;
   void* lds_mem = nullptr;
   DevColChunk* dev_image = nullptr;
@@ -128,7 +129,7 @@ hbmc_status_t upload_columns(Plan* p);
 // elements of e bytes), cached in the plan: the communicator's column_bytes
 // when set; otherwise, of the lengths 16 B, 32 B, ... that fit one
 // workgroup's LDS, the one of least modelled time (ties: the longer).
-// Sets p->lds_col (0 when none fits) and p->lds_longest.
+// Sets p->lds_col (0 when none fits), p->lds_chunks and p->lds_longest.
 hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t e);
 // Build and upload the LDS-resident kernel's tables for p->lds_col: column
 // g's chunks in order at [col_off[g], col_off[g+1]), each with its byte range

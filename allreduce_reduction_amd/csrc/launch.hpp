@@ -65,9 +65,15 @@ struct alignas(16) DevColChunk {
   uint32_t lo, hi, step;
   uint32_t shape;                  // mode | nsrc << 8 | ndst << 16
   uint64_t dst_mask;               // bit r set when rank r is a destination
-  uint32_t pad0, pad1;
+  uint32_t batch;                  // see below
+  uint32_t pad;
   uint8_t rank[2 * kDevRanks];     // sources, then destinations
 };
+// `batch`: on the first record of a run of 2, 4 or 8 consecutive records of
+// one step with the same byte range and the same two-source-one-destination
+// reduce or one-to-one copy shape, the run's length; 0 on the run's other
+// records; 1 on every record outside such runs.  The chunks of one step never
+// conflict, so a lane may apply a run's chunks together.
 static_assert(sizeof(DevColChunk) == 160, "column chunk record");
 
 // One kernel launch: kernel, shape and argument values, usable with

@@ -105,6 +105,55 @@ __device__ __forceinline__ void lds_chunk(unsigned char* lds, uint32_t slot_byte
   }
 }
 
+// This lane's positions of a batch of NB chunks of one step that share the
+// byte range [lo, hi) and a shape: two-source reduce (MODE kRecvFold:
+// rank[k] = src0 | src1 << 8 | dst << 16) or copy (kCopy: src | dst << 8).
+// The chunks are independent, so every load of the batch is issued before
+// any result is combined; the element-wise edges go chunk by chunk.
+template <int DT, int OP, int MODE, int NB>
+__device__ __forceinline__ void lds_batch(unsigned char* lds, uint32_t slot_bytes, uint32_t lo, uint32_t hi,
+                                          const uint32_t* rank) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  const uint32_t nthr = blockDim.x;  // a power of two
+  const uint32_t p_lo = lo >> 4, p_hi = (hi + 15) >> 4;
+  uint32_t p = p_lo + ((threadIdx.x - p_lo) & (nthr - 1));
+  auto slot = [&](int k, int which) { return lds + ((rank[k] >> (8 * which)) & 0xffu) * slot_bytes; };
+  for (; p < p_hi; p += nthr) {
+    const uint32_t a = p * 16, b = a + 16;
+    if (a >= lo && b <= hi) {
+      u32x4 x[NB], y[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        x[k] = *reinterpret_cast<const u32x4*>(slot(k, 0) + a);
+        if constexpr (MODE == kRecvFold) y[k] = *reinterpret_cast<const u32x4*>(slot(k, 1) + a);
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if constexpr (MODE == kRecvFold) *reinterpret_cast<u32x4*>(slot(k, 2) + a) = op_vec<DT, OP>(x[k], y[k]);
+        else *reinterpret_cast<u32x4*>(slot(k, 1) + a) = x[k];
+      }
+    } else {
+      const uint32_t l = a > lo ? a : lo, h = b < hi ? b : hi;
+      for (uint32_t o = l; o < h; o += E) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          if constexpr (MODE == kRecvFold)
+            store_elem<E>(slot(k, 2) + o, op_word<DT, OP>(load_elem<E>(slot(k, 0) + o), load_elem<E>(slot(k, 1) + o)));
+          else
+            store_elem<E>(slot(k, 1) + o, load_elem<E>(slot(k, 0) + o));
+        }
+      }
+    }
+  }
+}
+
+template <int DT, int OP, int NB>
+__device__ __forceinline__ void run_batch(unsigned char* lds, uint32_t slot_bytes, uint32_t lo, uint32_t hi,
+                                          uint32_t mode, const uint32_t* rank) {
+  if (mode == kRecvFold) lds_batch<DT, OP, kRecvFold, NB>(lds, slot_bytes, lo, hi, rank);
+  else lds_batch<DT, kSum, kCopy, NB>(lds, slot_bytes, lo, hi, rank);
+}
+
 // Global <-> LDS for this lane's positions of every rank in `mask`: the
 // column's bytes are slot offsets [phase, phase + n*E); whole positions move
 // as 16-byte vectors, the cut first / last positions element by element.
@@ -187,6 +236,26 @@ plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uin
       const uint32_t lo = phase + uni(h.x), hi = phase + uni(h.y), shape = uni(h.w);
       const u32x4 mv = *reinterpret_cast<const u32x4*>(&meta[j].dst_mask);
       dirty |= uint64_t(uni(mv.x)) | (uint64_t(uni(mv.y)) << 32);
+      const uint32_t nb = uni(mv.z);
+      if (nb > 1) {
+        // a batch: the same step, range and shape; its first ranks and masks
+        uint32_t rank[8];
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k) {
+          if (k >= nb) break;
+          rank[k] = uni(*reinterpret_cast<const uint32_t*>(meta[j + k].rank));
+          if (k > 0) {
+            const u32x4 mk = *reinterpret_cast<const u32x4*>(&meta[j + k].dst_mask);
+            dirty |= uint64_t(uni(mk.x)) | (uint64_t(uni(mk.y)) << 32);
+          }
+        }
+        const uint32_t mode = shape & 0xffu;
+        if (nb == 8) run_batch<DT, OP, 8>(lds, slot_bytes, lo, hi, mode, rank);
+        else if (nb == 4) run_batch<DT, OP, 4>(lds, slot_bytes, lo, hi, mode, rank);
+        else run_batch<DT, OP, 2>(lds, slot_bytes, lo, hi, mode, rank);
+        j += nb - 1;
+        continue;
+      }
       const u32x4 rv = *reinterpret_cast<const u32x4*>(meta[j].rank);
       const uint32_t rw[4] = {uni(rv.x), uni(rv.y), uni(rv.z), uni(rv.w)};
       const uint8_t* lr = meta[j].rank;

@@ -141,8 +141,9 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    step + bytes / 33 GB/s; columns 4 us + 0.85 us per chunk of the longest
  *    column + bytes / 6 TB/s (bytes: the algorithmic HBM bytes of the
  *    steps); lds 4 us + R * H * N * 0.56 us + 2 P count e / 5 TB/s, with R
- *    the columns each workgroup runs one after another, H the chunks of the
- *    longest column and N the 16-byte positions per lane.
+ *    the columns each workgroup runs one after another, H the serial chunk
+ *    passes of the busiest column (a run of n same-range chunks of one step
+ *    counting 1 + 0.75 (n - 1)) and N the 16-byte positions per lane.
  * A forced form falls back to STEPS where it is not eligible.  Eligibility:
  * both one-launch forms need rank buffers of one 16-byte phase; FUSED needs
  * at most 256 items per step and at most `max_bytes` algorithmic bytes in

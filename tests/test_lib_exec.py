@@ -33,10 +33,12 @@ def test_auto_small_rhd_p16_prefers_the_single_workgroup():
 
 
 def test_auto_prefers_steps_where_launches_are_few_and_bytes_many():
-    # RHD at P=16 has 8 steps: at 1 MiB per rank eight launches beat the
-    # column kernel's 30-chunk columns
-    with hc.Comm(16, "rhd") as c:
-        assert c.exec_choice("allreduce", 512 << 10, "fp16") == "steps"
+    # Flat has two steps: at 4 MiB per rank (64 MiB in all, within the column
+    # limit) two launches beat streaming every rank buffer through LDS and
+    # folding 16 sources per chunk there
+    with hc.Comm(16, "flat") as c:
+        assert c.exec_choice("allreduce", 2 << 20, "fp16") == "steps"
+        assert c.exec_choice("allreduce", 32 << 10, "fp16") == "lds"
 
 
 def test_forced_forms_and_fallbacks():
