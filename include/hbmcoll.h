@@ -25,6 +25,15 @@
  *     cached schedules and their device tables.  A communicator is not
  *     thread-safe; calls that overlap on one communicator from several host
  *     threads race.
+ *   - The first call of a (collective, root, count, dtype) builds its schedule
+ *     and uploads its device tables with hipMalloc and blocking copies (and
+ *     so does the first call in the LDS or column form, and one after the
+ *     column length changes, which also synchronises the device before
+ *     freeing the old tables); later calls with the same shape only enqueue
+ *     kernels.  Tables live on the device current at that first call: a
+ *     communicator serves one device, and a call made with another device
+ *     current returns HBMC_ERR_INVALID_ARG.  Cached schedules are kept until
+ *     hbmc_comm_destroy.
  *   - count == 0 and P == 1 are valid and enqueue nothing.
  */
 #ifndef HBMCOLL_H
