@@ -162,3 +162,25 @@ def test_max_ranks(algo, mode):
             oracle.run("allreduce", algo, want, dtype, op)
             for r in range(P):
                 refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{mode} {algo} P=64 rank {r}")
+
+
+@pytest.mark.parametrize("algo,P,dtype,L", [("ring", 8, "fp32", 8 << 20), ("rhd", 5, "bf16", 32 << 20)])
+def test_lds_past_the_default_limit(algo, P, dtype, L):
+    """With the column limit raised, the LDS form runs calls of 256-320 MiB in
+    all (hundreds of thousands of columns); its result equals one launch per
+    step bit for bit (that form is pinned to the oracle at full size)."""
+    xs = make_inputs(dtype, "sum", P, L, seed=5)
+    with hc.Comm(P, algo) as comm:
+        comm.set_columns(1 << 40, 0)
+        comm.set_exec_mode("lds")
+        say(f"case lds large algo={algo} P={P} dtype={dtype} L={L} form={comm.exec_choice('allreduce', L, dtype)}")
+        assert comm.exec_choice("allreduce", L, dtype) == "lds"
+        a = [to_dev(x, dtype) for x in xs]
+        comm.allreduce(a, dtype, "sum")
+        comm.set_exec_mode("steps")
+        b = [to_dev(x, dtype) for x in xs]
+        comm.allreduce(b, dtype, "sum")
+        torch.cuda.synchronize()
+        for r in range(P):
+            assert torch.equal(a[r].view(torch.int16 if dtype == "bf16" else torch.int32),
+                               b[r].view(torch.int16 if dtype == "bf16" else torch.int32)), f"rank {r}"
