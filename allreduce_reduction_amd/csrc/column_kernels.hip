@@ -50,7 +50,7 @@ __device__ __forceinline__ void column_body(const RankPtrs& ptrs, const DevItem*
       u32x4 x[NS][kColUnroll];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[s]] + base);
+        const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, s) + base);
 #pragma unroll
         for (int u = 0; u < kColUnroll; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kColThreads;
@@ -75,7 +75,7 @@ __device__ __forceinline__ void column_body(const RankPtrs& ptrs, const DevItem*
     } else {
       const int first = MODE == kRecvFold ? 1 : 0;
       {
-        const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[first]] + base);
+        const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, first) + base);
 #pragma unroll
         for (int u = 0; u < kColUnroll; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kColThreads;
@@ -84,7 +84,7 @@ __device__ __forceinline__ void column_body(const RankPtrs& ptrs, const DevItem*
       }
       if constexpr (MODE != kCopy) {
         for (int s = first + 1; s < ns; ++s) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[s]] + base);
+          const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, s) + base);
 #pragma unroll
           for (int u = 0; u < kColUnroll; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kColThreads;
@@ -92,7 +92,7 @@ __device__ __forceinline__ void column_body(const RankPtrs& ptrs, const DevItem*
           }
         }
         if constexpr (MODE == kRecvFold) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[0]] + base);
+          const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, 0) + base);
 #pragma unroll
           for (int u = 0; u < kColUnroll; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kColThreads;
@@ -102,7 +102,7 @@ __device__ __forceinline__ void column_body(const RankPtrs& ptrs, const DevItem*
       }
     }
     for (int d = 0; d < (ND > 0 ? ND : nd); ++d) {
-      u32x4* q = reinterpret_cast<u32x4*>(ptrs.p[it->rank[ns + d]] + base);
+      u32x4* q = reinterpret_cast<u32x4*>(rank_buf(ptrs, it, ns + d) + base);
 #pragma unroll
       for (int u = 0; u < kColUnroll; ++u) {
         const uint64_t v = v0 + uint64_t(u) * kColThreads;

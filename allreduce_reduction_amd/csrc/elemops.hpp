@@ -140,21 +140,30 @@ __device__ __forceinline__ void store_elem(unsigned char* p, uint32_t v) {
   else *p = static_cast<unsigned char>(v);
 }
 
+// Buffer of an item's i-th rank.  The rank index is read as part of its
+// aligned 32-bit word: gfx950 has no scalar byte load, and a byte read becomes
+// a vector load that waits behind the streaming traffic before any data load
+// of the workgroup can be addressed.
+__device__ __forceinline__ unsigned char* rank_buf(const RankPtrs& ptrs, const DevItem* it, int i) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(it->rank)[i >> 2];
+  return ptrs.p[(w >> ((i & 3) * 8)) & 0xffu];
+}
+
 // Combination of an item's sources at one element (byte offset `off`).
 template <int DT, int OP, int MODE>
 __device__ __forceinline__ uint32_t combine_elem(const RankPtrs& ptrs, const DevItem* it, int ns,
                                                  uint64_t off) {
   constexpr uint32_t E = Width<DT>::bytes;
   if constexpr (MODE == kCopy) {
-    return load_elem<E>(ptrs.p[it->rank[0]] + off);
+    return load_elem<E>(rank_buf(ptrs, it, 0) + off);
   } else if constexpr (MODE == kFold) {
-    uint32_t acc = load_elem<E>(ptrs.p[it->rank[0]] + off);
-    for (int s = 1; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(ptrs.p[it->rank[s]] + off));
+    uint32_t acc = load_elem<E>(rank_buf(ptrs, it, 0) + off);
+    for (int s = 1; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(rank_buf(ptrs, it, s) + off));
     return acc;
   } else {
-    uint32_t acc = load_elem<E>(ptrs.p[it->rank[1]] + off);
-    for (int s = 2; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(ptrs.p[it->rank[s]] + off));
-    return op_word<DT, OP>(load_elem<E>(ptrs.p[it->rank[0]] + off), acc);
+    uint32_t acc = load_elem<E>(rank_buf(ptrs, it, 1) + off);
+    for (int s = 2; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(rank_buf(ptrs, it, s) + off));
+    return op_word<DT, OP>(load_elem<E>(rank_buf(ptrs, it, 0) + off), acc);
   }
 }
 
@@ -164,7 +173,7 @@ __device__ __forceinline__ void do_elem(const RankPtrs& ptrs, const DevItem* it,
   constexpr uint32_t E = Width<DT>::bytes;
   const uint64_t off = elem * E;
   const uint32_t v = combine_elem<DT, OP, MODE>(ptrs, it, ns, off);
-  for (int d = 0; d < nd; ++d) store_elem<E>(ptrs.p[it->rank[ns + d]] + off, v);
+  for (int d = 0; d < nd; ++d) store_elem<E>(rank_buf(ptrs, it, ns + d) + off, v);
 }
 
 

@@ -23,7 +23,7 @@ constexpr int kFusedThreads = 1024;
 
 template <int DT, int OP, int MODE>
 __device__ __forceinline__ u32x4 combine_vec(const RankPtrs& ptrs, const DevItem* it, int ns, uint64_t off) {
-  auto ld = [&](int s) { return *reinterpret_cast<const u32x4*>(ptrs.p[it->rank[s]] + off); };
+  auto ld = [&](int s) { return *reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, s) + off); };
   if constexpr (MODE == kCopy) {
     return ld(0);
   } else if constexpr (MODE == kFold) {
@@ -68,7 +68,7 @@ __device__ void fused_step(const RankPtrs& ptrs, const DevItem* its, uint32_t ni
     const int ns = static_cast<int>(it->nsrc), nd = static_cast<int>(it->ndst);
     const uint64_t off = (it->begin + s_head[lo]) * E + (v - s_start[lo]) * 16;
     const u32x4 r = combine_vec<DT, OP, MODE>(ptrs, it, ns, off);
-    for (int d = 0; d < nd; ++d) *reinterpret_cast<u32x4*>(ptrs.p[it->rank[ns + d]] + off) = r;
+    for (int d = 0; d < nd; ++d) *reinterpret_cast<u32x4*>(rank_buf(ptrs, it, ns + d) + off) = r;
   }
   for (uint32_t k = threadIdx.x; k < nitems * 32; k += blockDim.x) {
     const uint32_t i = k / 32, lane = k % 32;

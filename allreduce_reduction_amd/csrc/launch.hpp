@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cstddef>
 #include <cstdint>
 
 namespace hbmc {
@@ -17,11 +18,14 @@ struct RankPtrs {
 // A work item as the kernels read it from device memory: every destination's
 // elements [begin, begin+count) receive the step's combination of the
 // sources' same elements.  rank[0..nsrc) are sources, then ndst destinations.
+// The ranks follow the shape words directly, so that one scalar load reads
+// an item's range, shape and first eight ranks.
 struct alignas(16) DevItem {
   uint64_t begin, count;
-  uint32_t nsrc, ndst, pad0, pad1;
+  uint32_t nsrc, ndst;
   uint8_t rank[2 * kDevRanks];
 };
+static_assert(offsetof(DevItem, rank) == 24 && sizeof(DevItem) == 160, "work item record");
 
 struct StepLaunch {
   int dtype, op, mode;    // element type, reduce op, Mode of plan.hpp

@@ -40,15 +40,13 @@ constexpr int kElemThreads = 256;   // element-wise kernel
 
 // Vector kernel.  NS / ND > 0 fix the item shape at compile time (all loads
 // of a tile issued before any combine); 0 reads it from the item.
-// Workgroup -> (item, tile).  Workgroups are dealt to the 8 XCDs round-robin
-// by linear id; with `xcd_split` each XCD instead walks one contiguous range
-// of the step's tiles.
-__device__ __forceinline__ void wg_tile(bool xcd_split, uint32_t* item, uint32_t* tile) {
+// Workgroup -> (item, tile): grid.y is the item and grid.x the tile, and the
+// hardware deals workgroups to the 8 XCDs round-robin by linear id.  With
+// `xcd_split` each XCD instead walks one contiguous range of the step's tiles.
+__device__ __forceinline__ void xcd_tile(uint32_t* item, uint32_t* tile) {
   uint32_t lin = blockIdx.y * gridDim.x + blockIdx.x;
-  if (xcd_split) {
-    const uint32_t per = (gridDim.x * gridDim.y) / 8;
-    lin = (lin % 8) * per + lin / 8;
-  }
+  const uint32_t per = (gridDim.x * gridDim.y) / 8;
+  lin = (lin % 8) * per + lin / 8;
   *item = lin / gridDim.x;
   *tile = lin % gridDim.x;
 }
@@ -59,12 +57,22 @@ template <int DT, int OP, int MODE, int NS, int ND, bool NT>
 __global__ void __launch_bounds__(kThreads)
 step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint32_t flags) {
   constexpr uint32_t E = Width<DT>::bytes;
-  uint32_t item, tile;
-  wg_tile((flags & kFlagXcdSplit) != 0, &item, &tile);
+  uint32_t item = blockIdx.y, tile = blockIdx.x;
+  if (flags & kFlagXcdSplit) xcd_tile(&item, &tile);
   const DevItem* it = items + item;
   const uint64_t begin = it->begin, count = it->count;
   const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
   const int nd = ND > 0 ? ND : static_cast<int>(it->ndst);
+  // A fixed-shape item's buffer addresses, all taken before the first data
+  // load: the scalar loads behind them are then issued together, and the
+  // workgroup waits on one chain (kernel arguments, item record, addresses)
+  // rather than on one address after another.
+  constexpr int NB = NS > 0 && ND > 0 ? NS + ND : 1;
+  unsigned char* buf[NB];
+  if constexpr (NS > 0 && ND > 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) buf[b] = rank_buf(ptrs, it, b);
+  }
 
   uint64_t head = ((16u - ((phase + begin * E) & 15u)) & 15u) / E;
   if (head > count) head = count;
@@ -80,7 +88,10 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint3
       u32x4 x[NS][kVecPerThread];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[s]] + base);
+        const unsigned char* src;
+        if constexpr (ND > 0) src = buf[s];
+        else src = rank_buf(ptrs, it, s);
+        const u32x4* p = reinterpret_cast<const u32x4*>(src + base);
 #pragma unroll
         for (int u = 0; u < kVecPerThread; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
@@ -105,7 +116,7 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint3
     } else {
       const int first = MODE == kRecvFold ? 1 : 0;
       {
-        const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[first]] + base);
+        const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, first) + base);
 #pragma unroll
         for (int u = 0; u < kVecPerThread; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
@@ -114,7 +125,7 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint3
       }
       if constexpr (MODE != kCopy) {
         for (int s = first + 1; s < ns; ++s) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[s]] + base);
+          const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, s) + base);
 #pragma unroll
           for (int u = 0; u < kVecPerThread; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
@@ -122,7 +133,7 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint3
           }
         }
         if constexpr (MODE == kRecvFold) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(ptrs.p[it->rank[0]] + base);
+          const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, 0) + base);
 #pragma unroll
           for (int u = 0; u < kVecPerThread; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
@@ -133,7 +144,10 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint3
     }
 #pragma unroll
     for (int d = 0; d < (ND > 0 ? ND : nd); ++d) {
-      u32x4* q = reinterpret_cast<u32x4*>(ptrs.p[it->rank[ns + d]] + base);
+      unsigned char* dst;
+      if constexpr (NS > 0 && ND > 0) dst = buf[NS + d];
+      else dst = rank_buf(ptrs, it, ns + d);
+      u32x4* q = reinterpret_cast<u32x4*>(dst + base);
 #pragma unroll
       for (int u = 0; u < kVecPerThread; ++u) {
         const uint64_t v = v0 + uint64_t(u) * kThreads;
