@@ -132,8 +132,11 @@ struct KernelDesc {
       argv[9] = &nranks;
       argv[10] = &slot_bytes;
     } else {
-      argv[2] = &phase;
-      argv[3] = &flags;
+      // step kernels: the small arguments first (preloaded into registers)
+      argv[0] = &items;
+      argv[1] = &phase;
+      argv[2] = &flags;
+      argv[3] = &ptrs;
     }
   }
 };

@@ -55,7 +55,7 @@ __device__ __forceinline__ void xcd_tile(uint32_t* item, uint32_t* tile) {
 // merges the two stores of a run-time branch into one plain store).
 template <int DT, int OP, int MODE, int NS, int ND, bool NT>
 __global__ void __launch_bounds__(kThreads)
-step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint32_t flags) {
+step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, RankPtrs ptrs) {
   constexpr uint32_t E = Width<DT>::bytes;
   uint32_t item = blockIdx.y, tile = blockIdx.x;
   if (flags & kFlagXcdSplit) xcd_tile(&item, &tile);
@@ -170,7 +170,7 @@ step_vec(RankPtrs ptrs, const DevItem* __restrict__ items, uint32_t phase, uint3
 // Element-wise kernel for buffers whose 16-byte phases differ.
 template <int DT, int OP, int MODE>
 __global__ void __launch_bounds__(kElemThreads)
-step_elem(RankPtrs ptrs, const DevItem* __restrict__ items) {
+step_elem(const DevItem* __restrict__ items, uint32_t, uint32_t, RankPtrs ptrs) {
   const DevItem* it = items + blockIdx.y;
   const uint64_t begin = it->begin, count = it->count;
   const int ns = static_cast<int>(it->nsrc), nd = static_cast<int>(it->ndst);
@@ -231,8 +231,10 @@ void describe_typed(const StepLaunch& s, KernelDesc* k) {
     }
     return;
   }
-  const uint64_t vecs = s.max_count * E / 16 + 1;
-  const uint64_t gx = (vecs + kTileVecs - 1) / kTileVecs;
+  // body vectors of the largest item (a head of fewer than 16 bytes only
+  // shortens the body); tile 0 of each item also takes the head and tail
+  const uint64_t vecs = s.max_count * E / 16;
+  const uint64_t gx = vecs > kTileVecs ? (vecs + kTileVecs - 1) / kTileVecs : 1;
   k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
   k->block = dim3(kThreads);
   k->kind = KernelDesc::kVector;

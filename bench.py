@@ -46,7 +46,7 @@ def measured_traffic():
     import hashlib
     path = os.path.join(ROOT, "profiles", "ring_rs_step_p8_fp32_64Mi_hbm_traffic.md")
     src = b"".join(open(os.path.join(ROOT, "allreduce_reduction_amd", "csrc", f), "rb").read()
-                   for f in ("step_kernels.hip", "elemops.hpp"))
+                   for f in ("step_kernels.hip", "elemops.hpp", "launch.hpp"))
     digest = hashlib.sha256(src).hexdigest()[:16]
     try:
         kv = dict(line.strip().split(": ", 1) for line in open(path, encoding="utf-8")
