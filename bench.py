@@ -23,8 +23,9 @@ Reported (one JSON line):
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --suite    (one JSON line per other workload: RHD small
                                    messages, launch forms across sizes, the P=16
-                                   ring / RHD sweep, the 4x8 pipeline; not the
-                                   headline line)
+                                   ring / RHD sweep, the 4x8 pipeline; calls of
+                                   at most 256 MiB in all are also timed with
+                                   cold caches; not the headline line)
 """
 from __future__ import annotations
 
@@ -94,6 +95,27 @@ def time_calls(fn, reps, warmup):
     return out[1]
 
 
+def time_cold(fn, reps, scrub):
+    """Median GPU time of one call (s) with cold caches: before every call a
+    fill of `scrub` (512 MiB) evicts the L2s and the 256 MiB memory-side cache
+    from the call's buffers; HIP events bracket the call alone."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    out = []
+    for i in range(reps):
+        scrub.fill_(i & 0xFF)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        out.append(a.elapsed_time(b) / 1e3)
+    out.sort()
+    return out[len(out) // 2]
+
+
 def suite(a):
     """Timing of the other workloads: RHD small messages (P = 8 and 5), the P=16
     ring / RHD sweep (AllReduce, reduce-scatter, all-gather) and the 4 x 8
@@ -116,6 +138,10 @@ def suite(a):
     def emit(**kw):
         print(json.dumps(kw), flush=True)
 
+    # calls of at most 256 MiB in all are also timed with cold caches
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold_limit = 256 << 20
+
     # RHD small messages: launch-bound; report us per AllReduce and per step
     for P in (8, 5):
         for recipe, op in (("rhd_bf16_normal", "sum"), ("rhd_int32_uniform", "max")):
@@ -131,6 +157,7 @@ def suite(a):
                         b.copy_(q)
                     form = c.exec_choice("allreduce", L, dtype)
                     t = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
+                    t_cold = time_cold(lambda: c.allreduce(bufs, dtype, op), 31, scrub)
                     c.set_exec_mode("steps")
                     t_steps = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
                     c.set_exec_mode("auto")
@@ -146,7 +173,8 @@ def suite(a):
                         g10.build()
                         tg10 = time_calls(lambda: g10.launch(), 50, 5) / 10
                 emit(workload="rhd_small", algo="rhd", coll="allreduce", P=P, dtype=dtype, op=op,
-                     bytes_per_rank=L * e, launch_form=form, us=round(t * 1e6, 2), steps=n,
+                     bytes_per_rank=L * e, launch_form=form, us=round(t * 1e6, 2), cold_us=round(t_cold * 1e6, 2),
+                     steps=n,
                      us_per_step=round(t * 1e6 / n, 2), one_launch_per_step_us=round(t_steps * 1e6, 2),
                      one_launch_per_step_us_per_step=round(t_steps * 1e6 / n, 2),
                      graph_us=round(tg * 1e6, 2), graph_us_per_step=round(tg * 1e6 / n, 2),
@@ -169,9 +197,15 @@ def suite(a):
                     info = c.plan_info(coll, L, "fp16")
                     reps = max(3, min(200, int(2e8 // max(info["hbm_bytes"], 1))))
                     t = time_calls(lambda: getattr(c, coll)(bufs, "fp16", "sum"), reps, 2)
+                    cold = None
+                    if P * nbytes <= cold_limit:
+                        for b, q in zip(bufs, pristine):
+                            b.copy_(q)
+                        cold = round(time_cold(lambda: getattr(c, coll)(bufs, "fp16", "sum"), 15, scrub) * 1e6, 2)
                     factor = 2 * (P - 1) / P if coll == "allreduce" else (P - 1) / P
                     emit(workload="sweep_p16_fp16", algo=algo, coll=coll, P=P, bytes_per_rank=nbytes,
-                         launch_form=c.exec_choice(coll, L, "fp16"), us=round(t * 1e6, 2), steps=info["nsteps"],
+                         launch_form=c.exec_choice(coll, L, "fp16"), us=round(t * 1e6, 2), cold_us=cold,
+                         steps=info["nsteps"],
                          busbw_GBps=round(nbytes / t * factor / 1e9, 3),
                          pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2))
         del bufs, pristine
@@ -198,6 +232,8 @@ def suite(a):
                         if form == "fused" and kib > 64:
                             continue  # one compute unit: far slower, skip the long runs
                         row[form] = round(time_calls(lambda: c.allreduce(bufs, "fp16", "max"), reps, 3) * 1e6, 2)
+                    if P * (kib << 10) <= cold_limit:
+                        row["auto_cold"] = round(time_cold(lambda: c.allreduce(bufs, "fp16", "max"), 15, scrub) * 1e6, 2)
                 emit(workload="launch_forms", algo=algo, P=P, dtype="fp16", op="max", bytes_per_rank=kib << 10,
                      hbm_bytes=info["hbm_bytes"], steps=info["nsteps"], auto_form=auto_form, us=row)
                 del bufs
