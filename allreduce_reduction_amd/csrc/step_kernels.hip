@@ -208,8 +208,10 @@ const void* vector_kernel(const StepLaunch& s) {
       default: return fn(step_vec<DT, OP, kFold, 0, 1, NT>);
     }
   }
-  // several destinations: the runtime-count store loop measured faster than
-  // an unrolled one (1 read, 8 writes: 5.8 vs 5.4 TB/s)
+  // several destinations: the runtime-count store loop, which fetches each
+  // destination's address just before its store, measured faster than
+  // compile-time counts that fetch all addresses first (1 read, 8 writes:
+  // 5.8 vs 5.4 TB/s; 1 read, 7 writes of 256 MiB: 389 vs 410 us)
   if (s.ndst == 1) return fn(step_vec<DT, kSum, kCopy, 1, 1, NT>);
   return fn(step_vec<DT, kSum, kCopy, 1, 0, NT>);
 }
