@@ -166,13 +166,18 @@ def test_parity_rooted(coll, dtype):
                     refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{coll} P={P} root={root} r={r}")
 
 
-@pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
-def test_parity_many_ranks(algo):
+@pytest.mark.parametrize("exec_mode", ["steps", "auto"])
+@pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline", "flat"])
+def test_parity_many_ranks(algo, exec_mode):
+    """Up to 64 ranks: item rank lists that run past the first 32-bit word of
+    rank numbers (the pipeline's 9 sources, Flat's 64 sources and 63
+    destinations), through one launch per step and through AUTO's form."""
     for P in (13, 16, 32, 64):
         if algo == "pipeline" and P == 13:
             continue
         for dtype, op in (("fp32", "sum"), ("bf16", "sum"), ("int8", "max")):
-            check_case(algo, "allreduce", dtype, op, P, 20_000 + P, seed=P, loop_bytes=16384)
+            check_case(algo, "allreduce", dtype, op, P, 20_000 + P, seed=P, loop_bytes=16384,
+                       exec_mode=exec_mode)
 
 
 @pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
