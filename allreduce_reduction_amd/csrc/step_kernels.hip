@@ -36,23 +36,24 @@ constexpr int kVecPerThread = 1;    // 16-byte vectors per lane per operand
 constexpr uint64_t kTileVecs = uint64_t(kThreads) * kVecPerThread;
 constexpr int kElemThreads = 256;   // element-wise kernel
 
-// Resident workgroups per compute unit for steps whose workgroups each keep
-// many HBM streams open, capped by reserving LDS the kernel never touches
+// Resident workgroups per compute unit for steps of many items whose
+// workgroups each keep many HBM streams open (the pipeline's steps: 512
+// items of 1 MiB), capped by reserving LDS the kernel never touches
 // (160 KiB per compute unit / cap).  Measured on MI355X against uncapped
 // launches, same session:
 // - folds with all 8 or 9 sources' loads issued at once (the compile-time
-//   shapes): 16 per CU made the pipeline's reduce steps 1-2% and an 8-rank
-//   Flat fold 2% faster; folds that loop over a run-time source count issue
-//   one load at a time and need every resident workgroup (16 sources: 34%
-//   slower capped), so they stay uncapped;
-// - copies to several destinations in steps of many items (the pipeline's
-//   fan-out, 512 items of 1 MiB): 20 per CU, 6-8% faster; one large item
-//   (Flat's copy to P-1 ranks) was 5-9% slower capped and stays uncapped;
-// - the ring's 2-source reduce and 1-to-1 copy: every cap was slower.
+//   shapes): 16 per CU made the pipeline's reduce steps 1-2% faster;
+// - copies to several destinations: 20 per CU made the pipeline's fan-out
+//   steps 6-8% faster;
+// - left uncapped, where a cap lost: folds that loop over a run-time source
+//   count (one load at a time; 16 sources: 34% slower capped), Flat's
+//   single-item fold and copy (the whole 8-rank AllReduce 2% slower with the
+//   fold capped, the copy 5-9% slower), and the ring's 2-source reduce and
+//   1-to-1 copy (every cap slower).
 constexpr uint32_t kLdsPerCu = 160u * 1024u;
 constexpr uint32_t kFoldWgPerCu = 16;
 constexpr uint32_t kFanWgPerCu = 20;
-constexpr int kFanMinItems = 8;
+constexpr int kCapMinItems = 8;
 
 // ------------------------------------------------------------- kernels
 
@@ -260,10 +261,12 @@ void describe_typed(const StepLaunch& s, KernelDesc* k) {
   k->kind = KernelDesc::kVector;
   k->flags = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? kFlagXcdSplit : 0u;
   k->func = s.write_bytes > kCacheBytes ? vector_kernel<DT, OP, true>(s) : vector_kernel<DT, OP, false>(s);
-  if ((s.mode == kFold && s.nsrc == 8) || (s.mode == kRecvFold && s.nsrc == 9))
-    k->shared_bytes = kLdsPerCu / kFoldWgPerCu;
-  else if (s.mode == kCopy && s.ndst > 1 && s.nitems >= kFanMinItems)
-    k->shared_bytes = kLdsPerCu / kFanWgPerCu;
+  if (s.nitems >= kCapMinItems) {
+    if ((s.mode == kFold && s.nsrc == 8) || (s.mode == kRecvFold && s.nsrc == 9))
+      k->shared_bytes = kLdsPerCu / kFoldWgPerCu;
+    else if (s.mode == kCopy && s.ndst > 1)
+      k->shared_bytes = kLdsPerCu / kFanWgPerCu;
+  }
 }
 
 template <int DT>
