@@ -53,7 +53,7 @@ constexpr int kElemThreads = 256;   // element-wise kernel
 constexpr uint32_t kLdsPerCu = 160u * 1024u;
 constexpr uint32_t kFoldWgPerCu = 16;
 constexpr uint32_t kFanWgPerCu = 20;
-constexpr int kCapMinItems = 8;
+constexpr int kCapMinItems = 64;  // above any tree level (at most 32 parents)
 
 // ------------------------------------------------------------- kernels
 
