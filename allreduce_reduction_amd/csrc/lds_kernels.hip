@@ -230,20 +230,23 @@ plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uin
     __syncthreads();
     uint64_t dirty = 0;
     for (uint32_t j = 0; j < nk; ++j) {
+      // the record's three 16-byte words together: one LDS round trip
       const u32x4 h = *reinterpret_cast<const u32x4*>(&meta[j]);
-      const uint32_t step = uni(h.z);
-      if (step < s_lo || step >= s_hi) continue;
-      const uint32_t lo = phase + uni(h.x), hi = phase + uni(h.y), shape = uni(h.w);
       const u32x4 mv = *reinterpret_cast<const u32x4*>(&meta[j].dst_mask);
-      dirty |= uint64_t(uni(mv.x)) | (uint64_t(uni(mv.y)) << 32);
-      const uint32_t nb = uni(mv.z);
+      const u32x4 rv = *reinterpret_cast<const u32x4*>(meta[j].rank);
+      const uint32_t step = uni(h.z);
+      const uint32_t lo = phase + uni(h.x), hi = phase + uni(h.y), shape = uni(h.w);
+      const uint32_t m0 = uni(mv.x), m1 = uni(mv.y), nb = uni(mv.z);
+      const uint32_t rw[4] = {uni(rv.x), uni(rv.y), uni(rv.z), uni(rv.w)};
+      if (step < s_lo || step >= s_hi) continue;
+      dirty |= uint64_t(m0) | (uint64_t(m1) << 32);
       if (nb > 1) {
         // a batch: the same step, range and shape; its first ranks and masks
         uint32_t rank[8];
 #pragma unroll
         for (uint32_t k = 0; k < 8; ++k) {
           if (k >= nb) break;
-          rank[k] = uni(*reinterpret_cast<const uint32_t*>(meta[j + k].rank));
+          rank[k] = k == 0 ? rw[0] : uni(*reinterpret_cast<const uint32_t*>(meta[j + k].rank));
           if (k > 0) {
             const u32x4 mk = *reinterpret_cast<const u32x4*>(&meta[j + k].dst_mask);
             dirty |= uint64_t(uni(mk.x)) | (uint64_t(uni(mk.y)) << 32);
@@ -256,8 +259,6 @@ plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uin
         j += nb - 1;
         continue;
       }
-      const u32x4 rv = *reinterpret_cast<const u32x4*>(meta[j].rank);
-      const uint32_t rw[4] = {uni(rv.x), uni(rv.y), uni(rv.z), uni(rv.w)};
       const uint8_t* lr = meta[j].rank;
       const uint32_t mode = shape & 0xffu;
       const int ns = static_cast<int>((shape >> 8) & 0xffu), nd = static_cast<int>(shape >> 16);
