@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--algo", default="ring", choices=["ring", "rhd"])
     ap.add_argument("--suite", action="store_true", help="time the other workloads instead")
     ap.add_argument("--max-sweep-bytes", type=int, default=1 << 30)
+    ap.add_argument("--workloads", default="rhd_small,sweep,forms,algorithms,pipe",
+                    help="suite workloads to run (comma-separated)")
     return ap.parse_args()
 
 
@@ -138,146 +140,153 @@ def suite(a):
     def emit(**kw):
         print(json.dumps(kw), flush=True)
 
+    workloads = set(a.workloads.split(","))
+
     # calls of at most 256 MiB in all are also timed with cold caches
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     cold_limit = 256 << 20
 
-    # RHD small messages: launch-bound; report us per AllReduce and per step
-    for P in (8, 5):
-        for recipe, op in (("rhd_bf16_normal", "sum"), ("rhd_int32_uniform", "max")):
-            dtype = synth.RECIPES[recipe]["dtype"]
-            e = 2 if dtype == "bf16" else 4
-            for kib in (1, 2, 4, 8, 16, 32, 64):
-                L = kib * 1024 // e
-                bufs = upload(recipe, P, L)
-                pristine = [b.clone() for b in bufs]
-                with hc.Comm(P, "rhd") as c:
-                    n = c.plan_info("allreduce", L, dtype)["nsteps"]
-                    for b, q in zip(bufs, pristine):
-                        b.copy_(q)
-                    form = c.exec_choice("allreduce", L, dtype)
-                    t = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
-                    t_cold = time_cold(lambda: c.allreduce(bufs, dtype, op), 31, scrub)
-                    c.set_exec_mode("steps")
-                    t_steps = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
-                    c.set_exec_mode("auto")
-                    # graph mode: the same AllReduce as one graph launch, and a
-                    # graph of 10 AllReduces on these buffers (one launch)
-                    with hc.Graph() as g:
-                        g.add(c, "allreduce", bufs, dtype, op)
-                        g.build()
-                        tg = time_calls(lambda: g.launch(), 200, 20)
-                    with hc.Graph() as g10:
-                        for _ in range(10):
-                            g10.add(c, "allreduce", bufs, dtype, op)
-                        g10.build()
-                        tg10 = time_calls(lambda: g10.launch(), 50, 5) / 10
-                emit(workload="rhd_small", algo="rhd", coll="allreduce", P=P, dtype=dtype, op=op,
-                     bytes_per_rank=L * e, launch_form=form, us=round(t * 1e6, 2), cold_us=round(t_cold * 1e6, 2),
-                     steps=n,
-                     us_per_step=round(t * 1e6 / n, 2), one_launch_per_step_us=round(t_steps * 1e6, 2),
-                     one_launch_per_step_us_per_step=round(t_steps * 1e6 / n, 2),
-                     graph_us=round(tg * 1e6, 2), graph_us_per_step=round(tg * 1e6 / n, 2),
-                     graph10_us_per_allreduce=round(tg10 * 1e6, 2),
-                     busbw_GBps=round(L * e / t * 2 * (P - 1) / P / 1e9, 3),
-                     graph_busbw_GBps=round(L * e / tg * 2 * (P - 1) / P / 1e9, 3))
-
-    # P=16 fp16 sweep, ring vs RHD, AR / RS / AG
-    P = 16
-    nbytes = 4096
-    while nbytes <= a.max_sweep_bytes:
-        L = nbytes // 2
-        bufs = upload("sweep_p16_fp16", P, L)
-        pristine = [b.clone() for b in bufs]
-        for algo in ("ring", "rhd"):
-            with hc.Comm(P, algo) as c:
-                for coll in ("allreduce", "reduce_scatter", "all_gather"):
-                    for b, q in zip(bufs, pristine):
-                        b.copy_(q)
-                    info = c.plan_info(coll, L, "fp16")
-                    reps = max(3, min(200, int(2e8 // max(info["hbm_bytes"], 1))))
-                    t = time_calls(lambda: getattr(c, coll)(bufs, "fp16", "sum"), reps, 2)
-                    cold = None
-                    if P * nbytes <= cold_limit:
+    if "rhd_small" in workloads:
+        # RHD small messages: launch-bound; report us per AllReduce and per step
+        for P in (8, 5):
+            for recipe, op in (("rhd_bf16_normal", "sum"), ("rhd_int32_uniform", "max")):
+                dtype = synth.RECIPES[recipe]["dtype"]
+                e = 2 if dtype == "bf16" else 4
+                for kib in (1, 2, 4, 8, 16, 32, 64):
+                    L = kib * 1024 // e
+                    bufs = upload(recipe, P, L)
+                    pristine = [b.clone() for b in bufs]
+                    with hc.Comm(P, "rhd") as c:
+                        n = c.plan_info("allreduce", L, dtype)["nsteps"]
                         for b, q in zip(bufs, pristine):
                             b.copy_(q)
-                        cold = round(time_cold(lambda: getattr(c, coll)(bufs, "fp16", "sum"), 15, scrub) * 1e6, 2)
-                    factor = 2 * (P - 1) / P if coll == "allreduce" else (P - 1) / P
-                    emit(workload="sweep_p16_fp16", algo=algo, coll=coll, P=P, bytes_per_rank=nbytes,
-                         launch_form=c.exec_choice(coll, L, "fp16"), us=round(t * 1e6, 2), cold_us=cold,
-                         steps=info["nsteps"],
-                         busbw_GBps=round(nbytes / t * factor / 1e9, 3),
-                         pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2))
-        del bufs, pristine
-        torch.cuda.empty_cache()
-        nbytes *= 4
+                        form = c.exec_choice("allreduce", L, dtype)
+                        t = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
+                        t_cold = time_cold(lambda: c.allreduce(bufs, dtype, op), 31, scrub)
+                        c.set_exec_mode("steps")
+                        t_steps = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
+                        c.set_exec_mode("auto")
+                        # graph mode: the same AllReduce as one graph launch, and a
+                        # graph of 10 AllReduces on these buffers (one launch)
+                        with hc.Graph() as g:
+                            g.add(c, "allreduce", bufs, dtype, op)
+                            g.build()
+                            tg = time_calls(lambda: g.launch(), 200, 20)
+                        with hc.Graph() as g10:
+                            for _ in range(10):
+                                g10.add(c, "allreduce", bufs, dtype, op)
+                            g10.build()
+                            tg10 = time_calls(lambda: g10.launch(), 50, 5) / 10
+                    emit(workload="rhd_small", algo="rhd", coll="allreduce", P=P, dtype=dtype, op=op,
+                         bytes_per_rank=L * e, launch_form=form, us=round(t * 1e6, 2), cold_us=round(t_cold * 1e6, 2),
+                         steps=n,
+                         us_per_step=round(t * 1e6 / n, 2), one_launch_per_step_us=round(t_steps * 1e6, 2),
+                         one_launch_per_step_us_per_step=round(t_steps * 1e6 / n, 2),
+                         graph_us=round(tg * 1e6, 2), graph_us_per_step=round(tg * 1e6 / n, 2),
+                         graph10_us_per_allreduce=round(tg10 * 1e6, 2),
+                         busbw_GBps=round(L * e / t * 2 * (P - 1) / P / 1e9, 3),
+                         graph_busbw_GBps=round(L * e / tg * 2 * (P - 1) / P / 1e9, 3))
 
-    # launch forms across sizes: one launch per step, the single-workgroup
-    # kernel, the column kernel, and the form the communicator picks
-    for P in (8, 16):
-        for algo in ("ring", "rhd"):
-            kib = 1
-            while kib <= min(16384, a.max_sweep_bytes >> 10):
-                L = kib * 512
-                bufs = upload("sweep_p16_fp16", P, L)
-                row = {}
-                with hc.Comm(P, algo) as c:
-                    info = c.plan_info("allreduce", L, "fp16")
-                    reps = max(5, min(200, int(1e8 // info["hbm_bytes"])))
-                    auto_form = c.exec_choice("allreduce", L, "fp16")
-                    for form in ("steps", "fused", "columns", "lds", "auto"):
-                        c.set_exec_mode(form)
-                        if form != "auto" and c.exec_choice("allreduce", L, "fp16") != form:
-                            continue
-                        if form == "fused" and kib > 64:
-                            continue  # one compute unit: far slower, skip the long runs
-                        row[form] = round(time_calls(lambda: c.allreduce(bufs, "fp16", "max"), reps, 3) * 1e6, 2)
-                    if P * (kib << 10) <= cold_limit:
-                        row["auto_cold"] = round(time_cold(lambda: c.allreduce(bufs, "fp16", "max"), 15, scrub) * 1e6, 2)
-                emit(workload="launch_forms", algo=algo, P=P, dtype="fp16", op="max", bytes_per_rank=kib << 10,
-                     hbm_bytes=info["hbm_bytes"], steps=info["nsteps"], auto_form=auto_form, us=row)
-                del bufs
-                kib *= 4
-
-    # AllReduce algorithms side by side, and the AUTO communicator's choice
-    for P in (8, 16):
+    if "sweep" in workloads:
+        # P=16 fp16 sweep, ring vs RHD, AR / RS / AG
+        P = 16
         nbytes = 4096
-        while nbytes <= min(a.max_sweep_bytes, 256 << 20):
+        while nbytes <= a.max_sweep_bytes:
             L = nbytes // 2
             bufs = upload("sweep_p16_fp16", P, L)
             pristine = [b.clone() for b in bufs]
-            row = {}
-            for algo, args in (("ring", (P, "ring")), ("rhd", (P, "rhd")), ("flat", (P, "flat")),
-                               ("tree", (P, "tree", 0, 2)), ("auto", (P, "auto"))):
-                with hc.Comm(*args) as c:
-                    for b, q in zip(bufs, pristine):
-                        b.copy_(q)
-                    info = c.plan_info("allreduce", L, "fp16")
-                    reps = max(3, min(200, int(2e8 // max(info["hbm_bytes"], 1))))
-                    row[algo] = round(time_calls(lambda: c.allreduce(bufs, "fp16", "sum"), reps, 2) * 1e6, 2)
-                    if algo == "auto":
-                        row["auto_choice"] = c.auto_choice("allreduce", L, "fp16")
-            emit(workload="allreduce_algorithms", P=P, dtype="fp16", bytes_per_rank=nbytes, us=row)
+            for algo in ("ring", "rhd"):
+                with hc.Comm(P, algo) as c:
+                    for coll in ("allreduce", "reduce_scatter", "all_gather"):
+                        for b, q in zip(bufs, pristine):
+                            b.copy_(q)
+                        info = c.plan_info(coll, L, "fp16")
+                        reps = max(3, min(200, int(2e8 // max(info["hbm_bytes"], 1))))
+                        t = time_calls(lambda: getattr(c, coll)(bufs, "fp16", "sum"), reps, 2)
+                        cold = None
+                        if P * nbytes <= cold_limit:
+                            for b, q in zip(bufs, pristine):
+                                b.copy_(q)
+                            cold = round(time_cold(lambda: getattr(c, coll)(bufs, "fp16", "sum"), 15, scrub) * 1e6, 2)
+                        factor = 2 * (P - 1) / P if coll == "allreduce" else (P - 1) / P
+                        emit(workload="sweep_p16_fp16", algo=algo, coll=coll, P=P, bytes_per_rank=nbytes,
+                             launch_form=c.exec_choice(coll, L, "fp16"), us=round(t * 1e6, 2), cold_us=cold,
+                             steps=info["nsteps"],
+                             busbw_GBps=round(nbytes / t * factor / 1e9, 3),
+                             pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2))
             del bufs, pristine
             torch.cuda.empty_cache()
-            nbytes *= 16
+            nbytes *= 4
 
-    # pipeline 4 x 8, bf16, 512 MiB per rank, 32 MiB loops
-    S, M = 4, 8
-    P, L = S * M, 256 << 20
-    bufs = upload("pipe_4x8_bf16", P, L)
-    with hc.Comm(P, "pipeline", S, M, 32 << 20) as c:
-        info = c.plan_info("allreduce", L, "bf16")
-        t = time_calls(lambda: c.allreduce(bufs, "bf16", "sum"), 3, 1)
-        steps = []
-        for s in range(info["nsteps"]):
-            si = c.step_info("allreduce", L, "bf16", s)
-            ts = time_calls(lambda: c.run_steps("allreduce", bufs, s, s + 1, "bf16", "sum"), 3, 1)
-            steps.append(dict(step=s, us=round(ts * 1e6, 1), GBps=round(si["hbm_bytes"] / ts / 1e9, 1)))
-    emit(workload="pipe_4x8_bf16", algo="pipeline", coll="allreduce", P=P, S=S, M=M,
-         bytes_per_rank=L * 2, us=round(t * 1e6, 1), steps=info["nsteps"],
-         busbw_GBps=round(L * 2 / t * 2 * (P - 1) / P / 1e9, 3),
-         pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2), per_step=steps)
+    if "forms" in workloads:
+        # launch forms across sizes: one launch per step, the single-workgroup
+        # kernel, the column kernel, and the form the communicator picks
+        for P in (8, 16):
+            for algo in ("ring", "rhd"):
+                kib = 1
+                while kib <= min(16384, a.max_sweep_bytes >> 10):
+                    L = kib * 512
+                    bufs = upload("sweep_p16_fp16", P, L)
+                    row = {}
+                    with hc.Comm(P, algo) as c:
+                        info = c.plan_info("allreduce", L, "fp16")
+                        reps = max(5, min(200, int(1e8 // info["hbm_bytes"])))
+                        auto_form = c.exec_choice("allreduce", L, "fp16")
+                        for form in ("steps", "fused", "columns", "lds", "auto"):
+                            c.set_exec_mode(form)
+                            if form != "auto" and c.exec_choice("allreduce", L, "fp16") != form:
+                                continue
+                            if form == "fused" and kib > 64:
+                                continue  # one compute unit: far slower, skip the long runs
+                            row[form] = round(time_calls(lambda: c.allreduce(bufs, "fp16", "max"), reps, 3) * 1e6, 2)
+                        if P * (kib << 10) <= cold_limit:
+                            row["auto_cold"] = round(time_cold(lambda: c.allreduce(bufs, "fp16", "max"), 15, scrub) * 1e6, 2)
+                    emit(workload="launch_forms", algo=algo, P=P, dtype="fp16", op="max", bytes_per_rank=kib << 10,
+                         hbm_bytes=info["hbm_bytes"], steps=info["nsteps"], auto_form=auto_form, us=row)
+                    del bufs
+                    kib *= 4
+
+    if "algorithms" in workloads:
+        # AllReduce algorithms side by side, and the AUTO communicator's choice
+        for P in (8, 16):
+            nbytes = 4096
+            while nbytes <= min(a.max_sweep_bytes, 256 << 20):
+                L = nbytes // 2
+                bufs = upload("sweep_p16_fp16", P, L)
+                pristine = [b.clone() for b in bufs]
+                row = {}
+                for algo, args in (("ring", (P, "ring")), ("rhd", (P, "rhd")), ("flat", (P, "flat")),
+                                   ("tree", (P, "tree", 0, 2)), ("auto", (P, "auto"))):
+                    with hc.Comm(*args) as c:
+                        for b, q in zip(bufs, pristine):
+                            b.copy_(q)
+                        info = c.plan_info("allreduce", L, "fp16")
+                        reps = max(3, min(200, int(2e8 // max(info["hbm_bytes"], 1))))
+                        row[algo] = round(time_calls(lambda: c.allreduce(bufs, "fp16", "sum"), reps, 2) * 1e6, 2)
+                        if algo == "auto":
+                            row["auto_choice"] = c.auto_choice("allreduce", L, "fp16")
+                emit(workload="allreduce_algorithms", P=P, dtype="fp16", bytes_per_rank=nbytes, us=row)
+                del bufs, pristine
+                torch.cuda.empty_cache()
+                nbytes *= 16
+
+    if "pipe" in workloads:
+        # pipeline 4 x 8, bf16, 512 MiB per rank, 32 MiB loops
+        S, M = 4, 8
+        P, L = S * M, 256 << 20
+        bufs = upload("pipe_4x8_bf16", P, L)
+        with hc.Comm(P, "pipeline", S, M, 32 << 20) as c:
+            info = c.plan_info("allreduce", L, "bf16")
+            t = time_calls(lambda: c.allreduce(bufs, "bf16", "sum"), 3, 1)
+            steps = []
+            for s in range(info["nsteps"]):
+                si = c.step_info("allreduce", L, "bf16", s)
+                ts = time_calls(lambda: c.run_steps("allreduce", bufs, s, s + 1, "bf16", "sum"), 3, 1)
+                steps.append(dict(step=s, us=round(ts * 1e6, 1), GBps=round(si["hbm_bytes"] / ts / 1e9, 1)))
+        emit(workload="pipe_4x8_bf16", algo="pipeline", coll="allreduce", P=P, S=S, M=M,
+             bytes_per_rank=L * 2, us=round(t * 1e6, 1), steps=info["nsteps"],
+             busbw_GBps=round(L * 2 / t * 2 * (P - 1) / P / 1e9, 3),
+             pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2), per_step=steps)
 
 
 def main():
