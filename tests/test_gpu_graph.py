@@ -49,6 +49,39 @@ def test_graph_single_allreduce_replays(algo, P):
                     refops.assert_same(dtype, to_host(bufs[r], dtype), want[r], f"replay {rep} rank {r}")
 
 
+def test_graph_pipeline_many_items():
+    """A 4 x 8 pipeline with 8 KiB loops, one launch per step: over 1000 items per
+    step, so the fold and fan-out launches reserve LDS to cap the workgroups a
+    compute unit holds; as graph nodes they replay bit for bit like the eager
+    calls, which match the oracle."""
+    import oracle
+    S, M, loop = 4, 8, 8192
+    P, L, dtype = S * M, 128 * 1024 + 5, "bf16"
+    xs = inputs(P, L, dtype, seed=7)
+    with hc.Comm(P, "pipeline", S, M, loop) as comm:
+        comm.set_exec_mode("steps")
+        assert comm.step_info("allreduce", L, dtype, 0)["nitems"] >= 64
+        ref = [to_dev(x, dtype) for x in xs]
+        eager([(comm, "allreduce", ref)], dtype)
+        want = [to_host(t, dtype) for t in ref]
+        expect = [x.copy() for x in xs]
+        oracle.run("allreduce", "pipeline", expect, dtype, "sum", S=S, M=M, loop_bytes=loop)
+        for r in range(P):
+            refops.assert_same(dtype, want[r], expect[r], f"eager rank {r}")
+        bufs = [to_dev(x, dtype) for x in xs]
+        with hc.Graph() as g:
+            g.add(comm, "allreduce", bufs, dtype, "sum")
+            g.build()
+            for rep in range(3):
+                for b, x in zip(bufs, xs):
+                    b.copy_(to_dev(x, dtype))
+                torch.cuda.synchronize()
+                g.launch()
+                torch.cuda.synchronize()
+                for r in range(P):
+                    refops.assert_same(dtype, to_host(bufs[r], dtype), want[r], f"replay {rep} rank {r}")
+
+
 def test_graph_independent_and_dependent_nodes():
     """Two AllReduces on disjoint buffer sets (may overlap in time), then a
     reduce-scatter + all-gather on the first set (depends on the first node)."""
