@@ -23,6 +23,13 @@
 // LDS layout (dynamic): nranks slots of slot_bytes (element col_begin + i of
 // rank r at slot r + phase + i*E, so LDS and global 16-byte phases agree),
 // then one DevColChunk record per entry of the column's chunk list.
+//
+// A chunk's cost is a short dependent chain (record words, then its data,
+// then the op and the store), so the loop is kept lean: ONE marks launches
+// in which every lane owns at most one position (lane t takes position t,
+// no position loop), and the two single-chunk shapes the schedules mostly
+// use, a two-source reduce and a one-to-one copy, are tested right after
+// the batches and run without the generic shape dispatch.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -89,19 +96,24 @@ __device__ __forceinline__ void pos_elems(unsigned char* lds, uint32_t slot_byte
 }
 
 // This lane's positions of one chunk covering slot bytes [lo, hi).
-template <int DT, int OP, int MODE, int NS, int ND>
+template <int DT, int OP, int MODE, int NS, int ND, bool ONE>
 __device__ __forceinline__ void lds_chunk(unsigned char* lds, uint32_t slot_bytes, uint32_t lo, uint32_t hi,
                                           int ns_rt, int nd_rt, const uint32_t* rw, const uint8_t* lr) {
   const int ns = NS > 0 ? NS : ns_rt;
   const int nd = ND > 0 ? ND : nd_rt;
-  const uint32_t nthr = blockDim.x;  // a power of two
   const uint32_t p_lo = lo >> 4, p_hi = (hi + 15) >> 4;
-  // first position >= p_lo owned by this lane
-  uint32_t p = p_lo + ((threadIdx.x - p_lo) & (nthr - 1));
-  for (; p < p_hi; p += nthr) {
+  auto one = [&](uint32_t p) {
     const uint32_t a = p * 16, b = a + 16;
     if (a >= lo && b <= hi) pos_vec<DT, OP, MODE, NS, ND>(lds, slot_bytes, a, ns, nd, rw, lr);
     else pos_elems<DT, OP, MODE, NS, ND>(lds, slot_bytes, a > lo ? a : lo, b < hi ? b : hi, ns, nd, rw, lr);
+  };
+  if constexpr (ONE) {
+    // lane t owns position t only
+    if (threadIdx.x >= p_lo && threadIdx.x < p_hi) one(threadIdx.x);
+  } else {
+    const uint32_t nthr = blockDim.x;  // a power of two
+    // first position >= p_lo owned by this lane
+    for (uint32_t p = p_lo + ((threadIdx.x - p_lo) & (nthr - 1)); p < p_hi; p += nthr) one(p);
   }
 }
 
@@ -206,7 +218,7 @@ __device__ __forceinline__ void move_positions(unsigned char* lds, uint32_t slot
 // Workgroup w runs columns w, w + gridDim.x, ...; of each column only the
 // chunks of steps [s_lo, s_hi).  Chunk headers are read into scalar
 // registers, so every branch on them is uniform.
-template <int DT, int OP>
+template <int DT, int OP, bool ONE>
 __global__ void __launch_bounds__(kLdsMaxThreads)
 plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uint32_t* __restrict__ col_off,
                  uint32_t ncols, uint32_t s_lo, uint32_t s_hi, uint32_t phase, uint64_t col_elems, uint64_t count,
@@ -259,17 +271,26 @@ plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uin
         j += nb - 1;
         continue;
       }
+      // the common single chunks: a two-source reduce, a one-to-one copy
+      if (shape == (kRecvFold | 2u << 8 | 1u << 16)) {
+        lds_chunk<DT, OP, kRecvFold, 2, 1, ONE>(lds, slot_bytes, lo, hi, 2, 1, rw, meta[j].rank);
+        continue;
+      }
+      if (shape == (kCopy | 1u << 8 | 1u << 16)) {
+        lds_chunk<DT, kSum, kCopy, 1, 1, ONE>(lds, slot_bytes, lo, hi, 1, 1, rw, meta[j].rank);
+        continue;
+      }
       const uint8_t* lr = meta[j].rank;
       const uint32_t mode = shape & 0xffu;
       const int ns = static_cast<int>((shape >> 8) & 0xffu), nd = static_cast<int>(shape >> 16);
       if (mode == kRecvFold) {
-        if (ns == 2 && nd == 1) lds_chunk<DT, OP, kRecvFold, 2, 1>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
-        else lds_chunk<DT, OP, kRecvFold, 0, 0>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
+        if (ns == 2 && nd == 1) lds_chunk<DT, OP, kRecvFold, 2, 1, ONE>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
+        else lds_chunk<DT, OP, kRecvFold, 0, 0, ONE>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
       } else if (mode == kFold) {
-        lds_chunk<DT, OP, kFold, 0, 0>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
+        lds_chunk<DT, OP, kFold, 0, 0, ONE>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
       } else {
-        if (ns == 1 && nd == 1) lds_chunk<DT, kSum, kCopy, 1, 1>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
-        else lds_chunk<DT, kSum, kCopy, 0, 0>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
+        if (ns == 1 && nd == 1) lds_chunk<DT, kSum, kCopy, 1, 1, ONE>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
+        else lds_chunk<DT, kSum, kCopy, 0, 0, ONE>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
       }
     }
     move_positions<DT, false>(lds, slot_bytes, ptrs, col_begin * E, dirty, nranks, phase, n);
@@ -277,14 +298,19 @@ plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uin
   }
 }
 
-template <int DT>
+template <int DT, bool ONE>
 const void* lds_fn(int op) {
   switch (op) {
-    case kSum: return reinterpret_cast<const void*>(plan_columns_lds<DT, kSum>);
-    case kProd: return reinterpret_cast<const void*>(plan_columns_lds<DT, kProd>);
-    case kMax: return reinterpret_cast<const void*>(plan_columns_lds<DT, kMax>);
-    default: return reinterpret_cast<const void*>(plan_columns_lds<DT, kMin>);
+    case kSum: return reinterpret_cast<const void*>(plan_columns_lds<DT, kSum, ONE>);
+    case kProd: return reinterpret_cast<const void*>(plan_columns_lds<DT, kProd, ONE>);
+    case kMax: return reinterpret_cast<const void*>(plan_columns_lds<DT, kMax, ONE>);
+    default: return reinterpret_cast<const void*>(plan_columns_lds<DT, kMin, ONE>);
   }
+}
+
+template <int DT>
+const void* lds_fn(int op, bool one) {
+  return one ? lds_fn<DT, true>(op) : lds_fn<DT, false>(op);
 }
 
 }  // namespace
@@ -310,12 +336,14 @@ void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColC
                           uint64_t count, uint32_t nranks, uint64_t max_chunks_per_col, uint32_t grid,
                           KernelDesc* k) {
   const uint32_t e = dtype == kF32 || dtype == kI32 ? 4 : (dtype == kI8 ? 1 : 2);
+  // every lane owns at most one 16-byte position of the column
+  const bool one = (phase + col_elems * e + 15) / 16 <= lds_threads(col_elems, e);
   switch (dtype) {
-    case kF32: k->func = lds_fn<kF32>(op); break;
-    case kF16: k->func = lds_fn<kF16>(op); break;
-    case kBF16: k->func = lds_fn<kBF16>(op); break;
-    case kI32: k->func = lds_fn<kI32>(op); break;
-    default: k->func = lds_fn<kI8>(op); break;
+    case kF32: k->func = lds_fn<kF32>(op, one); break;
+    case kF16: k->func = lds_fn<kF16>(op, one); break;
+    case kBF16: k->func = lds_fn<kBF16>(op, one); break;
+    case kI32: k->func = lds_fn<kI32>(op, one); break;
+    default: k->func = lds_fn<kI8>(op, one); break;
   }
   k->kind = KernelDesc::kColumnsLds;
   k->grid = dim3(grid);
