@@ -180,6 +180,16 @@ def test_parity_many_ranks(algo, exec_mode):
                        exec_mode=exec_mode)
 
 
+def test_parity_items_past_grid_y():
+    """A step of more than 65536 items (the pipeline with 1 KiB loops): the
+    step kernels take the item from grid.y, past the device's reported
+    maxGridSize[1] of 65536, which the runtime launches in full."""
+    P, L = 32, (1 << 20) + 3
+    with hc.Comm(P, "pipeline", 4, 8, 1024) as comm:
+        assert comm.step_info("allreduce", L, "bf16", 0)["nitems"] > 65536
+    check_case("pipeline", "allreduce", "bf16", "sum", P, L, seed=11, loop_bytes=1024, exec_mode="steps")
+
+
 @pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
 def test_parity_small_and_empty_segments(algo):
     for P in (3, 5, 8, 16):
