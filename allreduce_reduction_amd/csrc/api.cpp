@@ -5,6 +5,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <new>
 #include <string>
 
@@ -12,12 +13,11 @@
 
 using namespace hbmc;
 
-extern "C" {
+namespace {
 
-hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_per_server,
-                               size_t loop_bytes, hbmc_comm_t* out) {
-  if (!out) return HBMC_ERR_INVALID_ARG;
-  *out = nullptr;
+// Body of hbmc_comm_create (out is non-null and cleared).
+hbmc_status_t comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_per_server, size_t loop_bytes,
+                          hbmc_comm_t* out) {
   if (nranks < 1 || nranks > kMaxRanks) return HBMC_ERR_INVALID_ARG;
   int a = algo;
   if (a == HBMC_ALGO_ENV) {
@@ -48,7 +48,7 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
     case HBMC_ALGO_PIPELINE:
     case HBMC_ALGO_HIER:
       t.algo = a == HBMC_ALGO_PIPELINE ? kPipeline : kHier;
-      if (servers < 1 || ranks_per_server < 1 || servers * ranks_per_server != nranks)
+      if (servers < 1 || ranks_per_server < 1 || int64_t(servers) * ranks_per_server != nranks)
         return HBMC_ERR_INVALID_ARG;
       t.S = servers;
       t.M = ranks_per_server;
@@ -63,7 +63,7 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
         topos.push_back(c);
       }
       if (servers > 0 || ranks_per_server > 0) {
-        if (servers < 1 || ranks_per_server < 1 || servers * ranks_per_server != nranks)
+        if (servers < 1 || ranks_per_server < 1 || int64_t(servers) * ranks_per_server != nranks)
           return HBMC_ERR_INVALID_ARG;
         for (Algo al : {kPipeline, kHier}) {
           Topology c = t;
@@ -79,7 +79,7 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
     default: return HBMC_ERR_INVALID_ARG;
   }
   if (topos.empty()) topos.push_back(t);
-  hbmc_comm* c = new (std::nothrow) hbmc_comm;
+  std::unique_ptr<hbmc_comm> c(new (std::nothrow) hbmc_comm);
   if (!c) return HBMC_ERR_NOMEM;
   c->topos = topos;
   c->auto_select = a == HBMC_ALGO_AUTO;
@@ -95,8 +95,19 @@ hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ra
   }
   const char* xs = std::getenv("HBMC_XCD_SPLIT");
   c->xcd_split = xs && xs[0] == '1';
-  *out = c;
+  *out = c.release();
   return HBMC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hbmc_status_t hbmc_comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_per_server,
+                               size_t loop_bytes, hbmc_comm_t* out) {
+  if (!out) return HBMC_ERR_INVALID_ARG;
+  *out = nullptr;
+  return no_throw([&] { return comm_create(nranks, algo, servers, ranks_per_server, loop_bytes, out); });
 }
 
 hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes) {
@@ -121,20 +132,22 @@ hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode) {
 
 hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
                                int first_step, int last_step, hbmc_exec_t* mode) {
-  if (!mode) return HBMC_ERR_INVALID_ARG;
-  Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
-  if (st != HBMC_OK) return st;
-  const int nsteps = static_cast<int>(p->sched.steps.size());
-  if (first_step == 0 && last_step == 0) last_step = nsteps;
-  if (first_step < 0 || last_step > nsteps || first_step > last_step) return HBMC_ERR_INVALID_ARG;
-  *mode = HBMC_EXEC_STEPS;
-  if (count == 0 || comm->topos[0].P == 1 || first_step == last_step) return HBMC_OK;
-  int m = kExecSteps;
-  st = choose_exec(comm, p, first_step, last_step, count, elem_bytes(dtype), true, &m);
-  if (st != HBMC_OK) return st;
-  *mode = static_cast<hbmc_exec_t>(m);
-  return HBMC_OK;
+  return no_throw([&]() -> hbmc_status_t {
+    if (!mode) return HBMC_ERR_INVALID_ARG;
+    Plan* p = nullptr;
+    hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+    if (st != HBMC_OK) return st;
+    const int nsteps = static_cast<int>(p->sched.steps.size());
+    if (first_step == 0 && last_step == 0) last_step = nsteps;
+    if (first_step < 0 || last_step > nsteps || first_step > last_step) return HBMC_ERR_INVALID_ARG;
+    *mode = HBMC_EXEC_STEPS;
+    if (count == 0 || comm->topos[0].P == 1 || first_step == last_step) return HBMC_OK;
+    int m = kExecSteps;
+    st = choose_exec(comm, p, first_step, last_step, count, elem_bytes(dtype), true, &m);
+    if (st != HBMC_OK) return st;
+    *mode = static_cast<hbmc_exec_t>(m);
+    return HBMC_OK;
+  });
 }
 
 hbmc_status_t hbmc_comm_set_cost_model(hbmc_comm_t comm, double alpha_us, double beta_gbps) {
@@ -147,19 +160,21 @@ hbmc_status_t hbmc_comm_set_cost_model(hbmc_comm_t comm, double alpha_us, double
 
 hbmc_status_t hbmc_auto_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                                hbmc_dtype_t dtype, hbmc_algo_t* algo) {
-  if (!algo) return HBMC_ERR_INVALID_ARG;
-  int ti = 0;
-  hbmc_status_t st = choose_topology(comm, coll, root, count, dtype, &ti);
-  if (st != HBMC_OK) return st;
-  switch (comm->topos[ti].algo) {
-    case kRing: *algo = HBMC_ALGO_RING; break;
-    case kRhd: *algo = HBMC_ALGO_RHD; break;
-    case kPipeline: *algo = HBMC_ALGO_PIPELINE; break;
-    case kFlat: *algo = HBMC_ALGO_FLAT; break;
-    case kTree: *algo = HBMC_ALGO_TREE; break;
-    default: *algo = HBMC_ALGO_HIER; break;
-  }
-  return HBMC_OK;
+  return no_throw([&]() -> hbmc_status_t {
+    if (!algo) return HBMC_ERR_INVALID_ARG;
+    int ti = 0;
+    hbmc_status_t st = choose_topology(comm, coll, root, count, dtype, &ti);
+    if (st != HBMC_OK) return st;
+    switch (comm->topos[ti].algo) {
+      case kRing: *algo = HBMC_ALGO_RING; break;
+      case kRhd: *algo = HBMC_ALGO_RHD; break;
+      case kPipeline: *algo = HBMC_ALGO_PIPELINE; break;
+      case kFlat: *algo = HBMC_ALGO_FLAT; break;
+      case kTree: *algo = HBMC_ALGO_TREE; break;
+      default: *algo = HBMC_ALGO_HIER; break;
+    }
+    return HBMC_OK;
+  });
 }
 
 hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
@@ -176,109 +191,117 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
 
 hbmc_status_t hbmc_allreduce(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
                              hbmc_op_t op, void* stream) {
-  return run(comm, HBMC_COLL_ALLREDUCE, 0, bufs, count, dtype, op, 0, 0, true, stream);
+  return no_throw([&] { return run(comm, HBMC_COLL_ALLREDUCE, 0, bufs, count, dtype, op, 0, 0, true, stream); });
 }
 
 hbmc_status_t hbmc_reduce_scatter(hbmc_comm_t comm, void* const bufs[], size_t count,
                                   hbmc_dtype_t dtype, hbmc_op_t op, void* stream) {
-  return run(comm, HBMC_COLL_REDUCE_SCATTER, 0, bufs, count, dtype, op, 0, 0, true, stream);
+  return no_throw([&] { return run(comm, HBMC_COLL_REDUCE_SCATTER, 0, bufs, count, dtype, op, 0, 0, true, stream); });
 }
 
 hbmc_status_t hbmc_all_gather(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
                               hbmc_op_t op, void* stream) {
-  return run(comm, HBMC_COLL_ALL_GATHER, 0, bufs, count, dtype, op, 0, 0, true, stream);
+  return no_throw([&] { return run(comm, HBMC_COLL_ALL_GATHER, 0, bufs, count, dtype, op, 0, 0, true, stream); });
 }
 
 hbmc_status_t hbmc_reduce(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
                           hbmc_op_t op, int root, void* stream) {
-  return run(comm, HBMC_COLL_REDUCE, root, bufs, count, dtype, op, 0, 0, true, stream);
+  return no_throw([&] { return run(comm, HBMC_COLL_REDUCE, root, bufs, count, dtype, op, 0, 0, true, stream); });
 }
 
 hbmc_status_t hbmc_broadcast(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
                              int root, void* stream) {
-  return run(comm, HBMC_COLL_BROADCAST, root, bufs, count, dtype, HBMC_SUM, 0, 0, true, stream);
+  return no_throw([&] { return run(comm, HBMC_COLL_BROADCAST, root, bufs, count, dtype, HBMC_SUM, 0, 0, true, stream); });
 }
 
 hbmc_status_t hbmc_collective_oop(hbmc_comm_t comm, hbmc_coll_t coll, int root, const void* const send[],
                                   void* const recv[], size_t count, hbmc_dtype_t dtype, hbmc_op_t op,
                                   void* stream) {
-  return run_out_of_place(comm, coll, root, send, recv, count, dtype, op, stream);
+  return no_throw([&] { return run_out_of_place(comm, coll, root, send, recv, count, dtype, op, stream); });
 }
 
 hbmc_status_t hbmc_run_steps(hbmc_comm_t comm, hbmc_coll_t coll, int root, void* const bufs[],
                              size_t count, hbmc_dtype_t dtype, hbmc_op_t op, int first_step,
                              int last_step, void* stream) {
-  return run(comm, coll, root, bufs, count, dtype, op, first_step, last_step, false, stream);
+  return no_throw([&] { return run(comm, coll, root, bufs, count, dtype, op, first_step, last_step, false, stream); });
 }
 
 hbmc_status_t hbmc_plan_info(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                              hbmc_dtype_t dtype, int* nsteps, uint64_t* hbm_bytes,
                              uint64_t* max_recv_bytes) {
-  Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
-  if (st != HBMC_OK) return st;
-  if (nsteps) *nsteps = static_cast<int>(p->sched.steps.size());
-  if (hbm_bytes) *hbm_bytes = p->sched.hbm_bytes;
-  if (max_recv_bytes) *max_recv_bytes = p->sched.max_recv_bytes;
-  return HBMC_OK;
+  return no_throw([&]() -> hbmc_status_t {
+    Plan* p = nullptr;
+    hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+    if (st != HBMC_OK) return st;
+    if (nsteps) *nsteps = static_cast<int>(p->sched.steps.size());
+    if (hbm_bytes) *hbm_bytes = p->sched.hbm_bytes;
+    if (max_recv_bytes) *max_recv_bytes = p->sched.max_recv_bytes;
+    return HBMC_OK;
+  });
 }
 
 hbmc_status_t hbmc_plan_step_info(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                                   hbmc_dtype_t dtype, int step, int* nitems, uint64_t* hbm_bytes) {
-  Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
-  if (st != HBMC_OK) return st;
-  if (step < 0 || step >= static_cast<int>(p->sched.steps.size())) return HBMC_ERR_INVALID_ARG;
-  const Step& s = p->sched.steps[step];
-  if (nitems) *nitems = static_cast<int>(s.items.size());
-  if (hbm_bytes) *hbm_bytes = s.hbm_bytes;
-  return HBMC_OK;
+  return no_throw([&]() -> hbmc_status_t {
+    Plan* p = nullptr;
+    hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+    if (st != HBMC_OK) return st;
+    if (step < 0 || step >= static_cast<int>(p->sched.steps.size())) return HBMC_ERR_INVALID_ARG;
+    const Step& s = p->sched.steps[step];
+    if (nitems) *nitems = static_cast<int>(s.items.size());
+    if (hbm_bytes) *hbm_bytes = s.hbm_bytes;
+    return HBMC_OK;
+  });
 }
 
 hbmc_status_t hbmc_plan_items(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                               hbmc_dtype_t dtype, hbmc_item_t* out, size_t cap, size_t* n_items) {
-  Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
-  if (st != HBMC_OK) return st;
-  size_t k = 0;
-  for (size_t s = 0; s < p->sched.steps.size(); ++s) {
-    const Step& step = p->sched.steps[s];
-    for (const Item& it : step.items) {
-      if (out && k < cap) {
-        hbmc_item_t& o = out[k];
-        o.step = static_cast<int32_t>(s);
-        o.mode = step.mode;
-        o.nsrc = it.nsrc;
-        o.ndst = it.ndst;
-        o.begin = it.begin;
-        o.count = it.count;
-        std::memcpy(o.rank, it.rank, sizeof(o.rank));
+  return no_throw([&]() -> hbmc_status_t {
+    Plan* p = nullptr;
+    hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+    if (st != HBMC_OK) return st;
+    size_t k = 0;
+    for (size_t s = 0; s < p->sched.steps.size(); ++s) {
+      const Step& step = p->sched.steps[s];
+      for (const Item& it : step.items) {
+        if (out && k < cap) {
+          hbmc_item_t& o = out[k];
+          o.step = static_cast<int32_t>(s);
+          o.mode = step.mode;
+          o.nsrc = it.nsrc;
+          o.ndst = it.ndst;
+          o.begin = it.begin;
+          o.count = it.count;
+          std::memcpy(o.rank, it.rank, sizeof(o.rank));
+        }
+        ++k;
       }
-      ++k;
     }
-  }
-  if (n_items) *n_items = k;
-  return HBMC_OK;
+    if (n_items) *n_items = k;
+    return HBMC_OK;
+  });
 }
 
 hbmc_status_t hbmc_plan_chunks(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                                hbmc_dtype_t dtype, uint64_t chunk_bytes, hbmc_chunk_t* chunks, size_t cap,
                                size_t* n_chunks, uint32_t* deps, size_t dcap, size_t* n_deps) {
-  if (chunk_bytes < 16 || chunk_bytes > (uint64_t(1) << 31)) return HBMC_ERR_INVALID_ARG;
-  Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
-  if (st != HBMC_OK) return st;
-  ColumnTable f;
-  if (!build_columns(p->sched, comm->topos[0].P, column_elems(chunk_bytes, count, elem_bytes(dtype), 1), true, &f))
-    return HBMC_ERR_INVALID_ARG;
-  for (size_t i = 0; chunks && i < f.chunks.size() && i < cap; ++i) {
-    const ColumnChunk& c = f.chunks[i];
-    chunks[i] = hbmc_chunk_t{c.begin, c.count, c.item, c.step, c.dep_lo, c.dep_hi, 0};
-  }
-  for (size_t i = 0; deps && i < f.deps.size() && i < dcap; ++i) deps[i] = f.deps[i];
-  if (n_chunks) *n_chunks = f.chunks.size();
-  if (n_deps) *n_deps = f.deps.size();
-  return HBMC_OK;
+  return no_throw([&]() -> hbmc_status_t {
+    if (chunk_bytes < 16 || chunk_bytes > (uint64_t(1) << 31)) return HBMC_ERR_INVALID_ARG;
+    Plan* p = nullptr;
+    hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+    if (st != HBMC_OK) return st;
+    ColumnTable f;
+    if (!build_columns(p->sched, comm->topos[0].P, column_elems(chunk_bytes, count, elem_bytes(dtype), 1), true, &f))
+      return HBMC_ERR_INVALID_ARG;
+    for (size_t i = 0; chunks && i < f.chunks.size() && i < cap; ++i) {
+      const ColumnChunk& c = f.chunks[i];
+      chunks[i] = hbmc_chunk_t{c.begin, c.count, c.item, c.step, c.dep_lo, c.dep_hi, 0};
+    }
+    for (size_t i = 0; deps && i < f.deps.size() && i < dcap; ++i) deps[i] = f.deps[i];
+    if (n_chunks) *n_chunks = f.chunks.size();
+    if (n_deps) *n_deps = f.deps.size();
+    return HBMC_OK;
+  });
 }
 
 const char* hbmc_status_string(hbmc_status_t status) {

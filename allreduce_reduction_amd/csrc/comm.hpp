@@ -159,4 +159,17 @@ hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t c
 hbmc_status_t run_out_of_place(hbmc_comm* c, int coll, int root, const void* const send[],
                                void* const recv[], size_t count, int dtype, int op, void* stream);
 
+// Runs an entry point's body so that no C++ exception crosses the C ABI.  The
+// host code throws only when allocating its tables fails (std::bad_alloc,
+// std::length_error), which is reported as HBMC_ERR_NOMEM; a plan is cached
+// only once complete, so a failed call leaves the communicator usable.
+template <typename F>
+hbmc_status_t no_throw(F&& body) noexcept {
+  try {
+    return body();
+  } catch (...) {
+    return HBMC_ERR_NOMEM;
+  }
+}
+
 }  // namespace hbmc

@@ -48,35 +48,8 @@ void release(hbmc_graph* g) {
   g->graph = nullptr;
 }
 
-}  // namespace
-
-extern "C" {
-
-hbmc_status_t hbmc_graph_create(hbmc_graph_t* out) {
-  if (!out) return HBMC_ERR_INVALID_ARG;
-  *out = new (std::nothrow) hbmc_graph;
-  return *out ? HBMC_OK : HBMC_ERR_NOMEM;
-}
-
-hbmc_status_t hbmc_graph_add(hbmc_graph_t g, hbmc_comm_t comm, hbmc_coll_t coll, int root,
-                             void* const bufs[], size_t count, hbmc_dtype_t dtype, hbmc_op_t op) {
-  if (!g || g->built || !comm || !valid_op(op) || !valid_coll(coll) || elem_bytes(dtype) == 0)
-    return HBMC_ERR_INVALID_ARG;
-  Plan* p = nullptr;
-  hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
-  if (st != HBMC_OK) return st;
-  hbmc_graph::Node n{comm, coll, root, {}, count, dtype, op};
-  if (count > 0 && comm->topos[0].P > 1) {
-    st = check_bufs(comm->topos[0].P, bufs, count, elem_bytes(dtype));
-    if (st != HBMC_OK) return st;
-    n.bufs.assign(bufs, bufs + comm->topos[0].P);
-  }
-  g->nodes.push_back(std::move(n));
-  return HBMC_OK;
-}
-
-hbmc_status_t hbmc_graph_build(hbmc_graph_t g) {
-  if (!g || g->built) return HBMC_ERR_INVALID_ARG;
+// Body of hbmc_graph_build (the caller releases the graph on failure).
+hbmc_status_t graph_build(hbmc_graph* g) {
   if (hipGraphCreate(&g->graph, 0) != hipSuccess) return HBMC_ERR_HIP;
   hbmc_status_t st = HBMC_OK;
   std::vector<hipGraphNode_t> last(g->nodes.size(), nullptr);  // each collective's final node
@@ -112,12 +85,44 @@ hbmc_status_t hbmc_graph_build(hbmc_graph_t g) {
   }
   if (st == HBMC_OK && hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0) != hipSuccess)
     st = HBMC_ERR_HIP;
-  if (st != HBMC_OK) {
-    release(g);
-    return st;
-  }
-  g->built = true;
-  return HBMC_OK;
+  if (st == HBMC_OK) g->built = true;
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+hbmc_status_t hbmc_graph_create(hbmc_graph_t* out) {
+  if (!out) return HBMC_ERR_INVALID_ARG;
+  *out = new (std::nothrow) hbmc_graph;
+  return *out ? HBMC_OK : HBMC_ERR_NOMEM;
+}
+
+hbmc_status_t hbmc_graph_add(hbmc_graph_t g, hbmc_comm_t comm, hbmc_coll_t coll, int root,
+                             void* const bufs[], size_t count, hbmc_dtype_t dtype, hbmc_op_t op) {
+  if (!g || g->built || !comm || !valid_op(op) || !valid_coll(coll) || elem_bytes(dtype) == 0)
+    return HBMC_ERR_INVALID_ARG;
+  return no_throw([&]() -> hbmc_status_t {
+    Plan* p = nullptr;
+    hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+    if (st != HBMC_OK) return st;
+    hbmc_graph::Node n{comm, coll, root, {}, count, dtype, op};
+    if (count > 0 && comm->topos[0].P > 1) {
+      st = check_bufs(comm->topos[0].P, bufs, count, elem_bytes(dtype));
+      if (st != HBMC_OK) return st;
+      n.bufs.assign(bufs, bufs + comm->topos[0].P);
+    }
+    g->nodes.push_back(std::move(n));
+    return HBMC_OK;
+  });
+}
+
+hbmc_status_t hbmc_graph_build(hbmc_graph_t g) {
+  if (!g || g->built) return HBMC_ERR_INVALID_ARG;
+  const hbmc_status_t st = no_throw([&] { return graph_build(g); });
+  if (st != HBMC_OK) release(g);  // also after an allocation failure part-way
+  return st;
 }
 
 hbmc_status_t hbmc_graph_launch(hbmc_graph_t g, void* stream) {

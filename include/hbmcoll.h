@@ -35,6 +35,9 @@
  *     current returns HBMC_ERR_INVALID_ARG.  Cached schedules are kept until
  *     hbmc_comm_destroy.
  *   - count == 0 and P == 1 are valid and enqueue nothing.
+ *   - No C++ exception leaves the library: a host allocation that fails while
+ *     building schedules, tables or graphs returns HBMC_ERR_NOMEM, and the
+ *     communicator (or graph) stays usable, with nothing half-built cached.
  */
 #ifndef HBMCOLL_H
 #define HBMCOLL_H

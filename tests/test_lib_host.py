@@ -189,6 +189,10 @@ def test_validation_status_codes():
     assert lib.hbmc_comm_create(8, 9, 0, 0, 0, ctypes.byref(h)) == 1
     assert lib.hbmc_comm_create(8, 2, 3, 3, 0, ctypes.byref(h)) == 1       # S*M != P
     assert lib.hbmc_comm_create(8, 6, 3, 3, 0, ctypes.byref(h)) == 1       # hierarchical S*M != P
+    # S*M whose 32-bit product wraps to P: 4 * (2^30 + 2) = 2^32 + 8
+    assert lib.hbmc_comm_create(8, 2, 4, (1 << 30) + 2, 0, ctypes.byref(h)) == 1
+    assert lib.hbmc_comm_create(8, 6, 4, (1 << 30) + 2, 0, ctypes.byref(h)) == 1
+    assert lib.hbmc_comm_create(8, 7, 4, (1 << 30) + 2, 0, ctypes.byref(h)) == 1
     assert lib.hbmc_comm_create(8, 5, 0, 1, 0, ctypes.byref(h)) == 1       # tree arity 1
     assert lib.hbmc_comm_create(8, 0, 0, 0, 0, None) == 1
     assert lib.hbmc_comm_destroy(None) == 1
