@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -302,38 +303,47 @@ hbmc_status_t check_bufs(int P, void* const bufs[], size_t count, uint32_t e) {
 
 namespace {
 
+// Device attributes are cached per device in atomics: communicators on other
+// host threads may query them at the same time.
 uint32_t compute_units() {
-  static uint32_t cached[64] = {};
+  static std::atomic<uint32_t> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
+  uint32_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    cached[dev] = static_cast<uint32_t>(cus);
+    v = static_cast<uint32_t>(cus);
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 // Dynamic LDS one workgroup may use, and LDS per compute unit, of the current
 // device.
 void lds_limits(uint64_t* per_block, uint64_t* per_cu) {
-  static uint64_t blk[64] = {}, cu[64] = {};
+  static std::atomic<uint64_t> blk[64] = {}, cu[64] = {};
   int dev = 0;
   *per_block = 64 << 10;
   *per_cu = 64 << 10;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
-  if (blk[dev] == 0) {
-    int b = 0, m = 0;
-    if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || b <= 0)
-      b = 64 << 10;
-    if (hipDeviceGetAttribute(&m, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || m < b)
-      m = b;
-    blk[dev] = static_cast<uint64_t>(b);
-    cu[dev] = static_cast<uint64_t>(m);
+  // cu is published before blk, so a reader that sees blk sees cu
+  const uint64_t b0 = blk[dev].load(std::memory_order_acquire);
+  if (b0 != 0) {
+    *per_block = b0;
+    *per_cu = cu[dev].load(std::memory_order_relaxed);
+    return;
   }
-  *per_block = blk[dev];
-  *per_cu = cu[dev];
+  int b = 0, m = 0;
+  if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || b <= 0)
+    b = 64 << 10;
+  if (hipDeviceGetAttribute(&m, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || m < b)
+    m = b;
+  cu[dev].store(static_cast<uint64_t>(m), std::memory_order_relaxed);
+  blk[dev].store(static_cast<uint64_t>(b), std::memory_order_release);
+  *per_block = static_cast<uint64_t>(b);
+  *per_cu = static_cast<uint64_t>(m);
 }
 
 // Workgroups of the LDS-resident column kernel: one per column, at most as
