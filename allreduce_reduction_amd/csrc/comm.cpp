@@ -653,12 +653,14 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
   return HBMC_OK;
 }
 
+// hipLaunchKernel reports its own failure; hipGetLastError is not consulted,
+// so an earlier, unrelated error of the calling thread is neither reported
+// here nor cleared.
 hbmc_status_t launch(KernelDesc& k, void* stream) {
   k.bind();
   const hipError_t e =
       hipLaunchKernel(k.func, k.grid, k.block, k.argv, k.shared_bytes, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return HBMC_ERR_HIP;
-  return hipGetLastError() == hipSuccess ? HBMC_OK : HBMC_ERR_HIP;
+  return e == hipSuccess ? HBMC_OK : HBMC_ERR_HIP;
 }
 
 hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t count, int dtype,

@@ -303,8 +303,7 @@ hipError_t launch_step(const StepLaunch& s, const RankPtrs& ptrs, hipStream_t st
   KernelDesc k;
   const hipError_t e = describe_step(s, ptrs, &k);
   if (e != hipSuccess) return e;
-  const hipError_t l = hipLaunchKernel(k.func, k.grid, k.block, k.argv, k.shared_bytes, stream);
-  return l != hipSuccess ? l : hipGetLastError();
+  return hipLaunchKernel(k.func, k.grid, k.block, k.argv, k.shared_bytes, stream);
 }
 
 }  // namespace hbmc
