@@ -90,11 +90,26 @@ __device__ __forceinline__ int op_int(int x, int y) {
   return x <= y ? x : y;
 }
 
+// bf16 sum / product of both halves of a word: each half widened exactly
+// to fp32, combined in fp32, and both rounded to nearest even by one packed
+// conversion (v_cvt_pk_bf16_f32, which quiets NaNs like narrow_bf16).
+template <int OP>
+__device__ __forceinline__ uint32_t op_bf16x2(uint32_t a, uint32_t b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const float xl = u2f(a << 16), xh = u2f(a & 0xffff0000u);
+  const float yl = u2f(b << 16), yh = u2f(b & 0xffff0000u);
+  const f32x2 z = OP == kSum ? f32x2{xl + yl, xh + yh} : f32x2{xl * yl, xh * yh};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2));
+}
+
 // The op on one 32-bit word of packed elements.
 template <int DT, int OP>
 __device__ __forceinline__ uint32_t op_word(uint32_t a, uint32_t b) {
   if constexpr (DT == kF32) {
     return op_f32<OP>(a, b);
+  } else if constexpr (DT == kBF16 && (OP == kSum || OP == kProd)) {
+    return op_bf16x2<OP>(a, b);
   } else if constexpr (DT == kF16 || DT == kBF16) {
     return op_h16<DT, OP>(a & 0xffffu, b & 0xffffu) | (op_h16<DT, OP>(a >> 16, b >> 16) << 16);
   } else if constexpr (DT == kI32) {
