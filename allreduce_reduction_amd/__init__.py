@@ -154,6 +154,8 @@ def _ptrs(bufs):
         t0, n = b0.dtype, b0.numel()
         addrs = []
         for b in bufs:
+            if not hasattr(b, "data_ptr"):
+                raise TypeError("buffers must be all tensors or all raw device addresses")
             if b.dtype != t0 or not b.is_cuda or not b.is_contiguous() or b.numel() != n:
                 raise ValueError("buffers must be contiguous device tensors of one dtype and size")
             addrs.append(b.data_ptr())
@@ -162,6 +164,17 @@ def _ptrs(bufs):
     for i, b in enumerate(bufs):
         arr[i] = int(b)
     return arr, None, None
+
+
+def _args(bufs, dtype, count):
+    """(void*[P], count, dtype name) for a call: count and dtype default to
+    the tensors'; raw addresses need both given."""
+    arr, n, dt = _ptrs(bufs)
+    dtype = dtype or dt
+    count = n if count is None else count
+    if count is None or dtype is None:
+        raise ValueError("raw device addresses need an explicit count and dtype")
+    return arr, count, dtype
 
 
 _RAW_STREAM = None
@@ -207,9 +220,7 @@ class Comm:
 
     # -- collectives
     def _coll(self, fn, bufs, dtype, op, count, stream):
-        arr, n, dt = _ptrs(bufs)
-        dtype = dtype or dt
-        count = n if count is None else count
+        arr, count, dtype = _args(bufs, dtype, count)
         _check(getattr(load_library(), fn)(self._h, arr, count, DTYPE[dtype], OP[op], _stream(stream)), fn)
 
     def allreduce(self, bufs, dtype=None, op="sum", *, count=None, stream=None):
@@ -222,16 +233,12 @@ class Comm:
         self._coll("hbmc_all_gather", bufs, dtype, op, count, stream)
 
     def reduce(self, bufs, dtype=None, op="sum", *, root=0, count=None, stream=None):
-        arr, n, dt = _ptrs(bufs)
-        dtype = dtype or dt
-        count = n if count is None else count
+        arr, count, dtype = _args(bufs, dtype, count)
         _check(load_library().hbmc_reduce(self._h, arr, count, DTYPE[dtype], OP[op], root, _stream(stream)),
                "hbmc_reduce")
 
     def broadcast(self, bufs, dtype=None, *, root=0, count=None, stream=None):
-        arr, n, dt = _ptrs(bufs)
-        dtype = dtype or dt
-        count = n if count is None else count
+        arr, count, dtype = _args(bufs, dtype, count)
         _check(load_library().hbmc_broadcast(self._h, arr, count, DTYPE[dtype], root, _stream(stream)),
                "hbmc_broadcast")
 
@@ -243,18 +250,18 @@ class Comm:
             raise ValueError("send and recv must match in size and dtype")
         dtype = dtype or dt
         count = n if count is None else count
+        if count is None or dtype is None:
+            raise ValueError("raw device addresses need an explicit count and dtype")
         _check(load_library().hbmc_collective_oop(self._h, COLL[coll], root, sarr, rarr, count, DTYPE[dtype],
                                                   OP[op], _stream(stream)), "hbmc_collective_oop")
 
     def run_steps(self, coll, bufs, first, last, dtype=None, op="sum", *, root=0, count=None, stream=None):
-        arr, n, dt = _ptrs(bufs)
-        dtype = dtype or dt
-        count = n if count is None else count
+        arr, count, dtype = _args(bufs, dtype, count)
         _check(load_library().hbmc_run_steps(self._h, COLL[coll], root, arr, count, DTYPE[dtype], OP[op],
                                              first, last, _stream(stream)), "hbmc_run_steps")
 
     def set_exec_mode(self, mode: str):
-        """Launch form of every call: "auto" (default), "steps", "fused" or "columns"."""
+        """Launch form of every call: "auto" (default), "steps", "fused", "columns" or "lds"."""
         _check(load_library().hbmc_comm_set_exec_mode(self._h, EXEC[mode]), "hbmc_comm_set_exec_mode")
 
     def exec_choice(self, coll: str, count: int, dtype: str, root: int = 0, first: int = 0, last: int = 0) -> str:
@@ -338,9 +345,7 @@ class Graph:
         _check(load_library().hbmc_graph_create(ctypes.byref(self._h)), "hbmc_graph_create")
 
     def add(self, comm: Comm, coll: str, bufs, dtype=None, op="sum", *, root=0, count=None):
-        arr, n, dt = _ptrs(bufs)
-        dtype = dtype or dt
-        count = n if count is None else count
+        arr, count, dtype = _args(bufs, dtype, count)
         self._keep.append((arr, list(bufs)))
         _check(load_library().hbmc_graph_add(self._h, comm._h, COLL[coll], root, arr, count, DTYPE[dtype],
                                              OP[op]), "hbmc_graph_add")
