@@ -103,6 +103,29 @@ __device__ __forceinline__ uint32_t op_bf16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2));
 }
 
+// fp16 / bf16 max or min of both halves of a word at once: each half's order
+// key (as order_key), the packed unsigned max / min of the keys, the winning
+// key turned back into its bits, and the canonical quiet NaN in every half
+// where either operand is a NaN (a saturating subtract of the infinity
+// pattern is nonzero exactly there).
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t minmax_h16x2(uint32_t a, uint32_t b) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+  constexpr uint16_t inf = DT == kF16 ? 0x7c00u : 0x7f80u;
+  constexpr uint32_t qnan2 = DT == kF16 ? 0x7e007e00u : 0x7fc07fc0u;
+  const u16x2 top = {0x8000u, 0x8000u}, low = {0x7fffu, 0x7fffu}, lim = {inf, inf}, one = {1u, 1u};
+  const u16x2 A = __builtin_bit_cast(u16x2, a), B = __builtin_bit_cast(u16x2, b);
+  const u16x2 ka = A ^ (__builtin_bit_cast(u16x2, __builtin_bit_cast(i16x2, A) >> 15) | top);
+  const u16x2 kb = B ^ (__builtin_bit_cast(u16x2, __builtin_bit_cast(i16x2, B) >> 15) | top);
+  const u16x2 k = OP == kMax ? __builtin_elementwise_max(ka, kb) : __builtin_elementwise_min(ka, kb);
+  const u16x2 r = k ^ (~__builtin_bit_cast(u16x2, __builtin_bit_cast(i16x2, k) >> 15) | top);
+  const u16x2 d = __builtin_elementwise_sub_sat(__builtin_elementwise_max(A & low, B & low), lim);
+  const u16x2 zero = {0u, 0u};
+  const uint32_t mask = __builtin_bit_cast(uint32_t, u16x2(zero - __builtin_elementwise_min(d, one)));
+  return (__builtin_bit_cast(uint32_t, r) & ~mask) | (qnan2 & mask);
+}
+
 // The op on one 32-bit word of packed elements.
 template <int DT, int OP>
 __device__ __forceinline__ uint32_t op_word(uint32_t a, uint32_t b) {
@@ -110,6 +133,8 @@ __device__ __forceinline__ uint32_t op_word(uint32_t a, uint32_t b) {
     return op_f32<OP>(a, b);
   } else if constexpr (DT == kBF16 && (OP == kSum || OP == kProd)) {
     return op_bf16x2<OP>(a, b);
+  } else if constexpr ((DT == kF16 || DT == kBF16) && (OP == kMax || OP == kMin)) {
+    return minmax_h16x2<DT, OP>(a, b);
   } else if constexpr (DT == kF16 || DT == kBF16) {
     return op_h16<DT, OP>(a & 0xffffu, b & 0xffffu) | (op_h16<DT, OP>(a >> 16, b >> 16) << 16);
   } else if constexpr (DT == kI32) {
