@@ -41,11 +41,14 @@ __device__ __forceinline__ uint32_t op_f32(uint32_t a, uint32_t b) {
   } else if constexpr (OP == kProd) {
     return f2u(u2f(a) * u2f(b));
   } else {
-    const bool nan = ((a & 0x7fffffffu) > 0x7f800000u) | ((b & 0x7fffffffu) > 0x7f800000u);
-    const uint32_t ka = order_key<0x80000000u, 0xffffffffu>(a);
-    const uint32_t kb = order_key<0x80000000u, 0xffffffffu>(b);
-    const uint32_t r = (OP == kMax) ? (ka >= kb ? a : b) : (ka <= kb ? a : b);
-    return nan ? 0x7fc00000u : r;
+    // order keys without a branch (an arithmetic shift spreads the sign),
+    // the unsigned max / min of the keys, and the winner's key turned back
+    const uint32_t ka = a ^ (static_cast<uint32_t>(static_cast<int32_t>(a) >> 31) | 0x80000000u);
+    const uint32_t kb = b ^ (static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u);
+    const uint32_t k = OP == kMax ? (ka > kb ? ka : kb) : (ka < kb ? ka : kb);
+    const uint32_t r = k ^ (~static_cast<uint32_t>(static_cast<int32_t>(k) >> 31) | 0x80000000u);
+    const uint32_t ma = a & 0x7fffffffu, mb = b & 0x7fffffffu;
+    return (ma > mb ? ma : mb) > 0x7f800000u ? 0x7fc00000u : r;
   }
 }
 
@@ -139,6 +142,10 @@ __device__ __forceinline__ uint32_t op_word(uint32_t a, uint32_t b) {
     return op_h16<DT, OP>(a & 0xffffu, b & 0xffffu) | (op_h16<DT, OP>(a >> 16, b >> 16) << 16);
   } else if constexpr (DT == kI32) {
     return static_cast<uint32_t>(op_int<OP>(static_cast<int>(a), static_cast<int>(b)));
+  } else if constexpr (OP == kSum) {
+    // four wrapping int8 adds: the low 7 bits of each byte cannot carry into
+    // the next byte, and each byte's top bit is its carry-in xor both top bits
+    return ((a & 0x7f7f7f7fu) + (b & 0x7f7f7f7fu)) ^ ((a ^ b) & 0x80808080u);
   } else {
     uint32_t r = 0;
 #pragma unroll
