@@ -33,7 +33,10 @@
  *     kernels.  Tables live on the device current at that first call: a
  *     communicator serves one device, and a call made with another device
  *     current returns HBMC_ERR_INVALID_ARG.  Cached schedules are kept until
- *     hbmc_comm_destroy.
+ *     hbmc_comm_destroy.  A later call of a cached shape allocates, copies and
+ *     synchronises nothing; it only enqueues kernels on `stream`, so a caller
+ *     may capture it into a graph (the first call of a shape, and the first in
+ *     a new launch form or column length, must not be made while capturing).
  *   - count == 0 and P == 1 are valid and enqueue nothing.
  *   - No C++ exception leaves the library: a host allocation that fails while
  *     building schedules, tables or graphs returns HBMC_ERR_NOMEM, and the
