@@ -1,7 +1,10 @@
-// Device element ops shared by the step kernels and the single-workgroup
-// plan kernel: fp16 / bf16 lanes widen to fp32, combine and round back to
-// nearest even per operation; integers wrap; max / min order -0 below +0
-// and give the canonical quiet NaN when either operand is NaN.
+// Device element ops shared by every kernel family (step, single-workgroup,
+// column and LDS-resident kernels): fp16 / bf16 sums and products widen to
+// fp32, combine and round back to nearest even per operation; integers wrap;
+// max / min order -0 below +0 and give the canonical quiet NaN when either
+// operand is NaN.  Floating max / min compare order keys: the bit pattern
+// with all bits flipped when the sign bit is set, else with the sign bit
+// set, which sorts negative values below positive ones and -0 under +0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,13 +30,6 @@ struct Width {
 __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
 
-// Monotone map of an IEEE bit pattern (sign bit `sb`) to an unsigned key:
-// negative values reversed below positive ones, so -0 sorts under +0.
-template <uint32_t SB, uint32_t MASK>
-__device__ __forceinline__ uint32_t order_key(uint32_t u) {
-  return (u & SB) ? (~u & MASK) : (u | SB);
-}
-
 template <int OP>
 __device__ __forceinline__ uint32_t op_f32(uint32_t a, uint32_t b) {
   if constexpr (OP == kSum) {
@@ -58,31 +54,12 @@ __device__ __forceinline__ float widen_f16(uint32_t h) {
 __device__ __forceinline__ uint32_t narrow_f16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // v_cvt_f16_f32, nearest even
 }
-__device__ __forceinline__ float widen_bf16(uint32_t h) { return u2f(h << 16); }
-__device__ __forceinline__ uint32_t narrow_bf16(float f) {
-  const uint32_t u = f2u(f);
-  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // nearest even
-  const uint32_t qnan = (u >> 16) | 0x40u;                      // the NaN, quieted
-  return (u & 0x7fffffffu) > 0x7f800000u ? qnan : rne;          // a select, no branch
-}
-
-// One 16-bit lane (value in the low half of the word).
-template <int DT, int OP>
-__device__ __forceinline__ uint32_t op_h16(uint32_t a, uint32_t b) {
-  if constexpr (OP == kSum || OP == kProd) {
-    const float x = DT == kF16 ? widen_f16(a) : widen_bf16(a);
-    const float y = DT == kF16 ? widen_f16(b) : widen_bf16(b);
-    const float z = OP == kSum ? x + y : x * y;
-    return DT == kF16 ? narrow_f16(z) : narrow_bf16(z);
-  } else {
-    constexpr uint32_t inf = DT == kF16 ? 0x7c00u : 0x7f80u;
-    constexpr uint32_t qnan = DT == kF16 ? 0x7e00u : 0x7fc0u;
-    const bool nan = ((a & 0x7fffu) > inf) | ((b & 0x7fffu) > inf);
-    const uint32_t ka = order_key<0x8000u, 0xffffu>(a);
-    const uint32_t kb = order_key<0x8000u, 0xffffu>(b);
-    const uint32_t r = (OP == kMax) ? (ka >= kb ? a : b) : (ka <= kb ? a : b);
-    return nan ? qnan : r;
-  }
+// fp16 sum / product of one 16-bit lane (value in the low half of the word).
+template <int OP>
+__device__ __forceinline__ uint32_t op_f16(uint32_t a, uint32_t b) {
+  static_assert(OP == kSum || OP == kProd, "fp16 max / min take minmax_h16x2");
+  const float x = widen_f16(a), y = widen_f16(b);
+  return narrow_f16(OP == kSum ? x + y : x * y);
 }
 
 template <int OP>
@@ -95,7 +72,7 @@ __device__ __forceinline__ int op_int(int x, int y) {
 
 // bf16 sum / product of both halves of a word: each half widened exactly
 // to fp32, combined in fp32, and both rounded to nearest even by one packed
-// conversion (v_cvt_pk_bf16_f32, which quiets NaNs like narrow_bf16).
+// conversion (v_cvt_pk_bf16_f32: a NaN keeps its sign and payload, quieted).
 template <int OP>
 __device__ __forceinline__ uint32_t op_bf16x2(uint32_t a, uint32_t b) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -107,7 +84,7 @@ __device__ __forceinline__ uint32_t op_bf16x2(uint32_t a, uint32_t b) {
 }
 
 // fp16 / bf16 max or min of both halves of a word at once: each half's order
-// key (as order_key), the packed unsigned max / min of the keys, the winning
+// key, the packed unsigned max / min of the keys, the winning
 // key turned back into its bits, and the canonical quiet NaN in every half
 // where either operand is a NaN (a saturating subtract of the infinity
 // pattern is nonzero exactly there).
@@ -138,8 +115,8 @@ __device__ __forceinline__ uint32_t op_word(uint32_t a, uint32_t b) {
     return op_bf16x2<OP>(a, b);
   } else if constexpr ((DT == kF16 || DT == kBF16) && (OP == kMax || OP == kMin)) {
     return minmax_h16x2<DT, OP>(a, b);
-  } else if constexpr (DT == kF16 || DT == kBF16) {
-    return op_h16<DT, OP>(a & 0xffffu, b & 0xffffu) | (op_h16<DT, OP>(a >> 16, b >> 16) << 16);
+  } else if constexpr (DT == kF16) {
+    return op_f16<OP>(a & 0xffffu, b & 0xffffu) | (op_f16<OP>(a >> 16, b >> 16) << 16);
   } else if constexpr (DT == kI32) {
     return static_cast<uint32_t>(op_int<OP>(static_cast<int>(a), static_cast<int>(b)));
   } else if constexpr (OP == kSum) {

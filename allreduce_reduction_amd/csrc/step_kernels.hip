@@ -10,8 +10,9 @@
 //
 // Data path: every operand of an item sits at the same element offset, and
 // when all rank buffers share one 16-byte phase the item's body is moved as
-// 16-byte vectors (global_load_dwordx4 with the nontemporal hint, plain
-// global_store_dwordx4): one wave per workgroup and one vector per lane per
+// 16-byte vectors (global_load_dwordx4 with the nontemporal hint;
+// global_store_dwordx4, with that hint only in steps that write more than the
+// memory-side cache holds): one wave per workgroup and one vector per lane per
 // operand, i.e. 1 KiB tiles of every operand per workgroup, which measured
 // fastest for streams far larger than the caches; the few head / tail
 // elements are done one by one.  Buffers with different phases take an
