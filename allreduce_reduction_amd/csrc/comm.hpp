@@ -20,7 +20,9 @@ enum ExecMode : int { kExecAuto = 0, kExecSteps = 1, kExecFused = 2, kExecColumn
 
 // Modelled time (us) of a range of steps in each launch form, fitted to
 // measurements on MI355X (one launch per step, the single-workgroup kernel,
-// the column kernel; see choose_exec).
+// the column kernel and the LDS-resident column kernel; see choose_exec).
+// The LDS form's per-chunk cost was fitted on fp16 max, its slowest element
+// op; cheaper ops run their chunks faster than modelled.
 struct ExecModel {
   double launch_us = 4.2;       // host-side cost of one step launch (bounds eager small steps)
   double step_us = 3.0;         // fixed GPU cost of one step kernel
