@@ -629,6 +629,7 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     launches->push_back(k);
     return HBMC_OK;
   }
+  launches->reserve(static_cast<size_t>(last - first));
   for (int s = first; s < last; ++s) {
     const Step& step = p->sched.steps[s];
     if (step.items.empty()) continue;
@@ -639,6 +640,7 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     L.nsrc = step.nsrc;
     L.ndst = step.ndst;
     L.items = p->dev + p->first_item[s];
+    L.host_items = step.items.data();
     L.nitems = static_cast<int>(step.items.size());
     L.max_count = step.max_count;
     L.aligned = aligned;
@@ -646,9 +648,8 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     L.xcd_split = c->xcd_split;
     L.write_bytes = 0;
     for (const Item& it : step.items) L.write_bytes += it.count * uint64_t(it.ndst) * elem_bytes(dtype);
-    KernelDesc k;
-    if (describe_step(L, ptrs, &k) != hipSuccess) return HBMC_ERR_HIP;
-    launches->push_back(k);
+    launches->emplace_back();
+    if (describe_step(L, ptrs, &launches->back()) != hipSuccess) return HBMC_ERR_HIP;
   }
   return HBMC_OK;
 }
@@ -760,6 +761,7 @@ hbmc_status_t run_out_of_place(hbmc_comm* c, int coll, int root, const void* con
       L.mode = kCopy;
       L.nsrc = L.ndst = 1;
       L.items = lc->dev;
+      L.host_items = lc->sched.steps[0].items.data();
       L.nitems = n;
       L.max_count = count;
       L.aligned = aligned;

@@ -173,33 +173,53 @@ __device__ __forceinline__ unsigned char* rank_buf(const RankPtrs& ptrs, const D
   return ptrs.p[(w >> ((i & 3) * 8)) & 0xffu];
 }
 
-// Combination of an item's sources at one element (byte offset `off`).
-template <int DT, int OP, int MODE>
-__device__ __forceinline__ uint32_t combine_elem(const RankPtrs& ptrs, const DevItem* it, int ns,
-                                                 uint64_t off) {
+// An item's operands read from the device item table: the i-th is the
+// buffer of the item's i-th rank, element offsets count from its start.
+struct ItemBufs {
+  const RankPtrs& ptrs;
+  const DevItem* it;
+  __device__ __forceinline__ unsigned char* operator()(int i) const { return rank_buf(ptrs, it, i); }
+};
+
+// An item's operands resolved on the host (kernel arguments): the i-th is
+// the address of the item's first element in that operand.
+template <int NB>
+struct ArgBufs {
+  const ArgItem<NB>* a;
+  __device__ __forceinline__ unsigned char* operator()(int i) const { return a->buf[i]; }
+};
+
+// Combination of an item's sources at one element (byte offset `off` from
+// each operand address `b(i)`).
+template <int DT, int OP, int MODE, typename B>
+__device__ __forceinline__ uint32_t combine_elem(const B& b, int ns, uint64_t off) {
   constexpr uint32_t E = Width<DT>::bytes;
   if constexpr (MODE == kCopy) {
-    return load_elem<E>(rank_buf(ptrs, it, 0) + off);
+    return load_elem<E>(b(0) + off);
   } else if constexpr (MODE == kFold) {
-    uint32_t acc = load_elem<E>(rank_buf(ptrs, it, 0) + off);
-    for (int s = 1; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(rank_buf(ptrs, it, s) + off));
+    uint32_t acc = load_elem<E>(b(0) + off);
+    for (int s = 1; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(b(s) + off));
     return acc;
   } else {
-    uint32_t acc = load_elem<E>(rank_buf(ptrs, it, 1) + off);
-    for (int s = 2; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(rank_buf(ptrs, it, s) + off));
-    return op_word<DT, OP>(load_elem<E>(rank_buf(ptrs, it, 0) + off), acc);
+    uint32_t acc = load_elem<E>(b(1) + off);
+    for (int s = 2; s < ns; ++s) acc = op_word<DT, OP>(acc, load_elem<E>(b(s) + off));
+    return op_word<DT, OP>(load_elem<E>(b(0) + off), acc);
   }
+}
+
+template <int DT, int OP, int MODE, typename B>
+__device__ __forceinline__ void do_elem(const B& b, int ns, int nd, uint64_t elem) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  const uint64_t off = elem * E;
+  const uint32_t v = combine_elem<DT, OP, MODE>(b, ns, off);
+  for (int d = 0; d < nd; ++d) store_elem<E>(b(ns + d) + off, v);
 }
 
 template <int DT, int OP, int MODE>
 __device__ __forceinline__ void do_elem(const RankPtrs& ptrs, const DevItem* it, int ns, int nd,
                                         uint64_t elem) {
-  constexpr uint32_t E = Width<DT>::bytes;
-  const uint64_t off = elem * E;
-  const uint32_t v = combine_elem<DT, OP, MODE>(ptrs, it, ns, off);
-  for (int d = 0; d < nd; ++d) store_elem<E>(rank_buf(ptrs, it, ns + d) + off, v);
+  do_elem<DT, OP, MODE>(ItemBufs{ptrs, it}, ns, nd, elem);
 }
-
 
 }  // namespace dev
 }  // namespace hbmc

@@ -1,5 +1,9 @@
 // gfx950 step kernels.  One launch executes one schedule step for all ranks:
-// grid.y indexes the step's work items, grid.x tiles an item's elements.
+// grid.y indexes the step's work items, grid.x tiles an item's elements.  A
+// workgroup takes its item either from the plan's device item table
+// (step_vec: the item's rank numbers index the call's pointer table) or, for
+// steps of a few items, from the kernel arguments with its operand addresses
+// already resolved by the host (step_arg).
 //
 // The reduce is the pages' reduce_op(recv, local) over a received block and
 // the local block ([RING-RHD] "Ring AllReduce带宽最优的环形流水线" listing;
@@ -22,6 +26,8 @@
 // back to nearest even per operation; integers wrap; max / min order -0 below
 // +0 and give the canonical quiet NaN when either operand is NaN.
 #include <hip/hip_runtime.h>
+
+#include <new>
 
 #include "elemops.hpp"
 #include "launch.hpp"
@@ -58,9 +64,7 @@ constexpr int kCapMinItems = 64;  // above any tree level (at most 32 parents)
 
 // ------------------------------------------------------------- kernels
 
-// Vector kernel.  NS / ND > 0 fix the item shape at compile time (all loads
-// of a tile issued before any combine); 0 reads it from the item.
-// Workgroup -> (item, tile): grid.y is the item and grid.x the tile, and the
+// Vector kernels.  Workgroup -> (item, tile): grid.y is the item and grid.x the tile, and the
 // hardware deals workgroups to the 8 XCDs round-robin by linear id.  With
 // `xcd_split` each XCD instead walks one contiguous range of the step's tiles.
 __device__ __forceinline__ void xcd_tile(uint32_t* item, uint32_t* tile) {
@@ -71,18 +75,17 @@ __device__ __forceinline__ void xcd_tile(uint32_t* item, uint32_t* tile) {
   *tile = lin % gridDim.x;
 }
 
+// One workgroup's tile of one item.  `bufs(i)` is the item's i-th operand
+// (sources, then destinations) and element j of the item sits at byte
+// (begin + j) * E from it; `phase` is the 16-byte phase the operand addresses
+// share.  NS / ND > 0 fix the item shape at compile time (all loads of a tile
+// issued before any combine); 0 takes ns / nd.
 // NT: stores with the nontemporal hint (a compile-time choice: the compiler
 // merges the two stores of a run-time branch into one plain store).
-template <int DT, int OP, int MODE, int NS, int ND, bool NT>
-__global__ void __launch_bounds__(kThreads)
-step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, RankPtrs ptrs) {
+template <int DT, int OP, int MODE, int NS, int ND, bool NT, typename B>
+__device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t count, uint32_t phase,
+                                         uint32_t tile, int ns, int nd) {
   constexpr uint32_t E = Width<DT>::bytes;
-  uint32_t item = blockIdx.y, tile = blockIdx.x;
-  if (flags & kFlagXcdSplit) xcd_tile(&item, &tile);
-  const DevItem* it = items + item;
-  const uint64_t begin = it->begin, count = it->count;
-  const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
-  const int nd = ND > 0 ? ND : static_cast<int>(it->ndst);
   // A fixed-shape item's buffer addresses, all taken before the first data
   // load: the scalar loads behind them are then issued together, and the
   // workgroup waits on one chain (kernel arguments, item record, addresses)
@@ -91,7 +94,7 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
   unsigned char* buf[NB];
   if constexpr (NS > 0 && ND > 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) buf[b] = rank_buf(ptrs, it, b);
+    for (int b = 0; b < NB; ++b) buf[b] = bufs(b);
   }
 
   uint64_t head = ((16u - ((phase + begin * E) & 15u)) & 15u) / E;
@@ -110,7 +113,7 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
       for (int s = 0; s < NS; ++s) {
         const unsigned char* src;
         if constexpr (ND > 0) src = buf[s];
-        else src = rank_buf(ptrs, it, s);
+        else src = bufs(s);
         const u32x4* p = reinterpret_cast<const u32x4*>(src + base);
 #pragma unroll
         for (int u = 0; u < kVecPerThread; ++u) {
@@ -136,7 +139,7 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
     } else {
       const int first = MODE == kRecvFold ? 1 : 0;
       {
-        const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, first) + base);
+        const u32x4* p = reinterpret_cast<const u32x4*>(bufs(first) + base);
 #pragma unroll
         for (int u = 0; u < kVecPerThread; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
@@ -145,7 +148,7 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
       }
       if constexpr (MODE != kCopy) {
         for (int s = first + 1; s < ns; ++s) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, s) + base);
+          const u32x4* p = reinterpret_cast<const u32x4*>(bufs(s) + base);
 #pragma unroll
           for (int u = 0; u < kVecPerThread; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
@@ -153,7 +156,7 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
           }
         }
         if constexpr (MODE == kRecvFold) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(rank_buf(ptrs, it, 0) + base);
+          const u32x4* p = reinterpret_cast<const u32x4*>(bufs(0) + base);
 #pragma unroll
           for (int u = 0; u < kVecPerThread; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
@@ -166,7 +169,7 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
     for (int d = 0; d < (ND > 0 ? ND : nd); ++d) {
       unsigned char* dst;
       if constexpr (NS > 0 && ND > 0) dst = buf[NS + d];
-      else dst = rank_buf(ptrs, it, ns + d);
+      else dst = bufs(ns + d);
       u32x4* q = reinterpret_cast<u32x4*>(dst + base);
 #pragma unroll
       for (int u = 0; u < kVecPerThread; ++u) {
@@ -182,9 +185,34 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
   // head and tail elements (fewer than 16 bytes each), by the item's first tile
   if (tile == 0) {
     const uint64_t t = threadIdx.x;
-    if (t < head) do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + t);
-    if (t >= 32 && t - 32 < count - body_end) do_elem<DT, OP, MODE>(ptrs, it, ns, nd, begin + body_end + (t - 32));
+    if (t < head) do_elem<DT, OP, MODE>(bufs, ns, nd, begin + t);
+    if (t >= 32 && t - 32 < count - body_end) do_elem<DT, OP, MODE>(bufs, ns, nd, begin + body_end + (t - 32));
   }
+}
+
+// Vector kernel, items from the device table.
+template <int DT, int OP, int MODE, int NS, int ND, bool NT>
+__global__ void __launch_bounds__(kThreads)
+step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, RankPtrs ptrs) {
+  uint32_t item = blockIdx.y, tile = blockIdx.x;
+  if (flags & kFlagXcdSplit) xcd_tile(&item, &tile);
+  const DevItem* it = items + item;
+  const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
+  const int nd = ND > 0 ? ND : static_cast<int>(it->ndst);
+  vec_item<DT, OP, MODE, NS, ND, NT>(ItemBufs{ptrs, it}, it->begin, it->count, phase, tile, ns, nd);
+}
+
+// Vector kernel, items resolved into the kernel arguments (compile-time
+// shapes, plain stores): the operand addresses already point at the item's
+// first element, whose 16-byte phase they carry.
+template <int DT, int OP, int MODE, int NS, int ND>
+__global__ void __launch_bounds__(kThreads)
+step_arg(uint32_t flags, ArgItems<NS + ND> args) {
+  uint32_t item = blockIdx.y, tile = blockIdx.x;
+  if (flags & kFlagXcdSplit) xcd_tile(&item, &tile);
+  const ArgItem<NS + ND>* a = &args.it[item];
+  const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a->buf[0]) & 15u);
+  vec_item<DT, OP, MODE, NS, ND, false>(ArgBufs<NS + ND>{a}, 0, a->count, phase, tile, NS, ND);
 }
 
 // Element-wise kernel for buffers whose 16-byte phases differ.
@@ -236,9 +264,53 @@ const void* vector_kernel(const StepLaunch& s) {
   return fn(step_vec<DT, kSum, kCopy, 1, 0, NT>);
 }
 
-template <int DT, int OP>
-void describe_typed(const StepLaunch& s, KernelDesc* k) {
+// Kernel-argument form of a compile-time shape: write the step's items,
+// operands resolved, into k->args and return the kernel.
+template <int DT, int OP, int MODE, int NS, int ND>
+const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
+  constexpr int NB = NS + ND;
   constexpr uint32_t E = Width<DT>::bytes;
+  static_assert(NB <= kArgMaxBufs && sizeof(ArgItems<NB>) <= kArgBytes, "argument items");
+  ArgItems<NB>* a = new (k->args) ArgItems<NB>;
+  for (int i = 0; i < s.nitems; ++i) {
+    const Item& it = s.host_items[i];
+    for (int b = 0; b < NB; ++b) a->it[i].buf[b] = ptrs.p[it.rank[b]] + it.begin * E;
+    a->it[i].count = it.count;
+  }
+  return fn(step_arg<DT, OP, MODE, NS, ND>);
+}
+
+// The kernel-argument form for a step of at most kArgItems items of a
+// compile-time shape whose stores take no hint; nullptr otherwise.
+template <int DT, int OP>
+const void* arg_kernel(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
+  if (!s.host_items || s.nitems > kArgItems || s.write_bytes > kCacheBytes || s.ndst != 1) return nullptr;
+  if (s.mode == kRecvFold) {
+    switch (s.nsrc) {
+      case 2: return arg_items<DT, OP, kRecvFold, 2, 1>(s, ptrs, k);
+      case 3: return arg_items<DT, OP, kRecvFold, 3, 1>(s, ptrs, k);
+      case 5: return arg_items<DT, OP, kRecvFold, 5, 1>(s, ptrs, k);
+      case 9: return arg_items<DT, OP, kRecvFold, 9, 1>(s, ptrs, k);
+      default: return nullptr;
+    }
+  }
+  if (s.mode == kFold) {
+    switch (s.nsrc) {
+      case 2: return arg_items<DT, OP, kFold, 2, 1>(s, ptrs, k);
+      case 4: return arg_items<DT, OP, kFold, 4, 1>(s, ptrs, k);
+      case 8: return arg_items<DT, OP, kFold, 8, 1>(s, ptrs, k);
+      default: return nullptr;
+    }
+  }
+  return s.nsrc == 1 ? arg_items<DT, kSum, kCopy, 1, 1>(s, ptrs, k) : nullptr;
+}
+
+template <int DT, int OP>
+void describe_typed(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  k->ptrs = ptrs;
+  k->items = s.items;
+  k->phase = s.phase;
   if (!s.aligned) {
     uint64_t gx = (s.max_count + kElemThreads - 1) / kElemThreads;
     if (gx > 2048) gx = 2048;
@@ -259,8 +331,13 @@ void describe_typed(const StepLaunch& s, KernelDesc* k) {
   const uint64_t gx = vecs > kTileVecs ? (vecs + kTileVecs - 1) / kTileVecs : 1;
   k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
   k->block = dim3(kThreads);
-  k->kind = KernelDesc::kVector;
   k->flags = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? kFlagXcdSplit : 0u;
+  if (const void* f = arg_kernel<DT, OP>(s, ptrs, k)) {
+    k->kind = KernelDesc::kVectorArgs;
+    k->func = f;
+    return;
+  }
+  k->kind = KernelDesc::kVector;
   k->func = s.write_bytes > kCacheBytes ? vector_kernel<DT, OP, true>(s) : vector_kernel<DT, OP, false>(s);
   if (s.nitems >= kCapMinItems) {
     if ((s.mode == kFold && s.nsrc == 8) || (s.mode == kRecvFold && s.nsrc == 9))
@@ -271,12 +348,12 @@ void describe_typed(const StepLaunch& s, KernelDesc* k) {
 }
 
 template <int DT>
-void describe_op(const StepLaunch& s, KernelDesc* k) {
+void describe_op(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
   switch (s.op) {
-    case kSum: describe_typed<DT, kSum>(s, k); break;
-    case kProd: describe_typed<DT, kProd>(s, k); break;
-    case kMax: describe_typed<DT, kMax>(s, k); break;
-    default: describe_typed<DT, kMin>(s, k); break;
+    case kSum: describe_typed<DT, kSum>(s, ptrs, k); break;
+    case kProd: describe_typed<DT, kProd>(s, ptrs, k); break;
+    case kMax: describe_typed<DT, kMax>(s, ptrs, k); break;
+    default: describe_typed<DT, kMin>(s, ptrs, k); break;
   }
 }
 
@@ -285,15 +362,12 @@ void describe_op(const StepLaunch& s, KernelDesc* k) {
 hipError_t describe_step(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
   if (s.nitems <= 0) return hipErrorInvalidValue;
   if (s.ndst > 1 && s.mode != kCopy) return hipErrorInvalidValue;  // no such schedule step
-  k->ptrs = ptrs;
-  k->items = s.items;
-  k->phase = s.phase;
   switch (s.dtype) {
-    case kF32: describe_op<kF32>(s, k); break;
-    case kF16: describe_op<kF16>(s, k); break;
-    case kBF16: describe_op<kBF16>(s, k); break;
-    case kI32: describe_op<kI32>(s, k); break;
-    default: describe_op<kI8>(s, k); break;
+    case kF32: describe_op<kF32>(s, ptrs, k); break;
+    case kF16: describe_op<kF16>(s, ptrs, k); break;
+    case kBF16: describe_op<kBF16>(s, ptrs, k); break;
+    case kI32: describe_op<kI32>(s, ptrs, k); break;
+    default: describe_op<kI8>(s, ptrs, k); break;
   }
   k->bind();
   return hipSuccess;

@@ -399,6 +399,11 @@ def main():
     algbw = D / t
     busbw = algbw * 2 * (P - 1) / P
     achieved = rs_bytes / (rs_ms / 1e3)
+    # the library passes a step of at most 16 items that writes at most 256 MiB
+    # in the kernel arguments (step_arg), any other through its item table
+    # (step_vec); the reduce step writes a third of the bytes it moves
+    rs_items = comm.step_info("allreduce", L, dtype, rs_steps[0])["nitems"]
+    kern = "step_arg" if rs_items <= 16 and rs_bytes // 3 <= 256 << 20 else "step_vec"
 
     out = {
         "metric": "AllReduce busbw GB/s on 1 GPU (P simulated ranks) + % of HBM peak",
@@ -420,7 +425,7 @@ def main():
                    "P": P, "elems_per_rank": L, "algo": a.algo, "kernel_launches": nsteps},
         "algbw_GBps": round(algbw / 1e9, 3),
         "pct_hbm": round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2),
-        "roofline": {"bound": "hbm", "kernel": "step_vec<fp32,sum,recv_fold,2,1> (ring reduce step)",
+        "roofline": {"bound": "hbm", "kernel": f"{kern}<fp32,sum,recv_fold,2,1> (ring reduce step)",
                      "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4),
                      "traffic": measured_traffic() if (P, L, a.algo) == (8, 64 << 20, "ring") else None,
@@ -432,7 +437,7 @@ def main():
     }
     if ag_ms:
         ag_bytes = comm.step_info("allreduce", L, dtype, ag_steps[0])["hbm_bytes"]
-        out["copy_step"] = {"kernel": "step_vec<fp32,copy,1,1> (ring all-gather step)",
+        out["copy_step"] = {"kernel": f"{kern}<fp32,copy,1,1> (ring all-gather step)",
                             "mean_launch_us": round(ag_ms * 1e3, 2),
                             "achieved_GBps": round(ag_bytes / (ag_ms / 1e3) / 1e9, 1),
                             "frac": round(ag_bytes / (ag_ms / 1e3) / HBM_PEAK, 4),

@@ -227,6 +227,38 @@ def test_unaligned_buffers(dtype, phases):
         assert int((backing[mask] != 0).sum()) == 0
 
 
+@pytest.mark.parametrize("phase", ["aligned", "same_nonzero"])
+def test_step_item_sources(phase):
+    """One launch per step, around the size limit of the kernel-argument item
+    form (steps of at most 16 items; larger ones read the device item table):
+    ring with 15, 16 and 17 ranks, RHD with 16 and 17, Flat's single 8-source
+    fold and the 2 x 2 pipeline, over buffers on one 16-byte phase, zero or
+    not (head and tail elements then come before and after the vectors)."""
+    cases = [("ring", 15), ("ring", 16), ("ring", 17), ("rhd", 16), ("rhd", 17), ("flat", 8), ("pipeline", 4)]
+    for algo, P in cases:
+        for dtype, op in (("fp32", "sum"), ("fp16", "max"), ("bf16", "prod"), ("int8", "sum")):
+            esz = np.dtype(refops.STORAGE[dtype]).itemsize
+            L = 16 * 1024 + 3 * P + 5
+            say(f"case item sources {phase} algo={algo} P={P} dtype={dtype} op={op} L={L}")
+            xs = make_inputs(dtype, op, P, L, seed=P)
+            offs = [0 if phase == "aligned" else max(1, 4 // esz)] * P
+            views, backing = strided_buffers(xs, dtype, offs)
+            comm, S, M = comm_for(algo, P)
+            with comm:
+                comm.set_exec_mode("steps")
+                comm.allreduce(views, dtype, op)
+                torch.cuda.synchronize()
+            want = [x.copy() for x in xs]
+            oracle.run("allreduce", algo, want, dtype, op, S=S, M=M)
+            for r in range(P):
+                refops.assert_same(dtype, to_host(views[r], dtype), want[r], f"{algo} P={P} {dtype} {op} rank {r}")
+            mask = torch.ones_like(backing, dtype=torch.bool)
+            for v in views:
+                off = (v.data_ptr() - backing.data_ptr()) // esz
+                mask[off:off + L] = False
+            assert int((backing[mask] != 0).sum()) == 0
+
+
 @pytest.mark.parametrize("algo,coll,P", [("ring", "allreduce", 8), ("rhd", "allreduce", 5),
                                          ("rhd", "allreduce", 8), ("rhd", "reduce_scatter", 8),
                                          ("rhd", "reduce_scatter", 6), ("rhd", "all_gather", 7),
