@@ -311,10 +311,13 @@ def test_non_default_stream():
         refops.assert_same("fp32", to_host(dev[r], "fp32"), want[r])
 
 
-@pytest.mark.parametrize("algo,P", [("ring", 5), ("rhd", 6), ("pipeline", 8), ("flat", 4), ("rhd", 1)])
+@pytest.mark.parametrize("algo,P", [("ring", 5), ("rhd", 6), ("pipeline", 8), ("flat", 4), ("rhd", 1),
+                                    ("ring", 17), ("ring", 34)])
 def test_out_of_place(algo, P):
     """recv holds what the in-place call would leave; send is untouched; ranks
-    with send == recv run in place in the same call."""
+    with send == recv run in place in the same call.  The copies go 32 ranks
+    per launch, a launch of at most 16 with its items in the kernel arguments:
+    17 ranks (rank 0 in place) copy 16 in one launch, 34 ranks copy 32, then 1."""
     dtype = "fp16"
     colls = ["allreduce", "reduce_scatter", "all_gather"] if algo != "flat" else ["allreduce"]
     if algo == "rhd":
