@@ -224,7 +224,40 @@ hbmc_status_t upload_columns(Plan* p) {
   return HBMC_OK;
 }
 
-hbmc_status_t upload_lds_tables(Plan* p, int P, uint32_t e) {
+namespace {
+
+void lds_limits(uint64_t* per_block, uint64_t* per_cu);
+
+// Trailing copy steps a column must have for its copies to be composed into
+// stores: fewer copy passes (RHD with 8 ranks: 3, in batches) cost about as
+// little as the store records that would replace them.
+constexpr uint32_t kMinStoreSteps = 4;
+
+// Bytes [lo, hi) of a column of one rank's final values come from the LDS
+// copy of rank `src`.
+struct Piece {
+  uint32_t lo, hi, src;
+};
+
+// `pieces` (ascending, covering [0, n)) with [lo, hi) replaced by `with`.
+void replace_range(std::vector<Piece>& pieces, uint32_t lo, uint32_t hi, const std::vector<Piece>& with,
+                   std::vector<Piece>& tmp) {
+  tmp.clear();
+  for (const Piece& q : pieces)
+    if (q.lo < lo) tmp.push_back({q.lo, std::min(q.hi, lo), q.src});
+  for (const Piece& q : with) tmp.push_back(q);
+  for (const Piece& q : pieces)
+    if (q.hi > hi) tmp.push_back({std::max(q.lo, hi), q.hi, q.src});
+  pieces.clear();
+  for (const Piece& q : tmp) {
+    if (!pieces.empty() && pieces.back().src == q.src && pieces.back().hi == q.lo) pieces.back().hi = q.hi;
+    else pieces.push_back(q);
+  }
+}
+
+}  // namespace
+
+hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
   if (p->lds_mem) return HBMC_OK;
   if (p->lds_cols.chunk_elems != p->lds_col || p->lds_cols.col_off.empty())
     if (!build_columns(p->sched, P, p->lds_col, false, &p->lds_cols)) return HBMC_ERR_INVALID_ARG;
@@ -270,19 +303,92 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint32_t e) {
       }
     }
   }
-  const size_t b_image = (host.size() * sizeof(DevColChunk) + 255) & ~size_t(255);
-  const size_t b_off = f.col_off.size() * sizeof(uint32_t);
+  // Launches of all steps: each column's trailing copy chunks composed into
+  // store records.  Every rank starts as its own source; a copy chunk gives
+  // each destination, over the chunk's range, the sources its source has
+  // there.  Every rank some chunk of the column writes is stored.
+  std::vector<DevColStore> stores;
+  std::vector<uint32_t> col_run(ncols), st_off(ncols + 1, 0);
+  std::vector<std::vector<Piece>> map(P);
+  std::vector<Piece> part, tmp;
+  uint64_t meta_steps = 0, meta_whole = 0;
+  bool any_tail = false;
+  for (size_t g = 0; g < ncols; ++g) {
+    const uint64_t col_begin = uint64_t(g) * f.chunk_elems;
+    const uint32_t nbytes = static_cast<uint32_t>(std::min<uint64_t>(f.chunk_elems, count - col_begin) * e);
+    const uint32_t k0 = f.col_off[g], k1 = f.col_off[g + 1];
+    uint32_t cut = k1;
+    while (cut > k0 && (host[cut - 1].shape & 0xffu) == uint32_t(kCopy)) --cut;
+    col_run[g] = cut - k0;
+    uint64_t dirty = 0;
+    for (uint32_t k = k0; k < k1; ++k) dirty |= host[k].dst_mask;
+    for (int r = 0; r < P; ++r) map[r].assign(1, Piece{0, nbytes, static_cast<uint32_t>(r)});
+    for (uint32_t k = cut; k < k1; ++k) {
+      const DevColChunk& c = host[k];
+      const int nd = static_cast<int>(c.shape >> 16);
+      part.clear();
+      for (const Piece& q : map[c.rank[0]])
+        if (q.hi > c.lo && q.lo < c.hi) part.push_back({std::max(q.lo, c.lo), std::min(q.hi, c.hi), q.src});
+      for (int q = 1; q <= nd; ++q) replace_range(map[c.rank[q]], c.lo, c.hi, part, tmp);
+    }
+    // composed only where every written rank takes its bytes from at most two
+    // copies (a column within one or two segments): the kernel walks store
+    // records one after another, while the copy chunks it would skip go in
+    // batches; other columns run every chunk and store their written ranks
+    // whole (no store records)
+    size_t nrec = 0;
+    for (int r = 0; r < P; ++r)
+      if ((dirty >> r) & 1u) nrec += map[r].size();
+    uint32_t tail_steps = 0;
+    for (uint32_t k = cut; k < k1; ++k) tail_steps += (k == cut || host[k].step != host[k - 1].step) ? 1u : 0u;
+    if (tail_steps >= kMinStoreSteps && nrec <= 2 * size_t(__builtin_popcountll(dirty))) {
+      for (int r = 0; r < P; ++r) {
+        if (!((dirty >> r) & 1u)) continue;
+        for (const Piece& q : map[r]) stores.push_back(DevColStore{q.lo, q.hi, static_cast<uint32_t>(r), q.src});
+      }
+    } else {
+      cut = k1;
+      col_run[g] = k1 - k0;
+    }
+    st_off[g + 1] = static_cast<uint32_t>(stores.size());
+    any_tail = any_tail || cut < k1;
+    meta_steps = std::max<uint64_t>(meta_steps, uint64_t(k1 - k0) * sizeof(DevColChunk));
+    meta_whole = std::max<uint64_t>(meta_whole, uint64_t(cut - k0) * sizeof(DevColChunk) +
+                                                    uint64_t(st_off[g + 1] - st_off[g]) * sizeof(DevColStore));
+  }
+  uint64_t per_block = 0, per_cu = 0;
+  lds_limits(&per_block, &per_cu);
+
+  auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+  const size_t b_image = up(host.size() * sizeof(DevColChunk));
+  const size_t b_off = up(f.col_off.size() * sizeof(uint32_t));
+  const size_t b_st = up((stores.size() + 1) * sizeof(DevColStore));
+  const size_t b_run = up(col_run.size() * sizeof(uint32_t) + 4);
+  const size_t b_st_off = st_off.size() * sizeof(uint32_t);
   void* mem = nullptr;
-  if (hipMalloc(&mem, b_image + b_off) != hipSuccess) return HBMC_ERR_NOMEM;
+  if (hipMalloc(&mem, b_image + b_off + b_st + b_run + b_st_off) != hipSuccess) return HBMC_ERR_NOMEM;
   char* base = static_cast<char*>(mem);
   if (hipMemcpy(base, host.data(), host.size() * sizeof(DevColChunk), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(base + b_image, f.col_off.data(), b_off, hipMemcpyHostToDevice) != hipSuccess) {
+      hipMemcpy(base + b_image, f.col_off.data(), f.col_off.size() * sizeof(uint32_t), hipMemcpyHostToDevice) !=
+          hipSuccess ||
+      (!stores.empty() && hipMemcpy(base + b_image + b_off, stores.data(), stores.size() * sizeof(DevColStore),
+                                    hipMemcpyHostToDevice) != hipSuccess) ||
+      hipMemcpy(base + b_image + b_off + b_st, col_run.data(), col_run.size() * sizeof(uint32_t),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(base + b_image + b_off + b_st + b_run, st_off.data(), b_st_off, hipMemcpyHostToDevice) !=
+          hipSuccess) {
     (void)hipFree(mem);
     return HBMC_ERR_HIP;
   }
   p->lds_mem = mem;
   p->dev_image = reinterpret_cast<DevColChunk*>(base);
   p->dev_lds_col_off = reinterpret_cast<uint32_t*>(base + b_image);
+  p->dev_stores = reinterpret_cast<DevColStore*>(base + b_image + b_off);
+  p->dev_col_run = reinterpret_cast<uint32_t*>(base + b_image + b_off + b_st);
+  p->dev_st_off = reinterpret_cast<uint32_t*>(base + b_image + b_off + b_st + b_run);
+  p->lds_meta_steps = meta_steps;
+  p->lds_meta_whole = meta_whole;
+  p->lds_stores = any_tail && uint64_t(P) * lds_slot_bytes(p->lds_col, e) + meta_whole <= per_block;
   return HBMC_OK;
 }
 
@@ -380,14 +486,15 @@ uint64_t longest_column(const Schedule& s, uint64_t count, uint64_t col) {
 // same-range chunks, assuming one shape per step), a batch of n costing
 // 1 + 0.75 (n - 1) passes (fitted on MI355X: a batch's loads overlap, its
 // element ops mostly do not); every chunk that covers part of a column goes
-// alone.  Beyond
-// 2^24 column-steps it falls back to counting every chunk.
-double longest_passes(const Schedule& s, uint64_t count, uint64_t col) {
+// alone.  Only steps before `steps_end` count.  Beyond 2^24 column-steps it
+// falls back to counting every chunk.
+double longest_passes(const Schedule& s, uint64_t count, uint64_t col, size_t steps_end) {
   const uint64_t ncols = (count + col - 1) / col;
   if (ncols * s.steps.size() > (uint64_t(1) << 24)) return double(longest_column(s, count, col));
   std::vector<double> passes(ncols, 0.0);
   std::vector<int64_t> full(ncols + 1), part(ncols + 1);
-  for (const Step& st : s.steps) {
+  for (size_t si = 0; si < steps_end && si < s.steps.size(); ++si) {
+    const Step& st = s.steps[si];
     std::fill(full.begin(), full.end(), 0);
     std::fill(part.begin(), part.end(), 0);
     for (const Item& it : st.items) {
@@ -454,13 +561,31 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
   p->lds_chunks = 0;
   p->lds_longest = 0.0;
   auto fits = [&](uint64_t col, uint64_t longest) { return lds_bytes(P, col, e, longest) <= per_block; };
+  // the schedule's trailing copy steps, which a launch of all steps replaces
+  // by composed stores
+  size_t body = p->sched.steps.size();
+  while (body > 0 && (p->sched.steps[body - 1].mode == kCopy || p->sched.steps[body - 1].items.empty())) --body;
+  const size_t all = p->sched.steps.size();
+  // the stores replace those copies only in columns that meet at most two of
+  // their items per rank: taken as columns no longer than the shortest
+  uint64_t tail_item = UINT64_MAX;
+  for (size_t si = body; si < all; ++si)
+    for (const Item& it : p->sched.steps[si].items) tail_item = std::min(tail_item, it.count);
+  const bool composable = all - body >= kMinStoreSteps;
+  auto whole_end = [&](uint64_t col) { return composable && col <= tail_item ? body : all; };
+  // the composed stores cost about one chunk pass
+  auto whole_passes = [&](uint64_t col) {
+    const size_t end = whole_end(col);
+    return longest_passes(p->sched, count, col, end) + (end < all ? 1.0 : 0.0);
+  };
   if (c->column_bytes > 0) {
     const uint64_t col = column_elems(c->column_bytes, count, e, compute_units());
     const uint64_t chunks = longest_column(p->sched, count, col);
     if (fits(col, chunks)) {
       p->lds_col = col;
       p->lds_chunks = chunks;
-      p->lds_longest = longest_passes(p->sched, count, col);
+      p->lds_longest = longest_passes(p->sched, count, col, all);
+      p->lds_longest_whole = whole_passes(col);
     }
   } else {
     // 16-byte multiples from the longest that can fit down to 16 bytes
@@ -471,13 +596,14 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
       const uint64_t col = bytes / e;
       const uint64_t chunks = longest_column(p->sched, count, col);
       if (!fits(col, chunks)) continue;
-      const double passes = longest_passes(p->sched, count, col);
+      const double passes = whole_passes(col);
       const double t = lds_time(c->model, P, count, e, col, chunks, passes, 1.0);
       if (p->lds_col == 0 || t < best * 0.98) {
         best = t;
         p->lds_col = col;
         p->lds_chunks = chunks;
-        p->lds_longest = passes;
+        p->lds_longest = longest_passes(p->sched, count, col, all);
+        p->lds_longest_whole = passes;
       }
     }
   }
@@ -545,8 +671,11 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     }
   }
   if (lds_ok) {
-    const double t = lds_time(m, P, count, e, p->lds_col, p->lds_chunks, p->lds_longest,
-                              double(busy) / std::max(1, busy_all));
+    // a launch of all steps stores the trailing copies' results directly
+    const bool all_steps = first == 0 && last == static_cast<int>(p->sched.steps.size());
+    const double t = lds_time(m, P, count, e, p->lds_col, p->lds_chunks,
+                              all_steps ? p->lds_longest_whole : p->lds_longest,
+                              all_steps ? 1.0 : double(busy) / std::max(1, busy_all));
     if (t < best) {
       best = t;
       *mode = kExecLds;
@@ -612,16 +741,20 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     return HBMC_OK;
   }
   if (mode == kExecLds) {
-    // the whole step range as one LDS-resident column-kernel launch
-    st = upload_lds_tables(p, P, e);
+    // the whole step range as one LDS-resident column-kernel launch; a
+    // launch of all steps stores the trailing copies' results directly
+    st = upload_lds_tables(p, P, count, e);
     if (st != HBMC_OK) return st;
     const ColumnTable& f = p->lds_cols;
     const uint32_t ncols = static_cast<uint32_t>(f.col_off.size() - 1);
-    const uint64_t shared = lds_bytes(P, p->lds_col, e, f.max_per_col);
+    const bool stores = p->lds_stores && first == 0 && last == nsteps;
+    const uint64_t meta = stores ? p->lds_meta_whole : p->lds_meta_steps;
+    const uint64_t shared = uint64_t(P) * lds_slot_bytes(p->lds_col, e) + meta;
     KernelDesc k;
     describe_columns_lds(dtype, op, ptrs, p->dev_image, p->dev_lds_col_off, ncols, static_cast<uint32_t>(first),
-                         static_cast<uint32_t>(last), phase, p->lds_col, count, static_cast<uint32_t>(P),
-                         f.max_per_col, lds_grid(ncols, shared), &k);
+                         static_cast<uint32_t>(last), phase, p->lds_col, count, static_cast<uint32_t>(P), meta,
+                         lds_grid(ncols, shared), stores ? p->dev_stores : nullptr,
+                         stores ? p->dev_col_run : nullptr, stores ? p->dev_st_off : nullptr, &k);
     if (shared > (64u << 10) &&
         hipFuncSetAttribute(k.func, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shared)) !=
             hipSuccess)

@@ -64,10 +64,21 @@ struct Plan {
   uint64_t lds_col = 0;  // 0: no column length fits one workgroup's LDS
   uint64_t lds_chunks = 0;   // chunks of the longest column (its LDS records)
   double lds_longest = 0.0;  // serial chunk passes of the busiest column (for the cost model)
+  double lds_longest_whole = 0.0;  // the same without the schedule's trailing copy steps
   ColumnTable lds_cols;
   void* lds_mem = nullptr;
   DevColChunk* dev_image = nullptr;
   uint32_t* dev_lds_col_off = nullptr;
+  // composed stores for launches of all steps (see DevColStore), built with
+  // the tables: per column the chunk records to run and its store records;
+  // the LDS the records of one column need at most (all chunks; leading
+  // chunks and stores); stores used only when the latter fits
+  DevColStore* dev_stores = nullptr;
+  uint32_t* dev_col_run = nullptr;
+  uint32_t* dev_st_off = nullptr;
+  uint64_t lds_meta_steps = 0;
+  uint64_t lds_meta_whole = 0;
+  bool lds_stores = false;
 };
 
 }  // namespace hbmc
@@ -133,10 +144,13 @@ hbmc_status_t upload_columns(Plan* p);
 // workgroup's LDS, the one of least modelled time (ties: the longer).
 // Sets p->lds_col (0 when none fits), p->lds_chunks and p->lds_longest.
 hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t e);
-// Build and upload the LDS-resident kernel's tables for p->lds_col: column
-// g's chunks in order at [col_off[g], col_off[g+1]), each with its byte range
-// relative to the column, step, shape, rank numbers and destination mask.
-hbmc_status_t upload_lds_tables(Plan* p, int P, uint32_t e);
+// Build and upload the LDS-resident kernel's tables for p->lds_col (count
+// elements of e bytes): column g's chunks in order at [col_off[g],
+// col_off[g+1]), each with its byte range relative to the column, step,
+// shape, rank numbers and destination mask; and for launches of all steps
+// the number of chunks before the column's trailing copies and the store
+// records those copies compose into (see DevColStore).
+hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e);
 // Launch form of steps [first, last) of plan `p` (count elements of e bytes,
 // buffers of one 16-byte phase when `aligned`): the communicator's mode when
 // not AUTO and the form is eligible; for AUTO the eligible form of least

@@ -105,6 +105,17 @@ struct alignas(16) DevColChunk {
 // conflict, so a lane may apply a run's chunks together.
 static_assert(sizeof(DevColChunk) == 160, "column chunk record");
 
+// The end of a column in a launch of all of a call's steps (device table):
+// the column's trailing copy chunks only move finished values between rank
+// copies, so instead of running them the kernel writes each destination
+// rank's bytes [lo, hi) of the column (relative to its first element)
+// straight from the LDS copy of rank `src`, which holds them once the
+// column's other chunks have run.
+struct alignas(16) DevColStore {
+  uint32_t lo, hi, dst, src;
+};
+static_assert(sizeof(DevColStore) == 16, "column store record");
+
 // One kernel launch: kernel, shape and argument values, usable with
 // hipLaunchKernel or as a kernel graph node.
 struct KernelDesc {
@@ -132,8 +143,14 @@ struct KernelDesc {
   const DevColChunk* image = nullptr;
   uint64_t col_elems = 0, count = 0;
   uint32_t nranks = 0, slot_bytes = 0, s_lo = 0, s_hi = 0;
+  // and in a launch of all steps with composed stores: column g runs its
+  // first col_run[g] chunk records, then store records [st_off[g],
+  // st_off[g+1]) (nullptr: every chunk runs, dirty ranks stored whole)
+  const DevColStore* stores = nullptr;
+  const uint32_t* col_run = nullptr;
+  const uint32_t* st_off = nullptr;
   uint32_t shared_bytes = 0;  // dynamic LDS per workgroup
-  void* argv[12];  // filled by bind(); valid while this object lives
+  void* argv[16];  // filled by bind(); valid while this object lives
   void bind() {
     argv[0] = &ptrs;
     argv[1] = &items;
@@ -161,6 +178,9 @@ struct KernelDesc {
       argv[8] = &count;
       argv[9] = &nranks;
       argv[10] = &slot_bytes;
+      argv[11] = &stores;
+      argv[12] = &col_run;
+      argv[13] = &st_off;
     } else if (kind == kVectorArgs) {
       argv[0] = &flags;
       argv[1] = args;
@@ -192,10 +212,15 @@ uint64_t lds_bytes(int nranks, uint64_t col_elems, uint32_t e, uint64_t max_chun
 // The LDS-resident column kernel over steps [s_lo, s_hi) of a plan: `grid`
 // workgroups, workgroup w running columns w, w + grid, ... of `col_elems`
 // elements (the last one cut at `count`); column g's chunk records are
-// image[col_off[g] .. col_off[g+1]).
+// image[col_off[g] .. col_off[g+1]).  With `stores` (a launch of all steps)
+// column g runs its first col_run[g] records and then its store records
+// stores[st_off[g] .. st_off[g+1]).  `meta_bytes`: the LDS after the rank
+// copies that the records of the largest column need.
 void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColChunk* image, const uint32_t* col_off,
                           uint32_t ncols, uint32_t s_lo, uint32_t s_hi, uint32_t phase, uint64_t col_elems,
-                          uint64_t count, uint32_t nranks, uint64_t max_chunks_per_col, uint32_t grid, KernelDesc* k);
+                          uint64_t count, uint32_t nranks, uint64_t meta_bytes, uint32_t grid,
+                          const DevColStore* stores, const uint32_t* col_run, const uint32_t* st_off,
+                          KernelDesc* k);
 
 // The single-workgroup kernel running `nsteps` steps of a plan.
 void describe_fused(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const FusedStep* steps,

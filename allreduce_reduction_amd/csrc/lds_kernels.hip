@@ -20,9 +20,19 @@
 // the chunk records (copied into LDS by wave 0 while the lanes load their
 // data) visible to every wave.
 //
+// In a launch of all of a call's steps, a column whose chunk list ends in
+// copies over four or more steps (the ring's all-gather, RHD's doubling and
+// restore, a stand-alone all-gather) does not run those copies: they only
+// pass finished values from one rank's copy to another's, so the host
+// composes them into store records (DevColStore) that write each rank's
+// final bytes from the LDS copy holding them.  The bits are the same; the
+// column's chain of dependent chunk passes is shorter (ring: P - 1 instead
+// of 2 (P - 1)).
+//
 // LDS layout (dynamic): nranks slots of slot_bytes (element col_begin + i of
 // rank r at slot r + phase + i*E, so LDS and global 16-byte phases agree),
-// then one DevColChunk record per entry of the column's chunk list.
+// then one DevColChunk record per chunk the column runs, then its store
+// records.
 //
 // A chunk's cost is a short dependent chain (record words, then its data,
 // then the op and the store), so the loop is kept lean: ONE marks launches
@@ -215,6 +225,29 @@ __device__ __forceinline__ void move_positions(unsigned char* lds, uint32_t slot
   }
 }
 
+// This lane's positions of slot bytes [lo, hi) of one LDS copy (`src`) into
+// a rank's global buffer (`g`: the global address of slot byte 0).
+template <int DT, bool ONE>
+__device__ __forceinline__ void store_range(const unsigned char* src, unsigned char* g, uint32_t lo, uint32_t hi) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  const uint32_t p_lo = lo >> 4, p_hi = (hi + 15) >> 4;
+  auto one = [&](uint32_t p) {
+    const uint32_t a = p * 16, b = a + 16;
+    if (a >= lo && b <= hi) {
+      store_vec(reinterpret_cast<u32x4*>(g + a), *reinterpret_cast<const u32x4*>(src + a));
+    } else {
+      const uint32_t l = a > lo ? a : lo, h = b < hi ? b : hi;
+      for (uint32_t o = l; o < h; o += E) store_elem<E>(g + o, load_elem<E>(src + o));
+    }
+  };
+  if constexpr (ONE) {
+    if (threadIdx.x >= p_lo && threadIdx.x < p_hi) one(threadIdx.x);
+  } else {
+    const uint32_t nthr = blockDim.x;  // a power of two
+    for (uint32_t p = p_lo + ((threadIdx.x - p_lo) & (nthr - 1)); p < p_hi; p += nthr) one(p);
+  }
+}
+
 // Workgroup w runs columns w, w + gridDim.x, ...; of each column only the
 // chunks of steps [s_lo, s_hi).  Chunk headers are read into scalar
 // registers, so every branch on them is uniform.
@@ -222,7 +255,8 @@ template <int DT, int OP, bool ONE>
 __global__ void __launch_bounds__(kLdsMaxThreads)
 plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uint32_t* __restrict__ col_off,
                  uint32_t ncols, uint32_t s_lo, uint32_t s_hi, uint32_t phase, uint64_t col_elems, uint64_t count,
-                 uint32_t nranks, uint32_t slot_bytes) {
+                 uint32_t nranks, uint32_t slot_bytes, const DevColStore* __restrict__ stores,
+                 const uint32_t* __restrict__ col_run, const uint32_t* __restrict__ st_off) {
   constexpr uint32_t E = Width<DT>::bytes;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   DevColChunk* meta = reinterpret_cast<DevColChunk*>(lds + nranks * slot_bytes);
@@ -231,12 +265,19 @@ plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uin
   for (uint32_t g = blockIdx.x; g < ncols; g += gridDim.x) {
     const uint64_t col_begin = uint64_t(g) * col_elems;
     const uint32_t n = static_cast<uint32_t>(count - col_begin < col_elems ? count - col_begin : col_elems);
-    const uint32_t k0 = col_off[g], nk = col_off[g + 1] - k0;
+    const uint32_t k0 = col_off[g];
+    const uint32_t nk = stores ? col_run[g] : col_off[g + 1] - k0;
+    const uint32_t st0 = stores ? st_off[g] : 0, nst = stores ? st_off[g + 1] - st0 : 0;
+    const DevColStore* st_lds = reinterpret_cast<const DevColStore*>(meta + nk);
     if (threadIdx.x < 64) {
-      // the column's chunk records into LDS (ten 16-byte words each)
+      // the column's chunk records into LDS (ten 16-byte words each), then
+      // its store records (one word each)
       const u32x4* src = reinterpret_cast<const u32x4*>(image + k0);
       u32x4* dst = reinterpret_cast<u32x4*>(meta);
       for (uint32_t w = threadIdx.x; w < nk * 10; w += 64) dst[w] = src[w];
+      const u32x4* ssrc = reinterpret_cast<const u32x4*>(stores + st0);
+      u32x4* sdst = reinterpret_cast<u32x4*>(meta + nk);
+      for (uint32_t w = threadIdx.x; w < nst; w += 64) sdst[w] = ssrc[w];
     }
     move_positions<DT, true>(lds, slot_bytes, ptrs, col_begin * E, all, nranks, phase, n);
     __syncthreads();
@@ -293,7 +334,26 @@ plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uin
         else lds_chunk<DT, kSum, kCopy, 0, 0, ONE>(lds, slot_bytes, lo, hi, ns, nd, rw, lr);
       }
     }
-    move_positions<DT, false>(lds, slot_bytes, ptrs, col_begin * E, dirty, nranks, phase, n);
+    if (nst > 0) {
+      // four records at a time: their LDS reads go out together
+      for (uint32_t i = 0; i < nst; i += 4) {
+        uint32_t lo[4], hi[4], dst[4], src[4];
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+          const u32x4 r = i + q < nst ? *reinterpret_cast<const u32x4*>(st_lds + i + q) : u32x4{0, 0, 0, 0};
+          lo[q] = phase + uni(r.x);
+          hi[q] = phase + uni(r.y);
+          dst[q] = uni(r.z);
+          src[q] = uni(r.w);
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q)
+          if (i + q < nst)
+            store_range<DT, ONE>(lds + src[q] * slot_bytes, ptrs.p[dst[q]] + col_begin * E - phase, lo[q], hi[q]);
+      }
+    } else {
+      move_positions<DT, false>(lds, slot_bytes, ptrs, col_begin * E, dirty, nranks, phase, n);
+    }
     __syncthreads();  // the chunk records are refilled for the next column
   }
 }
@@ -333,7 +393,8 @@ uint64_t lds_bytes(int nranks, uint64_t col_elems, uint32_t e, uint64_t max_chun
 
 void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColChunk* image, const uint32_t* col_off,
                           uint32_t ncols, uint32_t s_lo, uint32_t s_hi, uint32_t phase, uint64_t col_elems,
-                          uint64_t count, uint32_t nranks, uint64_t max_chunks_per_col, uint32_t grid,
+                          uint64_t count, uint32_t nranks, uint64_t meta_bytes, uint32_t grid,
+                          const DevColStore* stores, const uint32_t* col_run, const uint32_t* st_off,
                           KernelDesc* k) {
   const uint32_t e = dtype == kF32 || dtype == kI32 ? 4 : (dtype == kI8 ? 1 : 2);
   // every lane owns at most one 16-byte position of the column
@@ -359,7 +420,10 @@ void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColC
   k->count = count;
   k->nranks = nranks;
   k->slot_bytes = lds_slot_bytes(col_elems, e);
-  k->shared_bytes = static_cast<uint32_t>(lds_bytes(static_cast<int>(nranks), col_elems, e, max_chunks_per_col));
+  k->shared_bytes = static_cast<uint32_t>(uint64_t(nranks) * k->slot_bytes + meta_bytes);
+  k->stores = stores;
+  k->col_run = col_run;
+  k->st_off = st_off;
   k->bind();
 }
 

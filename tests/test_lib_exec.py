@@ -24,12 +24,17 @@ def test_auto_regimes_ring_p8_fp16():
         assert c.exec_choice("allreduce", 64 << 20, "fp32") == "steps"     # the 256 MiB per rank workload
 
 
-def test_auto_small_rhd_p16_prefers_the_single_workgroup():
-    # 1 KiB per rank over 16 ranks: every LDS column holds a chunk of all 16
-    # ranks' 64-byte segments' steps; one workgroup is cheaper
-    with hc.Comm(16, "rhd") as c:
+def test_auto_small_rhd_many_ranks_prefers_the_single_workgroup():
+    # 1 KiB per rank over 64 ranks: 16-byte segments, so every LDS column
+    # holds chunks of many segments' steps; one workgroup is cheaper
+    with hc.Comm(64, "rhd") as c:
         assert c.exec_choice("allreduce", 512, "fp16") == "fused"
         assert c.exec_choice("allreduce", 8 << 10, "fp16") == "lds"
+    # over 16 ranks (64-byte segments) the LDS form's columns fit within a
+    # segment and its halving passes alone count (on MI355X: 12.3-12.5 us
+    # against 14.9-15.1 us for the single workgroup)
+    with hc.Comm(16, "rhd") as c:
+        assert c.exec_choice("allreduce", 512, "fp16") == "lds"
 
 
 def test_auto_prefers_steps_where_launches_are_few_and_bytes_many():
