@@ -184,3 +184,48 @@ def test_lds_past_the_default_limit(algo, P, dtype, L):
         for r in range(P):
             assert torch.equal(a[r].view(torch.int16 if dtype == "bf16" else torch.int32),
                                b[r].view(torch.int16 if dtype == "bf16" else torch.int32)), f"rank {r}"
+
+
+COMPOSED = [  # trailing copy steps: ring 15, RHD 16 ranks 4, 17 ranks 5 (with the restore), pipeline 5
+    ("ring", 16, (16, "ring"), {}),
+    ("rhd", 16, (16, "rhd"), {}),
+    ("rhd", 17, (17, "rhd"), {}),
+    ("pipeline", 20, (20, "pipeline", 5, 4, 4096), dict(S=5, M=4, loop_bytes=4096)),
+]
+
+
+@pytest.mark.parametrize("case", COMPOSED, ids=[f"{c[0]}{c[1]}" for c in COMPOSED])
+def test_lds_composed_stores(case):
+    """LDS form, whole calls: columns whose chunk lists end in copies over four
+    or more steps store the copies' results directly instead of running them.
+    Columns inside one segment, across two and across many (which keep their
+    copies), ragged lengths, buffers on a shared non-zero 16-byte phase;
+    AllReduce, stand-alone AllGather and ReduceScatter."""
+    algo, P, args, kw = case
+    dtypes = ["fp32", "bf16", "int8", "fp16"]
+    with hc.Comm(*args) as comm:
+        comm.set_exec_mode("lds")
+        i = 0
+        for coll in ("allreduce", "all_gather", "reduce_scatter"):
+            for chunk in (16, 48, 1024):
+                for L in (16 * 97 + 5, 40_003):
+                    for ph in (0, 1):
+                        dtype, op = dtypes[i % len(dtypes)], OPS[i % len(OPS)]
+                        i += 1
+                        comm.set_columns(1 << 40, chunk)
+                        say(f"case composed algo={algo} P={P} coll={coll} chunk={chunk} L={L} phase={ph} "
+                            f"dtype={dtype} op={op}")
+                        assert comm.exec_choice(coll, L, dtype) == "lds"
+                        xs = make_inputs(dtype, op, P, L, seed=L + chunk + ph)
+                        if ph:
+                            esz = np.dtype(refops.STORAGE[dtype]).itemsize
+                            dev, _keep = strided_buffers(xs, dtype, [max(1, 4 // esz)] * P)
+                        else:
+                            dev = [to_dev(x, dtype) for x in xs]
+                        getattr(comm, coll)(dev, dtype, op)
+                        torch.cuda.synchronize()
+                        want = [x.copy() for x in xs]
+                        oracle.run(coll, algo, want, dtype, op, **kw)
+                        for r in range(P):
+                            refops.assert_same(dtype, to_host(dev[r], dtype), want[r],
+                                               f"composed {algo} {coll} chunk={chunk} L={L} rank {r}")
