@@ -309,6 +309,8 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
   // there.  Every rank some chunk of the column writes is stored.
   std::vector<DevColStore> stores;
   std::vector<uint32_t> col_run(ncols), st_off(ncols + 1, 0);
+  const uint64_t all_ranks = P >= 64 ? ~uint64_t(0) : ((uint64_t(1) << P) - 1);
+  std::vector<uint64_t> col_load(ncols, all_ranks);
   std::vector<std::vector<Piece>> map(P);
   std::vector<Piece> part, tmp;
   uint64_t meta_steps = 0, meta_whole = 0;
@@ -342,10 +344,20 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
     uint32_t tail_steps = 0;
     for (uint32_t k = cut; k < k1; ++k) tail_steps += (k == cut || host[k].step != host[k - 1].step) ? 1u : 0u;
     if (tail_steps >= kMinStoreSteps && nrec <= 2 * size_t(__builtin_popcountll(dirty))) {
+      // loaded: the ranks the remaining chunks name and the stores' sources
+      uint64_t load = 0;
+      for (uint32_t k = k0; k < cut; ++k) {
+        const int nr = static_cast<int>(((host[k].shape >> 8) & 0xffu) + (host[k].shape >> 16));
+        for (int q = 0; q < nr; ++q) load |= uint64_t(1) << host[k].rank[q];
+      }
       for (int r = 0; r < P; ++r) {
         if (!((dirty >> r) & 1u)) continue;
-        for (const Piece& q : map[r]) stores.push_back(DevColStore{q.lo, q.hi, static_cast<uint32_t>(r), q.src});
+        for (const Piece& q : map[r]) {
+          stores.push_back(DevColStore{q.lo, q.hi, static_cast<uint32_t>(r), q.src});
+          load |= uint64_t(1) << q.src;
+        }
       }
+      col_load[g] = load;
     } else {
       cut = k1;
       col_run[g] = k1 - k0;
@@ -364,9 +376,10 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
   const size_t b_off = up(f.col_off.size() * sizeof(uint32_t));
   const size_t b_st = up((stores.size() + 1) * sizeof(DevColStore));
   const size_t b_run = up(col_run.size() * sizeof(uint32_t) + 4);
-  const size_t b_st_off = st_off.size() * sizeof(uint32_t);
+  const size_t b_st_off = up(st_off.size() * sizeof(uint32_t));
+  const size_t b_load = col_load.size() * sizeof(uint64_t) + 8;
   void* mem = nullptr;
-  if (hipMalloc(&mem, b_image + b_off + b_st + b_run + b_st_off) != hipSuccess) return HBMC_ERR_NOMEM;
+  if (hipMalloc(&mem, b_image + b_off + b_st + b_run + b_st_off + b_load) != hipSuccess) return HBMC_ERR_NOMEM;
   char* base = static_cast<char*>(mem);
   if (hipMemcpy(base, host.data(), host.size() * sizeof(DevColChunk), hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(base + b_image, f.col_off.data(), f.col_off.size() * sizeof(uint32_t), hipMemcpyHostToDevice) !=
@@ -375,8 +388,10 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
                                     hipMemcpyHostToDevice) != hipSuccess) ||
       hipMemcpy(base + b_image + b_off + b_st, col_run.data(), col_run.size() * sizeof(uint32_t),
                 hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(base + b_image + b_off + b_st + b_run, st_off.data(), b_st_off, hipMemcpyHostToDevice) !=
-          hipSuccess) {
+      hipMemcpy(base + b_image + b_off + b_st + b_run, st_off.data(), st_off.size() * sizeof(uint32_t),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(base + b_image + b_off + b_st + b_run + b_st_off, col_load.data(),
+                col_load.size() * sizeof(uint64_t), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(mem);
     return HBMC_ERR_HIP;
   }
@@ -386,6 +401,7 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
   p->dev_stores = reinterpret_cast<DevColStore*>(base + b_image + b_off);
   p->dev_col_run = reinterpret_cast<uint32_t*>(base + b_image + b_off + b_st);
   p->dev_st_off = reinterpret_cast<uint32_t*>(base + b_image + b_off + b_st + b_run);
+  p->dev_col_load = reinterpret_cast<uint64_t*>(base + b_image + b_off + b_st + b_run + b_st_off);
   p->lds_meta_steps = meta_steps;
   p->lds_meta_whole = meta_whole;
   p->lds_stores = any_tail && uint64_t(P) * lds_slot_bytes(p->lds_col, e) + meta_whole <= per_block;
@@ -754,7 +770,8 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     describe_columns_lds(dtype, op, ptrs, p->dev_image, p->dev_lds_col_off, ncols, static_cast<uint32_t>(first),
                          static_cast<uint32_t>(last), phase, p->lds_col, count, static_cast<uint32_t>(P), meta,
                          lds_grid(ncols, shared), stores ? p->dev_stores : nullptr,
-                         stores ? p->dev_col_run : nullptr, stores ? p->dev_st_off : nullptr, &k);
+                         stores ? p->dev_col_run : nullptr, stores ? p->dev_st_off : nullptr,
+                         stores ? p->dev_col_load : nullptr, &k);
     if (shared > (64u << 10) &&
         hipFuncSetAttribute(k.func, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shared)) !=
             hipSuccess)

@@ -76,6 +76,7 @@ struct Plan {
   DevColStore* dev_stores = nullptr;
   uint32_t* dev_col_run = nullptr;
   uint32_t* dev_st_off = nullptr;
+  uint64_t* dev_col_load = nullptr;
   uint64_t lds_meta_steps = 0;
   uint64_t lds_meta_whole = 0;
   bool lds_stores = false;

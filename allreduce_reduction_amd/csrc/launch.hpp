@@ -149,6 +149,7 @@ struct KernelDesc {
   const DevColStore* stores = nullptr;
   const uint32_t* col_run = nullptr;
   const uint32_t* st_off = nullptr;
+  const uint64_t* col_load = nullptr;  // per column, the ranks whose copies are ever read
   uint32_t shared_bytes = 0;  // dynamic LDS per workgroup
   void* argv[16];  // filled by bind(); valid while this object lives
   void bind() {
@@ -181,6 +182,7 @@ struct KernelDesc {
       argv[11] = &stores;
       argv[12] = &col_run;
       argv[13] = &st_off;
+      argv[14] = &col_load;
     } else if (kind == kVectorArgs) {
       argv[0] = &flags;
       argv[1] = args;
@@ -213,14 +215,15 @@ uint64_t lds_bytes(int nranks, uint64_t col_elems, uint32_t e, uint64_t max_chun
 // workgroups, workgroup w running columns w, w + grid, ... of `col_elems`
 // elements (the last one cut at `count`); column g's chunk records are
 // image[col_off[g] .. col_off[g+1]).  With `stores` (a launch of all steps)
-// column g runs its first col_run[g] records and then its store records
-// stores[st_off[g] .. st_off[g+1]).  `meta_bytes`: the LDS after the rank
-// copies that the records of the largest column need.
+// column g loads the ranks in col_load[g], runs its first col_run[g] records
+// and then its store records stores[st_off[g] .. st_off[g+1]).
+// `meta_bytes`: the LDS after the rank copies that the records of the
+// largest column need.
 void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColChunk* image, const uint32_t* col_off,
                           uint32_t ncols, uint32_t s_lo, uint32_t s_hi, uint32_t phase, uint64_t col_elems,
                           uint64_t count, uint32_t nranks, uint64_t meta_bytes, uint32_t grid,
                           const DevColStore* stores, const uint32_t* col_run, const uint32_t* st_off,
-                          KernelDesc* k);
+                          const uint64_t* col_load, KernelDesc* k);
 
 // The single-workgroup kernel running `nsteps` steps of a plan.
 void describe_fused(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const FusedStep* steps,

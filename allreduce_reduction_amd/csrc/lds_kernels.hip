@@ -27,7 +27,8 @@
 // composes them into store records (DevColStore) that write each rank's
 // final bytes from the LDS copy holding them.  The bits are the same; the
 // column's chain of dependent chunk passes is shorter (ring: P - 1 instead
-// of 2 (P - 1)).
+// of 2 (P - 1)), and ranks that neither a remaining chunk nor a store record
+// reads are not loaded (a stand-alone all-gather loads only the owners).
 //
 // LDS layout (dynamic): nranks slots of slot_bytes (element col_begin + i of
 // rank r at slot r + phase + i*E, so LDS and global 16-byte phases agree),
@@ -256,7 +257,8 @@ __global__ void __launch_bounds__(kLdsMaxThreads)
 plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uint32_t* __restrict__ col_off,
                  uint32_t ncols, uint32_t s_lo, uint32_t s_hi, uint32_t phase, uint64_t col_elems, uint64_t count,
                  uint32_t nranks, uint32_t slot_bytes, const DevColStore* __restrict__ stores,
-                 const uint32_t* __restrict__ col_run, const uint32_t* __restrict__ st_off) {
+                 const uint32_t* __restrict__ col_run, const uint32_t* __restrict__ st_off,
+                 const uint64_t* __restrict__ col_load) {
   constexpr uint32_t E = Width<DT>::bytes;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   DevColChunk* meta = reinterpret_cast<DevColChunk*>(lds + nranks * slot_bytes);
@@ -279,7 +281,7 @@ plan_columns_lds(RankPtrs ptrs, const DevColChunk* __restrict__ image, const uin
       u32x4* sdst = reinterpret_cast<u32x4*>(meta + nk);
       for (uint32_t w = threadIdx.x; w < nst; w += 64) sdst[w] = ssrc[w];
     }
-    move_positions<DT, true>(lds, slot_bytes, ptrs, col_begin * E, all, nranks, phase, n);
+    move_positions<DT, true>(lds, slot_bytes, ptrs, col_begin * E, stores ? col_load[g] : all, nranks, phase, n);
     __syncthreads();
     uint64_t dirty = 0;
     for (uint32_t j = 0; j < nk; ++j) {
@@ -395,7 +397,7 @@ void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColC
                           uint32_t ncols, uint32_t s_lo, uint32_t s_hi, uint32_t phase, uint64_t col_elems,
                           uint64_t count, uint32_t nranks, uint64_t meta_bytes, uint32_t grid,
                           const DevColStore* stores, const uint32_t* col_run, const uint32_t* st_off,
-                          KernelDesc* k) {
+                          const uint64_t* col_load, KernelDesc* k) {
   const uint32_t e = dtype == kF32 || dtype == kI32 ? 4 : (dtype == kI8 ? 1 : 2);
   // every lane owns at most one 16-byte position of the column
   const bool one = (phase + col_elems * e + 15) / 16 <= lds_threads(col_elems, e);
@@ -424,6 +426,7 @@ void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColC
   k->stores = stores;
   k->col_run = col_run;
   k->st_off = st_off;
+  k->col_load = col_load;
   k->bind();
 }
 
