@@ -547,10 +547,10 @@ double longest_passes(const Schedule& s, uint64_t count, uint64_t col, size_t st
 // `longest` serial chunk passes in the busiest column (`share`: the
 // fraction of the schedule's busy steps the launch runs): the columns a
 // workgroup runs one after another, times those passes, times the 16-byte
-// positions each lane takes per chunk; plus loading and storing every rank
-// buffer.
+// positions each lane takes per chunk; plus moving `buffers` rank buffers'
+// worth of bytes (2 P: every rank loaded and stored).
 double lds_time(const ExecModel& m, int P, uint64_t count, uint32_t e, uint64_t col, uint64_t chunks,
-                double longest, double share) {
+                double longest, double share, double buffers) {
   const uint64_t ncols = (count + col - 1) / col;
   const uint32_t grid = lds_grid(static_cast<uint32_t>(std::min<uint64_t>(ncols, UINT32_MAX)),
                                  lds_bytes(P, col, e, chunks));
@@ -559,7 +559,7 @@ double lds_time(const ExecModel& m, int P, uint64_t count, uint32_t e, uint64_t 
   const uint64_t lanes = lds_threads(col, e);
   const double per_lane = std::ceil(double(positions) / lanes);
   return m.lds_us + rounds * longest * share * per_lane * m.lds_chunk_us +
-         2.0 * double(P) * double(count) * e / (m.lds_gbps * 1e3);
+         buffers * double(count) * e / (m.lds_gbps * 1e3);
 }
 
 }  // namespace
@@ -613,7 +613,7 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
       const uint64_t chunks = longest_column(p->sched, count, col);
       if (!fits(col, chunks)) continue;
       const double passes = whole_passes(col);
-      const double t = lds_time(c->model, P, count, e, col, chunks, passes, 1.0);
+      const double t = lds_time(c->model, P, count, e, col, chunks, passes, 1.0, 2.0 * P);
       if (p->lds_col == 0 || t < best * 0.98) {
         best = t;
         p->lds_col = col;
@@ -623,6 +623,9 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
       }
     }
   }
+  // a schedule of copies only (a stand-alone all-gather), composed: each
+  // column loads its owners' copies alone, about one rank buffer in all
+  p->lds_whole_buffers = body == 0 && whole_end(p->lds_col) == body ? P + 1.0 : 2.0 * P;
   p->lds_key = c->column_bytes;
   return HBMC_OK;
 }
@@ -691,7 +694,8 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     const bool all_steps = first == 0 && last == static_cast<int>(p->sched.steps.size());
     const double t = lds_time(m, P, count, e, p->lds_col, p->lds_chunks,
                               all_steps ? p->lds_longest_whole : p->lds_longest,
-                              all_steps ? 1.0 : double(busy) / std::max(1, busy_all));
+                              all_steps ? 1.0 : double(busy) / std::max(1, busy_all),
+                              all_steps ? p->lds_whole_buffers : 2.0 * P);
     if (t < best) {
       best = t;
       *mode = kExecLds;

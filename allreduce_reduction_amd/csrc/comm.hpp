@@ -65,6 +65,7 @@ struct Plan {
   uint64_t lds_chunks = 0;   // chunks of the longest column (its LDS records)
   double lds_longest = 0.0;  // serial chunk passes of the busiest column (for the cost model)
   double lds_longest_whole = 0.0;  // the same without the schedule's trailing copy steps
+  double lds_whole_buffers = 0.0;  // rank buffers' worth of bytes a launch of all steps moves
   ColumnTable lds_cols;
   void* lds_mem = nullptr;
   DevColChunk* dev_image = nullptr;
