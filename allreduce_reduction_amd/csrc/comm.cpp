@@ -229,9 +229,10 @@ namespace {
 void lds_limits(uint64_t* per_block, uint64_t* per_cu);
 
 // Trailing copy steps a column must have for its copies to be composed into
-// stores: fewer copy passes (RHD with 8 ranks: 3, in batches) cost about as
-// little as the store records that would replace them.
-constexpr uint32_t kMinStoreSteps = 4;
+// stores (measured on MI355X: with 3, RHD over 8 ranks at 4 MiB per rank
+// took 12.9 instead of 14.0 us per AllReduce and 9.1 instead of 15.0 us per
+// all-gather; at 1-64 KiB per rank no difference showed).
+constexpr uint32_t kMinStoreSteps = 3;
 
 // Bytes [lo, hi) of a column of one rank's final values come from the LDS
 // copy of rank `src`.

@@ -21,7 +21,7 @@
 // data) visible to every wave.
 //
 // In a launch of all of a call's steps, a column whose chunk list ends in
-// copies over four or more steps (the ring's all-gather, RHD's doubling and
+// copies over three or more steps (the ring's all-gather, RHD's doubling and
 // restore, a stand-alone all-gather) does not run those copies: they only
 // pass finished values from one rank's copy to another's, so the host
 // composes them into store records (DevColStore) that write each rank's

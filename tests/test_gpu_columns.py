@@ -196,7 +196,7 @@ COMPOSED = [  # trailing copy steps: ring 15, RHD 16 ranks 4, 17 ranks 5 (with t
 
 @pytest.mark.parametrize("case", COMPOSED, ids=[f"{c[0]}{c[1]}" for c in COMPOSED])
 def test_lds_composed_stores(case):
-    """LDS form, whole calls: columns whose chunk lists end in copies over four
+    """LDS form, whole calls: columns whose chunk lists end in copies over three
     or more steps store the copies' results directly instead of running them.
     Columns inside one segment, across two and across many (which keep their
     copies), ragged lengths, buffers on a shared non-zero 16-byte phase;
