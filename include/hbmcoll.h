@@ -37,6 +37,9 @@
  *     synchronises nothing; it only enqueues kernels on `stream`, so a caller
  *     may capture it into a graph (the first call of a shape, and the first in
  *     a new launch form or column length, must not be made while capturing).
+ *     A graph captured or built (hbmc_graph_build) before the column length
+ *     of one of its shapes changes refers to the freed tables: build or
+ *     capture it again after such a change.
  *   - count == 0 and P == 1 are valid and enqueue nothing.
  *   - No C++ exception leaves the library: a host allocation that fails while
  *     building schedules, tables or graphs returns HBMC_ERR_NOMEM, and the
