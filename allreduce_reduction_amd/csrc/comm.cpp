@@ -804,7 +804,9 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     L.write_bytes = 0;
     for (const Item& it : step.items) L.write_bytes += it.count * uint64_t(it.ndst) * elem_bytes(dtype);
     launches->emplace_back();
-    if (describe_step(L, ptrs, &launches->back()) != hipSuccess) return HBMC_ERR_HIP;
+    // describe_step calls no HIP function; it refuses only a step whose
+    // items exceed what one launch's grid can hold
+    if (describe_step(L, ptrs, &launches->back()) != hipSuccess) return HBMC_ERR_INVALID_ARG;
   }
   return HBMC_OK;
 }

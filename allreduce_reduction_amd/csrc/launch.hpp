@@ -130,6 +130,7 @@ struct KernelDesc {
     alignas(16) unsigned char args[kArgBytes];
   };
   const DevItem* items = nullptr;
+  uint32_t nitems = 0;               // step kernels: items of the step
   const FusedStep* steps = nullptr;  // plan kernel only
   uint32_t nsteps = 0;               // plan kernel only
   uint32_t phase = 0;
@@ -192,6 +193,7 @@ struct KernelDesc {
       argv[1] = &phase;
       argv[2] = &flags;
       argv[3] = &ptrs;
+      argv[4] = &nitems;
     }
   }
 };

@@ -1,5 +1,8 @@
 // gfx950 step kernels.  One launch executes one schedule step for all ranks:
-// grid.y indexes the step's work items, grid.x tiles an item's elements.  A
+// grid.x tiles an item's elements and grid.y indexes the step's work items;
+// a step of more items than grid.y may hold (the device reports 65536) also
+// spreads them over grid.z, item = z * grid.y + y, and the workgroups past
+// the last item return at once.  A
 // workgroup takes its item either from the plan's device item table
 // (step_vec: the item's rank numbers index the call's pointer table) or, for
 // steps of a few items, from the kernel arguments with its operand addresses
@@ -42,6 +45,12 @@ constexpr int kThreads = 64;        // vector kernel: one wave per workgroup
 constexpr int kVecPerThread = 1;    // 16-byte vectors per lane per operand
 constexpr uint64_t kTileVecs = uint64_t(kThreads) * kVecPerThread;
 constexpr int kElemThreads = 256;   // element-wise kernel
+// Items per grid row when a step's items do not fit grid.y alone (below the
+// device's reported grid.y and grid.z limits of 65536).
+constexpr uint32_t kGridRows = 32768;
+// Largest item a step kernel takes: grid.x times the workgroup size must stay
+// below 2^32 work-items, so at most 2^26 one-wave tiles of 1 KiB.
+constexpr uint64_t kMaxItemBytes = (uint64_t(1) << 26) * kTileVecs * 16;
 
 // Resident workgroups per compute unit for steps of many items whose
 // workgroups each keep many HBM streams open (the pipeline's steps: 512
@@ -193,9 +202,14 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
 // Vector kernel, items from the device table.
 template <int DT, int OP, int MODE, int NS, int ND, bool NT>
 __global__ void __launch_bounds__(kThreads)
-step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, RankPtrs ptrs) {
+step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, RankPtrs ptrs, uint32_t nitems) {
   uint32_t item = blockIdx.y, tile = blockIdx.x;
-  if (flags & kFlagXcdSplit) xcd_tile(&item, &tile);
+  if (gridDim.z > 1) {
+    item += blockIdx.z * gridDim.y;
+    if (item >= nitems) return;
+  } else if (flags & kFlagXcdSplit) {
+    xcd_tile(&item, &tile);
+  }
   const DevItem* it = items + item;
   const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
   const int nd = ND > 0 ? ND : static_cast<int>(it->ndst);
@@ -218,8 +232,10 @@ step_arg(uint32_t flags, ArgItems<NS + ND> args) {
 // Element-wise kernel for buffers whose 16-byte phases differ.
 template <int DT, int OP, int MODE>
 __global__ void __launch_bounds__(kElemThreads)
-step_elem(const DevItem* __restrict__ items, uint32_t, uint32_t, RankPtrs ptrs) {
-  const DevItem* it = items + blockIdx.y;
+step_elem(const DevItem* __restrict__ items, uint32_t, uint32_t, RankPtrs ptrs, uint32_t nitems) {
+  const uint32_t item = blockIdx.z * gridDim.y + blockIdx.y;
+  if (item >= nitems) return;
+  const DevItem* it = items + item;
   const uint64_t begin = it->begin, count = it->count;
   const int ns = static_cast<int>(it->nsrc), nd = static_cast<int>(it->ndst);
   const uint64_t stride = uint64_t(gridDim.x) * kElemThreads;
@@ -305,17 +321,26 @@ const void* arg_kernel(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k)
   return s.nsrc == 1 ? arg_items<DT, kSum, kCopy, 1, 1>(s, ptrs, k) : nullptr;
 }
 
+// Grid of `gx` tiles by `nitems` items: items along y, and along z as well
+// when there are more than kGridRows.
+dim3 item_grid(uint32_t gx, int nitems) {
+  const uint32_t n = static_cast<uint32_t>(nitems);
+  if (n <= kGridRows) return dim3(gx, n, 1);
+  return dim3(gx, kGridRows, (n + kGridRows - 1) / kGridRows);
+}
+
 template <int DT, int OP>
 void describe_typed(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
   constexpr uint32_t E = Width<DT>::bytes;
   k->ptrs = ptrs;
   k->items = s.items;
   k->phase = s.phase;
+  k->nitems = static_cast<uint32_t>(s.nitems);
   if (!s.aligned) {
     uint64_t gx = (s.max_count + kElemThreads - 1) / kElemThreads;
     if (gx > 2048) gx = 2048;
     if (gx < 1) gx = 1;
-    k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
+    k->grid = item_grid(static_cast<uint32_t>(gx), s.nitems);
     k->block = dim3(kElemThreads);
     k->kind = KernelDesc::kElement;
     switch (s.mode) {
@@ -329,9 +354,9 @@ void describe_typed(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
   // shortens the body); tile 0 of each item also takes the head and tail
   const uint64_t vecs = s.max_count * E / 16;
   const uint64_t gx = vecs > kTileVecs ? (vecs + kTileVecs - 1) / kTileVecs : 1;
-  k->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(s.nitems));
+  k->grid = item_grid(static_cast<uint32_t>(gx), s.nitems);
   k->block = dim3(kThreads);
-  k->flags = (s.xcd_split && (gx * s.nitems) % 8 == 0) ? kFlagXcdSplit : 0u;
+  k->flags = (s.xcd_split && k->grid.z == 1 && (gx * s.nitems) % 8 == 0) ? kFlagXcdSplit : 0u;
   if (const void* f = arg_kernel<DT, OP>(s, ptrs, k)) {
     k->kind = KernelDesc::kVectorArgs;
     k->func = f;
@@ -362,6 +387,11 @@ void describe_op(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
 hipError_t describe_step(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
   if (s.nitems <= 0) return hipErrorInvalidValue;
   if (s.ndst > 1 && s.mode != kCopy) return hipErrorInvalidValue;  // no such schedule step
+  // grid.x * workgroup size must stay below 2^32 work-items: at most 2^26
+  // one-wave tiles of 1 KiB, i.e. items of at most 64 GiB
+  const uint32_t e = s.dtype == kF32 || s.dtype == kI32 ? 4u : (s.dtype == kI8 ? 1u : 2u);
+  if (s.max_count > kMaxItemBytes / e) return hipErrorInvalidValue;
+  if (static_cast<uint64_t>(s.nitems) > uint64_t(kGridRows) * kGridRows) return hipErrorInvalidValue;
   switch (s.dtype) {
     case kF32: describe_op<kF32>(s, ptrs, k); break;
     case kF16: describe_op<kF16>(s, ptrs, k); break;
