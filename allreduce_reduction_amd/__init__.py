@@ -18,7 +18,8 @@ STATUS = {0: "HBMC_OK", 1: "HBMC_ERR_INVALID_ARG", 2: "HBMC_ERR_UNSUPPORTED", 3:
 DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2, "int32": 3, "int8": 4}
 ESIZE = {"fp32": 4, "fp16": 2, "bf16": 2, "int32": 4, "int8": 1}
 OP = {"sum": 0, "prod": 1, "max": 2, "min": 3}
-ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3, "flat": 4, "tree": 5, "hier": 6, "auto": 7}
+ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3, "flat": 4, "tree": 5, "hier": 6, "auto": 7,
+        "auto_rules": 8}
 ALGO_NAME = {v: k for k, v in ALGO.items()}
 COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 MODE = {0: "copy", 1: "fold", 2: "recv_fold"}

@@ -31,6 +31,7 @@ hbmc_status_t comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_p
     else if (v == "tree") a = HBMC_ALGO_TREE;
     else if (v == "hier") a = HBMC_ALGO_HIER;
     else if (v == "auto") a = HBMC_ALGO_AUTO;
+    else if (v == "auto_rules") a = HBMC_ALGO_AUTO_RULES;
     else return HBMC_ERR_INVALID_ARG;
   }
   Topology t;
@@ -76,13 +77,22 @@ hbmc_status_t comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_p
       }
       break;
     }
+    case HBMC_ALGO_AUTO_RULES:
+      // the rules pick among these three, by index (see choose_topology)
+      for (Algo al : {kRing, kRhd, kFlat}) {
+        Topology c = t;
+        c.algo = al;
+        topos.push_back(c);
+      }
+      break;
     default: return HBMC_ERR_INVALID_ARG;
   }
   if (topos.empty()) topos.push_back(t);
   std::unique_ptr<hbmc_comm> c(new (std::nothrow) hbmc_comm);
   if (!c) return HBMC_ERR_NOMEM;
   c->topos = topos;
-  c->auto_select = a == HBMC_ALGO_AUTO;
+  c->auto_select = a == HBMC_ALGO_AUTO || a == HBMC_ALGO_AUTO_RULES;
+  c->auto_rules = a == HBMC_ALGO_AUTO_RULES;
   if (const char* fl = std::getenv("HBMC_FUSED_LIMIT")) c->fused_limit = std::strtoull(fl, nullptr, 10);
   if (const char* cl = std::getenv("HBMC_COLUMNS_LIMIT")) c->columns_limit = std::strtoull(cl, nullptr, 10);
   if (const char* ex = std::getenv("HBMC_EXEC")) {
@@ -184,6 +194,8 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
     if (kv.second->dev && hipFree(kv.second->dev) != hipSuccess) st = HBMC_ERR_HIP;
     if (kv.second->cols_mem && hipFree(kv.second->cols_mem) != hipSuccess) st = HBMC_ERR_HIP;
     if (kv.second->lds_mem && hipFree(kv.second->lds_mem) != hipSuccess) st = HBMC_ERR_HIP;
+    for (void* m : kv.second->retired)
+      if (hipFree(m) != hipSuccess) st = HBMC_ERR_HIP;
   }
   delete comm;
   return st;

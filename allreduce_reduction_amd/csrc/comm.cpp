@@ -81,6 +81,15 @@ hbmc_status_t choose_topology(hbmc_comm* c, int coll, int root, size_t count, in
     *index = 0;
     return HBMC_OK;
   }
+  if (c->auto_rules) {
+    // topos: 0 ring, 1 RHD, 2 Flat
+    const int P = c->topos[0].P;
+    const bool pow2 = (P & (P - 1)) == 0;
+    if (coll == HBMC_COLL_ALLREDUCE && uint64_t(count) * elem_bytes(dtype) < kFlatRuleBytes) *index = 2;
+    else if (coll == HBMC_COLL_REDUCE || coll == HBMC_COLL_BROADCAST) *index = 1;
+    else *index = pow2 ? 1 : 0;
+    return HBMC_OK;
+  }
   auto key = std::make_tuple(coll, root, static_cast<uint64_t>(count), dtype);
   auto it = c->chosen.find(key);
   if (it != c->chosen.end()) {
@@ -178,8 +187,9 @@ uint64_t column_elems(uint64_t column_bytes, uint64_t count, uint32_t e, uint32_
 hbmc_status_t column_table(Plan* p, int P, uint64_t chunk_elems, const ColumnTable** out) {
   if (p->cols.chunk_elems != chunk_elems || p->cols.col_off.empty()) {
     if (p->cols_mem) {
-      // the device copy belongs to the old length
-      if (hipDeviceSynchronize() != hipSuccess || hipFree(p->cols_mem) != hipSuccess) return HBMC_ERR_HIP;
+      // the device copy belongs to the old length; launches already enqueued
+      // and graphs built earlier may still read it
+      p->retired.push_back(p->cols_mem);
       p->cols_mem = nullptr;
     }
     if (!build_columns(p->sched, P, chunk_elems, false, &p->cols)) return HBMC_ERR_INVALID_ARG;
@@ -568,8 +578,9 @@ double lds_time(const ExecModel& m, int P, uint64_t count, uint32_t e, uint64_t 
 hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t e) {
   if (p->lds_key == c->column_bytes) return HBMC_OK;
   if (p->lds_mem) {
-    // the device tables belong to the old length
-    if (hipDeviceSynchronize() != hipSuccess || hipFree(p->lds_mem) != hipSuccess) return HBMC_ERR_HIP;
+    // the device tables belong to the old length; launches already enqueued
+    // and graphs built earlier may still read them
+    p->retired.push_back(p->lds_mem);
     p->lds_mem = nullptr;
   }
   uint64_t per_block = 0, per_cu = 0;

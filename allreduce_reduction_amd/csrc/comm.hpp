@@ -81,6 +81,10 @@ struct Plan {
   uint64_t lds_meta_steps = 0;
   uint64_t lds_meta_whole = 0;
   bool lds_stores = false;
+  // device tables of earlier column lengths: graphs built or captured before
+  // the length changed still point at them, so they are kept until the
+  // communicator is destroyed
+  std::vector<void*> retired;
 };
 
 }  // namespace hbmc
@@ -89,6 +93,7 @@ struct hbmc_comm {
   // One topology, or for AUTO the candidates the cost model chooses among.
   std::vector<hbmc::Topology> topos;
   bool auto_select = false;
+  bool auto_rules = false;    // AUTO_RULES: topos = {ring, RHD, Flat}, picked by the pages' rules
   double alpha_us = 4.4;      // launch-to-launch cost of one step, measured eager on MI355X
   double beta_gbps = 6400.0;  // sustained HBM rate of the step kernels, measured
   int exec_mode = hbmc::kExecAuto;
@@ -114,6 +119,10 @@ namespace hbmc {
 hbmc_status_t get_plan(hbmc_comm* c, int coll, int root, size_t count, int dtype, Plan** out);
 // AUTO: index into c->topos of the candidate with the least modelled time
 // steps * alpha + hbm_bytes / beta (ties: fewer steps, then lower index).
+// AUTO_RULES: Flat for an AllReduce below kFlatRuleBytes per rank, else RHD
+// when P is a power of two and the ring otherwise; RHD for Reduce and
+// Broadcast.
+constexpr uint64_t kFlatRuleBytes = uint64_t(64) << 10;
 hbmc_status_t choose_topology(hbmc_comm* c, int coll, int root, size_t count, int dtype, int* index);
 // Copy the plan's item table to the current device (once per plan).
 hbmc_status_t upload(Plan* p);
@@ -137,8 +146,7 @@ uint64_t column_elems(uint64_t column_bytes, uint64_t count, uint32_t e, uint32_
 // once per length, without dependency lists).
 hbmc_status_t column_table(Plan* p, int P, uint64_t chunk_elems, const ColumnTable** out);
 // Upload the plan's column table to the current device (again after the
-// column length changed; the old tables are freed after a device
-// synchronisation).
+// column length changed; the old tables are retired, not freed).
 hbmc_status_t upload_columns(Plan* p);
 // Column length of the LDS-resident column kernel for plan p (P ranks, count
 // elements of e bytes), cached in the plan: the communicator's column_bytes

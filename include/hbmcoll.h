@@ -28,19 +28,17 @@
  *   - The first call of a (collective, root, count, dtype) builds its schedule
  *     and uploads its device tables with hipMalloc and blocking copies (and
  *     so does the first call in the LDS or column form, and one after the
- *     column length changes, which also synchronises the device before
- *     freeing the old tables); later calls with the same shape only enqueue
- *     kernels.  Tables live on the device current at that first call: a
+ *     column length changes; the tables of the earlier length are kept until
+ *     hbmc_comm_destroy, so launches still queued and graphs built or
+ *     captured before the change stay valid); later calls with the same
+ *     shape only enqueue kernels.  Tables live on the device current at that first call: a
  *     communicator serves one device, and a call made with another device
  *     current returns HBMC_ERR_INVALID_ARG.  Cached schedules are kept until
  *     hbmc_comm_destroy.  A later call of a cached shape allocates, copies and
  *     synchronises nothing; it only enqueues kernels on `stream`, so a caller
  *     may capture it into a graph (the first call of a shape, and the first in
  *     a new launch form or column length, must not be made while capturing).
- *     A graph captured or built (hbmc_graph_build) before the column length
- *     of one of its shapes changes refers to the freed tables: build or
- *     capture it again after such a change.
- *   - count == 0 and P == 1 are valid and enqueue nothing.
+ * *   - count == 0 and P == 1 are valid and enqueue nothing.
  *   - No C++ exception leaves the library: a host allocation that fails while
  *     building schedules, tables or graphs returns HBMC_ERR_NOMEM, and the
  *     communicator (or graph) stays usable, with nothing half-built cached.
@@ -88,10 +86,17 @@ typedef enum { HBMC_SUM = 0, HBMC_PROD = 1, HBMC_MAX = 2, HBMC_MIN = 3 } hbmc_op
  * intra-server reduce-scatter, inter-server ring AllReduce, intra-server
  * all-gather, not pipelined ([PIPE] "与其它分级算法的关系").  FLAT, TREE and
  * HIER offer AllReduce only.  AUTO: per call, the candidate schedule with
- * the least modelled time (see hbmc_comm_set_cost_model).  ENV: take the
+ * the least modelled time (see hbmc_comm_set_cost_model).  AUTO_RULES: per
+ * call, the pages' default rules instead of the cost model: an AllReduce of
+ * fewer than 64 KiB per rank takes Flat ([TOPO] "拓扑感知路由": below the
+ * 64 KB threshold every device talks to the root directly); otherwise RHD
+ * when P is a power of two and the ring when it is not ([RHD] "RHD 在 HCCL
+ * 中的定位与启用方式": ring by default for a rank count that is not a power
+ * of two, H-D_R otherwise); Reduce and Broadcast take RHD.  ENV: take the
  * algorithm from the environment variable HBMC_ALGO ("ring", "rhd" or
- * "H-D_R", "pipeline", "flat", "tree", "hier", "auto"), the way the pages'
- * HCCL_ALGO selects an algorithm ([RHD] "RHD 在 HCCL 中的定位与启用方式"). */
+ * "H-D_R", "pipeline", "flat", "tree", "hier", "auto", "auto_rules"), the
+ * way the pages' HCCL_ALGO selects an algorithm ([RHD] "RHD 在 HCCL 中的定位
+ * 与启用方式"). */
 typedef enum {
   HBMC_ALGO_RING = 0,
   HBMC_ALGO_RHD = 1,
@@ -100,7 +105,8 @@ typedef enum {
   HBMC_ALGO_FLAT = 4,
   HBMC_ALGO_TREE = 5,
   HBMC_ALGO_HIER = 6,
-  HBMC_ALGO_AUTO = 7
+  HBMC_ALGO_AUTO = 7,
+  HBMC_ALGO_AUTO_RULES = 8
 } hbmc_algo_t;
 
 typedef enum {
@@ -200,8 +206,10 @@ hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
  * (ties: fewer launches), caching the choice.  Defaults are this library's
  * measurements on MI355X: alpha = 4.4 us per step launch, beta = 6400 GB/s.
  * hbmc_comm_set_cost_model replaces alpha (us, >= 0) and beta (GB/s, > 0)
- * and forgets earlier choices; hbmc_auto_choice reports the algorithm a call
- * would use (for any communicator: its own algorithm).  Host only.
+ * and forgets earlier choices (an AUTO_RULES communicator accepts it and
+ * keeps its rules); hbmc_auto_choice reports the algorithm a call would use
+ * (for any communicator: its own algorithm; for AUTO_RULES: the rules'
+ * pick).  Host only.
  */
 hbmc_status_t hbmc_comm_set_cost_model(hbmc_comm_t comm, double alpha_us, double beta_gbps);
 hbmc_status_t hbmc_auto_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,

@@ -132,3 +132,43 @@ def test_graph_on_a_side_stream():
             s.synchronize()
         for r in range(P):
             assert np.array_equal(to_host(bufs[r], dtype).view(np.uint32), want[r].view(np.uint32))
+
+
+@pytest.mark.parametrize("form", ["lds", "columns"])
+def test_graph_survives_a_column_length_change(form):
+    """A graph built in a one-launch form keeps the device tables of its column
+    length: after the communicator's column length changes and an eager call
+    builds the tables of the new length, replays of the old graph still match
+    the oracle bit for bit, and so do eager calls at the new length."""
+    import oracle
+    P, L, dtype = 8, 40_000 + 3, "bf16"
+    xs = inputs(P, L, dtype, seed=11)
+    expect = [x.copy() for x in xs]
+    oracle.run("allreduce", "ring", expect, dtype, "sum")
+    with hc.Comm(P, "ring") as comm:
+        comm.set_exec_mode(form)
+        comm.set_columns(64 << 20, 4096)
+        assert comm.exec_choice("allreduce", L, dtype) == form
+        bufs = [to_dev(x, dtype) for x in xs]
+        with hc.Graph() as g:
+            g.add(comm, "allreduce", bufs, dtype, "sum")
+            g.build()
+            g.launch()
+            torch.cuda.synchronize()
+            for r in range(P):
+                refops.assert_same(dtype, to_host(bufs[r], dtype), expect[r], f"first replay rank {r}")
+            # a new column length: the next eager call builds new tables
+            comm.set_columns(64 << 20, 1024)
+            other = [to_dev(x, dtype) for x in xs]
+            comm.allreduce(other, dtype, "sum")
+            torch.cuda.synchronize()
+            for r in range(P):
+                refops.assert_same(dtype, to_host(other[r], dtype), expect[r], f"new length rank {r}")
+            for rep in range(3):
+                for b, x in zip(bufs, xs):
+                    b.copy_(to_dev(x, dtype))
+                torch.cuda.synchronize()
+                g.launch()
+                torch.cuda.synchronize()
+                for r in range(P):
+                    refops.assert_same(dtype, to_host(bufs[r], dtype), expect[r], f"replay {rep} rank {r}")

@@ -331,6 +331,40 @@ def test_auto_defaults_on_one_gpu():
     assert lib.hbmc_comm_create(8, 7, 3, 3, 0, ctypes.byref(h)) == 1  # bad server shape
 
 
+@pytest.mark.parametrize("P", [2, 4, 5, 6, 8, 12, 16, 32])
+def test_auto_rules_follow_the_pages_defaults(P, monkeypatch):
+    """AUTO_RULES: an AllReduce below 64 KiB per rank takes Flat ([TOPO] 64 KB
+    threshold); otherwise RHD (H-D_R) for a power-of-two rank count and the
+    ring for any other ([RHD] default algorithm rule); Reduce / Broadcast RHD.
+    The pick's schedule is the explicit communicator's, item for item."""
+    pow2 = (P & (P - 1)) == 0
+    big = "rhd" if pow2 else "ring"
+    with hc.Comm(P, "auto_rules") as a:
+        for dtype, e in (("fp32", 4), ("bf16", 2), ("int8", 1)):
+            below, at = (64 << 10) // e - 1, (64 << 10) // e
+            assert a.auto_choice("allreduce", below, dtype) == "flat"
+            assert a.auto_choice("allreduce", 1, dtype) == "flat"
+            assert a.auto_choice("allreduce", at, dtype) == big
+            assert a.auto_choice("allreduce", 1 << 24, dtype) == big
+            for coll in ("reduce_scatter", "all_gather"):
+                assert a.auto_choice(coll, below, dtype) == big
+                assert a.auto_choice(coll, 1 << 20, dtype) == big
+            assert a.auto_choice("reduce", 1000, dtype, root=P - 1) == "rhd"
+            assert a.auto_choice("broadcast", 1 << 20, dtype, root=0) == "rhd"
+        # the cost model does not move the rules
+        a.set_cost_model(0.0, 1.0)
+        assert a.auto_choice("allreduce", 1 << 24, "fp32") == big
+        for coll, count, name in (("allreduce", 100, "flat"), ("allreduce", 1 << 16, big),
+                                  ("reduce_scatter", 1 << 16, big)):
+            with hc.Comm(P, name) as c:
+                assert a.plan_items(coll, count, "fp32") == c.plan_items(coll, count, "fp32")
+                assert a.plan_info(coll, count, "fp32") == c.plan_info(coll, count, "fp32")
+    monkeypatch.setenv("HBMC_ALGO", "auto_rules")
+    with hc.Comm(P, "env") as c:
+        assert c.auto_choice("allreduce", 1 << 20, "fp32") == big
+        assert c.auto_choice("allreduce", 16, "fp32") == "flat"
+
+
 def test_out_of_place_validation_without_device():
     lib = hc.load_library()
     P = 4
