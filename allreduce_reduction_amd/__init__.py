@@ -32,7 +32,7 @@ EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_redu
            "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy", "hbmc_comm_set_cost_model",
            "hbmc_auto_choice", "hbmc_comm_set_fused_limit",
            "hbmc_comm_set_columns", "hbmc_plan_chunks",
-           "hbmc_comm_set_exec_mode", "hbmc_exec_choice")
+           "hbmc_comm_set_exec_mode", "hbmc_exec_choice", "hbmc_exec_bytes")
 
 
 class HbmcError(RuntimeError):
@@ -112,6 +112,8 @@ def load_library():
         L.hbmc_comm_set_exec_mode.argtypes = [vp, ci]
         L.hbmc_exec_choice.restype = ci
         L.hbmc_exec_choice.argtypes = [vp, ci, ci, sz, ci, ci, ci, ctypes.POINTER(ci)]
+        L.hbmc_exec_bytes.restype = ci
+        L.hbmc_exec_bytes.argtypes = [vp, ci, ci, sz, ci, ci, ci, ci, u64p]
         L.hbmc_comm_set_cost_model.restype = ci
         L.hbmc_comm_set_cost_model.argtypes = [vp, ctypes.c_double, ctypes.c_double]
         L.hbmc_auto_choice.restype = ci
@@ -271,6 +273,15 @@ class Comm:
         _check(load_library().hbmc_exec_choice(self._h, COLL[coll], root, count, DTYPE[dtype], first, last,
                                                ctypes.byref(m)), "hbmc_exec_choice")
         return {v: k for k, v in EXEC.items()}[m.value]
+
+    def exec_bytes(self, coll: str, count: int, dtype: str, mode: str = "auto", root: int = 0,
+                   first: int = 0, last: int = 0) -> int:
+        """Bytes a call (or steps [first, last)) moves to and from memory in a
+        launch form (see hbmc_exec_bytes), host only."""
+        b = ctypes.c_uint64()
+        _check(load_library().hbmc_exec_bytes(self._h, COLL[coll], root, count, DTYPE[dtype], first, last,
+                                              EXEC[mode], ctypes.byref(b)), "hbmc_exec_bytes")
+        return b.value
 
     def set_fused_limit(self, max_bytes: int):
         """Single-workgroup form eligible for calls moving at most max_bytes."""

@@ -160,6 +160,28 @@ hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
   });
 }
 
+hbmc_status_t hbmc_exec_bytes(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
+                              int first_step, int last_step, hbmc_exec_t mode, uint64_t* bytes) {
+  return no_throw([&]() -> hbmc_status_t {
+    if (!bytes || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_LDS) return HBMC_ERR_INVALID_ARG;
+    Plan* p = nullptr;
+    hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+    if (st != HBMC_OK) return st;
+    const int nsteps = static_cast<int>(p->sched.steps.size());
+    if (first_step == 0 && last_step == 0) last_step = nsteps;
+    if (first_step < 0 || last_step > nsteps || first_step > last_step) return HBMC_ERR_INVALID_ARG;
+    int m = static_cast<int>(mode);
+    if (m == kExecAuto) {
+      m = kExecSteps;
+      if (count > 0 && comm->topos[0].P > 1 && first_step < last_step) {
+        st = choose_exec(comm, p, first_step, last_step, count, elem_bytes(dtype), true, &m);
+        if (st != HBMC_OK) return st;
+      }
+    }
+    return exec_bytes(comm, p, first_step, last_step, count, elem_bytes(dtype), m, bytes);
+  });
+}
+
 hbmc_status_t hbmc_comm_set_cost_model(hbmc_comm_t comm, double alpha_us, double beta_gbps) {
   if (!comm || !(alpha_us >= 0.0) || !(beta_gbps > 0.0)) return HBMC_ERR_INVALID_ARG;
   comm->alpha_us = alpha_us;

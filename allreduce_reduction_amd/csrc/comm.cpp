@@ -268,14 +268,15 @@ void replace_range(std::vector<Piece>& pieces, uint32_t lo, uint32_t hi, const s
 
 }  // namespace
 
-hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
-  if (p->lds_mem) return HBMC_OK;
+hbmc_status_t lds_host_tables(Plan* p, int P, uint64_t count, uint32_t e) {
+  if (p->lh.built_col == p->lds_col && p->lds_col > 0) return HBMC_OK;
   if (p->lds_cols.chunk_elems != p->lds_col || p->lds_cols.col_off.empty())
     if (!build_columns(p->sched, P, p->lds_col, false, &p->lds_cols)) return HBMC_ERR_INVALID_ARG;
   const ColumnTable& f = p->lds_cols;
   const size_t n = f.col_list.size();
   const size_t ncols = f.col_off.size() - 1;
-  std::vector<DevColChunk> host(n + 1);
+  std::vector<DevColChunk>& host = p->lh.image;
+  host.assign(n + 1, DevColChunk{});
   std::memset(host.data(), 0, host.size() * sizeof(DevColChunk));
   for (size_t g = 0; g < ncols; ++g) {
     const uint64_t col_begin = uint64_t(g) * f.chunk_elems;
@@ -318,10 +319,15 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
   // store records.  Every rank starts as its own source; a copy chunk gives
   // each destination, over the chunk's range, the sources its source has
   // there.  Every rank some chunk of the column writes is stored.
-  std::vector<DevColStore> stores;
-  std::vector<uint32_t> col_run(ncols), st_off(ncols + 1, 0);
+  std::vector<DevColStore>& stores = p->lh.stores;
+  std::vector<uint32_t>& col_run = p->lh.col_run;
+  std::vector<uint32_t>& st_off = p->lh.st_off;
+  stores.clear();
+  col_run.assign(ncols, 0);
+  st_off.assign(ncols + 1, 0);
   const uint64_t all_ranks = P >= 64 ? ~uint64_t(0) : ((uint64_t(1) << P) - 1);
-  std::vector<uint64_t> col_load(ncols, all_ranks);
+  std::vector<uint64_t>& col_load = p->lh.col_load;
+  col_load.assign(ncols, all_ranks);
   std::vector<std::vector<Piece>> map(P);
   std::vector<Piece> part, tmp;
   uint64_t meta_steps = 0, meta_whole = 0;
@@ -379,8 +385,27 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
     meta_whole = std::max<uint64_t>(meta_whole, uint64_t(cut - k0) * sizeof(DevColChunk) +
                                                     uint64_t(st_off[g + 1] - st_off[g]) * sizeof(DevColStore));
   }
+  p->lh.meta_steps = meta_steps;
+  p->lh.meta_whole = meta_whole;
+  p->lh.any_tail = any_tail;
   uint64_t per_block = 0, per_cu = 0;
   lds_limits(&per_block, &per_cu);
+  p->lh.stores_fit = any_tail && uint64_t(P) * lds_slot_bytes(p->lds_col, e) + meta_whole <= per_block;
+  p->lh.built_col = p->lds_col;
+  return HBMC_OK;
+}
+
+hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
+  if (p->lds_mem) return HBMC_OK;
+  hbmc_status_t hs = lds_host_tables(p, P, count, e);
+  if (hs != HBMC_OK) return hs;
+  const ColumnTable& f = p->lds_cols;
+  const std::vector<DevColChunk>& host = p->lh.image;
+  const std::vector<DevColStore>& stores = p->lh.stores;
+  const std::vector<uint32_t>& col_run = p->lh.col_run;
+  const std::vector<uint32_t>& st_off = p->lh.st_off;
+  const std::vector<uint64_t>& col_load = p->lh.col_load;
+  const uint64_t meta_steps = p->lh.meta_steps, meta_whole = p->lh.meta_whole;
 
   auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
   const size_t b_image = up(host.size() * sizeof(DevColChunk));
@@ -415,7 +440,7 @@ hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e) {
   p->dev_col_load = reinterpret_cast<uint64_t*>(base + b_image + b_off + b_st + b_run + b_st_off);
   p->lds_meta_steps = meta_steps;
   p->lds_meta_whole = meta_whole;
-  p->lds_stores = any_tail && uint64_t(P) * lds_slot_bytes(p->lds_col, e) + meta_whole <= per_block;
+  p->lds_stores = p->lh.stores_fit;
   return HBMC_OK;
 }
 
@@ -711,6 +736,78 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     if (t < best) {
       best = t;
       *mode = kExecLds;
+    }
+  }
+  return HBMC_OK;
+}
+
+namespace {
+
+// Length of the union of half-open ranges (sorted in place).
+uint64_t union_length(std::vector<std::pair<uint64_t, uint64_t>>& v) {
+  std::sort(v.begin(), v.end());
+  uint64_t total = 0, lo = 0, hi = 0;
+  bool open = false;
+  for (const auto& r : v) {
+    if (open && r.first <= hi) {
+      hi = std::max(hi, r.second);
+      continue;
+    }
+    if (open) total += hi - lo;
+    lo = r.first;
+    hi = r.second;
+    open = true;
+  }
+  if (open) total += hi - lo;
+  return total;
+}
+
+}  // namespace
+
+hbmc_status_t exec_bytes(hbmc_comm* c, Plan* p, int first, int last, uint64_t count, uint32_t e, int mode,
+                         uint64_t* bytes) {
+  const int P = c->topos[0].P;
+  *bytes = 0;
+  if (count == 0 || P == 1) return HBMC_OK;
+  if (mode == kExecSteps) {
+    for (int s = first; s < last; ++s) *bytes += p->sched.steps[s].hbm_bytes;
+    return HBMC_OK;
+  }
+  if (mode == kExecFused || mode == kExecColumns) {
+    // each rank's elements read by some step once, and those written once
+    std::vector<std::vector<std::pair<uint64_t, uint64_t>>> rd(P), wr(P);
+    for (int s = first; s < last; ++s)
+      for (const Item& it : p->sched.steps[s].items) {
+        for (int q = 0; q < it.nsrc; ++q) rd[it.rank[q]].emplace_back(it.begin, it.begin + it.count);
+        for (int q = it.nsrc; q < it.nsrc + it.ndst; ++q) wr[it.rank[q]].emplace_back(it.begin, it.begin + it.count);
+      }
+    for (int r = 0; r < P; ++r) *bytes += (union_length(rd[r]) + union_length(wr[r])) * e;
+    return HBMC_OK;
+  }
+  if (mode != kExecLds) return HBMC_ERR_INVALID_ARG;
+  hbmc_status_t st = lds_layout(c, p, P, count, e);
+  if (st != HBMC_OK) return st;
+  if (p->lds_col == 0) return HBMC_ERR_INVALID_ARG;
+  st = lds_host_tables(p, P, count, e);
+  if (st != HBMC_OK) return st;
+  const LdsHost& h = p->lh;
+  const ColumnTable& f = p->lds_cols;
+  const size_t ncols = f.col_off.size() - 1;
+  const bool stores = h.stores_fit && first == 0 && last == static_cast<int>(p->sched.steps.size());
+  for (size_t g = 0; g < ncols; ++g) {
+    const uint64_t nbytes = std::min<uint64_t>(p->lds_col, count - uint64_t(g) * p->lds_col) * e;
+    const uint32_t k0 = f.col_off[g];
+    const uint32_t k1 = stores ? k0 + h.col_run[g] : f.col_off[g + 1];
+    const uint32_t nst = stores ? h.st_off[g + 1] - h.st_off[g] : 0;
+    const uint64_t loaded = stores ? h.col_load[g] : (P >= 64 ? ~uint64_t(0) : (uint64_t(1) << P) - 1);
+    *bytes += uint64_t(__builtin_popcountll(loaded)) * nbytes;
+    if (nst > 0) {
+      for (uint32_t i = h.st_off[g]; i < h.st_off[g + 1]; ++i) *bytes += h.stores[i].hi - h.stores[i].lo;
+    } else {
+      uint64_t dirty = 0;
+      for (uint32_t k = k0; k < k1; ++k)
+        if (h.image[k].step >= uint32_t(first) && h.image[k].step < uint32_t(last)) dirty |= h.image[k].dst_mask;
+      *bytes += uint64_t(__builtin_popcountll(dirty)) * nbytes;
     }
   }
   return HBMC_OK;

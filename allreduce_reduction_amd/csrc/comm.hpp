@@ -42,6 +42,21 @@ uint32_t elem_bytes(int dtype);
 bool valid_coll(int c);
 bool valid_op(int op);
 
+// The LDS-resident column kernel's tables on the host, for the column
+// length `built_col` (see upload_lds_tables): chunk records column after
+// column, store records, per column the records run before the stores, the
+// store records' offsets and the ranks loaded; the LDS their records need.
+struct LdsHost {
+  uint64_t built_col = 0;
+  std::vector<DevColChunk> image;
+  std::vector<DevColStore> stores;
+  std::vector<uint32_t> col_run, st_off;
+  std::vector<uint64_t> col_load;
+  uint64_t meta_steps = 0, meta_whole = 0;
+  bool any_tail = false;
+  bool stores_fit = false;  // launches of all steps use the store records
+};
+
 // A cached schedule and its device item table (uploaded on first use).
 struct Plan {
   Schedule sched;
@@ -67,6 +82,7 @@ struct Plan {
   double lds_longest_whole = 0.0;  // the same without the schedule's trailing copy steps
   double lds_whole_buffers = 0.0;  // rank buffers' worth of bytes a launch of all steps moves
   ColumnTable lds_cols;
+  LdsHost lh;
   void* lds_mem = nullptr;
   DevColChunk* dev_image = nullptr;
   uint32_t* dev_lds_col_off = nullptr;
@@ -161,6 +177,12 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
 // the number of chunks before the column's trailing copies and the store
 // records those copies compose into (see DevColStore).
 hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e);
+// The same tables built on the host only (p->lh), once per column length.
+hbmc_status_t lds_host_tables(Plan* p, int P, uint64_t count, uint32_t e);
+// Bytes a launch of steps [first, last) in form `mode` moves between the
+// compute units and memory (see hbmc_exec_bytes).
+hbmc_status_t exec_bytes(hbmc_comm* c, Plan* p, int first, int last, uint64_t count, uint32_t e, int mode,
+                         uint64_t* bytes);
 // Launch form of steps [first, last) of plan `p` (count elements of e bytes,
 // buffers of one 16-byte phase when `aligned`): the communicator's mode when
 // not AUTO and the form is eligible; for AUTO the eligible form of least

@@ -16,9 +16,15 @@ Reported (one JSON line):
              the launch stream around the P-1 back-to-back reduce-scatter
              launches (copy_step: the same for the all-gather launches); a
              pass with an event between every two steps is reported beside it
-  cpu_baseline  the CPU oracle replaying the same AllReduce (single thread)
+  cpu_baseline  the CPU oracle replaying the same AllReduce on the host:
+             `value` from its windowed replay on T threads (disjoint element
+             ranges side by side, T = the CPUs this process may use, at most
+             16), `single_thread` from the one-thread replay; the host's CPU
+             model and counts beside them
   auto_allreduce_same_workload  not the headline: the AUTO communicator's
-             AllReduce of the same buffers (its cost model picks Flat)
+             AllReduce of the same buffers (its cost model picks Flat, which
+             moves (2P+1) D bytes in 2 launches; the ring's bus factor does not
+             apply to it, so it reports algbw and its own %HBM only)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --suite    (one JSON line per other workload: RHD small
@@ -177,8 +183,11 @@ def suite(a):
                                 g10.add(c, "allreduce", bufs, dtype, op)
                             g10.build()
                             tg10 = time_calls(lambda: g10.launch(), 50, 5) / 10
+                    moved = c.exec_bytes("allreduce", L, dtype, form)
                     emit(workload="rhd_small", algo="rhd", coll="allreduce", P=P, dtype=dtype, op=op,
-                         bytes_per_rank=L * e, launch_form=form, us=round(t * 1e6, 2), cold_us=round(t_cold * 1e6, 2),
+                         bytes_per_rank=L * e, launch_form=form, moved_bytes=moved,
+                         pct_hbm_moved=round(100 * moved / t / HBM_PEAK, 2),
+                         us=round(t * 1e6, 2), cold_us=round(t_cold * 1e6, 2),
                          steps=n,
                          us_per_step=round(t * 1e6 / n, 2), one_launch_per_step_us=round(t_steps * 1e6, 2),
                          one_launch_per_step_us_per_step=round(t_steps * 1e6 / n, 2),
@@ -209,11 +218,15 @@ def suite(a):
                                 b.copy_(q)
                             cold = round(time_cold(lambda: getattr(c, coll)(bufs, "fp16", "sum"), 15, scrub) * 1e6, 2)
                         factor = 2 * (P - 1) / P if coll == "allreduce" else (P - 1) / P
+                        form = c.exec_choice(coll, L, "fp16")
+                        moved = c.exec_bytes(coll, L, "fp16", form)
                         emit(workload="sweep_p16_fp16", algo=algo, coll=coll, P=P, bytes_per_rank=nbytes,
-                             launch_form=c.exec_choice(coll, L, "fp16"), us=round(t * 1e6, 2), cold_us=cold,
+                             launch_form=form, us=round(t * 1e6, 2), cold_us=cold,
                              steps=info["nsteps"],
                              busbw_GBps=round(nbytes / t * factor / 1e9, 3),
-                             pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2))
+                             algorithmic_bytes=info["hbm_bytes"], moved_bytes=moved,
+                             pct_hbm_algorithmic=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2),
+                             pct_hbm_moved=round(100 * moved / t / HBM_PEAK, 2))
             del bufs, pristine
             torch.cuda.empty_cache()
             nbytes *= 4
@@ -232,17 +245,22 @@ def suite(a):
                         info = c.plan_info("allreduce", L, "fp16")
                         reps = max(5, min(200, int(1e8 // info["hbm_bytes"])))
                         auto_form = c.exec_choice("allreduce", L, "fp16")
+                        pct = {}
                         for form in ("steps", "fused", "columns", "lds", "auto"):
                             c.set_exec_mode(form)
                             if form != "auto" and c.exec_choice("allreduce", L, "fp16") != form:
                                 continue
                             if form == "fused" and kib > 64:
                                 continue  # one compute unit: far slower, skip the long runs
-                            row[form] = round(time_calls(lambda: c.allreduce(bufs, "fp16", "max"), reps, 3) * 1e6, 2)
+                            tf = time_calls(lambda: c.allreduce(bufs, "fp16", "max"), reps, 3)
+                            row[form] = round(tf * 1e6, 2)
+                            moved = c.exec_bytes("allreduce", L, "fp16", form if form != "auto" else auto_form)
+                            pct[form] = round(100 * moved / tf / HBM_PEAK, 2)
                         if P * (kib << 10) <= cold_limit:
                             row["auto_cold"] = round(time_cold(lambda: c.allreduce(bufs, "fp16", "max"), 15, scrub) * 1e6, 2)
                     emit(workload="launch_forms", algo=algo, P=P, dtype="fp16", op="max", bytes_per_rank=kib << 10,
-                         hbm_bytes=info["hbm_bytes"], steps=info["nsteps"], auto_form=auto_form, us=row)
+                         hbm_bytes=info["hbm_bytes"], steps=info["nsteps"], auto_form=auto_form, us=row,
+                         pct_hbm_moved=pct)
                     del bufs
                     kib *= 4
 
@@ -287,6 +305,54 @@ def suite(a):
              bytes_per_rank=L * 2, us=round(t * 1e6, 1), steps=info["nsteps"],
              busbw_GBps=round(L * 2 / t * 2 * (P - 1) / P / 1e9, 3),
              pct_hbm=round(100 * info["hbm_bytes"] / t / HBM_PEAK, 2), per_step=steps)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(a, P, L, D, dtype, recipe):
+    """The oracle replaying the whole workload on the host: one thread, and
+    disjoint windows on every CPU this process may use (at most 16; the same
+    arithmetic, window by window).  Inputs are restored from a host copy
+    before each replay (untimed)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    pristine = [np.empty(L, np.float32) for _ in range(P)]
+    for r in range(P):
+        synth.fill_ptr(pristine[r].ctypes.data, dtype, L, recipe["dist"], recipe["p0"], recipe["p1"],
+                       seed=0, stream=recipe["stream"], rank=r)
+    xs = [np.empty_like(x) for x in pristine]
+
+    def timed(fn, reps):
+        times = []
+        for _ in range(reps):
+            for x, q in zip(xs, pristine):
+                np.copyto(x, q)
+            c0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - c0)
+        return float(np.median(times))
+
+    t1 = timed(lambda: oracle.run("allreduce", a.algo, xs, dtype, "sum"), max(1, a.cpu_reps // 3))
+    T = oracle.threads_available()
+    tt = timed(lambda: oracle.run_parallel("allreduce", a.algo, xs, dtype, "sum", threads=T), a.cpu_reps)
+    busbw = lambda t: round(D / t * 2 * (P - 1) / P / 1e9, 4)  # noqa: E731
+    return {"value": busbw(tt), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": f"the full workload, {a.cpu_reps} AllReduces replayed by the oracle as {T} disjoint "
+                      f"element windows on {T} threads, median {tt:.3f} s each",
+            "single_thread": {"value": busbw(t1), "cores": 1, "median_s": round(t1, 3),
+                              "reps": max(1, a.cpu_reps // 3)},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0))}
 
 
 def main():
@@ -462,27 +528,15 @@ def main():
         ta = e0.elapsed_time(e1) / 1e3 / K
         ainfo = auto.plan_info("allreduce", L, dtype)
     out["auto_allreduce_same_workload"] = {
-        "note": "not the headline value: AUTO communicator on this workload",
-        "algo": choice, "ms": round(ta * 1e3, 4), "busbw_GBps": round(D / ta * 2 * (P - 1) / P / 1e9, 3),
-        "pct_hbm": round(100 * ainfo["hbm_bytes"] / ta / HBM_PEAK, 2), "kernel_launches": ainfo["nsteps"]}
+        "note": "not the headline value: AUTO communicator on this workload; no busbw, since the "
+                "ring's bus factor 2(P-1)/P does not apply to the schedule it picks",
+        "algo": choice, "ms": round(ta * 1e3, 4), "algbw_GBps": round(D / ta / 1e9, 3),
+        "hbm_bytes": ainfo["hbm_bytes"], "pct_hbm": round(100 * ainfo["hbm_bytes"] / ta / HBM_PEAK, 2),
+        "kernel_launches": ainfo["nsteps"]}
     del pristine
 
     if not a.no_cpu:
-        import oracle
-        xs = [np.empty(L, np.float32) for _ in range(P)]
-        times = []
-        for rep in range(a.cpu_reps):
-            for r in range(P):
-                synth.fill_ptr(xs[r].ctypes.data, dtype, L, recipe["dist"], recipe["p0"], recipe["p1"],
-                               seed=0, stream=recipe["stream"], rank=r)
-            c0 = time.perf_counter()
-            oracle.run("allreduce", a.algo, xs, dtype, "sum")
-            times.append(time.perf_counter() - c0)
-        tc = float(np.median(times))
-        out["cpu_baseline"] = {"value": round(D / tc * 2 * (P - 1) / P / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
-                               "sample": f"the full workload, {a.cpu_reps} AllReduces replayed by the "
-                                         f"single-threaded oracle, median {tc:.2f} s each"}
+        out["cpu_baseline"] = cpu_baseline(a, P, L, D, dtype, recipe)
     comm.close()
     print(json.dumps(out), flush=True)
 

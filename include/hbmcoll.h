@@ -193,6 +193,23 @@ hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, 
  * plan and, for AUTO, its host column table). */
 hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
                                int first_step, int last_step, hbmc_exec_t* mode);
+/* Bytes that steps [first_step, last_step) of a call (0, 0: all steps) move
+ * between the compute units and memory in launch form `mode` (AUTO: the form
+ * hbmc_exec_choice reports), host only:
+ *  - STEPS: the steps' algorithmic HBM bytes (every distinct block a step
+ *    reads counted once, every block it writes once, step after step);
+ *  - FUSED, COLUMNS: each rank's elements that some step reads, once, plus
+ *    those some step writes, once -- what crosses to memory when the caches
+ *    hold the call's working set, as they do within these forms' limits;
+ *  - LDS: exactly what the kernel loads and stores: every column of every
+ *    rank it loads, and every column range it stores (composed store
+ *    records in a launch of all steps), for the column length the
+ *    communicator would use.
+ * HBMC_ERR_INVALID_ARG for a bad step range, or for LDS when no column
+ * length fits one workgroup's LDS.  The figure does not depend on whether
+ * the form is eligible for the call. */
+hbmc_status_t hbmc_exec_bytes(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
+                              int first_step, int last_step, hbmc_exec_t mode, uint64_t* bytes);
 
 /*
  * AUTO selection ([RHD] "RHD 在 HCCL 中的定位与启用方式": the algorithm is

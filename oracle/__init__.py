@@ -123,6 +123,56 @@ def num_steps(coll: str, algo: str, P: int, S: int = 1, M: int = 1) -> int:
     return int(lib().orc_num_steps(COLL[coll], ALGO[algo], P, S, M, 0, 0, 0))
 
 
+def threads_available() -> int:
+    """Host threads a parallel replay uses: the CPUs this process may run on,
+    at most 16 (a GPU machine's share of its host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_parallel(coll: str, algo: str, bufs: list[np.ndarray], dtype: str, op: str, *,
+                 threads: int | None = None, S: int = 1, M: int = 1, loop_bytes: int = 0,
+                 root: int = 0) -> int:
+    """The whole replay of ``run`` (all steps, full vectors), as ``threads``
+    windowed replays of disjoint element ranges run side by side.
+
+    Every step combines the operands of an element at that element's own
+    offset in each rank, so an element's result depends only on its values
+    in every rank and on the segment / block / loop it lies in: each window,
+    replayed with the full-size schedule, equals that window of the full
+    replay (the windowed-replay pins hold this).  The arithmetic is the
+    oracle's own, unchanged; ctypes releases the GIL for each call.  Returns
+    the number of threads used."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    P = len(bufs)
+    n = bufs[0].size if P else 0
+    T = threads_available() if threads is None else max(1, int(threads))
+    T = max(1, min(T, n // 4096 if n >= 4096 else 1))
+    if T == 1:
+        run(coll, algo, bufs, dtype, op, S=S, M=M, loop_bytes=loop_bytes, root=root)
+        return 1
+    for b in bufs:
+        if b.dtype != NP_STORAGE[dtype] or not b.flags.c_contiguous or b.size != n:
+            raise ValueError("buffers must be contiguous storage arrays of one length")
+    cuts = [n * k // T for k in range(T + 1)]
+
+    def window(k):
+        w0, w1 = cuts[k], cuts[k + 1]
+        if w1 <= w0:
+            return OK
+        views = [b[w0:w1] for b in bufs]
+        ptrs = (ctypes.c_void_p * P)(*[v.ctypes.data for v in views])
+        tlen = ctypes.c_size_t(0)
+        return lib().orc_collective(COLL[coll], ALGO[algo], P, S, M, loop_bytes, root, ptrs, n, w0, w1,
+                                    DTYPE[dtype], OP[op], 0, -1, None, 0, ctypes.byref(tlen))
+
+    with ThreadPoolExecutor(max_workers=T) as ex:
+        codes = list(ex.map(window, range(T)))
+    for rc in codes:
+        _check(rc)
+    return T
+
+
 def run(coll: str, algo: str, bufs: list[np.ndarray], dtype: str, op: str, *, L: int | None = None,
         w0: int = 0, S: int = 1, M: int = 1, loop_bytes: int = 0, root: int = 0,
         first_step: int = 0, last_step: int = -1, trace: bool = False, trace_cap: int = 1 << 16):

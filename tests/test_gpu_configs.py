@@ -1,13 +1,16 @@
 """The five workloads at their full sizes, on the GPU, against the oracle.
 
-Small workloads are replayed whole by the oracle; large ones are checked on
-windows: every element within 64 of a segment / block / loop boundary plus
-random 64 Ki-element windows, replayed by the oracle with the full-size
-schedule (an element's result depends only on its own column and on the
-segment or block it lies in).  On the GPU every rank's buffer must equal
-rank 0's bit for bit.  Accuracy against the binary64 direct sum: norm-wise
-relative error <= 1e-5 (fp32) or 2^-7 (P-1) (fp16 / bf16), and the
-per-element bound of a (P-1)-addition sum.
+Every workload is compared with the oracle's replay of the whole vector of
+every rank, bit for bit, with one exception: the sweep's largest size (1 GiB
+per rank, 32 GiB of rank buffers and pristine copies) is checked on windows
+(every element within 64 of a segment boundary plus random 64 Ki-element
+windows), replayed by the oracle with the full-size schedule, since an
+element's result depends only on its own values in every rank and on the
+segment or block it lies in; there every rank's buffer must also equal rank
+0's bit for bit.  Large replays run as disjoint windows on the host's cores
+(oracle.run_parallel: the same arithmetic, window by window).  Accuracy
+against the binary64 direct sum: norm-wise relative error <= 1e-5 (fp32) or
+2^-7 (P-1) (fp16 / bf16), and the per-element bound of a (P-1)-addition sum.
 
 Workloads:
   ring_p4   ring AllReduce, P=4, L=4096, fp32 integers in [-8, 8]
@@ -106,6 +109,53 @@ def check_windows(coll, algo, recipe, P, L, dev, spans, *, S=1, M=1, loop_bytes=
     return num, den
 
 
+def bits(dtype, x):
+    return np.ascontiguousarray(x).view({4: np.uint32, 2: np.uint16, 1: np.uint8}[x.dtype.itemsize])
+
+
+def assert_same_fast(dtype, got, want, what):
+    """Bit equality of whole vectors; only on a mismatch the NaN-aware
+    comparison (any two NaNs equal) decides and reports."""
+    if np.array_equal(bits(dtype, got), bits(dtype, want)):
+        return
+    refops.assert_same(dtype, got, want, what)
+
+
+def sum_accuracy(dtype, y, xs, chunk=1 << 20):
+    """Per-element bound of a (P-1)-addition sum over the whole vector, and
+    the norm-wise relative error against the binary64 direct sum."""
+    num = den = 0.0
+    for a in range(0, y.size, chunk):
+        b = min(y.size, a + chunk)
+        part = [x[a:b] for x in xs]
+        assert refops.sum_bound_ok(dtype, y[a:b], part).all(), f"per-element bound fails in [{a},{b})"
+        exact = np.zeros(b - a)
+        for x in part:
+            exact += refops.to_f64(dtype, x)
+        num += float(np.sum((refops.to_f64(dtype, y[a:b]) - exact) ** 2))
+        den += float(np.sum(exact ** 2))
+    return np.sqrt(num / den)
+
+
+def check_full(coll, algo, xs, dev, dtype, *, S=1, M=1, loop_bytes=0, op="sum"):
+    """Oracle replay of the whole vectors (run in windows on the host's cores)
+    against every rank's GPU buffer; a reduce-scatter compares each rank's
+    own segment.  Returns the oracle's result."""
+    P, L = len(xs), xs[0].size
+    want = [x.copy() for x in xs]
+    T = oracle.run_parallel(coll, algo, want, dtype, op, S=S, M=M, loop_bytes=loop_bytes)
+    say(f"  oracle replay of {algo} {coll} P={P} L={L} on {T} threads done")
+    for r in range(P):
+        got = to_host(dev[r], dtype)
+        if coll == "reduce_scatter":
+            b, e = refops.seg_bounds(L, P, r)
+            assert_same_fast(dtype, got[b:e], want[r][b:e], f"{algo} rs rank {r}")
+        else:
+            assert_same_fast(dtype, got, want[r], f"{algo} {coll} rank {r}")
+        del got
+    return want
+
+
 def test_ring_p4_fp32_integers():
     P, L = 4, 4096
     xs = synth.rank_inputs("ring_p4_fp32_int", P, L)
@@ -125,22 +175,23 @@ def test_ring_p4_fp32_integers():
 
 @pytest.mark.parametrize("columns", [False, True])
 def test_ring_p8_fp32_64Mi(columns):
+    """The benchmark's workload, every element of every rank against the oracle."""
     P, L = 8, 64 << 20
-    say(f"case ring_p8 fp32 64Mi columns={columns}: upload")
-    dev = upload_recipe("ring_p8_fp32_grad", P, L)
+    say(f"case ring_p8 fp32 64Mi columns={columns}: generate and upload")
+    xs = synth.rank_inputs("ring_p8_fp32_grad", P, L)
+    dev = [to_dev(x, "fp32") for x in xs]
     with hc.Comm(P, "ring") as c:
         if columns:
             c.set_columns(1 << 40)
             c.set_exec_mode("columns")
+            assert c.exec_choice("allreduce", L, "fp32") == "columns"
+        else:
+            assert c.exec_choice("allreduce", L, "fp32") == "steps"
         say("case ring_p8 fp32 64Mi: allreduce")
         c.allreduce(dev, "fp32", "sum")
         torch.cuda.synchronize()
-    assert ranks_identical(dev, "fp32")
-    q = L // P
-    spans = windows([k * q for k in range(P + 1)], L, seed=2)
-    say(f"case ring_p8: {len(spans)} windows")
-    num, den = check_windows("allreduce", "ring", "ring_p8_fp32_grad", P, L, dev, spans)
-    assert np.sqrt(num / den) <= 1e-5
+    want = check_full("allreduce", "ring", xs, dev, "fp32")
+    assert sum_accuracy("fp32", want[0], xs) <= 1e-5
     del dev
     torch.cuda.empty_cache()
 
@@ -176,6 +227,7 @@ def test_rhd_small_messages(P, exec_mode):
 
 
 SWEEP = [4096 * 4 ** i for i in range(10)]  # bytes per rank: 4 KiB .. 1 GiB
+FULL_SWEEP_BYTES = 256 << 20  # whole-vector oracle comparison up to this size per rank
 
 
 @pytest.mark.parametrize("nbytes", SWEEP)
@@ -183,12 +235,15 @@ def test_sweep_p16_fp16(nbytes):
     P, dtype, recipe = 16, "fp16", "sweep_p16_fp16"
     L = nbytes // 2
     say(f"case sweep P=16 fp16 {nbytes} B/rank: upload")
-    pristine = upload_recipe(recipe, P, L)
-    dev = [torch.empty_like(t) for t in pristine]
-    full = nbytes <= (4 << 20)
-    if not full:
+    full = nbytes <= FULL_SWEEP_BYTES
+    if full:
+        xs = synth.rank_inputs(recipe, P, L)
+        pristine = [to_dev(x, dtype) for x in xs]
+    else:
+        pristine = upload_recipe(recipe, P, L)
         bounds = sorted(set([k * (-(-L // P)) for k in range(P + 1)]))
         spans = windows(bounds, L, seed=nbytes % 1000)
+    dev = [torch.empty_like(t) for t in pristine]
     for algo in ("ring", "rhd"):
         with hc.Comm(P, algo) as c:
             for coll in ("allreduce", "reduce_scatter", "all_gather"):
@@ -200,21 +255,10 @@ def test_sweep_p16_fp16(nbytes):
                 if coll != "reduce_scatter":
                     assert ranks_identical(dev, dtype)
                 if full:
-                    xs = synth.rank_inputs(recipe, P, L)
-                    want = [x.copy() for x in xs]
-                    oracle.run(coll, algo, want, dtype, "sum")
-                    for r in range(P):
-                        got = to_host(dev[r], dtype)
-                        if coll == "reduce_scatter":
-                            b, e = refops.seg_bounds(L, P, r)
-                            refops.assert_same(dtype, got[b:e], want[r][b:e], f"{algo} rs rank {r}")
-                        else:
-                            refops.assert_same(dtype, got, want[r], f"{algo} {coll} rank {r}")
+                    want = check_full(coll, algo, xs, dev, dtype)
                     if coll == "allreduce":
-                        exact = np.stack([refops.to_f64(dtype, x) for x in xs]).sum(axis=0)
-                        rel = np.linalg.norm(refops.to_f64(dtype, want[0]) - exact) / np.linalg.norm(exact)
-                        assert rel <= 2.0 ** -7 * (P - 1)
-                        assert refops.sum_bound_ok(dtype, want[0], xs).all()
+                        assert sum_accuracy(dtype, want[0], xs) <= 2.0 ** -7 * (P - 1)
+                    del want
                 else:
                     num, den = check_windows(coll, algo, recipe, P, L, dev, spans,
                                              owner_only=(coll == "reduce_scatter"))
@@ -229,23 +273,15 @@ def test_pipeline_4x8_bf16_512MiB():
     P, dtype, recipe = S * M, "bf16", "pipe_4x8_bf16"
     L = 256 << 20  # 512 MiB per rank
     loop_bytes = 32 << 20
-    say("case pipeline 4x8 bf16 512MiB: upload")
-    dev = upload_recipe(recipe, P, L)
+    say("case pipeline 4x8 bf16 512MiB: generate and upload")
+    xs = synth.rank_inputs(recipe, P, L)
+    dev = [to_dev(x, dtype) for x in xs]
     with hc.Comm(P, "pipeline", S, M, loop_bytes) as c:
         assert c.plan_info("allreduce", L, dtype)["nsteps"] == 2 * S
         say("case pipeline 4x8: allreduce")
         c.allreduce(dev, dtype, "sum")
         torch.cuda.synchronize()
-    assert ranks_identical(dev, dtype)
-    C = loop_bytes // 2
-    bounds = []
-    for lb in (0, C * 7, L - C):
-        q = -(-C // P)
-        bounds += [lb + k * q for k in range(P + 1)]
-    spans = windows(sorted(set(bounds)), L, n_random=12, rand_width=4096, seed=5)
-    say(f"case pipeline 4x8: {len(spans)} windows")
-    num, den = check_windows("allreduce", "pipeline", recipe, P, L, dev, spans, S=S, M=M,
-                             loop_bytes=loop_bytes)
-    assert np.sqrt(num / den) <= 2.0 ** -7 * (P - 1)
-    del dev
+    want = check_full("allreduce", "pipeline", xs, dev, dtype, S=S, M=M, loop_bytes=loop_bytes)
+    assert sum_accuracy(dtype, want[0], xs) <= 2.0 ** -7 * (P - 1)
+    del dev, want
     torch.cuda.empty_cache()

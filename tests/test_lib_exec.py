@@ -99,3 +99,68 @@ def test_exec_choice_edges_and_validation():
         assert lib.hbmc_comm_set_exec_mode(c._h, 5) == 1
     with hc.Comm(1, "ring") as c:
         assert c.exec_choice("allreduce", 100, "fp32") == "steps"
+
+
+def _footprint(items, P, L, e):
+    """Each rank's elements read by some item once, plus those written once
+    (boolean masks per rank; independent of the library's interval union)."""
+    import numpy as np
+    rd = np.zeros((P, L), bool)
+    wr = np.zeros((P, L), bool)
+    for it in items:
+        for r in it["src"]:
+            rd[r, it["begin"]:it["begin"] + it["count"]] = True
+        for r in it["dst"]:
+            wr[r, it["begin"]:it["begin"] + it["count"]] = True
+    return int(rd.sum() + wr.sum()) * e
+
+
+@pytest.mark.parametrize("algo,P", [("ring", 8), ("rhd", 8), ("rhd", 5), ("ring", 16)])
+@pytest.mark.parametrize("coll", ["allreduce", "reduce_scatter", "all_gather"])
+def test_exec_bytes_per_form(algo, P, coll):
+    """hbmc_exec_bytes: steps = the plan's algorithmic bytes; fused / columns =
+    the compulsory footprint; LDS = what its kernel loads and stores, which
+    for a whole AllReduce is every rank loaded and stored once (2 P D) and
+    never more than 2 P D; AUTO reports its pick's figure."""
+    e, L = 2, 40_000 + 7
+    D = L * e
+    with hc.Comm(P, algo) as c:
+        info = c.plan_info(coll, L, "fp16")
+        assert c.exec_bytes(coll, L, "fp16", "steps") == info["hbm_bytes"]
+        items = c.plan_items(coll, L, "fp16")
+        fp = _footprint(items, P, L, e)
+        assert c.exec_bytes(coll, L, "fp16", "fused") == fp
+        assert c.exec_bytes(coll, L, "fp16", "columns") == fp
+        lds = c.exec_bytes(coll, L, "fp16", "lds")
+        assert lds <= 2 * P * D
+        if coll == "allreduce":
+            assert fp == 2 * P * D
+            assert lds == 2 * P * D
+        if coll == "all_gather":
+            # columns composed into stores load only the owners' copies
+            assert (P - 1) * D <= lds <= (P + 2) * D
+        form = c.exec_choice(coll, L, "fp16")
+        assert c.exec_bytes(coll, L, "fp16", "auto") == c.exec_bytes(coll, L, "fp16", form)
+        # a step range: every rank loaded, only the ranks its steps write stored
+        n = info["nsteps"]
+        if n >= 2:
+            first, last = 0, n // 2
+            part = [it for it in items if first <= it["step"] < last]
+            assert c.exec_bytes(coll, L, "fp16", "steps", first=first, last=last) == \
+                sum(c.step_info(coll, L, "fp16", s)["hbm_bytes"] for s in range(first, last))
+            assert c.exec_bytes(coll, L, "fp16", "columns", first=first, last=last) == _footprint(part, P, L, e)
+            r = c.exec_bytes(coll, L, "fp16", "lds", first=first, last=last)
+            written = len({d for it in part for d in it["dst"]})
+            assert P * D <= r <= P * D + written * D
+
+
+def test_exec_bytes_rejects_bad_ranges():
+    lib = hc.load_library()
+    import ctypes
+    with hc.Comm(8, "ring") as c:
+        b = ctypes.c_uint64()
+        assert lib.hbmc_exec_bytes(c._h, 0, 0, 1000, 1, 3, 2, 1, ctypes.byref(b)) == 1   # first > last
+        assert lib.hbmc_exec_bytes(c._h, 0, 0, 1000, 1, 0, 15, 1, ctypes.byref(b)) == 1  # past the end
+        assert lib.hbmc_exec_bytes(c._h, 0, 0, 1000, 1, 0, 0, 9, ctypes.byref(b)) == 1   # bad mode
+        assert lib.hbmc_exec_bytes(c._h, 0, 0, 1000, 1, 0, 0, 1, None) == 1
+        assert lib.hbmc_exec_bytes(c._h, 0, 0, 0, 1, 0, 0, 4, ctypes.byref(b)) == 0 and b.value == 0

@@ -302,6 +302,27 @@ def test_window_and_step_range_replay(algo, coll):
             refops.assert_same(dtype, part[r], full[r], f"cut at {cut}")
 
 
+@pytest.mark.parametrize("algo,kw", [("ring", {}), ("rhd", {}), ("pipeline", dict(S=2, M=3, loop_bytes=4096)),
+                                     ("flat", {}), ("tree", dict(M=3)), ("hier", dict(S=2, M=3))])
+@pytest.mark.parametrize("coll", ["allreduce", "reduce_scatter", "all_gather", "reduce", "broadcast"])
+def test_parallel_replay_equals_the_single_thread_replay(algo, kw, coll):
+    """run_parallel (disjoint windows side by side, ragged cuts) gives every
+    bit of the one-thread replay, for every algorithm and collective it offers."""
+    dtype, P, L = "fp16", 6, 50_021
+    xs = inputs(dtype, P, L, seed=9)
+    try:
+        full = replay(coll, algo, xs, dtype, "sum", root=4, **kw)
+    except oracle.OracleError as e:
+        assert e.code == oracle.EUNSUPPORTED
+        return
+    for T in (2, 5, 12):
+        par = [x.copy() for x in xs]
+        used = oracle.run_parallel(coll, algo, par, dtype, "sum", threads=T, root=4, **kw)
+        assert used == T
+        for r in range(P):
+            assert np.array_equal(par[r].view(np.uint16), full[r].view(np.uint16)), (T, r)
+
+
 def test_rooted_collectives_need_rhd_and_a_valid_root():
     xs = inputs("fp32", 6, 10)
     for algo in ("ring", "pipeline"):
