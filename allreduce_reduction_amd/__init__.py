@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libhbmcoll.so")
 
 OK = 0
 STATUS = {0: "HBMC_OK", 1: "HBMC_ERR_INVALID_ARG", 2: "HBMC_ERR_UNSUPPORTED", 3: "HBMC_ERR_HIP",
-          4: "HBMC_ERR_NOMEM"}
+          4: "HBMC_ERR_NOMEM", 5: "HBMC_ERR_SCRATCH"}
 DTYPE = {"fp32": 0, "fp16": 1, "bf16": 2, "int32": 3, "int8": 4}
 ESIZE = {"fp32": 4, "fp16": 2, "bf16": 2, "int32": 4, "int8": 1}
 OP = {"sum": 0, "prod": 1, "max": 2, "min": 3}
@@ -32,7 +32,7 @@ EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_redu
            "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy", "hbmc_comm_set_cost_model",
            "hbmc_auto_choice", "hbmc_comm_set_fused_limit",
            "hbmc_comm_set_columns", "hbmc_plan_chunks",
-           "hbmc_comm_set_exec_mode", "hbmc_exec_choice", "hbmc_exec_bytes")
+           "hbmc_comm_set_exec_mode", "hbmc_exec_choice", "hbmc_exec_bytes", "hbmc_allreduce_noalloc")
 
 
 class HbmcError(RuntimeError):
@@ -73,7 +73,7 @@ def load_library():
         L.hbmc_comm_create.argtypes = [ci, ci, ci, ci, sz, ctypes.POINTER(vp)]
         L.hbmc_comm_destroy.restype = ci
         L.hbmc_comm_destroy.argtypes = [vp]
-        for name in ("hbmc_allreduce", "hbmc_reduce_scatter", "hbmc_all_gather"):
+        for name in ("hbmc_allreduce", "hbmc_reduce_scatter", "hbmc_all_gather", "hbmc_allreduce_noalloc"):
             f = getattr(L, name)
             f.restype = ci
             f.argtypes = [vp, ctypes.POINTER(vp), sz, ci, ci, vp]
@@ -228,6 +228,11 @@ class Comm:
 
     def allreduce(self, bufs, dtype=None, op="sum", *, count=None, stream=None):
         self._coll("hbmc_allreduce", bufs, dtype, op, count, stream)
+
+    def allreduce_noalloc(self, bufs, dtype=None, op="sum", *, count=None, stream=None):
+        """AllReduce whose kernels take their tables from the library's fixed
+        device array (no device allocation; see hbmc_allreduce_noalloc)."""
+        self._coll("hbmc_allreduce_noalloc", bufs, dtype, op, count, stream)
 
     def reduce_scatter(self, bufs, dtype=None, op="sum", *, count=None, stream=None):
         self._coll("hbmc_reduce_scatter", bufs, dtype, op, count, stream)

@@ -228,6 +228,11 @@ hbmc_status_t hbmc_allreduce(hbmc_comm_t comm, void* const bufs[], size_t count,
   return no_throw([&] { return run(comm, HBMC_COLL_ALLREDUCE, 0, bufs, count, dtype, op, 0, 0, true, stream); });
 }
 
+hbmc_status_t hbmc_allreduce_noalloc(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
+                                     hbmc_op_t op, void* stream) {
+  return no_throw([&] { return allreduce_noalloc(comm, bufs, count, dtype, op, stream); });
+}
+
 hbmc_status_t hbmc_reduce_scatter(hbmc_comm_t comm, void* const bufs[], size_t count,
                                   hbmc_dtype_t dtype, hbmc_op_t op, void* stream) {
   return no_throw([&] { return run(comm, HBMC_COLL_REDUCE_SCATTER, 0, bufs, count, dtype, op, 0, 0, true, stream); });
@@ -345,6 +350,7 @@ const char* hbmc_status_string(hbmc_status_t status) {
     case HBMC_ERR_UNSUPPORTED: return "unsupported collective for this algorithm (Reduce / Broadcast: RHD only; Flat, tree, hierarchical: AllReduce only)";
     case HBMC_ERR_HIP: return "HIP error";
     case HBMC_ERR_NOMEM: return "out of memory";
+    case HBMC_ERR_SCRATCH: return "the schedule's work-item table exceeds the no-allocation AllReduce's 2 MiB device array";
     default: return "unknown status";
   }
 }

@@ -97,6 +97,11 @@ struct Plan {
   uint64_t lds_meta_steps = 0;
   uint64_t lds_meta_whole = 0;
   bool lds_stores = false;
+  // the item table as the step kernels read it, kept on the host for the
+  // no-allocation AllReduce, which copies it into its fixed device array on
+  // every call
+  std::vector<DevItem> host_table;
+  bool host_table_built = false;
   // device tables of earlier column lengths: graphs built or captured before
   // the length changed still point at them, so they are kept until the
   // communicator is destroyed
@@ -206,6 +211,10 @@ hbmc_status_t run(hbmc_comm* c, int coll, int root, void* const bufs[], size_t c
 // launch per 32 ranks), then the collective in place on recv.
 hbmc_status_t run_out_of_place(hbmc_comm* c, int coll, int root, const void* const send[],
                                void* const recv[], size_t count, int dtype, int op, void* stream);
+
+// AllReduce with the step kernels' item tables in the library's fixed
+// device array instead of allocated memory (see hbmc_allreduce_noalloc).
+hbmc_status_t allreduce_noalloc(hbmc_comm* c, void* const bufs[], size_t count, int dtype, int op, void* stream);
 
 // Runs an entry point's body so that no C++ exception crosses the C ABI.  The
 // host code throws only when allocating its tables fails (std::bad_alloc,

@@ -63,7 +63,9 @@ typedef enum {
                                other than RHD; anything but AllReduce for Flat, tree,
                                hierarchical                                               */
   HBMC_ERR_HIP = 3,         /* a HIP call or kernel launch failed                          */
-  HBMC_ERR_NOMEM = 4        /* host or device allocation failed                            */
+  HBMC_ERR_NOMEM = 4,       /* host or device allocation failed                            */
+  HBMC_ERR_SCRATCH = 5      /* hbmc_allreduce_noalloc: the schedule's work-item table
+                               exceeds the library's fixed device array                   */
 } hbmc_status_t;
 
 /* element types (the pages' HcclDataType) */
@@ -239,6 +241,30 @@ hbmc_status_t hbmc_auto_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
  */
 hbmc_status_t hbmc_allreduce(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
                              hbmc_op_t op, void* stream);
+
+/*
+ * AllReduce for callers that cannot allocate device memory (code that must
+ * not call hipMalloc: under stream capture, in tight serving loops, in
+ * harnesses that forbid it).  Same arguments, schedule, element ops and
+ * results (bit for bit) as hbmc_allreduce, one step kernel per non-empty
+ * step whatever the communicator's launch form; the step kernels read their
+ * work items from a fixed device array of 2 MiB that the library holds on
+ * every GPU it runs on until the process ends, not from memory it
+ * allocates.  Each call copies its schedule's item table (160 bytes per
+ * item) into that array with one host-to-device copy ordered on `stream`,
+ * then enqueues its kernels; it calls no hipMalloc or hipFree and no
+ * allocating library routine.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (on different streams, or
+ * from several host threads) race and must be serialised by the caller;
+ * calls on one stream follow each other safely.  The schedule's table must
+ * fit the array (at most 13107 items: e.g. ring or RHD with up to 64 ranks,
+ * the 4 x 8 pipeline with 32 MiB loops up to 1 GiB per rank), otherwise
+ * HBMC_ERR_SCRATCH is returned before anything is enqueued.  The host
+ * schedule is built and cached on the first call of a shape, as for
+ * hbmc_allreduce.
+ */
+hbmc_status_t hbmc_allreduce_noalloc(hbmc_comm_t comm, void* const bufs[], size_t count, hbmc_dtype_t dtype,
+                                     hbmc_op_t op, void* stream);
 
 /*
  * ReduceScatter.  The vector is split into P segments by the ceiling split

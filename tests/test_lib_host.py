@@ -365,6 +365,25 @@ def test_auto_rules_follow_the_pages_defaults(P, monkeypatch):
         assert c.auto_choice("allreduce", 16, "fp32") == "flat"
 
 
+def test_noalloc_refuses_before_any_device_work():
+    """hbmc_allreduce_noalloc checks its arguments and the size of the
+    schedule's item table against its fixed 2 MiB device array before touching
+    a device (these calls run on a host without a GPU)."""
+    lib = hc.load_library()
+    P = 32
+    bufs = (ctypes.c_void_p * P)(*[0x1000000 * (r + 1) for r in range(P)])
+    with hc.Comm(P, "pipeline", 4, 8, 1024) as c:
+        # 1 KiB loops over 128 KiB of bf16 per rank: 8 x 128 x 32 items of 160 B
+        assert lib.hbmc_allreduce_noalloc(c._h, bufs, 1 << 16, 2, 0, None) == 5
+        assert lib.hbmc_status_string(5).decode().startswith("the schedule's work-item table")
+        assert lib.hbmc_allreduce_noalloc(c._h, bufs, 1 << 16, 2, 9, None) == 1      # bad op
+        assert lib.hbmc_allreduce_noalloc(c._h, bufs, 1 << 16, 7, 0, None) == 1      # bad dtype
+        assert lib.hbmc_allreduce_noalloc(c._h, bufs, 0, 2, 0, None) == 0            # nothing to do
+        aliased = (ctypes.c_void_p * P)(*([0x1000000] * P))
+        assert lib.hbmc_allreduce_noalloc(c._h, aliased, 100, 2, 0, None) == 1
+    assert lib.hbmc_allreduce_noalloc(None, bufs, 100, 2, 0, None) == 1
+
+
 def test_out_of_place_validation_without_device():
     lib = hc.load_library()
     P = 4
