@@ -55,20 +55,24 @@ constexpr uint64_t kMaxItemBytes = (uint64_t(1) << 26) * kTileVecs * 16;
 // Resident workgroups per compute unit for steps of many items whose
 // workgroups each keep many HBM streams open (the pipeline's steps: 512
 // items of 1 MiB), capped by reserving LDS the kernel never touches
-// (160 KiB per compute unit / cap).  Measured on MI355X against uncapped
-// launches, same session:
+// (160 KiB per compute unit / cap).  Fewer resident workgroups keep the
+// addresses in flight closer together in each stream.  Measured on MI355X
+// (4 x 8 bf16 pipeline, 512 MiB per rank, same session; caps swept 6-32):
 // - folds with all 8 or 9 sources' loads issued at once (the compile-time
-//   shapes): 16 per CU made the pipeline's reduce steps 1-2% faster;
-// - copies to several destinations: 20 per CU made the pipeline's fan-out
-//   steps 6-8% faster;
+//   shapes): 10 per CU, 6.2-6.3 TB/s against 6.0-6.1 at 16 and 5.8 at 24;
+//   8 and 9 matched 10, 6 lost 7%;
+// - copies to several destinations: 12 per CU; the closing one-to-seven
+//   copy 6.1 TB/s against 5.7 at 20 and 5.8 at 10, the one-to-eight steps
+//   5.8 TB/s at 10-20 and 5.45 at 28; the whole AllReduce 6514-6523 us
+//   against 6652-6719 us at 16 / 20;
 // - left uncapped, where a cap lost: folds that loop over a run-time source
 //   count (one load at a time; 16 sources: 34% slower capped), Flat's
 //   single-item fold and copy (the whole 8-rank AllReduce 2% slower with the
 //   fold capped, the copy 5-9% slower), and the ring's 2-source reduce and
 //   1-to-1 copy (every cap slower).
 constexpr uint32_t kLdsPerCu = 160u * 1024u;
-constexpr uint32_t kFoldWgPerCu = 16;
-constexpr uint32_t kFanWgPerCu = 20;
+constexpr uint32_t kFoldWgPerCu = 10;
+constexpr uint32_t kFanWgPerCu = 12;
 constexpr int kCapMinItems = 64;  // above any tree level (at most 32 parents)
 
 // ------------------------------------------------------------- kernels

@@ -142,6 +142,36 @@ def test_parity_auto(P, S, M):
                         refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"{coll} {algo} rank {r}")
 
 
+@pytest.mark.parametrize("P", [4, 5, 8, 6])
+def test_parity_auto_rules(P):
+    """An AUTO_RULES communicator (the pages' defaults: Flat below 64 KiB per
+    rank for AllReduce, RHD for a power-of-two rank count, the ring otherwise)
+    runs the schedule its rules pick, bit for bit, on both sides of 64 KiB."""
+    pow2 = (P & (P - 1)) == 0
+    for dtype, op in (("fp16", "sum"), ("int32", "max")):
+        e = 2 if dtype == "fp16" else 4
+        with hc.Comm(P, "auto_rules") as comm:
+            for coll in ("allreduce", "reduce_scatter", "all_gather"):
+                for L in ((64 << 10) // e - 1, (64 << 10) // e, 100_003):
+                    algo = comm.auto_choice(coll, L, dtype)
+                    expect = "flat" if coll == "allreduce" and L * e < (64 << 10) else ("rhd" if pow2 else "ring")
+                    assert algo == expect, (coll, L, algo)
+                    say(f"case auto_rules P={P} {coll} {dtype} {op} L={L} -> {algo}")
+                    xs = make_inputs(dtype, op, P, L, seed=L + P)
+                    dev = [to_dev(x, dtype) for x in xs]
+                    getattr(comm, coll)(dev, dtype, op)
+                    torch.cuda.synchronize()
+                    want = [x.copy() for x in xs]
+                    oracle.run(coll, algo, want, dtype, op)
+                    for r in range(P):
+                        got = to_host(dev[r], dtype)
+                        if coll == "reduce_scatter":
+                            b, e2 = refops.seg_bounds(L, P, r)
+                            refops.assert_same(dtype, got[b:e2], want[r][b:e2], f"rules {coll} rank {r}")
+                        else:
+                            refops.assert_same(dtype, got, want[r], f"rules {coll} {algo} rank {r}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("coll", ["reduce", "broadcast"])
 def test_parity_rooted(coll, dtype):
