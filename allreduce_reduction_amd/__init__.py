@@ -23,7 +23,7 @@ ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3, "flat": 4, "tree": 5, "hie
 ALGO_NAME = {v: k for k, v in ALGO.items()}
 COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
-EXEC = {"auto": 0, "steps": 1, "fused": 2, "columns": 3, "lds": 4}
+EXEC = {"auto": 0, "steps": 1, "fused": 2, "columns": 3, "lds": 4, "regs": 5}
 
 # every symbol include/hbmcoll.h declares
 EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
@@ -269,7 +269,7 @@ class Comm:
                                              first, last, _stream(stream)), "hbmc_run_steps")
 
     def set_exec_mode(self, mode: str):
-        """Launch form of every call: "auto" (default), "steps", "fused", "columns" or "lds"."""
+        """Launch form of every call: "auto" (default), "steps", "fused", "columns", "lds" or "regs"."""
         _check(load_library().hbmc_comm_set_exec_mode(self._h, EXEC[mode]), "hbmc_comm_set_exec_mode")
 
     def exec_choice(self, coll: str, count: int, dtype: str, root: int = 0, first: int = 0, last: int = 0) -> str:

@@ -101,6 +101,7 @@ hbmc_status_t comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_p
     else if (v == "fused") c->exec_mode = kExecFused;
     else if (v == "columns") c->exec_mode = kExecColumns;
     else if (v == "lds") c->exec_mode = kExecLds;
+    else if (v == "regs") c->exec_mode = kExecRegs;
     else if (v == "auto") c->exec_mode = kExecAuto;
   }
   const char* xs = std::getenv("HBMC_XCD_SPLIT");
@@ -135,7 +136,7 @@ hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, 
 }
 
 hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode) {
-  if (!comm || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_LDS) return HBMC_ERR_INVALID_ARG;
+  if (!comm || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_REGS) return HBMC_ERR_INVALID_ARG;
   comm->exec_mode = static_cast<int>(mode);
   return HBMC_OK;
 }
@@ -163,7 +164,7 @@ hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
 hbmc_status_t hbmc_exec_bytes(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
                               int first_step, int last_step, hbmc_exec_t mode, uint64_t* bytes) {
   return no_throw([&]() -> hbmc_status_t {
-    if (!bytes || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_LDS) return HBMC_ERR_INVALID_ARG;
+    if (!bytes || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_REGS) return HBMC_ERR_INVALID_ARG;
     Plan* p = nullptr;
     hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
     if (st != HBMC_OK) return st;

@@ -16,7 +16,7 @@
 namespace hbmc {
 
 // How a call's steps are launched.
-enum ExecMode : int { kExecAuto = 0, kExecSteps = 1, kExecFused = 2, kExecColumns = 3, kExecLds = 4 };
+enum ExecMode : int { kExecAuto = 0, kExecSteps = 1, kExecFused = 2, kExecColumns = 3, kExecLds = 4, kExecRegs = 5 };
 
 // Modelled time (us) of a range of steps in each launch form, fitted to
 // measurements on MI355X (one launch per step, the single-workgroup kernel,
@@ -60,6 +60,10 @@ struct LdsHost {
 // A cached schedule and its device item table (uploaded on first use).
 struct Plan {
   Schedule sched;
+  int coll = 0;                    // the collective it implements
+  // the register form of a whole AllReduce, derived on first use
+  bool regs_built = false;
+  RegPlan regs;
   std::vector<size_t> first_item;  // offset of each step's items in the device table
   DevItem* dev = nullptr;          // all items, step after step
   FusedStep* dev_steps = nullptr;  // one entry per step, for the single-workgroup kernel

@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "plan.hpp"
+#include "regs.hpp"
 
 namespace hbmc {
 
@@ -116,18 +117,44 @@ struct alignas(16) DevColStore {
 };
 static_assert(sizeof(DevColStore) == 16, "column store record");
 
+// The register-form kernel's arguments (see regs.hpp), one record per region
+// of elements (grid.y): the region's whole 16-byte positions [vec_lo, vec_hi)
+// of the vector (position k holds the elements from head + k * 16 / e on,
+// head the elements before the buffers' first 16-byte boundary), the
+// region's elements outside them [el_lo[i], el_hi[i]), and the address of
+// element 0 of every operand: for the fold ptr[0..n) in fold order, for the
+// tree ptr[v] and ptr[16 + v] the two ranks of leaf v (nullptr for a leaf of
+// one rank).  Every operand is also a destination.
+constexpr int kRegThreads = 256;
+template <int NP>
+struct RegRegionArg {
+  uint32_t vec_lo, vec_hi;
+  uint32_t el_lo[2], el_hi[2];
+  unsigned char* ptr[NP];
+};
+template <int NP, int NR>
+struct RegCallT {
+  uint32_t n, phase;
+  uint64_t count;
+  RegRegionArg<NP> r[NR];
+};
+using RegFoldCall = RegCallT<kRegMaxLeaves, kRegMaxFoldRegions>;
+using RegTreeCall = RegCallT<2 * kRegMaxLeaves, kRegMaxTreeRegions>;
+constexpr size_t kRegCallBytes = sizeof(RegFoldCall) > sizeof(RegTreeCall) ? sizeof(RegFoldCall) : sizeof(RegTreeCall);
+
 // One kernel launch: kernel, shape and argument values, usable with
 // hipLaunchKernel or as a kernel graph node.
 struct KernelDesc {
-  enum Kind { kVector = 0, kElement = 1, kFused = 2, kColumns = 3, kColumnsLds = 4, kVectorArgs = 5 };
+  enum Kind { kVector = 0, kElement = 1, kFused = 2, kColumns = 3, kColumnsLds = 4, kVectorArgs = 5, kRegs = 6 };
   Kind kind = kVector;
   const void* func = nullptr;
   dim3 grid, block;
   // the call's buffer table, or for kVectorArgs the step's resolved items
-  // (an ArgItems of the kernel's operand count)
+  // (an ArgItems of the kernel's operand count), or for kRegs a RegFoldCall
+  // or RegTreeCall
   union {
     RankPtrs ptrs;
-    alignas(16) unsigned char args[kArgBytes];
+    alignas(16) unsigned char args[kArgBytes > kRegCallBytes ? kArgBytes : kRegCallBytes];
   };
   const DevItem* items = nullptr;
   uint32_t nitems = 0;               // step kernels: items of the step
@@ -187,6 +214,8 @@ struct KernelDesc {
     } else if (kind == kVectorArgs) {
       argv[0] = &flags;
       argv[1] = args;
+    } else if (kind == kRegs) {
+      argv[0] = args;
     } else {
       // step kernels: the small arguments first (preloaded into registers)
       argv[0] = &items;
@@ -226,6 +255,11 @@ void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColC
                           uint64_t count, uint32_t nranks, uint64_t meta_bytes, uint32_t grid,
                           const DevColStore* stores, const uint32_t* col_run, const uint32_t* st_off,
                           const uint64_t* col_load, KernelDesc* k);
+
+// The register-form kernel of a whole AllReduce of P ranks over `count`
+// elements whose rank buffers share the 16-byte `phase` (rp.ok).
+void describe_regs(int dtype, int op, const RankPtrs& ptrs, int P, const RegPlan& rp, uint64_t count,
+                   uint32_t phase, KernelDesc* k);
 
 // The single-workgroup kernel running `nsteps` steps of a plan.
 void describe_fused(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const FusedStep* steps,

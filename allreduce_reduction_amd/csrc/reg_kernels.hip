@@ -1,0 +1,213 @@
+// The register form of a whole AllReduce (see regs.hpp).  grid.y indexes the
+// regions of elements that share one expression; a lane of region g takes
+// one 16-byte position of the vector, loads every rank's value there into
+// registers at once, evaluates the schedule's expression in its grouping --
+// a left fold over a rank sequence, or a complete pairwise tree over single
+// ranks and merged pairs -- and stores the result to every rank.  A region's
+// operand addresses travel in its record in the kernel arguments, so a
+// workgroup waits on one round of scalar loads (its record) and one round of
+// data loads: no table in device memory, no LDS, no barrier.  The region's
+// elements outside its whole positions (where its edges cut a position, and
+// the head / tail of the vector) are taken one by one by the lanes of its
+// first workgroup.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "elemops.hpp"
+#include "launch.hpp"
+#include "regs.hpp"
+
+namespace hbmc {
+namespace {
+
+using namespace dev;
+
+// The expression of a region over values load(i) of its operands
+// (addresses ptr[i]), combined by op.
+template <int FORM, typename V, typename Load, typename Op>
+__device__ __forceinline__ V eval(uint32_t n, const unsigned char* const* ptr, Load load, Op op) {
+  V x[kRegMaxLeaves];
+  if constexpr (FORM == kRegFold) {
+#pragma unroll
+    for (uint32_t i = 0; i < kRegMaxLeaves; ++i)
+      if (i < n) x[i] = load(ptr[i]);
+    V acc = op(x[0], x[1]);
+#pragma unroll
+    for (uint32_t i = 2; i < kRegMaxLeaves; ++i)
+      if (i < n) acc = op(acc, x[i]);
+    return acc;
+  } else {
+    V y[kRegMaxLeaves];
+#pragma unroll
+    for (uint32_t v = 0; v < kRegMaxLeaves; ++v) {
+      if (v < n) {
+        x[v] = load(ptr[v]);
+        if (ptr[kRegMaxLeaves + v]) y[v] = load(ptr[kRegMaxLeaves + v]);
+      }
+    }
+#pragma unroll
+    for (uint32_t v = 0; v < kRegMaxLeaves; ++v)
+      if (v < n && ptr[kRegMaxLeaves + v]) x[v] = op(x[v], y[v]);
+    // pairs (0,1), (2,3), ..., then (0,2), (4,6), ...
+#pragma unroll
+    for (uint32_t w = 1; w < kRegMaxLeaves; w *= 2)
+#pragma unroll
+      for (uint32_t v = 0; v + w < kRegMaxLeaves; v += 2 * w)
+        if (v + w < n) x[v] = op(x[v], x[v + w]);
+    return x[0];
+  }
+}
+
+// Store v at byte offset off of every operand.
+template <int FORM, typename Store>
+__device__ __forceinline__ void store_all(uint32_t n, unsigned char* const* ptr, Store store) {
+#pragma unroll
+  for (uint32_t v = 0; v < kRegMaxLeaves; ++v) {
+    if (v < n) {
+      store(ptr[v]);
+      if constexpr (FORM == kRegTree)
+        if (ptr[kRegMaxLeaves + v]) store(ptr[kRegMaxLeaves + v]);
+    }
+  }
+}
+
+template <int DT, int OP, int FORM, typename Call>
+__global__ void __launch_bounds__(kRegThreads)
+plan_regs(Call c) {
+  constexpr uint32_t E = Width<DT>::bytes;
+  constexpr uint32_t EPV = 16 / E;
+  constexpr int NP = FORM == kRegTree ? 2 * kRegMaxLeaves : kRegMaxLeaves;
+  const auto& R0 = c.r[blockIdx.y];
+  // the region's record read whole before any branch on it, so that its
+  // scalar loads go out together
+  struct {
+    uint32_t vec_lo, vec_hi, el_lo[2], el_hi[2];
+    unsigned char* ptr[NP];
+  } R;
+  R.vec_lo = R0.vec_lo;
+  R.vec_hi = R0.vec_hi;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    R.el_lo[i] = R0.el_lo[i];
+    R.el_hi[i] = R0.el_hi[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) R.ptr[i] = R0.ptr[i];
+  uint64_t head = ((16u - (c.phase & 15u)) & 15u) / E;
+  if (head > c.count) head = c.count;
+  const uint64_t k = uint64_t(R.vec_lo) + uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (k < R.vec_hi) {
+    const uint64_t off = (head + k * EPV) * E;
+    const u32x4 v = eval<FORM, u32x4>(
+        c.n, R.ptr, [&](const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p + off); },
+        [](u32x4 a, u32x4 b) { return op_vec<DT, OP>(a, b); });
+    store_all<FORM>(c.n, R.ptr, [&](unsigned char* p) { store_vec(reinterpret_cast<u32x4*>(p + off), v); });
+  }
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      const uint64_t e = uint64_t(R.el_lo[part]) + threadIdx.x;
+      if (e < R.el_hi[part]) {
+        const uint64_t off = e * E;
+        const uint32_t v = eval<FORM, uint32_t>(
+            c.n, R.ptr, [&](const unsigned char* p) { return load_elem<E>(p + off); },
+            [](uint32_t a, uint32_t b) { return op_word<DT, OP>(a, b); });
+        store_all<FORM>(c.n, R.ptr, [&](unsigned char* p) { store_elem<E>(p + off, v); });
+      }
+    }
+  }
+}
+
+template <int DT, int OP>
+const void* regs_fn(uint32_t form) {
+  return form == kRegTree ? reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTree, RegTreeCall>)
+                          : reinterpret_cast<const void*>(plan_regs<DT, OP, kRegFold, RegFoldCall>);
+}
+
+template <int DT>
+const void* regs_op(int op, uint32_t form) {
+  switch (op) {
+    case kSum: return regs_fn<DT, kSum>(form);
+    case kProd: return regs_fn<DT, kProd>(form);
+    case kMax: return regs_fn<DT, kMax>(form);
+    default: return regs_fn<DT, kMin>(form);
+  }
+}
+
+// Fill a call's records from the derived regions; returns the largest
+// number of whole positions in one region.
+template <typename Call>
+uint64_t fill(Call* c, const RankPtrs& ptrs, const RegPlan& rp, uint64_t count, uint32_t phase, uint32_t E) {
+  constexpr int NP = sizeof(c->r[0].ptr) / sizeof(c->r[0].ptr[0]);
+  std::memset(c, 0, sizeof(*c));
+  c->n = rp.n;
+  c->phase = phase;
+  c->count = count;
+  const uint64_t EPV = 16 / E;
+  uint64_t head = ((16u - (phase & 15u)) & 15u) / E;
+  if (head > count) head = count;
+  const uint64_t nvec = (count - head) / EPV;
+  uint64_t most = 0, start = 0;
+  for (size_t g = 0; g < rp.regions.size(); ++g) {
+    const RegRegion& q = rp.regions[g];
+    auto& r = c->r[g];
+    const uint64_t end = q.end;
+    // whole positions inside [start, end)
+    uint64_t lo = start <= head ? 0 : (start - head + EPV - 1) / EPV;
+    uint64_t hi = end <= head ? 0 : (end - head) / EPV;
+    lo = std::min(lo, nvec);
+    hi = std::min(hi, nvec);
+    if (hi < lo) hi = lo;
+    r.vec_lo = static_cast<uint32_t>(lo);
+    r.vec_hi = static_cast<uint32_t>(hi);
+    if (hi > lo) {
+      r.el_lo[0] = static_cast<uint32_t>(start);
+      r.el_hi[0] = static_cast<uint32_t>(head + lo * EPV);
+      r.el_lo[1] = static_cast<uint32_t>(head + hi * EPV);
+      r.el_hi[1] = static_cast<uint32_t>(end);
+    } else {
+      r.el_lo[0] = static_cast<uint32_t>(start);
+      r.el_hi[0] = static_cast<uint32_t>(end);
+      r.el_lo[1] = r.el_hi[1] = 0;
+    }
+    for (uint32_t v = 0; v < rp.n; ++v) {
+      r.ptr[v] = ptrs.p[q.a[v]];
+      if (NP > kRegMaxLeaves && q.b[v] != 0xff) r.ptr[(kRegMaxLeaves + v) % NP] = ptrs.p[q.b[v]];
+    }
+    most = std::max<uint64_t>(most, hi - lo);
+    start = end;
+  }
+  return most;
+}
+
+}  // namespace
+
+void describe_regs(int dtype, int op, const RankPtrs& ptrs, int P, const RegPlan& rp, uint64_t count,
+                   uint32_t phase, KernelDesc* k) {
+  (void)P;
+  const uint32_t E = dtype == kF32 || dtype == kI32 ? 4u : (dtype == kI8 ? 1u : 2u);
+  uint64_t most = 0;
+  if (rp.form == kRegTree) most = fill(new (k->args) RegTreeCall, ptrs, rp, count, phase, E);
+  else most = fill(new (k->args) RegFoldCall, ptrs, rp, count, phase, E);
+  // at least one lane per element a region takes one by one (fewer than 16
+  // at each end of a region)
+  const uint64_t lanes = std::max<uint64_t>(most, 16);
+  const uint32_t block = lanes <= 64 ? 64u : (lanes <= 128 ? 128u : uint32_t(kRegThreads));
+  k->kind = KernelDesc::kRegs;
+  k->grid = dim3(static_cast<uint32_t>((lanes + block - 1) / block), static_cast<uint32_t>(rp.regions.size()));
+  k->block = dim3(block);
+  k->shared_bytes = 0;
+  switch (dtype) {
+    case kF32: k->func = regs_op<kF32>(op, rp.form); break;
+    case kF16: k->func = regs_op<kF16>(op, rp.form); break;
+    case kBF16: k->func = regs_op<kBF16>(op, rp.form); break;
+    case kI32: k->func = regs_op<kI32>(op, rp.form); break;
+    default: k->func = regs_op<kI8>(op, rp.form); break;
+  }
+  k->bind();
+}
+
+}  // namespace hbmc

@@ -48,6 +48,8 @@ constexpr int kElemThreads = 256;   // element-wise kernel
 // Items per grid row when a step's items do not fit grid.y alone (below the
 // device's reported grid.y and grid.z limits of 65536).
 constexpr uint32_t kGridRows = 32768;
+// Copy steps reading at most this many bytes take plain loads (see arg_kernel).
+constexpr uint64_t kPlainLoadCopyBytes = uint64_t(32) << 20;
 // Largest item a step kernel takes: grid.x times the workgroup size must stay
 // below 2^32 work-items, so at most 2^26 one-wave tiles of 1 KiB.
 constexpr uint64_t kMaxItemBytes = (uint64_t(1) << 26) * kTileVecs * 16;
@@ -94,8 +96,16 @@ __device__ __forceinline__ void xcd_tile(uint32_t* item, uint32_t* tile) {
 // share.  NS / ND > 0 fix the item shape at compile time (all loads of a tile
 // issued before any combine); 0 takes ns / nd.
 // NT: stores with the nontemporal hint (a compile-time choice: the compiler
-// merges the two stores of a run-time branch into one plain store).
-template <int DT, int OP, int MODE, int NS, int ND, bool NT, typename B>
+// merges the two stores of a run-time branch into one plain store).  PL: the
+// loads without the nontemporal hint.
+// A 16-byte load: with the nontemporal hint, or plain (PL).
+template <bool PL>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+  if constexpr (PL) return *p;
+  else return load_vec(p);
+}
+
+template <int DT, int OP, int MODE, int NS, int ND, bool NT, bool PL, typename B>
 __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t count, uint32_t phase,
                                          uint32_t tile, int ns, int nd) {
   constexpr uint32_t E = Width<DT>::bytes;
@@ -131,7 +141,7 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
 #pragma unroll
         for (int u = 0; u < kVecPerThread; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
-          if (v < nvec) x[s][u] = load_vec(p + v);
+          if (v < nvec) x[s][u] = ld<PL>(p + v);
         }
       }
 #pragma unroll
@@ -156,7 +166,7 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
 #pragma unroll
         for (int u = 0; u < kVecPerThread; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
-          if (v < nvec) acc[u] = load_vec(p + v);
+          if (v < nvec) acc[u] = ld<PL>(p + v);
         }
       }
       if constexpr (MODE != kCopy) {
@@ -165,7 +175,7 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
 #pragma unroll
           for (int u = 0; u < kVecPerThread; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
-            if (v < nvec) acc[u] = op_vec<DT, OP>(acc[u], load_vec(p + v));
+            if (v < nvec) acc[u] = op_vec<DT, OP>(acc[u], ld<PL>(p + v));
           }
         }
         if constexpr (MODE == kRecvFold) {
@@ -173,7 +183,7 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
 #pragma unroll
           for (int u = 0; u < kVecPerThread; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
-            if (v < nvec) acc[u] = op_vec<DT, OP>(load_vec(p + v), acc[u]);
+            if (v < nvec) acc[u] = op_vec<DT, OP>(ld<PL>(p + v), acc[u]);
           }
         }
       }
@@ -217,20 +227,20 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
   const DevItem* it = items + item;
   const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
   const int nd = ND > 0 ? ND : static_cast<int>(it->ndst);
-  vec_item<DT, OP, MODE, NS, ND, NT>(ItemBufs{ptrs, it}, it->begin, it->count, phase, tile, ns, nd);
+  vec_item<DT, OP, MODE, NS, ND, NT, false>(ItemBufs{ptrs, it}, it->begin, it->count, phase, tile, ns, nd);
 }
 
 // Vector kernel, items resolved into the kernel arguments (compile-time
 // shapes, plain stores): the operand addresses already point at the item's
 // first element, whose 16-byte phase they carry.
-template <int DT, int OP, int MODE, int NS, int ND>
+template <int DT, int OP, int MODE, int NS, int ND, bool PL>
 __global__ void __launch_bounds__(kThreads)
 step_arg(uint32_t flags, ArgItems<NS + ND> args) {
   uint32_t item = blockIdx.y, tile = blockIdx.x;
   if (flags & kFlagXcdSplit) xcd_tile(&item, &tile);
   const ArgItem<NS + ND>* a = &args.it[item];
   const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a->buf[0]) & 15u);
-  vec_item<DT, OP, MODE, NS, ND, false>(ArgBufs<NS + ND>{a}, 0, a->count, phase, tile, NS, ND);
+  vec_item<DT, OP, MODE, NS, ND, false, PL>(ArgBufs<NS + ND>{a}, 0, a->count, phase, tile, NS, ND);
 }
 
 // Element-wise kernel for buffers whose 16-byte phases differ.
@@ -285,9 +295,10 @@ const void* vector_kernel(const StepLaunch& s) {
 }
 
 // Kernel-argument form of a compile-time shape: write the step's items,
-// operands resolved, into k->args and return the kernel.
+// operands resolved, into k->args and return the kernel (plain loads for
+// `plain`).
 template <int DT, int OP, int MODE, int NS, int ND>
-const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
+const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k, bool plain) {
   constexpr int NB = NS + ND;
   constexpr uint32_t E = Width<DT>::bytes;
   static_assert(NB <= kArgMaxBufs && sizeof(ArgItems<NB>) <= kArgBytes, "argument items");
@@ -297,32 +308,42 @@ const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) 
     for (int b = 0; b < NB; ++b) a->it[i].buf[b] = ptrs.p[it.rank[b]] + it.begin * E;
     a->it[i].count = it.count;
   }
-  return fn(step_arg<DT, OP, MODE, NS, ND>);
+  return plain ? fn(step_arg<DT, OP, MODE, NS, ND, true>) : fn(step_arg<DT, OP, MODE, NS, ND, false>);
 }
 
 // The kernel-argument form for a step of at most kArgItems items of a
-// compile-time shape whose stores take no hint; nullptr otherwise.
+// compile-time shape whose stores take no hint; nullptr otherwise.  A copy
+// step that reads at most kPlainLoadCopyBytes takes plain loads: at these
+// sizes it reads blocks the step before has just written with plain stores.
+// Measured on MI355X, one launch per step, same session, us per AllReduce
+// (nontemporal loads everywhere / plain loads in copy steps of up to 32 MiB):
+// 16-rank fp16 ring at 16 MiB per rank 234.9 / 224.8, RHD 202.6 / 201.3;
+// 8-rank fp32 ring at 16 MiB 109.0 / 102.7, RHD 99.3 / 96.7; at 64 MiB per
+// rank no change (ring 790.0 / 790.1, RHD 754.4 / 753.9).  A limit of 64 MiB
+// made the 16-rank ring at 64 MiB 1% slower; plain loads in the reduce steps
+// as well gained at 8 ranks and lost at 16.
 template <int DT, int OP>
 const void* arg_kernel(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
   if (!s.host_items || s.nitems > kArgItems || s.write_bytes > kCacheBytes || s.ndst != 1) return nullptr;
+  const bool pl = s.mode == kCopy && s.write_bytes <= kPlainLoadCopyBytes;  // a copy reads what it writes
   if (s.mode == kRecvFold) {
     switch (s.nsrc) {
-      case 2: return arg_items<DT, OP, kRecvFold, 2, 1>(s, ptrs, k);
-      case 3: return arg_items<DT, OP, kRecvFold, 3, 1>(s, ptrs, k);
-      case 5: return arg_items<DT, OP, kRecvFold, 5, 1>(s, ptrs, k);
-      case 9: return arg_items<DT, OP, kRecvFold, 9, 1>(s, ptrs, k);
+      case 2: return arg_items<DT, OP, kRecvFold, 2, 1>(s, ptrs, k, pl);
+      case 3: return arg_items<DT, OP, kRecvFold, 3, 1>(s, ptrs, k, pl);
+      case 5: return arg_items<DT, OP, kRecvFold, 5, 1>(s, ptrs, k, pl);
+      case 9: return arg_items<DT, OP, kRecvFold, 9, 1>(s, ptrs, k, pl);
       default: return nullptr;
     }
   }
   if (s.mode == kFold) {
     switch (s.nsrc) {
-      case 2: return arg_items<DT, OP, kFold, 2, 1>(s, ptrs, k);
-      case 4: return arg_items<DT, OP, kFold, 4, 1>(s, ptrs, k);
-      case 8: return arg_items<DT, OP, kFold, 8, 1>(s, ptrs, k);
+      case 2: return arg_items<DT, OP, kFold, 2, 1>(s, ptrs, k, pl);
+      case 4: return arg_items<DT, OP, kFold, 4, 1>(s, ptrs, k, pl);
+      case 8: return arg_items<DT, OP, kFold, 8, 1>(s, ptrs, k, pl);
       default: return nullptr;
     }
   }
-  return s.nsrc == 1 ? arg_items<DT, kSum, kCopy, 1, 1>(s, ptrs, k) : nullptr;
+  return s.nsrc == 1 ? arg_items<DT, kSum, kCopy, 1, 1>(s, ptrs, k, pl) : nullptr;
 }
 
 // Grid of `gx` tiles by `nitems` items: items along y, and along z as well

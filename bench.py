@@ -78,7 +78,9 @@ def parse():
     ap.add_argument("--suite", action="store_true", help="time the other workloads instead")
     ap.add_argument("--max-sweep-bytes", type=int, default=1 << 30)
     ap.add_argument("--workloads", default="rhd_small,sweep,forms,algorithms,pipe",
-                    help="suite workloads to run (comma-separated)")
+                    help="suite workloads to run (comma-separated; also sweep_steps)")
+    ap.add_argument("--sweep-sizes", default=f"{16 << 20},{256 << 20},{1 << 30}",
+                    help="sweep_steps: bytes per rank (comma-separated)")
     return ap.parse_args()
 
 
@@ -230,6 +232,37 @@ def suite(a):
             del bufs, pristine
             torch.cuda.empty_cache()
             nbytes *= 4
+
+    if "sweep_steps" in workloads:
+        # every step of the P=16 fp16 sweep alone, one launch per step: per step,
+        # one untimed launch then three groups of 5 timed ones (HIP events around
+        # each group; the median group), for
+        # ring and RHD AllReduce / reduce-scatter / all-gather at the given sizes;
+        # steps with no items launch nothing and are skipped
+        P = 16
+        for nbytes in [int(x) for x in a.sweep_sizes.split(",") if x]:
+            L = nbytes // 2
+            bufs = upload("sweep_p16_fp16", P, L)
+            pristine = [b.clone() for b in bufs]
+            for algo in ("ring", "rhd"):
+                with hc.Comm(P, algo) as c:
+                    c.set_exec_mode("steps")
+                    for coll in ("allreduce", "reduce_scatter", "all_gather"):
+                        for b, q in zip(bufs, pristine):
+                            b.copy_(q)
+                        n = c.plan_info(coll, L, "fp16")["nsteps"]
+                        rows = []
+                        for st in range(n):
+                            si = c.step_info(coll, L, "fp16", st)
+                            if si["nitems"] == 0:
+                                continue
+                            ts = time_calls(lambda: c.run_steps(coll, bufs, st, st + 1, "fp16", "sum"), 5, 1)
+                            rows.append(dict(step=st, nitems=si["nitems"], hbm_bytes=si["hbm_bytes"],
+                                             us=round(ts * 1e6, 2), GBps=round(si["hbm_bytes"] / ts / 1e9, 1)))
+                        emit(workload="sweep_steps_p16_fp16", algo=algo, coll=coll, P=P, bytes_per_rank=nbytes,
+                             launch_form="steps", steps=rows)
+            del bufs, pristine
+            torch.cuda.empty_cache()
 
     if "forms" in workloads:
         # launch forms across sizes: one launch per step, the single-workgroup

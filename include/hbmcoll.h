@@ -160,8 +160,20 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    of the column for the whole launch, so steps need no barrier.  The
  *    column length is column_bytes when set, else chosen per call shape by
  *    the model below among 16 B, 32 B, ... lengths that fit LDS;
+ *  - HBMC_EXEC_REGS: a whole AllReduce in one launch that keeps every
+ *    operand in registers.  The schedule is replayed on the host over
+ *    symbols: each element's final value on each rank is an expression over
+ *    the P inputs at that element, in the schedule's grouping.  Where every
+ *    rank ends with the same expression, and it is a left fold over the
+ *    ranks (the ring: segment c folds ranks c+1, c+2, ..., c; Flat) or a
+ *    complete pairwise tree whose leaves are single ranks or merged pairs
+ *    (RHD, also with P not a power of two), with at most 16 folded terms
+ *    or tree leaves and at most 32 regions of distinct parameters, one lane
+ *    per 16-byte position loads every rank's value once, evaluates the
+ *    expression and stores the result to every rank ([RHD] "耗时计算":
+ *    every step pays alpha, which this form pays once);
  *  - HBMC_EXEC_AUTO (default, or the environment variable HBMC_EXEC = auto,
- *    steps, fused, columns or lds): per call the eligible form of least
+ *    steps, fused, columns, lds or regs): per call the eligible form of least
  *    modelled time, with constants measured on MI355X: steps sum over the
  *    steps max(4.2 us, 3 us + bytes / 6.4 TB/s); fused 2 us + 1.6 us per
  *    step + bytes / 33 GB/s; columns 4 us + 0.85 us per chunk of the longest
@@ -169,7 +181,10 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    steps); lds 4 us + R * H * N * 0.56 us + 2 P count e / 5 TB/s, with R
  *    the columns each workgroup runs one after another, H the serial chunk
  *    passes of the busiest column (a run of n same-range chunks of one step
- *    counting 1 + 0.75 (n - 1)) and N the 16-byte positions per lane.
+ *    counting 1 + 0.75 (n - 1)) and N the 16-byte positions per lane.  REGS,
+ *    where eligible, is taken before any other form: on MI355X it measured
+ *    fastest, or within 11% of the fastest, in every case timed (rings, RHD
+ *    and Flat of 3-16 ranks, 1 KiB-4 MiB per rank).
  * A forced form falls back to STEPS where it is not eligible.  Eligibility:
  * both one-launch forms need rank buffers of one 16-byte phase; FUSED needs
  * at most 256 items per step and at most `max_bytes` algorithmic bytes in
@@ -180,11 +195,15 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  * HBMC_COLUMNS_LIMIT): working sets the caches hold, so that larger calls
  * keep the per-step HBM traffic the schedule defines; LDS needs what COLUMNS
  * needs, and a column of every rank buffer plus 160 bytes per chunk of the
- * longest column within one workgroup's LDS.  The forms apply to
+ * longest column within one workgroup's LDS; REGS needs what COLUMNS needs,
+ * an AllReduce, all of its steps, and the expression forms above.  The
+ * element ops commute bit for bit, so every form gives the same bits.  The
+ * forms apply to
  * every call, hbmc_run_steps ranges and graph nodes.  Host only.
  */
 typedef enum {
-  HBMC_EXEC_AUTO = 0, HBMC_EXEC_STEPS = 1, HBMC_EXEC_FUSED = 2, HBMC_EXEC_COLUMNS = 3, HBMC_EXEC_LDS = 4
+  HBMC_EXEC_AUTO = 0, HBMC_EXEC_STEPS = 1, HBMC_EXEC_FUSED = 2, HBMC_EXEC_COLUMNS = 3, HBMC_EXEC_LDS = 4,
+  HBMC_EXEC_REGS = 5
 } hbmc_exec_t;
 hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode);
 hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes);
@@ -206,7 +225,8 @@ hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
  *  - LDS: exactly what the kernel loads and stores: every column of every
  *    rank it loads, and every column range it stores (composed store
  *    records in a launch of all steps), for the column length the
- *    communicator would use.
+ *    communicator would use;
+ *  - REGS: every rank's vector loaded once and stored once, 2 P count e.
  * HBMC_ERR_INVALID_ARG for a bad step range, or for LDS when no column
  * length fits one workgroup's LDS.  The figure does not depend on whether
  * the form is eligible for the call. */

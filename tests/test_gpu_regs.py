@@ -1,0 +1,66 @@
+"""GPU parity of the register form (HBMC_EXEC_REGS) against the oracle, bit for bit.
+
+The register form evaluates each element's expression, derived on the host
+from the schedule, in registers.  Cases span ring (a left fold rotated per
+segment), RHD (pairwise trees, with merged pairs when P is not a power of
+two) and Flat; all dtypes and ops; lengths whose segment edges cut 16-byte
+positions (element-wise lanes), lengths below one vector, and rank buffers
+at every 16-byte phase (head and tail elements).
+"""
+import numpy as np
+import pytest
+import torch
+
+import allreduce_reduction_amd as hc
+import oracle
+import refops
+from gpu_util import strided_buffers, to_dev, to_host
+from test_gpu_parity import make_inputs, say
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["fp32", "fp16", "bf16", "int32", "int8"]
+OPS = ["sum", "prod", "max", "min"]
+
+
+def run_regs(algo, P, L, dtype, op, seed, offsets=None):
+    xs = make_inputs(dtype, op, P, L, seed)
+    if offsets is None:
+        dev = [to_dev(x, dtype) for x in xs]
+    else:
+        dev, _keep = strided_buffers(xs, dtype, offsets)
+    with hc.Comm(P, algo) as c:
+        c.set_exec_mode("regs")
+        form = c.exec_choice("allreduce", L, dtype)
+        say(f"case regs {algo} P={P} L={L} {dtype} {op} offsets={offsets} -> {form}")
+        c.allreduce(dev, dtype, op)
+        torch.cuda.synchronize()
+    want = [x.copy() for x in xs]
+    oracle.run("allreduce", algo, want, dtype, op)
+    for r in range(P):
+        got = to_host(dev[r], dtype)
+        refops.assert_same(dtype, got, want[r], f"regs {algo} P={P} L={L} {dtype} {op} rank {r}")
+        if op in ("max", "min") and dtype in refops.FLOATS:
+            assert np.array_equal(got.view(np.uint8), want[r].view(np.uint8))
+    return form
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("algo,P", [("ring", 8), ("ring", 3), ("ring", 16), ("rhd", 8), ("rhd", 5),
+                                    ("rhd", 6), ("rhd", 16), ("flat", 7)])
+def test_regs_parity(algo, P, dtype):
+    forms = set()
+    for i, op in enumerate(OPS):
+        for L in (1, 7, 1001, 3 * 4096 + 5, 40_000 + 3):
+            forms.add(run_regs(algo, P, L, dtype, op, seed=1000 * i + L))
+    assert forms == {"regs"}
+
+
+@pytest.mark.parametrize("algo,P", [("ring", 8), ("rhd", 5)])
+def test_regs_phases(algo, P):
+    """Rank buffers at one shared 16-byte phase other than 0: the head and
+    tail elements go element by element."""
+    for dtype in ("fp16", "int8", "fp32"):
+        e = np.dtype(refops.STORAGE[dtype]).itemsize
+        for ph in range(0, 16 // e):
+            assert run_regs(algo, P, 2000 + ph, dtype, "sum", seed=ph, offsets=[ph] * P) == "regs"

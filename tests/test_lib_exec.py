@@ -17,31 +17,40 @@ import allreduce_reduction_amd as hc
 
 def test_auto_regimes_ring_p8_fp16():
     with hc.Comm(8, "ring") as c:
-        assert c.exec_choice("allreduce", 512, "fp16") == "lds"            # 1 KiB per rank
-        assert c.exec_choice("allreduce", 32 << 10, "fp16") == "lds"       # 64 KiB per rank
-        assert c.exec_choice("allreduce", 2 << 20, "fp16") in ("lds", "columns")  # 4 MiB per rank (32 MiB total)
+        assert c.exec_choice("allreduce", 512, "fp16") == "regs"           # 1 KiB per rank
+        assert c.exec_choice("allreduce", 32 << 10, "fp16") == "regs"      # 64 KiB per rank
+        assert c.exec_choice("allreduce", 2 << 20, "fp16") == "regs"       # 4 MiB per rank (32 MiB total)
         assert c.exec_choice("allreduce", 8 << 20, "fp16") == "steps"      # 16 MiB per rank: over the limit
         assert c.exec_choice("allreduce", 64 << 20, "fp32") == "steps"     # the 256 MiB per rank workload
+        # the stand-alone collectives have no single expression per element
+        assert c.exec_choice("reduce_scatter", 512, "fp16") == "lds"
+        assert c.exec_choice("all_gather", 32 << 10, "fp16") == "lds"
 
 
 def test_auto_small_rhd_many_ranks_prefers_the_single_workgroup():
-    # 1 KiB per rank over 64 ranks: 16-byte segments, so every LDS column
-    # holds chunks of many segments' steps; one workgroup is cheaper
+    # 1 KiB per rank over 64 ranks (a tree of 64 leaves: no register form):
+    # 16-byte segments, so every LDS column holds chunks of many segments'
+    # steps; one workgroup is cheaper
     with hc.Comm(64, "rhd") as c:
         assert c.exec_choice("allreduce", 512, "fp16") == "fused"
         assert c.exec_choice("allreduce", 8 << 10, "fp16") == "lds"
-    # over 16 ranks (64-byte segments) the LDS form's columns fit within a
-    # segment and its halving passes alone count (on MI355X: 12.3-12.5 us
-    # against 14.9-15.1 us for the single workgroup)
+    # over 16 ranks the register form takes the whole tree (on MI355X, graphs
+    # of ten: 7.0-7.1 us against 14.2 us in the LDS form and 15.4 us in the
+    # single workgroup); its reduce-scatter keeps the LDS form
     with hc.Comm(16, "rhd") as c:
-        assert c.exec_choice("allreduce", 512, "fp16") == "lds"
+        assert c.exec_choice("allreduce", 512, "fp16") == "regs"
+        assert c.exec_choice("reduce_scatter", 512, "fp16") != "regs"
 
 
 def test_auto_prefers_steps_where_launches_are_few_and_bytes_many():
     # Flat has two steps: at 4 MiB per rank (64 MiB in all, within the column
     # limit) two launches beat streaming every rank buffer through LDS and
-    # folding 16 sources per chunk there
+    # folding 17 sources per chunk there; a fold over 16 ranks fits the
+    # register form instead
     with hc.Comm(16, "flat") as c:
+        assert c.exec_choice("allreduce", 32 << 10, "fp16") == "regs"
+    # over 17 ranks the fold is too long for registers
+    with hc.Comm(17, "flat") as c:
         assert c.exec_choice("allreduce", 2 << 20, "fp16") == "steps"
         assert c.exec_choice("allreduce", 32 << 10, "fp16") == "lds"
 
@@ -67,7 +76,12 @@ def test_forced_forms_and_fallbacks():
         assert c.exec_choice("allreduce", 512, "fp16") == "steps"          # no one-launch form eligible
         c.set_fused_limit(64 << 20)
         c.set_columns(64 << 20)
-        assert c.exec_choice("allreduce", 512, "fp16") == "lds"
+        assert c.exec_choice("allreduce", 512, "fp16") == "regs"
+        c.set_exec_mode("regs")
+        assert c.exec_choice("allreduce", 512, "fp16") == "regs"
+        c.set_columns(0)
+        assert c.exec_choice("allreduce", 512, "fp16") == "steps"          # over the column limit
+        c.set_columns(64 << 20)
         c.set_exec_mode("lds")
         assert c.exec_choice("allreduce", 512, "fp16") == "lds"
         assert c.exec_choice("allreduce", 512, "fp16", first=0, last=1) == "steps"
@@ -96,7 +110,8 @@ def test_exec_choice_edges_and_validation():
         with pytest.raises(KeyError):
             c.set_exec_mode("bogus")
         lib = hc.load_library()
-        assert lib.hbmc_comm_set_exec_mode(c._h, 5) == 1
+        assert lib.hbmc_comm_set_exec_mode(c._h, 6) == 1
+        assert lib.hbmc_comm_set_exec_mode(c._h, 5) == 0
     with hc.Comm(1, "ring") as c:
         assert c.exec_choice("allreduce", 100, "fp32") == "steps"
 
@@ -164,3 +179,29 @@ def test_exec_bytes_rejects_bad_ranges():
         assert lib.hbmc_exec_bytes(c._h, 0, 0, 1000, 1, 0, 0, 9, ctypes.byref(b)) == 1   # bad mode
         assert lib.hbmc_exec_bytes(c._h, 0, 0, 1000, 1, 0, 0, 1, None) == 1
         assert lib.hbmc_exec_bytes(c._h, 0, 0, 0, 1, 0, 0, 4, ctypes.byref(b)) == 0 and b.value == 0
+
+
+def test_regs_only_where_the_expression_is_a_fold_or_tree():
+    """Pipeline, tree, hierarchical AllReduce and stand-alone collectives keep
+    another form; a forced REGS falls back to one launch per step."""
+    with hc.Comm(8, "pipeline", 2, 4) as c:
+        c.set_exec_mode("regs")
+        assert c.exec_choice("allreduce", 10_000, "fp32") == "steps"
+    with hc.Comm(8, "ring") as c:
+        c.set_exec_mode("regs")
+        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "steps"
+        assert c.exec_choice("allreduce", 10_000, "fp32") == "regs"
+        assert c.exec_choice("allreduce", 10_000, "fp32", first=0, last=3) == "steps"
+    with hc.Comm(64, "ring") as c:  # a fold of 64 terms: beyond 16
+        c.set_exec_mode("regs")
+        assert c.exec_choice("allreduce", 10_000, "fp32") == "steps"
+
+
+@pytest.mark.parametrize("algo,P", [("ring", 2), ("ring", 3), ("ring", 8), ("ring", 16), ("rhd", 5), ("rhd", 6),
+                                    ("rhd", 8), ("rhd", 16), ("rhd", 24), ("flat", 7), ("flat", 16)])
+def test_regs_offered_for_folds_and_trees(algo, P):
+    with hc.Comm(P, algo) as c:
+        c.set_exec_mode("regs")
+        for L in (1, 5, 1001, 100_003):
+            assert c.exec_choice("allreduce", L, "bf16") == "regs", L
+            assert c.exec_bytes("allreduce", L, "bf16", "regs") == 2 * P * L * 2
