@@ -169,6 +169,7 @@ def suite(a):
                         for b, q in zip(bufs, pristine):
                             b.copy_(q)
                         form = c.exec_choice("allreduce", L, dtype)
+                        moved = c.exec_bytes("allreduce", L, dtype, form)
                         t = time_calls(lambda: c.allreduce(bufs, dtype, op), 200, 20)
                         t_cold = time_cold(lambda: c.allreduce(bufs, dtype, op), 31, scrub)
                         c.set_exec_mode("steps")
@@ -185,7 +186,6 @@ def suite(a):
                                 g10.add(c, "allreduce", bufs, dtype, op)
                             g10.build()
                             tg10 = time_calls(lambda: g10.launch(), 50, 5) / 10
-                    moved = c.exec_bytes("allreduce", L, dtype, form)
                     emit(workload="rhd_small", algo="rhd", coll="allreduce", P=P, dtype=dtype, op=op,
                          bytes_per_rank=L * e, launch_form=form, moved_bytes=moved,
                          pct_hbm_moved=round(100 * moved / t / HBM_PEAK, 2),
@@ -279,7 +279,7 @@ def suite(a):
                         reps = max(5, min(200, int(1e8 // info["hbm_bytes"])))
                         auto_form = c.exec_choice("allreduce", L, "fp16")
                         pct = {}
-                        for form in ("steps", "fused", "columns", "lds", "auto"):
+                        for form in ("steps", "fused", "columns", "lds", "regs", "auto"):
                             c.set_exec_mode(form)
                             if form != "auto" and c.exec_choice("allreduce", L, "fp16") != form:
                                 continue
