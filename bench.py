@@ -532,7 +532,12 @@ def main():
                      "timing": ("HIP events around the P-1 back-to-back reduce-scatter launches of each of "
                                 "K AllReduces, mean per launch" if a.algo == "ring" else
                                 "HIP events between consecutive step launches, mean per launch"),
-                     "stepwise_events_mean_launch_us": round(stepwise_rs_ms * 1e3, 2)},
+                     "stepwise_events_mean_launch_us": round(stepwise_rs_ms * 1e3, 2),
+                     "traffic_note": ("counted at the L2-to-fabric interface (FETCH_SIZE x 1.9998 + WRITE_SIZE, "
+                                      "calibrated on a 256 MiB device copy); a read served by the 256 MiB "
+                                      "memory-side cache counts like one from HBM, and each step writes 256 MiB "
+                                      "with plain stores, so part of the next step's reads of those blocks "
+                                      "come from that cache rather than from HBM")},
     }
     if ag_ms:
         ag_bytes = comm.step_info("allreduce", L, dtype, ag_steps[0])["hbm_bytes"]
