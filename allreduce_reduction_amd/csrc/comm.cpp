@@ -694,12 +694,11 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     if (st != HBMC_OK) return st;
     lds_ok = p->lds_col > 0;
   }
-  // the register form: a whole AllReduce whose every element ends with one
-  // fold or pairwise tree of the ranks' inputs, within the column limit
+  // the register form: a whole call whose every element ends with one of
+  // the register form's expressions (see regs.hpp), within the column limit
   const bool whole = first == 0 && last == static_cast<int>(p->sched.steps.size());
   bool regs_ok = false;
-  if (cols_ok && whole && p->coll == HBMC_COLL_ALLREDUCE &&
-      (c->exec_mode == kExecRegs || c->exec_mode == kExecAuto)) {
+  if (cols_ok && whole && (c->exec_mode == kExecRegs || c->exec_mode == kExecAuto)) {
     if (!p->regs_built) {
       derive_regs(p->sched, P, count, &p->regs);
       p->regs_built = true;
@@ -756,9 +755,10 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     }
   }
   // the register form, where eligible, measured fastest or within 11% of the
-  // fastest form in every case timed on MI355X (rings, RHD and Flat of 3-16
-  // ranks, 1 KiB-4 MiB per rank, graphs of ten AllReduces), and 1.5-5x
-  // faster than the LDS form up to 1 MiB per rank
+  // fastest form in every case timed on MI355X (AllReduce over rings, RHD,
+  // Flat and trees of 3-17 ranks; the ring's reduce-scatter, ring and RHD
+  // all-gathers, RHD broadcast; 1 KiB-4 MiB per rank, graphs of ten calls),
+  // and 1.5-5x faster than the LDS form up to 1 MiB per rank
   if (regs_ok) *mode = kExecRegs;
   (void)best;
   return HBMC_OK;
@@ -808,8 +808,14 @@ hbmc_status_t exec_bytes(hbmc_comm* c, Plan* p, int first, int last, uint64_t co
     return HBMC_OK;
   }
   if (mode == kExecRegs) {
-    // every rank's vector loaded once and stored once
-    *bytes = 2 * uint64_t(P) * count * e;
+    // every operand's vector loaded once, every destination's stored once
+    if (first != 0 || last != static_cast<int>(p->sched.steps.size())) return HBMC_ERR_INVALID_ARG;
+    if (!p->regs_built) {
+      derive_regs(p->sched, P, count, &p->regs);
+      p->regs_built = true;
+    }
+    if (!p->regs.ok) return HBMC_ERR_INVALID_ARG;
+    *bytes = uint64_t(p->regs.loads + p->regs.stores) * count * e;
     return HBMC_OK;
   }
   if (mode != kExecLds) return HBMC_ERR_INVALID_ARG;
@@ -876,7 +882,7 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
   st = choose_exec(c, p, first, last, count, e, aligned, &mode);
   if (st != HBMC_OK) return st;
   if (mode == kExecRegs) {
-    // the whole AllReduce as one register-form launch
+    // the whole call as one register-form launch
     KernelDesc k;
     describe_regs(dtype, op, ptrs, P, p->regs, count, phase, &k);
     launches->push_back(k);

@@ -1,9 +1,10 @@
-// The register form of a whole AllReduce (see regs.hpp).  grid.y indexes the
+// The register form of a whole call (see regs.hpp).  grid.y indexes the
 // regions of elements that share one expression; a lane of region g takes
-// one 16-byte position of the vector, loads every rank's value there into
+// one 16-byte position of the vector, loads every operand there into
 // registers at once, evaluates the schedule's expression in its grouping --
-// a left fold over a rank sequence, or a complete pairwise tree over single
-// ranks and merged pairs -- and stores the result to every rank.  A region's
+// a left fold over a rank sequence, a complete pairwise tree over single
+// ranks and merged pairs, a copy of one rank, or the prefixes of a fold --
+// and stores every rank the schedule writes there.  A region's
 // operand addresses travel in its record in the kernel arguments, so a
 // workgroup waits on one round of scalar loads (its record) and one round of
 // data loads: no table in device memory, no LDS, no barrier.  The region's
@@ -74,6 +75,34 @@ __device__ __forceinline__ void store_all(uint32_t n, unsigned char* const* ptr,
   }
 }
 
+// One position (a 16-byte vector, or one element) of a region: the
+// operands loaded, combined and stored as the form says.
+template <int FORM, typename V, typename Load, typename Op, typename Store>
+__device__ __forceinline__ void position(uint32_t n, unsigned char* const* ptr, Load load, Op op, Store store) {
+  if constexpr (FORM == kRegCopy) {
+    const V v = load(ptr[0]);
+#pragma unroll
+    for (uint32_t i = 1; i < kRegMaxLeaves; ++i)
+      if (i < n) store(ptr[i], v);
+  } else if constexpr (FORM == kRegPrefix) {
+    V x[kRegMaxLeaves];
+#pragma unroll
+    for (uint32_t i = 0; i < kRegMaxLeaves; ++i)
+      if (i < n) x[i] = load(ptr[i]);
+    V acc = x[0];
+#pragma unroll
+    for (uint32_t i = 1; i < kRegMaxLeaves; ++i) {
+      if (i < n) {
+        acc = op(acc, x[i]);
+        store(ptr[i], acc);
+      }
+    }
+  } else {
+    const V v = eval<FORM, V>(n, ptr, load, op);
+    store_all<FORM>(n, ptr, [&](unsigned char* p) { store(p, v); });
+  }
+}
+
 template <int DT, int OP, int FORM, typename Call>
 __global__ void __launch_bounds__(kRegThreads)
 plan_regs(Call c) {
@@ -101,10 +130,10 @@ plan_regs(Call c) {
   const uint64_t k = uint64_t(R.vec_lo) + uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (k < R.vec_hi) {
     const uint64_t off = (head + k * EPV) * E;
-    const u32x4 v = eval<FORM, u32x4>(
+    position<FORM, u32x4>(
         c.n, R.ptr, [&](const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p + off); },
-        [](u32x4 a, u32x4 b) { return op_vec<DT, OP>(a, b); });
-    store_all<FORM>(c.n, R.ptr, [&](unsigned char* p) { store_vec(reinterpret_cast<u32x4*>(p + off), v); });
+        [](u32x4 a, u32x4 b) { return op_vec<DT, OP>(a, b); },
+        [&](unsigned char* p, u32x4 v) { store_vec(reinterpret_cast<u32x4*>(p + off), v); });
   }
   if (blockIdx.x == 0) {
 #pragma unroll
@@ -112,10 +141,10 @@ plan_regs(Call c) {
       const uint64_t e = uint64_t(R.el_lo[part]) + threadIdx.x;
       if (e < R.el_hi[part]) {
         const uint64_t off = e * E;
-        const uint32_t v = eval<FORM, uint32_t>(
+        position<FORM, uint32_t>(
             c.n, R.ptr, [&](const unsigned char* p) { return load_elem<E>(p + off); },
-            [](uint32_t a, uint32_t b) { return op_word<DT, OP>(a, b); });
-        store_all<FORM>(c.n, R.ptr, [&](unsigned char* p) { store_elem<E>(p + off, v); });
+            [](uint32_t a, uint32_t b) { return op_word<DT, OP>(a, b); },
+            [&](unsigned char* p, uint32_t v) { store_elem<E>(p + off, v); });
       }
     }
   }
@@ -123,8 +152,12 @@ plan_regs(Call c) {
 
 template <int DT, int OP>
 const void* regs_fn(uint32_t form) {
-  return form == kRegTree ? reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTree, RegTreeCall>)
-                          : reinterpret_cast<const void*>(plan_regs<DT, OP, kRegFold, RegFoldCall>);
+  switch (form) {
+    case kRegTree: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTree, RegTreeCall>);
+    case kRegCopy: return reinterpret_cast<const void*>(plan_regs<DT, kSum, kRegCopy, RegFoldCall>);
+    case kRegPrefix: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegPrefix, RegFoldCall>);
+    default: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegFold, RegFoldCall>);
+  }
 }
 
 template <int DT>

@@ -1,5 +1,5 @@
-// The register form of a whole AllReduce: deriving each element's expression
-// from the schedule (host only).
+// The register form of a whole call: deriving each element's expression from
+// the schedule (host only).
 #include "regs.hpp"
 
 #include <algorithm>
@@ -159,13 +159,6 @@ void derive_regs(const Schedule& s, int P, uint64_t count, RegPlan* out) {
         for (int q = it.nsrc; q < it.nsrc + it.ndst; ++q) v[it.rank[q]] = x;
       }
     }
-  // one expression for every rank of every interval, all of one form
-  std::vector<int> expr(nint);
-  for (size_t t = 0; t < nint; ++t) {
-    expr[t] = val[t * P];
-    for (int r = 1; r < P; ++r)
-      if (val[t * P + r] != expr[t]) return;
-  }
   std::vector<RegRegion> regs;
   auto push = [&](uint64_t end, const RegRegion& r) {
     if (!regs.empty() && std::memcmp(regs.back().a, r.a, sizeof(r.a)) == 0 &&
@@ -178,6 +171,63 @@ void derive_regs(const Schedule& s, int P, uint64_t count, RegPlan* out) {
   };
   std::vector<std::pair<int, int>> leaves;
   std::vector<int> seq;
+  auto finish = [&](RegForm form, uint32_t n, uint32_t loads, uint32_t stores) {
+    if (regs.size() > size_t(form == kRegTree ? kRegMaxTreeRegions : kRegMaxFoldRegions)) return;
+    out->ok = true;
+    out->form = form;
+    out->n = n;
+    out->loads = loads;
+    out->stores = stores;
+    out->regions = regs;
+  };
+  bool same = true;
+  std::vector<int> expr(nint);
+  for (size_t t = 0; t < nint; ++t) {
+    expr[t] = val[t * P];
+    for (int r = 1; r < P; ++r) same = same && val[t * P + r] == expr[t];
+  }
+  if (!same) {
+    // prefixes of one fold: the first rank holding a fold over all P ranks
+    // names the sequence; rank seq[0] keeps its input and rank seq[i] holds
+    // the fold over seq[0..i]
+    if (P > kRegMaxLeaves) return;
+    for (size_t t = 0; t < nint; ++t) {
+      const int* v = &val[t * P];
+      bool found = false;
+      for (int r = 0; r < P && !found; ++r) found = as_fold(X, v[r], &seq) && seq.size() == size_t(P);
+      if (!found) return;
+      // the first two operands of a fold commute: the one that keeps its input goes first
+      if (v[seq[0]] != seq[0]) std::swap(seq[0], seq[1]);
+      if (v[seq[0]] != seq[0]) return;
+      int pre = seq[0];
+      for (int i = 1; i < P; ++i) {
+        pre = X.op(pre, seq[i]);
+        if (v[seq[i]] != pre) return;
+      }
+      RegRegion r;
+      std::memset(&r, 0xff, sizeof(r));
+      for (int i = 0; i < P; ++i) r.a[i] = static_cast<uint8_t>(seq[i]);
+      push(cut[t + 1], r);
+    }
+    finish(kRegPrefix, static_cast<uint32_t>(P), static_cast<uint32_t>(P), static_cast<uint32_t>(P - 1));
+    return;
+  }
+  bool copy = true;
+  for (size_t t = 0; t < nint; ++t) copy = copy && X.leaf(expr[t]);
+  if (copy) {
+    // every rank ends with rank expr[t]'s input
+    if (P > kRegMaxLeaves) return;
+    for (size_t t = 0; t < nint; ++t) {
+      RegRegion r;
+      std::memset(&r, 0xff, sizeof(r));
+      r.a[0] = static_cast<uint8_t>(expr[t]);
+      for (int q = 0, i = 1; q < P; ++q)
+        if (q != expr[t]) r.a[i++] = static_cast<uint8_t>(q);
+      push(cut[t + 1], r);
+    }
+    finish(kRegCopy, static_cast<uint32_t>(P), 1, static_cast<uint32_t>(P - 1));
+    return;
+  }
   bool tree = true;
   uint32_t n = 0;
   for (size_t t = 0; t < nint && tree; ++t) {
@@ -206,7 +256,6 @@ void derive_regs(const Schedule& s, int P, uint64_t count, RegPlan* out) {
       push(cut[t + 1], r);
     }
   }
-  if (regs.size() > size_t(form == kRegTree ? kRegMaxTreeRegions : kRegMaxFoldRegions)) return;
   // every rank exactly once among each region's operands: they are also the
   // destinations the result is stored to
   for (const RegRegion& r : regs) {
@@ -218,10 +267,7 @@ void derive_regs(const Schedule& s, int P, uint64_t count, RegPlan* out) {
     for (int q = 0; q < P; ++q)
       if (!seen[q]) return;
   }
-  out->ok = true;
-  out->form = form;
-  out->n = n;
-  out->regions = regs;
+  finish(form, n, static_cast<uint32_t>(P), static_cast<uint32_t>(P));
 }
 
 }  // namespace hbmc

@@ -1,19 +1,23 @@
-// The register form of a whole AllReduce (host side).
+// The register form of a whole collective (host side).
 //
 // Every step combines operands at equal element offsets, so the value an
 // element ends with on a rank is one expression over the P inputs at that
 // offset, fixed by the schedule: which ranks' values each step combines, and
 // in which grouping.  The host derives that expression by replaying the
 // schedule symbolically over the intervals of elements that the same items
-// cover.  Where every rank ends with one and the same expression, and that
-// expression is
-//   - a left fold  ((x_s0 op x_s1) op x_s2) op ... over all P ranks (the
-//     ring, with the sequence rotated per segment; Flat), or
-//   - a complete binary tree of depth k whose 2^k leaves are single ranks
-//     or pairs (x_a op x_b) (recursive halving-doubling, its merged pairs
-//     included),
-// one kernel evaluates it in registers: every rank's value loaded once, the
-// expression's operations in its grouping, the result stored to every rank.
+// cover.  Where, in every interval,
+//   - every rank ends with one and the same expression, and it is a left
+//     fold ((x_s0 op x_s1) op x_s2) op ... over all P ranks (the ring's
+//     AllReduce, with the sequence rotated per segment; Flat), or a complete
+//     binary tree of depth k whose 2^k leaves are single ranks or pairs
+//     (x_a op x_b) (recursive halving-doubling, its merged pairs included),
+//   - or every rank ends with one rank's input (an all-gather, a
+//     broadcast: a copy),
+//   - or the ranks end with the prefixes of one left fold over all P ranks,
+//     each rank holding the prefix that ends with its own input (the ring's
+//     reduce-scatter),
+// one kernel evaluates it in registers: every operand loaded once, the
+// operations in the schedule's grouping, and every rank's result stored.
 // The element ops are commutative bit for bit (IEEE sum / product, wrapping
 // integers, max / min with a canonical NaN), so only the grouping fixes the
 // bits, and the kernel keeps it.
@@ -30,11 +34,14 @@ constexpr int kRegMaxLeaves = 16;       // fold length / tree leaves
 constexpr int kRegMaxFoldRegions = 16;  // intervals of distinct parameters, fold form
 constexpr int kRegMaxTreeRegions = 8;   // and tree form (each region's addresses travel in
                                         // the kernel arguments)
-enum RegForm : uint32_t { kRegFold = 0, kRegTree = 1 };
+enum RegForm : uint32_t { kRegFold = 0, kRegTree = 1, kRegCopy = 2, kRegPrefix = 3 };
 
 // Elements [previous region's end, end) take: for kRegFold the left fold over
-// a[0..n); for kRegTree the tree over leaves v < n = 2^k, leaf v being rank
-// a[v], or a[v] op b[v] when b[v] != 0xff.
+// a[0..n), stored to every rank; for kRegTree the tree over leaves v < n =
+// 2^k, leaf v being rank a[v], or a[v] op b[v] when b[v] != 0xff, stored to
+// every rank; for kRegCopy rank a[0]'s value, stored to ranks a[1..n); for
+// kRegPrefix the left fold over a[0..n), rank a[i] (i >= 1) receiving the
+// fold over a[0..i].
 struct RegRegion {
   uint64_t end;
   uint8_t a[kRegMaxLeaves];
@@ -43,13 +50,14 @@ struct RegRegion {
 static_assert(sizeof(RegRegion) == 40, "register-form region");
 
 struct RegPlan {
-  bool ok = false;  // the whole AllReduce can run in the register form
+  bool ok = false;  // the whole collective can run in the register form
   RegForm form = kRegFold;
-  uint32_t n = 0;   // fold length or tree leaves (one value for all regions)
+  uint32_t n = 0;   // operands (fold length, tree leaves; one value for all regions)
+  uint32_t loads = 0, stores = 0;  // per element position, every region
   std::vector<RegRegion> regions;
 };
 
-// Derive the register form of an AllReduce schedule of P ranks over `count`
+// Derive the register form of a whole schedule of P ranks over `count`
 // elements; out->ok is false where the form does not apply.
 void derive_regs(const Schedule& s, int P, uint64_t count, RegPlan* out);
 

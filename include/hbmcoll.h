@@ -160,18 +160,24 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    of the column for the whole launch, so steps need no barrier.  The
  *    column length is column_bytes when set, else chosen per call shape by
  *    the model below among 16 B, 32 B, ... lengths that fit LDS;
- *  - HBMC_EXEC_REGS: a whole AllReduce in one launch that keeps every
- *    operand in registers.  The schedule is replayed on the host over
- *    symbols: each element's final value on each rank is an expression over
- *    the P inputs at that element, in the schedule's grouping.  Where every
- *    rank ends with the same expression, and it is a left fold over the
- *    ranks (the ring: segment c folds ranks c+1, c+2, ..., c; Flat) or a
+ *  - HBMC_EXEC_REGS: a whole call in one launch that keeps every operand
+ *    in registers.  The schedule is replayed on the host over symbols: each
+ *    element's final value on each rank is an expression over the P inputs
+ *    at that element, in the schedule's grouping.  The form applies where,
+ *    in every interval of elements, either every rank ends with the same
+ *    expression and it is a left fold over the ranks (the ring's AllReduce:
+ *    segment c folds ranks c+1, c+2, ..., c; Flat; small trees) or a
  *    complete pairwise tree whose leaves are single ranks or merged pairs
- *    (RHD, also with P not a power of two), with at most 16 folded terms
- *    or tree leaves and at most 32 regions of distinct parameters, one lane
- *    per 16-byte position loads every rank's value once, evaluates the
- *    expression and stores the result to every rank ([RHD] "耗时计算":
- *    every step pays alpha, which this form pays once);
+ *    (RHD's AllReduce, also with P not a power of two); or every rank ends
+ *    with one rank's input (all-gathers of ring, RHD and pipeline, RHD's
+ *    broadcast); or the ranks hold the prefixes of one left fold over all
+ *    ranks (the ring's reduce-scatter, whose other segments keep the
+ *    schedule's partial sums).  At most 16 folded terms, tree leaves or
+ *    copies, and at most 16 (fold, copy, prefix) or 8 (tree) intervals of
+ *    distinct parameters.  One lane per 16-byte position loads every
+ *    operand once, evaluates the expression and stores every rank the
+ *    schedule writes there ([RHD] "耗时计算": every step pays alpha, which
+ *    this form pays once);
  *  - HBMC_EXEC_AUTO (default, or the environment variable HBMC_EXEC = auto,
  *    steps, fused, columns, lds or regs): per call the eligible form of least
  *    modelled time, with constants measured on MI355X: steps sum over the
@@ -196,7 +202,7 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  * keep the per-step HBM traffic the schedule defines; LDS needs what COLUMNS
  * needs, and a column of every rank buffer plus 160 bytes per chunk of the
  * longest column within one workgroup's LDS; REGS needs what COLUMNS needs,
- * an AllReduce, all of its steps, and the expression forms above.  The
+ * all of the call's steps, and the expression forms above.  The
  * element ops commute bit for bit, so every form gives the same bits.  The
  * forms apply to
  * every call, hbmc_run_steps ranges and graph nodes.  Host only.
@@ -226,10 +232,13 @@ hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
  *    rank it loads, and every column range it stores (composed store
  *    records in a launch of all steps), for the column length the
  *    communicator would use;
- *  - REGS: every rank's vector loaded once and stored once, 2 P count e.
- * HBMC_ERR_INVALID_ARG for a bad step range, or for LDS when no column
- * length fits one workgroup's LDS.  The figure does not depend on whether
- * the form is eligible for the call. */
+ *  - REGS: every operand loaded once and every written rank stored once:
+ *    2 P count e for an AllReduce, P count e for a copy (one load, P - 1
+ *    stores), (2 P - 1) count e for the ring's reduce-scatter.
+ * HBMC_ERR_INVALID_ARG for a bad step range, for LDS when no column length
+ * fits one workgroup's LDS, and for REGS when the call has no register form
+ * or the range is not all of its steps.  Otherwise the figure does not
+ * depend on whether the form is eligible for the call. */
 hbmc_status_t hbmc_exec_bytes(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
                               int first_step, int last_step, hbmc_exec_t mode, uint64_t* bytes);
 

@@ -23,20 +23,24 @@ DTYPES = ["fp32", "fp16", "bf16", "int32", "int8"]
 OPS = ["sum", "prod", "max", "min"]
 
 
-def run_regs(algo, P, L, dtype, op, seed, offsets=None):
+def run_regs(algo, P, L, dtype, op, seed, offsets=None, coll="allreduce", S=0, M=0, root=0):
     xs = make_inputs(dtype, op, P, L, seed)
     if offsets is None:
         dev = [to_dev(x, dtype) for x in xs]
     else:
         dev, _keep = strided_buffers(xs, dtype, offsets)
-    with hc.Comm(P, algo) as c:
+    with hc.Comm(P, algo, S, M) as c:
         c.set_exec_mode("regs")
-        form = c.exec_choice("allreduce", L, dtype)
-        say(f"case regs {algo} P={P} L={L} {dtype} {op} offsets={offsets} -> {form}")
-        c.allreduce(dev, dtype, op)
+        form = c.exec_choice(coll, L, dtype, root=root)
+        say(f"case regs {algo} {coll} P={P} L={L} {dtype} {op} offsets={offsets} -> {form}")
+        if coll == "broadcast":
+            c.broadcast(dev, dtype, root=root)
+        else:
+            getattr(c, coll)(dev, dtype, op)
         torch.cuda.synchronize()
     want = [x.copy() for x in xs]
-    oracle.run("allreduce", algo, want, dtype, op)
+    kw = dict(S=S, M=M) if algo == "pipeline" else (dict(M=M) if algo == "tree" else {})
+    oracle.run(coll, algo, want, dtype, op, root=root, **kw)
     for r in range(P):
         got = to_host(dev[r], dtype)
         refops.assert_same(dtype, got, want[r], f"regs {algo} P={P} L={L} {dtype} {op} rank {r}")
@@ -64,3 +68,22 @@ def test_regs_phases(algo, P):
         e = np.dtype(refops.STORAGE[dtype]).itemsize
         for ph in range(0, 16 // e):
             assert run_regs(algo, P, 2000 + ph, dtype, "sum", seed=ph, offsets=[ph] * P) == "regs"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("algo,P,coll,S,M", [("ring", 8, "reduce_scatter", 0, 0), ("ring", 3, "reduce_scatter", 0, 0),
+                                             ("ring", 16, "reduce_scatter", 0, 0), ("ring", 8, "all_gather", 0, 0),
+                                             ("ring", 5, "all_gather", 0, 0), ("rhd", 8, "all_gather", 0, 0),
+                                             ("rhd", 6, "all_gather", 0, 0), ("rhd", 5, "broadcast", 0, 0),
+                                             ("pipeline", 8, "all_gather", 2, 4), ("tree", 5, "allreduce", 0, 2),
+                                             ("tree", 3, "allreduce", 0, 2), ("rhd", 17, "allreduce", 0, 0)])
+def test_regs_other_collectives(algo, P, coll, S, M, dtype):
+    """Copies (all-gather, broadcast), prefixes of one fold (the ring's
+    reduce-scatter, whose other segments keep the schedule's partials) and a
+    small tree AllReduce whose nesting is a fold: every rank's whole buffer
+    against the oracle."""
+    forms = set()
+    for i, op in enumerate(OPS if coll in ("reduce_scatter", "allreduce") else ["sum"]):
+        for L in (7, 1001, 3 * 4096 + 5, 40_000 + 3):
+            forms.add(run_regs(algo, P, L, dtype, op, seed=77 * i + L, coll=coll, S=S, M=M, root=P - 2))
+    assert forms == {"regs"}

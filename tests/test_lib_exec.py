@@ -22,9 +22,10 @@ def test_auto_regimes_ring_p8_fp16():
         assert c.exec_choice("allreduce", 2 << 20, "fp16") == "regs"       # 4 MiB per rank (32 MiB total)
         assert c.exec_choice("allreduce", 8 << 20, "fp16") == "steps"      # 16 MiB per rank: over the limit
         assert c.exec_choice("allreduce", 64 << 20, "fp32") == "steps"     # the 256 MiB per rank workload
-        # the stand-alone collectives have no single expression per element
-        assert c.exec_choice("reduce_scatter", 512, "fp16") == "lds"
-        assert c.exec_choice("all_gather", 32 << 10, "fp16") == "lds"
+        # the ring's reduce-scatter (prefixes of one fold) and all-gather
+        # (copies) run in registers too
+        assert c.exec_choice("reduce_scatter", 512, "fp16") == "regs"
+        assert c.exec_choice("all_gather", 32 << 10, "fp16") == "regs"
 
 
 def test_auto_small_rhd_many_ranks_prefers_the_single_workgroup():
@@ -181,20 +182,40 @@ def test_exec_bytes_rejects_bad_ranges():
         assert lib.hbmc_exec_bytes(c._h, 0, 0, 0, 1, 0, 0, 4, ctypes.byref(b)) == 0 and b.value == 0
 
 
-def test_regs_only_where_the_expression_is_a_fold_or_tree():
-    """Pipeline, tree, hierarchical AllReduce and stand-alone collectives keep
-    another form; a forced REGS falls back to one launch per step."""
+def test_regs_only_where_the_expression_is_a_fold_tree_copy_or_prefix():
+    """Calls whose elements end with other expressions keep another form; a
+    forced REGS falls back to one launch per step."""
     with hc.Comm(8, "pipeline", 2, 4) as c:
         c.set_exec_mode("regs")
+        assert c.exec_choice("allreduce", 10_000, "fp32") == "steps"      # folds of folds
+        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "steps"
+        assert c.exec_choice("all_gather", 10_000, "fp32") == "regs"      # copies
+    with hc.Comm(8, "hier", 2, 4) as c:
+        c.set_exec_mode("regs")
         assert c.exec_choice("allreduce", 10_000, "fp32") == "steps"
+    with hc.Comm(8, "tree", 0, 2) as c:  # a binary heap of 8: neither fold nor complete tree
+        c.set_exec_mode("regs")
+        assert c.exec_choice("allreduce", 10_000, "fp32") == "steps"
+    with hc.Comm(8, "rhd") as c:
+        c.set_exec_mode("regs")
+        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "steps"  # partial trees
+        assert c.exec_choice("reduce", 10_000, "fp32", root=3) == "steps"
+        assert c.exec_choice("all_gather", 10_000, "fp32") == "regs"
+        assert c.exec_choice("broadcast", 10_000, "fp32", root=3) == "regs"
     with hc.Comm(8, "ring") as c:
         c.set_exec_mode("regs")
-        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "steps"
+        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "regs"
         assert c.exec_choice("allreduce", 10_000, "fp32") == "regs"
         assert c.exec_choice("allreduce", 10_000, "fp32", first=0, last=3) == "steps"
-    with hc.Comm(64, "ring") as c:  # a fold of 64 terms: beyond 16
+        # one-step calls are one launch anyway
+    with hc.Comm(2, "ring") as c:
         c.set_exec_mode("regs")
-        assert c.exec_choice("allreduce", 10_000, "fp32") == "steps"
+        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "steps"
+    for P in (17, 64):  # folds and copies of more than 16 ranks
+        with hc.Comm(P, "ring") as c:
+            c.set_exec_mode("regs")
+            for coll in ("allreduce", "reduce_scatter", "all_gather"):
+                assert c.exec_choice(coll, 10_000, "fp32") == "steps"
 
 
 @pytest.mark.parametrize("algo,P", [("ring", 2), ("ring", 3), ("ring", 8), ("ring", 16), ("rhd", 5), ("rhd", 6),
@@ -205,3 +226,8 @@ def test_regs_offered_for_folds_and_trees(algo, P):
         for L in (1, 5, 1001, 100_003):
             assert c.exec_choice("allreduce", L, "bf16") == "regs", L
             assert c.exec_bytes("allreduce", L, "bf16", "regs") == 2 * P * L * 2
+    with hc.Comm(P, algo) as c:
+        c.set_exec_mode("regs")
+        if algo == "ring" and P > 2:
+            assert c.exec_bytes("reduce_scatter", 1001, "bf16", "regs") == (2 * P - 1) * 1001 * 2
+            assert c.exec_bytes("all_gather", 1001, "bf16", "regs") == P * 1001 * 2
