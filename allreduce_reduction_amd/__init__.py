@@ -23,7 +23,7 @@ ALGO = {"ring": 0, "rhd": 1, "pipeline": 2, "env": 3, "flat": 4, "tree": 5, "hie
 ALGO_NAME = {v: k for k, v in ALGO.items()}
 COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
-EXEC = {"auto": 0, "steps": 1, "fused": 2, "columns": 3, "lds": 4, "regs": 5}
+EXEC = {"auto": 0, "steps": 1, "fused": 2, "columns": 3, "lds": 4, "regs": 5, "flow": 6}
 
 # every symbol include/hbmcoll.h declares
 EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
@@ -32,7 +32,8 @@ EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_redu
            "hbmc_graph_build", "hbmc_graph_launch", "hbmc_graph_destroy", "hbmc_comm_set_cost_model",
            "hbmc_auto_choice", "hbmc_comm_set_fused_limit",
            "hbmc_comm_set_columns", "hbmc_plan_chunks",
-           "hbmc_comm_set_exec_mode", "hbmc_exec_choice", "hbmc_exec_bytes", "hbmc_allreduce_noalloc")
+           "hbmc_comm_set_exec_mode", "hbmc_exec_choice", "hbmc_exec_bytes", "hbmc_allreduce_noalloc",
+           "hbmc_comm_set_flow", "hbmc_comm_flow_timeouts", "hbmc_plan_flow")
 
 
 class HbmcError(RuntimeError):
@@ -56,6 +57,15 @@ class Chunk(ctypes.Structure):
     _fields_ = [("begin", ctypes.c_uint64), ("count", ctypes.c_uint32), ("item", ctypes.c_uint32),
                 ("step", ctypes.c_uint32), ("dep_lo", ctypes.c_uint32), ("dep_hi", ctypes.c_uint32),
                 ("pad", ctypes.c_uint32)]
+
+
+class FlowTile(ctypes.Structure):
+    _fields_ = [("col", ctypes.c_uint32), ("seq", ctypes.c_uint32), ("step", ctypes.c_uint32),
+                ("c_lo", ctypes.c_uint32), ("c_hi", ctypes.c_uint32), ("pad", ctypes.c_uint32)]
+
+
+class FlowChunk(ctypes.Structure):
+    _fields_ = [("begin", ctypes.c_uint64), ("count", ctypes.c_uint32), ("item", ctypes.c_uint32)]
 
 
 _lib = None
@@ -108,6 +118,14 @@ def load_library():
         L.hbmc_comm_set_fused_limit.argtypes = [vp, ctypes.c_uint64]
         L.hbmc_comm_set_columns.restype = ci
         L.hbmc_comm_set_columns.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint64]
+        L.hbmc_comm_set_flow.restype = ci
+        L.hbmc_comm_set_flow.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                         ctypes.c_uint32]
+        L.hbmc_comm_flow_timeouts.restype = ci
+        L.hbmc_comm_flow_timeouts.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.hbmc_plan_flow.restype = ci
+        L.hbmc_plan_flow.argtypes = [vp, ci, ci, sz, ci, ctypes.c_uint64, ctypes.POINTER(FlowTile), sz,
+                                     ctypes.POINTER(sz), ctypes.POINTER(FlowChunk), sz, ctypes.POINTER(sz)]
         L.hbmc_comm_set_exec_mode.restype = ci
         L.hbmc_comm_set_exec_mode.argtypes = [vp, ci]
         L.hbmc_exec_choice.restype = ci
@@ -269,7 +287,8 @@ class Comm:
                                              first, last, _stream(stream)), "hbmc_run_steps")
 
     def set_exec_mode(self, mode: str):
-        """Launch form of every call: "auto" (default), "steps", "fused", "columns", "lds" or "regs"."""
+        """Launch form of every call: "auto" (default), "steps", "fused", "columns", "lds", "regs" or
+        "flow"."""
         _check(load_library().hbmc_comm_set_exec_mode(self._h, EXEC[mode]), "hbmc_comm_set_exec_mode")
 
     def exec_choice(self, coll: str, count: int, dtype: str, root: int = 0, first: int = 0, last: int = 0) -> str:
@@ -287,6 +306,20 @@ class Comm:
         _check(load_library().hbmc_exec_bytes(self._h, COLL[coll], root, count, DTYPE[dtype], first, last,
                                               EXEC[mode], ctypes.byref(b)), "hbmc_exec_bytes")
         return b.value
+
+    def set_flow(self, tile_bytes: int = 16 << 10, wgs_per_cu: int = 8, tiles_per_ticket: int = 1,
+                 wait_us: int = 1_000_000, unreachable: bool = False):
+        """Flow form: tile length per rank buffer, workgroups per compute unit,
+        tiles per ticket, bound on each wait (us); `unreachable` makes every
+        wait give up (a test of the give-up path)."""
+        _check(load_library().hbmc_comm_set_flow(self._h, tile_bytes, wgs_per_cu, tiles_per_ticket, wait_us,
+                                                 1 if unreachable else 0), "hbmc_comm_set_flow")
+
+    def flow_timeouts(self) -> int:
+        """Flow-form waits that gave up since the last call (then reset; waits for the device)."""
+        n = ctypes.c_uint32()
+        _check(load_library().hbmc_comm_flow_timeouts(self._h, ctypes.byref(n)), "hbmc_comm_flow_timeouts")
+        return n.value
 
     def set_fused_limit(self, max_bytes: int):
         """Single-workgroup form eligible for calls moving at most max_bytes."""
@@ -351,6 +384,20 @@ class Comm:
                                   ctypes.byref(n), deps, nd.value, ctypes.byref(nd)), "hbmc_plan_chunks")
         return [dict(begin=c.begin, count=c.count, item=c.item, step=c.step, deps=list(deps[c.dep_lo:c.dep_hi]))
                 for c in arr[:n.value]]
+
+    def plan_flow(self, coll: str, count: int, dtype: str, tile_bytes: int, root: int = 0):
+        """Flow-kernel tables (host only): tiles in ticket order (dicts: col, seq,
+        step, chunks) and chunks (dicts: begin, count, item)."""
+        L = load_library()
+        nt, nc = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(L.hbmc_plan_flow(self._h, COLL[coll], root, count, DTYPE[dtype], tile_bytes, None, 0,
+                                ctypes.byref(nt), None, 0, ctypes.byref(nc)), "hbmc_plan_flow")
+        tiles = (FlowTile * max(nt.value, 1))()
+        chunks = (FlowChunk * max(nc.value, 1))()
+        _check(L.hbmc_plan_flow(self._h, COLL[coll], root, count, DTYPE[dtype], tile_bytes, tiles, nt.value,
+                                ctypes.byref(nt), chunks, nc.value, ctypes.byref(nc)), "hbmc_plan_flow")
+        return ([dict(col=t.col, seq=t.seq, step=t.step, chunks=range(t.c_lo, t.c_hi)) for t in tiles[:nt.value]],
+                [dict(begin=c.begin, count=c.count, item=c.item) for c in chunks[:nc.value]])
 
 
 class Graph:

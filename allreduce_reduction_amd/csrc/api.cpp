@@ -102,6 +102,7 @@ hbmc_status_t comm_create(int nranks, hbmc_algo_t algo, int servers, int ranks_p
     else if (v == "columns") c->exec_mode = kExecColumns;
     else if (v == "lds") c->exec_mode = kExecLds;
     else if (v == "regs") c->exec_mode = kExecRegs;
+    else if (v == "flow") c->exec_mode = kExecFlow;
     else if (v == "auto") c->exec_mode = kExecAuto;
   }
   const char* xs = std::getenv("HBMC_XCD_SPLIT");
@@ -135,8 +136,27 @@ hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, 
   return HBMC_OK;
 }
 
+hbmc_status_t hbmc_comm_set_flow(hbmc_comm_t comm, uint64_t tile_bytes, uint32_t wgs_per_cu,
+                                 uint32_t tiles_per_ticket, uint32_t wait_us, uint32_t flags) {
+  if (!comm || tile_bytes < 16 || tile_bytes > (uint64_t(1) << 31) || wgs_per_cu == 0 || wgs_per_cu > 64 ||
+      tiles_per_ticket == 0 || tiles_per_ticket > 4096 || wait_us == 0 ||
+      (flags & ~uint32_t(HBMC_FLOW_UNREACHABLE)) != 0)
+    return HBMC_ERR_INVALID_ARG;
+  comm->flow_tile_bytes = tile_bytes;
+  comm->flow_wgs_per_cu = wgs_per_cu;
+  comm->flow_batch = tiles_per_ticket;
+  comm->flow_wait_us = wait_us;
+  comm->flow_flags = (flags & HBMC_FLOW_UNREACHABLE) ? kFlowUnreachable : 0u;
+  return HBMC_OK;
+}
+
+hbmc_status_t hbmc_comm_flow_timeouts(hbmc_comm_t comm, uint32_t* count) {
+  if (!comm || !count) return HBMC_ERR_INVALID_ARG;
+  return no_throw([&] { return flow_timeouts(comm, count); });
+}
+
 hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode) {
-  if (!comm || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_REGS) return HBMC_ERR_INVALID_ARG;
+  if (!comm || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_FLOW) return HBMC_ERR_INVALID_ARG;
   comm->exec_mode = static_cast<int>(mode);
   return HBMC_OK;
 }
@@ -164,7 +184,7 @@ hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
 hbmc_status_t hbmc_exec_bytes(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
                               int first_step, int last_step, hbmc_exec_t mode, uint64_t* bytes) {
   return no_throw([&]() -> hbmc_status_t {
-    if (!bytes || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_REGS) return HBMC_ERR_INVALID_ARG;
+    if (!bytes || mode < HBMC_EXEC_AUTO || mode > HBMC_EXEC_FLOW) return HBMC_ERR_INVALID_ARG;
     Plan* p = nullptr;
     hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
     if (st != HBMC_OK) return st;
@@ -217,9 +237,11 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
     if (kv.second->dev && hipFree(kv.second->dev) != hipSuccess) st = HBMC_ERR_HIP;
     if (kv.second->cols_mem && hipFree(kv.second->cols_mem) != hipSuccess) st = HBMC_ERR_HIP;
     if (kv.second->lds_mem && hipFree(kv.second->lds_mem) != hipSuccess) st = HBMC_ERR_HIP;
+    if (kv.second->flow_mem && hipFree(kv.second->flow_mem) != hipSuccess) st = HBMC_ERR_HIP;
     for (void* m : kv.second->retired)
       if (hipFree(m) != hipSuccess) st = HBMC_ERR_HIP;
   }
+  if (comm->flow_timeouts && hipFree(comm->flow_timeouts) != hipSuccess) st = HBMC_ERR_HIP;
   delete comm;
   return st;
 }
@@ -340,6 +362,29 @@ hbmc_status_t hbmc_plan_chunks(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
     for (size_t i = 0; deps && i < f.deps.size() && i < dcap; ++i) deps[i] = f.deps[i];
     if (n_chunks) *n_chunks = f.chunks.size();
     if (n_deps) *n_deps = f.deps.size();
+    return HBMC_OK;
+  });
+}
+
+hbmc_status_t hbmc_plan_flow(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
+                             uint64_t tile_bytes, hbmc_flow_tile_t* tiles, size_t cap, size_t* n_tiles,
+                             hbmc_flow_chunk_t* chunks, size_t ccap, size_t* n_chunks) {
+  return no_throw([&]() -> hbmc_status_t {
+    if (tile_bytes < 16 || tile_bytes > (uint64_t(1) << 31)) return HBMC_ERR_INVALID_ARG;
+    Plan* p = nullptr;
+    hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
+    if (st != HBMC_OK) return st;
+    const uint32_t e = elem_bytes(dtype);
+    FlowTable f;
+    if (!build_flow(p->sched, count, e, tile_bytes / 16 * 16 / e, &f)) return HBMC_ERR_UNSUPPORTED;
+    for (size_t i = 0; tiles && i < f.tiles.size() && i < cap; ++i) {
+      const FlowTile& t = f.tiles[i];
+      tiles[i] = hbmc_flow_tile_t{t.col, t.seq, f.tile_step[i], t.c_lo, t.c_hi, 0};
+    }
+    for (size_t i = 0; chunks && i < f.chunks.size() && i < ccap; ++i)
+      chunks[i] = hbmc_flow_chunk_t{f.chunks[i].begin, f.chunks[i].count, f.chunk_item[i]};
+    if (n_tiles) *n_tiles = f.tiles.size();
+    if (n_chunks) *n_chunks = f.chunks.size();
     return HBMC_OK;
   });
 }

@@ -235,6 +235,67 @@ hbmc_status_t upload_columns(Plan* p) {
   return HBMC_OK;
 }
 
+hbmc_status_t flow_host(hbmc_comm* c, Plan* p, uint64_t count, uint32_t e) {
+  const uint64_t col = std::max<uint64_t>(16, c->flow_tile_bytes / 16 * 16) / e;
+  if (p->flow_built && p->flow.col_elems == col) return HBMC_OK;
+  if (p->flow_mem) {
+    // launches already enqueued and graphs built earlier may still read it
+    p->retired.push_back(p->flow_mem);
+    p->flow_mem = nullptr;
+  }
+  p->flow_ok = build_flow(p->sched, count, e, col, &p->flow);
+  p->flow.col_elems = col;
+  p->flow_built = true;
+  return HBMC_OK;
+}
+
+hbmc_status_t upload_flow(hbmc_comm* c, Plan* p) {
+  if (!c->flow_timeouts) {
+    void* m = nullptr;
+    if (hipMalloc(&m, 256) != hipSuccess) return HBMC_ERR_NOMEM;
+    const std::vector<uint32_t> zero(64, 0);
+    if (hipMemcpy(m, zero.data(), 256, hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(m);
+      return HBMC_ERR_HIP;
+    }
+    c->flow_timeouts = static_cast<uint32_t*>(m);
+  }
+  if (p->flow_mem) return HBMC_OK;
+  const FlowTable& f = p->flow;
+  auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
+  const size_t b_ctrl = 256;
+  const size_t b_prog = up(size_t(f.ncols) * sizeof(uint32_t) + 4);
+  const size_t b_tiles = up(f.tiles.size() * sizeof(FlowTile) + 16);
+  const size_t b_chunks = up(f.chunks.size() * sizeof(FlowChunk) + 16);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, b_ctrl + b_prog + b_tiles + b_chunks) != hipSuccess) return HBMC_ERR_NOMEM;
+  char* base = static_cast<char*>(mem);
+  const std::vector<char> zero(b_ctrl + b_prog, 0);
+  if (hipMemcpy(base, zero.data(), zero.size(), hipMemcpyHostToDevice) != hipSuccess ||
+      (!f.tiles.empty() && hipMemcpy(base + b_ctrl + b_prog, f.tiles.data(), f.tiles.size() * sizeof(FlowTile),
+                                     hipMemcpyHostToDevice) != hipSuccess) ||
+      (!f.chunks.empty() && hipMemcpy(base + b_ctrl + b_prog + b_tiles, f.chunks.data(),
+                                      f.chunks.size() * sizeof(FlowChunk), hipMemcpyHostToDevice) != hipSuccess)) {
+    (void)hipFree(mem);
+    return HBMC_ERR_HIP;
+  }
+  p->flow_mem = mem;
+  p->dev_fctrl = reinterpret_cast<FlowCtrl*>(base);
+  p->dev_fprog = reinterpret_cast<uint32_t*>(base + b_ctrl);
+  p->dev_ftiles = reinterpret_cast<FlowTile*>(base + b_ctrl + b_prog);
+  p->dev_fchunks = reinterpret_cast<FlowChunk*>(base + b_ctrl + b_prog + b_tiles);
+  return HBMC_OK;
+}
+
+hbmc_status_t flow_timeouts(hbmc_comm* c, uint32_t* count) {
+  *count = 0;
+  if (!c->flow_timeouts) return HBMC_OK;
+  if (hipMemcpy(count, c->flow_timeouts, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return HBMC_ERR_HIP;
+  const uint32_t zero = 0;
+  if (hipMemcpy(c->flow_timeouts, &zero, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess) return HBMC_ERR_HIP;
+  return HBMC_OK;
+}
+
 namespace {
 
 void lds_limits(uint64_t* per_block, uint64_t* per_cu);
@@ -479,6 +540,22 @@ uint32_t compute_units() {
   return v;
 }
 
+// The wall clock's rate (kHz) on the current device: the unit of the flow
+// kernel's wait bound.
+uint64_t wall_clock_khz() {
+  static std::atomic<uint32_t> cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100000;
+  uint32_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
+    v = static_cast<uint32_t>(khz);
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 // Dynamic LDS one workgroup may use, and LDS per compute unit, of the current
 // device.
 void lds_limits(uint64_t* per_block, uint64_t* per_cu) {
@@ -706,6 +783,15 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     regs_ok = p->regs.ok;
   }
   *mode = kExecSteps;
+  if (c->exec_mode == kExecFlow) {
+    // a whole call of two or more busy steps, every item within the records
+    if (aligned && busy > 1 && whole) {
+      hbmc_status_t st = flow_host(c, p, count, e);
+      if (st != HBMC_OK) return st;
+      if (p->flow_ok) *mode = kExecFlow;
+    }
+    return HBMC_OK;
+  }
   if (c->exec_mode == kExecRegs) {
     if (regs_ok) *mode = kExecRegs;
     return HBMC_OK;
@@ -792,7 +878,8 @@ hbmc_status_t exec_bytes(hbmc_comm* c, Plan* p, int first, int last, uint64_t co
   const int P = c->topos[0].P;
   *bytes = 0;
   if (count == 0 || P == 1) return HBMC_OK;
-  if (mode == kExecSteps) {
+  if (mode == kExecSteps || mode == kExecFlow) {
+    // the flow kernel moves every step's bytes, as one launch per step does
     for (int s = first; s < last; ++s) *bytes += p->sched.steps[s].hbm_bytes;
     return HBMC_OK;
   }
@@ -885,6 +972,21 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     // the whole call as one register-form launch
     KernelDesc k;
     describe_regs(dtype, op, ptrs, P, p->regs, count, phase, &k);
+    launches->push_back(k);
+    return HBMC_OK;
+  }
+  if (mode == kExecFlow) {
+    // the whole call as one flow-kernel launch
+    st = upload_flow(c, p);
+    if (st != HBMC_OK) return st;
+    const FlowTable& f = p->flow;
+    const uint32_t grid = std::max<uint32_t>(1, compute_units() * std::max<uint32_t>(1, c->flow_wgs_per_cu));
+    const uint64_t ticks = uint64_t(c->flow_wait_us) * wall_clock_khz() / 1000;
+    const uint32_t flags = c->flow_flags | (f.max_step_write > kCacheBytes ? kFlowNtStores : 0u);
+    KernelDesc k;
+    describe_flow(dtype, op, ptrs, p->dev_ftiles, p->dev_fchunks, static_cast<uint32_t>(f.tiles.size()),
+                  p->dev_fctrl, p->dev_fprog, f.ncols, c->flow_timeouts, phase, flags, ticks,
+                  std::max<uint32_t>(1, c->flow_batch), grid, &k);
     launches->push_back(k);
     return HBMC_OK;
   }

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "columns.hpp"
+#include "flow.hpp"
 #include "hbmcoll.h"
 #include "launch.hpp"
 #include "plan.hpp"
@@ -16,7 +17,9 @@
 namespace hbmc {
 
 // How a call's steps are launched.
-enum ExecMode : int { kExecAuto = 0, kExecSteps = 1, kExecFused = 2, kExecColumns = 3, kExecLds = 4, kExecRegs = 5 };
+enum ExecMode : int {
+  kExecAuto = 0, kExecSteps = 1, kExecFused = 2, kExecColumns = 3, kExecLds = 4, kExecRegs = 5, kExecFlow = 6
+};
 
 // Modelled time (us) of a range of steps in each launch form, fitted to
 // measurements on MI355X (one launch per step, the single-workgroup kernel,
@@ -106,6 +109,17 @@ struct Plan {
   // every call
   std::vector<DevItem> host_table;
   bool host_table_built = false;
+  // the flow kernel: its host table for the communicator's tile length, and
+  // one device allocation holding the control block, the column counters,
+  // the tiles and the chunks (built on first launch)
+  FlowTable flow;
+  bool flow_built = false;
+  bool flow_ok = false;  // the schedule fits the flow records
+  void* flow_mem = nullptr;
+  FlowCtrl* dev_fctrl = nullptr;
+  uint32_t* dev_fprog = nullptr;
+  FlowTile* dev_ftiles = nullptr;
+  FlowChunk* dev_fchunks = nullptr;
   // device tables of earlier column lengths: graphs built or captured before
   // the length changed still point at them, so they are kept until the
   // communicator is destroyed
@@ -130,6 +144,15 @@ struct hbmc_comm {
   uint64_t columns_limit = uint64_t(64) << 20;
   uint64_t column_bytes = 0;   // column length in bytes; 0: chosen per call
   bool xcd_split = false;
+  // the flow kernel: tile length per rank buffer (bytes), workgroups per
+  // compute unit, wait bound, flags (kFlowUnreachable) and the device
+  // counter of waits that gave up (allocated on first use)
+  uint64_t flow_tile_bytes = uint64_t(16) << 10;
+  uint32_t flow_wgs_per_cu = 8;
+  uint32_t flow_wait_us = 1000000;
+  uint32_t flow_flags = 0;
+  uint32_t flow_batch = 1;  // tiles per ticket
+  uint32_t* flow_timeouts = nullptr;
   // (topology index, coll, root, count, dtype) -> plan
   std::map<std::tuple<int, int, int, uint64_t, int>, std::unique_ptr<hbmc::Plan>> plans;
   // AUTO: (coll, root, count, dtype) -> chosen topology index
@@ -188,6 +211,16 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
 hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e);
 // The same tables built on the host only (p->lh), once per column length.
 hbmc_status_t lds_host_tables(Plan* p, int P, uint64_t count, uint32_t e);
+// The flow kernel's host table of plan p for the communicator's tile length
+// (count elements of e bytes), built once per length; sets p->flow_ok.
+hbmc_status_t flow_host(hbmc_comm* c, Plan* p, uint64_t count, uint32_t e);
+// Upload it to the current device with zeroed counters (again after the
+// tile length changed; the old tables are retired, not freed), and allocate
+// the communicator's timeout counter.
+hbmc_status_t upload_flow(hbmc_comm* c, Plan* p);
+// Read the communicator's count of flow waits that gave up, and clear it
+// (synchronous; 0 when no flow launch ran).
+hbmc_status_t flow_timeouts(hbmc_comm* c, uint32_t* count);
 // Bytes a launch of steps [first, last) in form `mode` moves between the
 // compute units and memory (see hbmc_exec_bytes).
 hbmc_status_t exec_bytes(hbmc_comm* c, Plan* p, int first, int last, uint64_t count, uint32_t e, int mode,

@@ -7,6 +7,8 @@
 // buffers may run concurrently.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
+#include <map>
 #include <new>
 #include <vector>
 
@@ -53,6 +55,8 @@ hbmc_status_t graph_build(hbmc_graph* g) {
   if (hipGraphCreate(&g->graph, 0) != hipSuccess) return HBMC_ERR_HIP;
   hbmc_status_t st = HBMC_OK;
   std::vector<hipGraphNode_t> last(g->nodes.size(), nullptr);  // each collective's final node
+  // flow launches of one plan share its counters: each waits for the one before
+  std::map<const void*, hipGraphNode_t> flow_last;
   for (size_t i = 0; i < g->nodes.size() && st == HBMC_OK; ++i) {
     const hbmc_graph::Node& n = g->nodes[i];
     std::vector<hipGraphNode_t> deps;
@@ -67,6 +71,11 @@ hbmc_status_t graph_build(hbmc_graph* g) {
     }
     for (KernelDesc& k : launches) {
       k.bind();
+      if (k.kind == KernelDesc::kFlow) {
+        auto f = flow_last.find(k.fctrl);
+        if (f != flow_last.end() && std::find(deps.begin(), deps.end(), f->second) == deps.end())
+          deps.push_back(f->second);
+      }
       hipKernelNodeParams prm{};
       prm.func = const_cast<void*>(k.func);
       prm.gridDim = k.grid;
@@ -79,6 +88,7 @@ hbmc_status_t graph_build(hbmc_graph* g) {
         st = HBMC_ERR_HIP;
         break;
       }
+      if (k.kind == KernelDesc::kFlow) flow_last[k.fctrl] = node;
       deps.assign(1, node);  // the next launch waits for this one
       last[i] = node;
     }

@@ -117,6 +117,34 @@ struct alignas(16) DevColStore {
 };
 static_assert(sizeof(DevColStore) == 16, "column store record");
 
+// The flow kernel's tables (device; see flow.hpp).  A tile is the work of
+// one step on one column of elements: chunks [c_lo, c_hi) of the chunk table,
+// the seq-th tile of column `col`.  A chunk is elements [begin, begin+count)
+// of one item: shape = mode | nsrc << 8 | ndst << 16, rank[] its sources then
+// destinations.  The control block holds the ticket and exit counters and
+// the launch's give-up flag; the last workgroup to leave resets it and the
+// column counters for the next launch.
+constexpr int kFlowOperands = 32;
+struct alignas(16) FlowTile {
+  uint32_t col, seq, c_lo, c_hi;
+};
+struct alignas(16) FlowChunk {
+  uint64_t begin;
+  uint32_t count, shape;
+  uint8_t rank[kFlowOperands];
+};
+static_assert(sizeof(FlowTile) == 16 && sizeof(FlowChunk) == 48, "flow records");
+struct alignas(16) FlowCtrl {
+  uint32_t next, done, abort, pad;
+};
+// Flow kernel flags: every wait targets a count its column never reaches, so
+// each tile with a predecessor gives up after the wait bound (a host-forced
+// test of the give-up path).
+constexpr uint32_t kFlowUnreachable = 1u;
+// Host-side choice of the instantiation whose stores carry the nontemporal
+// hint (steps that write more than the memory-side cache holds).
+constexpr uint32_t kFlowNtStores = 2u;
+
 // The register-form kernel's arguments (see regs.hpp), one record per region
 // of elements (grid.y): the region's whole 16-byte positions [vec_lo, vec_hi)
 // of the vector (position k holds the elements from head + k * 16 / e on,
@@ -145,7 +173,8 @@ constexpr size_t kRegCallBytes = sizeof(RegFoldCall) > sizeof(RegTreeCall) ? siz
 // One kernel launch: kernel, shape and argument values, usable with
 // hipLaunchKernel or as a kernel graph node.
 struct KernelDesc {
-  enum Kind { kVector = 0, kElement = 1, kFused = 2, kColumns = 3, kColumnsLds = 4, kVectorArgs = 5, kRegs = 6 };
+  enum Kind { kVector = 0, kElement = 1, kFused = 2, kColumns = 3, kColumnsLds = 4, kVectorArgs = 5, kRegs = 6,
+              kFlow = 7 };
   Kind kind = kVector;
   const void* func = nullptr;
   dim3 grid, block;
@@ -178,6 +207,15 @@ struct KernelDesc {
   const uint32_t* col_run = nullptr;
   const uint32_t* st_off = nullptr;
   const uint64_t* col_load = nullptr;  // per column, the ranks whose copies are ever read
+  // flow kernel only: tables, control block, column counters, timeout
+  // counter (sticky, per communicator) and the wait bound in wall-clock ticks
+  const FlowTile* ftiles = nullptr;
+  const FlowChunk* fchunks = nullptr;
+  FlowCtrl* fctrl = nullptr;
+  uint32_t* fprog = nullptr;
+  uint32_t* ftimeouts = nullptr;
+  uint32_t ntiles = 0, fbatch = 1;
+  uint64_t wait_ticks = 0;
   uint32_t shared_bytes = 0;  // dynamic LDS per workgroup
   void* argv[16];  // filled by bind(); valid while this object lives
   void bind() {
@@ -216,6 +254,19 @@ struct KernelDesc {
       argv[1] = args;
     } else if (kind == kRegs) {
       argv[0] = args;
+    } else if (kind == kFlow) {
+      argv[0] = &ptrs;
+      argv[1] = &ftiles;
+      argv[2] = &fchunks;
+      argv[3] = &ntiles;
+      argv[4] = &fctrl;
+      argv[5] = &fprog;
+      argv[6] = &ncols;
+      argv[7] = &ftimeouts;
+      argv[8] = &phase;
+      argv[9] = &flags;
+      argv[10] = &wait_ticks;
+      argv[11] = &fbatch;
     } else {
       // step kernels: the small arguments first (preloaded into registers)
       argv[0] = &items;
@@ -260,6 +311,14 @@ void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColC
 // elements whose rank buffers share the 16-byte `phase` (rp.ok).
 void describe_regs(int dtype, int op, const RankPtrs& ptrs, int P, const RegPlan& rp, uint64_t count,
                    uint32_t phase, KernelDesc* k);
+
+// The flow kernel over a whole call's tiles: `grid` workgroups take tiles
+// in ticket order until none is left (see flow_kernels.hip).
+void describe_flow(int dtype, int op, const RankPtrs& ptrs, const FlowTile* tiles, const FlowChunk* chunks,
+                   uint32_t ntiles, FlowCtrl* ctrl, uint32_t* progress, uint32_t ncols, uint32_t* timeouts,
+                   uint32_t phase, uint32_t flags, uint64_t wait_ticks, uint32_t batch, uint32_t grid,
+                   KernelDesc* k);
+constexpr int kFlowThreads = 256;
 
 // The single-workgroup kernel running `nsteps` steps of a plan.
 void describe_fused(int dtype, int op, const RankPtrs& ptrs, const DevItem* items, const FusedStep* steps,

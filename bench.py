@@ -78,7 +78,7 @@ def parse():
     ap.add_argument("--suite", action="store_true", help="time the other workloads instead")
     ap.add_argument("--max-sweep-bytes", type=int, default=1 << 30)
     ap.add_argument("--workloads", default="rhd_small,sweep,forms,algorithms,pipe",
-                    help="suite workloads to run (comma-separated; also sweep_steps)")
+                    help="suite workloads to run (comma-separated; also sweep_steps, flow)")
     ap.add_argument("--sweep-sizes", default=f"{16 << 20},{256 << 20},{1 << 30}",
                     help="sweep_steps: bytes per rank (comma-separated)")
     return ap.parse_args()
@@ -262,6 +262,41 @@ def suite(a):
                         emit(workload="sweep_steps_p16_fp16", algo=algo, coll=coll, P=P, bytes_per_rank=nbytes,
                              launch_form="steps", steps=rows)
             del bufs, pristine
+            torch.cuda.empty_cache()
+
+    if "flow" in workloads:
+        # the flow form (all steps in one persistent launch, tiles in step
+        # order waiting on their column's counter) against one launch per step
+        # where the one-launch cache-resident forms do not apply: the P=16
+        # fp16 sum ring and RHD at 16 and 64 MiB per rank, and the 8-rank fp32
+        # ring at 256 MiB per rank
+        for P, algo, recipe, dtype, nbytes in ((16, "ring", "sweep_p16_fp16", "fp16", 16 << 20),
+                                               (16, "rhd", "sweep_p16_fp16", "fp16", 16 << 20),
+                                               (16, "ring", "sweep_p16_fp16", "fp16", 64 << 20),
+                                               (16, "rhd", "sweep_p16_fp16", "fp16", 64 << 20),
+                                               (8, "ring", "ring_p8_fp32_grad", "fp32", 256 << 20)):
+            e = 2 if dtype == "fp16" else 4
+            L = nbytes // e
+            bufs = upload(recipe, P, L)
+            row, pct = {}, {}
+            with hc.Comm(P, algo) as c:
+                alg = c.exec_bytes("allreduce", L, dtype, "steps")
+                variants = [("steps", None)] + [(f"flow_{t >> 10}K_w{w}_t{k}", (t, w, k))
+                                                for t in (16 << 10, 64 << 10) for w in (4, 8) for k in (1, 16)]
+                for name, cfg in variants:
+                    if cfg is None:
+                        c.set_exec_mode("steps")
+                    else:
+                        c.set_exec_mode("flow")
+                        c.set_flow(cfg[0], cfg[1], cfg[2])
+                    tf = time_calls(lambda: c.allreduce(bufs, dtype, "sum"), 3, 1)
+                    row[name] = round(tf * 1e6, 1)
+                    pct[name] = round(100 * alg / tf / HBM_PEAK, 1)
+                torch.cuda.synchronize()
+                timeouts = c.flow_timeouts()
+            emit(workload="flow_vs_steps", algo=algo, P=P, dtype=dtype, op="sum", bytes_per_rank=nbytes,
+                 hbm_bytes=alg, us=row, pct_hbm_algorithmic=pct, flow_timeouts=timeouts)
+            del bufs
             torch.cuda.empty_cache()
 
     if "forms" in workloads:

@@ -178,8 +178,19 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    operand once, evaluates the expression and stores every rank the
  *    schedule writes there ([RHD] "耗时计算": every step pays alpha, which
  *    this form pays once);
+ *  - HBMC_EXEC_FLOW: a whole call in one launch of a persistent kernel
+ *    that runs every step's work as the step kernels do (each step reads
+ *    and writes its own bytes in the rank buffers) but lets consecutive steps
+ *    overlap: items are cut into tiles at multiples of the tile length
+ *    (hbmc_comm_set_flow), tiles are handed out step after step by an atomic
+ *    ticket, and a tile waits until the tiles of earlier steps over its
+ *    elements are done ([RING-RHD] "Ring AllReduce带宽最优的环形流水线": no
+ *    rank waits for a whole step).  Only when set explicitly (AUTO does not
+ *    pick it).  Launches of one communicator's call of the same collective,
+ *    count and dtype share the plan's counters: they must not overlap in
+ *    time (one stream, or ordered; graphs order such nodes themselves);
  *  - HBMC_EXEC_AUTO (default, or the environment variable HBMC_EXEC = auto,
- *    steps, fused, columns, lds or regs): per call the eligible form of least
+ *    steps, fused, columns, lds, regs or flow): per call the eligible form of least
  *    modelled time, with constants measured on MI355X: steps sum over the
  *    steps max(4.2 us, 3 us + bytes / 6.4 TB/s); fused 2 us + 1.6 us per
  *    step + bytes / 33 GB/s; columns 4 us + 0.85 us per chunk of the longest
@@ -202,17 +213,38 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  * keep the per-step HBM traffic the schedule defines; LDS needs what COLUMNS
  * needs, and a column of every rank buffer plus 160 bytes per chunk of the
  * longest column within one workgroup's LDS; REGS needs what COLUMNS needs,
- * all of the call's steps, and the expression forms above.  The
+ * all of the call's steps, and the expression forms above; FLOW needs rank
+ * buffers of one 16-byte phase, all of the call's steps, two or more busy
+ * steps and at most 32 ranks per item.  The
  * element ops commute bit for bit, so every form gives the same bits.  The
  * forms apply to
  * every call, hbmc_run_steps ranges and graph nodes.  Host only.
  */
 typedef enum {
   HBMC_EXEC_AUTO = 0, HBMC_EXEC_STEPS = 1, HBMC_EXEC_FUSED = 2, HBMC_EXEC_COLUMNS = 3, HBMC_EXEC_LDS = 4,
-  HBMC_EXEC_REGS = 5
+  HBMC_EXEC_REGS = 5, HBMC_EXEC_FLOW = 6
 } hbmc_exec_t;
 hbmc_status_t hbmc_comm_set_exec_mode(hbmc_comm_t comm, hbmc_exec_t mode);
 hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes);
+/* The flow form's settings: tile_bytes per rank buffer (16 .. 2^31, rounded
+ * down to a multiple of 16; default 16 KiB), workgroups per compute unit
+ * (1 .. 64; default 8), tiles a workgroup takes per ticket (1 .. 4096,
+ * consecutive in ticket order and run in order; default 1), and the bound on
+ * each wait for an earlier tile in microseconds of the GPU's wall clock
+ * (default 1 s).  A wait past the bound
+ * gives up: the launch skips the rest of its tiles, ends normally, and the
+ * communicator's timeout counter grows (hbmc_comm_flow_timeouts); the
+ * buffers then hold a partial result.  flags: 0, or HBMC_FLOW_UNREACHABLE,
+ * which makes every wait target a count its column never reaches, so that
+ * every tile with an earlier tile gives up after the bound (a test of the
+ * give-up path, forced from the host).  Host only. */
+#define HBMC_FLOW_UNREACHABLE 1u
+hbmc_status_t hbmc_comm_set_flow(hbmc_comm_t comm, uint64_t tile_bytes, uint32_t wgs_per_cu,
+                                 uint32_t tiles_per_ticket, uint32_t wait_us, uint32_t flags);
+/* The number of flow-form waits that gave up since the last call, then
+ * reset to 0 (waits for the device: call it after the launches in
+ * question have completed). */
+hbmc_status_t hbmc_comm_flow_timeouts(hbmc_comm_t comm, uint32_t* count);
 /* column_bytes: 0, or 16 .. 2^31 (rounded down to a multiple of 16). */
 hbmc_status_t hbmc_comm_set_columns(hbmc_comm_t comm, uint64_t max_total_bytes, uint64_t column_bytes);
 /* The launch form steps [first_step, last_step) of a call would take (0, 0:
@@ -223,8 +255,8 @@ hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
 /* Bytes that steps [first_step, last_step) of a call (0, 0: all steps) move
  * between the compute units and memory in launch form `mode` (AUTO: the form
  * hbmc_exec_choice reports), host only:
- *  - STEPS: the steps' algorithmic HBM bytes (every distinct block a step
- *    reads counted once, every block it writes once, step after step);
+ *  - STEPS, FLOW: the steps' algorithmic HBM bytes (every distinct block a
+ *    step reads counted once, every block it writes once, step after step);
  *  - FUSED, COLUMNS: each rank's elements that some step reads, once, plus
  *    those some step writes, once -- what crosses to memory when the caches
  *    hold the call's working set, as they do within these forms' limits;
@@ -409,6 +441,27 @@ typedef struct {
 hbmc_status_t hbmc_plan_chunks(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count,
                                hbmc_dtype_t dtype, uint64_t chunk_bytes, hbmc_chunk_t* chunks, size_t cap,
                                size_t* n_chunks, uint32_t* deps, size_t dcap, size_t* n_deps);
+
+/* One tile of the flow kernel: the seq-th tile of column `col` (elements
+ * [col * tile, (col + 1) * tile) of every rank buffer), the work of step
+ * `step` there, chunks [c_lo, c_hi) of the chunk table; and one chunk:
+ * elements [begin, begin+count) of work item `item` (hbmc_plan_items order). */
+typedef struct {
+  uint32_t col, seq, step, c_lo, c_hi, pad;
+} hbmc_flow_tile_t;
+typedef struct {
+  uint64_t begin;
+  uint32_t count, item;
+} hbmc_flow_chunk_t;
+
+/* The flow kernel's tables for tiles of tile_bytes per rank buffer (rounded
+ * as hbmc_comm_set_flow does), host only: tiles in the order the kernel hands
+ * them out (step after step, columns ascending), at most `cap` tiles and
+ * `ccap` chunks written, totals in *n_tiles / *n_chunks.
+ * HBMC_ERR_UNSUPPORTED when an item has more than 32 ranks. */
+hbmc_status_t hbmc_plan_flow(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
+                             uint64_t tile_bytes, hbmc_flow_tile_t* tiles, size_t cap, size_t* n_tiles,
+                             hbmc_flow_chunk_t* chunks, size_t ccap, size_t* n_chunks);
 
 /*
  * Graph mode ([RING-RHD] section "Ascend950的AIVAICPU通信引擎与图模式": a

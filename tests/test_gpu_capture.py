@@ -24,6 +24,9 @@ pytestmark = pytest.mark.gpu
     ("columns", "ring", 5, 20_000, "fp16"),
     ("steps", "pipeline", 8, 30_000, "bf16"),
     ("auto", "rhd", 16, 1 << 16, "fp16"),
+    ("regs", "ring", 8, 20_003, "bf16"),
+    ("flow", "ring", 8, 50_001, "fp32"),
+    ("flow", "rhd", 6, 30_000, "int8"),
 ])
 def test_capture_after_first_call(mode, algo, P, L, dtype):
     xs = make_inputs(dtype, "sum", P, L, seed=L)

@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 
 DTYPES = ["fp32", "fp16", "bf16", "int32", "int8"]
 OPS = ["sum", "prod", "max", "min"]
-MODES = ["auto", "steps", "fused", "columns", "lds"]
+MODES = ["auto", "steps", "fused", "columns", "lds", "regs", "flow"]
 CASES_PER_BATCH = 60
 
 

@@ -53,7 +53,7 @@ def special_inputs(dtype, op, P, L, seed):
     return xs
 
 
-@pytest.mark.parametrize("mode", ["steps", "fused", "columns", "lds"])
+@pytest.mark.parametrize("mode", ["steps", "fused", "columns", "lds", "regs", "flow"])
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("algo,P", [("ring", 5), ("rhd", 5), ("flat", 4)])
 def test_specials(algo, P, dtype, mode):

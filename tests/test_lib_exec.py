@@ -111,8 +111,8 @@ def test_exec_choice_edges_and_validation():
         with pytest.raises(KeyError):
             c.set_exec_mode("bogus")
         lib = hc.load_library()
-        assert lib.hbmc_comm_set_exec_mode(c._h, 6) == 1
-        assert lib.hbmc_comm_set_exec_mode(c._h, 5) == 0
+        assert lib.hbmc_comm_set_exec_mode(c._h, 7) == 1
+        assert lib.hbmc_comm_set_exec_mode(c._h, 6) == 0
     with hc.Comm(1, "ring") as c:
         assert c.exec_choice("allreduce", 100, "fp32") == "steps"
 
