@@ -26,12 +26,39 @@ namespace {
 
 using namespace dev;
 
+// Kernel-side variants of the tree form, whose call records carry 16
+// addresses as the fold's do (fewer scalar registers and record loads): trees
+// whose leaves are all single ranks (P a power of two; no leaf tests for a
+// pair), and trees of at most 8 leaves with pairs (the pair's second address
+// at ptr[8 + v]).
+constexpr int kRegTreeSingles = 4;
+constexpr int kRegTreeSmall = 5;
+
+// Leaves a form's kernel handles and where a leaf's pair address sits (0:
+// no pairs).
+template <int FORM>
+struct RegShape {
+  static constexpr int leaves = FORM == kRegTreeSmall ? 8 : kRegMaxLeaves;
+  static constexpr int pair = FORM == kRegTree ? kRegMaxLeaves : (FORM == kRegTreeSmall ? 8 : 0);
+  static constexpr int ptrs = FORM == kRegTree ? 2 * kRegMaxLeaves : kRegMaxLeaves;
+};
+
 // The expression of a region over values load(i) of its operands
 // (addresses ptr[i]), combined by op.
 template <int FORM, typename V, typename Load, typename Op>
 __device__ __forceinline__ V eval(uint32_t n, const unsigned char* const* ptr, Load load, Op op) {
   V x[kRegMaxLeaves];
-  if constexpr (FORM == kRegFold) {
+  if constexpr (FORM == kRegTreeSingles) {
+#pragma unroll
+    for (uint32_t v = 0; v < kRegMaxLeaves; ++v)
+      if (v < n) x[v] = load(ptr[v]);
+#pragma unroll
+    for (uint32_t w = 1; w < kRegMaxLeaves; w *= 2)
+#pragma unroll
+      for (uint32_t v = 0; v + w < kRegMaxLeaves; v += 2 * w)
+        if (v + w < n) x[v] = op(x[v], x[v + w]);
+    return x[0];
+  } else if constexpr (FORM == kRegFold) {
 #pragma unroll
     for (uint32_t i = 0; i < kRegMaxLeaves; ++i)
       if (i < n) x[i] = load(ptr[i]);
@@ -41,22 +68,24 @@ __device__ __forceinline__ V eval(uint32_t n, const unsigned char* const* ptr, L
       if (i < n) acc = op(acc, x[i]);
     return acc;
   } else {
-    V y[kRegMaxLeaves];
+    // leaves that may be pairs (x_a op x_b), then pairs (0,1), (2,3), ...,
+    // then (0,2), (4,6), ...
+    constexpr uint32_t NL = RegShape<FORM>::leaves, PO = RegShape<FORM>::pair;
+    V y[NL];
 #pragma unroll
-    for (uint32_t v = 0; v < kRegMaxLeaves; ++v) {
+    for (uint32_t v = 0; v < NL; ++v) {
       if (v < n) {
         x[v] = load(ptr[v]);
-        if (ptr[kRegMaxLeaves + v]) y[v] = load(ptr[kRegMaxLeaves + v]);
+        if (ptr[PO + v]) y[v] = load(ptr[PO + v]);
       }
     }
 #pragma unroll
-    for (uint32_t v = 0; v < kRegMaxLeaves; ++v)
-      if (v < n && ptr[kRegMaxLeaves + v]) x[v] = op(x[v], y[v]);
-    // pairs (0,1), (2,3), ..., then (0,2), (4,6), ...
+    for (uint32_t v = 0; v < NL; ++v)
+      if (v < n && ptr[PO + v]) x[v] = op(x[v], y[v]);
 #pragma unroll
-    for (uint32_t w = 1; w < kRegMaxLeaves; w *= 2)
+    for (uint32_t w = 1; w < NL; w *= 2)
 #pragma unroll
-      for (uint32_t v = 0; v + w < kRegMaxLeaves; v += 2 * w)
+      for (uint32_t v = 0; v + w < NL; v += 2 * w)
         if (v + w < n) x[v] = op(x[v], x[v + w]);
     return x[0];
   }
@@ -65,12 +94,13 @@ __device__ __forceinline__ V eval(uint32_t n, const unsigned char* const* ptr, L
 // Store v at byte offset off of every operand.
 template <int FORM, typename Store>
 __device__ __forceinline__ void store_all(uint32_t n, unsigned char* const* ptr, Store store) {
+  constexpr uint32_t NL = RegShape<FORM>::leaves, PO = RegShape<FORM>::pair;
 #pragma unroll
-  for (uint32_t v = 0; v < kRegMaxLeaves; ++v) {
+  for (uint32_t v = 0; v < NL; ++v) {
     if (v < n) {
       store(ptr[v]);
-      if constexpr (FORM == kRegTree)
-        if (ptr[kRegMaxLeaves + v]) store(ptr[kRegMaxLeaves + v]);
+      if constexpr (PO > 0)
+        if (ptr[PO + v]) store(ptr[PO + v]);
     }
   }
 }
@@ -108,10 +138,12 @@ __global__ void __launch_bounds__(kRegThreads)
 plan_regs(Call c) {
   constexpr uint32_t E = Width<DT>::bytes;
   constexpr uint32_t EPV = 16 / E;
-  constexpr int NP = FORM == kRegTree ? 2 * kRegMaxLeaves : kRegMaxLeaves;
+  constexpr int NP = RegShape<FORM>::ptrs;
+  // the call's header and the region's record read whole before any branch
+  // on them, so that their scalar loads go out together
+  const uint32_t n = c.n, phase = c.phase;
+  const uint64_t count = c.count;
   const auto& R0 = c.r[blockIdx.y];
-  // the region's record read whole before any branch on it, so that its
-  // scalar loads go out together
   struct {
     uint32_t vec_lo, vec_hi, el_lo[2], el_hi[2];
     unsigned char* ptr[NP];
@@ -125,13 +157,13 @@ plan_regs(Call c) {
   }
 #pragma unroll
   for (int i = 0; i < NP; ++i) R.ptr[i] = R0.ptr[i];
-  uint64_t head = ((16u - (c.phase & 15u)) & 15u) / E;
-  if (head > c.count) head = c.count;
+  uint64_t head = ((16u - (phase & 15u)) & 15u) / E;
+  if (head > count) head = count;
   const uint64_t k = uint64_t(R.vec_lo) + uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (k < R.vec_hi) {
     const uint64_t off = (head + k * EPV) * E;
     position<FORM, u32x4>(
-        c.n, R.ptr, [&](const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p + off); },
+        n, R.ptr, [&](const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p + off); },
         [](u32x4 a, u32x4 b) { return op_vec<DT, OP>(a, b); },
         [&](unsigned char* p, u32x4 v) { store_vec(reinterpret_cast<u32x4*>(p + off), v); });
   }
@@ -142,7 +174,7 @@ plan_regs(Call c) {
       if (e < R.el_hi[part]) {
         const uint64_t off = e * E;
         position<FORM, uint32_t>(
-            c.n, R.ptr, [&](const unsigned char* p) { return load_elem<E>(p + off); },
+            n, R.ptr, [&](const unsigned char* p) { return load_elem<E>(p + off); },
             [](uint32_t a, uint32_t b) { return op_word<DT, OP>(a, b); },
             [&](unsigned char* p, uint32_t v) { store_elem<E>(p + off, v); });
       }
@@ -154,6 +186,8 @@ template <int DT, int OP>
 const void* regs_fn(uint32_t form) {
   switch (form) {
     case kRegTree: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTree, RegTreeCall>);
+    case kRegTreeSingles: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTreeSingles, RegFoldCall>);
+    case kRegTreeSmall: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTreeSmall, RegFoldCall>);
     case kRegCopy: return reinterpret_cast<const void*>(plan_regs<DT, kSum, kRegCopy, RegFoldCall>);
     case kRegPrefix: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegPrefix, RegFoldCall>);
     default: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegFold, RegFoldCall>);
@@ -173,8 +207,8 @@ const void* regs_op(int op, uint32_t form) {
 // Fill a call's records from the derived regions; returns the largest
 // number of whole positions in one region.
 template <typename Call>
-uint64_t fill(Call* c, const RankPtrs& ptrs, const RegPlan& rp, uint64_t count, uint32_t phase, uint32_t E) {
-  constexpr int NP = sizeof(c->r[0].ptr) / sizeof(c->r[0].ptr[0]);
+uint64_t fill(Call* c, const RankPtrs& ptrs, const RegPlan& rp, uint64_t count, uint32_t phase, uint32_t E,
+              uint32_t pair) {
   std::memset(c, 0, sizeof(*c));
   c->n = rp.n;
   c->phase = phase;
@@ -208,7 +242,7 @@ uint64_t fill(Call* c, const RankPtrs& ptrs, const RegPlan& rp, uint64_t count, 
     }
     for (uint32_t v = 0; v < rp.n; ++v) {
       r.ptr[v] = ptrs.p[q.a[v]];
-      if (NP > kRegMaxLeaves && q.b[v] != 0xff) r.ptr[(kRegMaxLeaves + v) % NP] = ptrs.p[q.b[v]];
+      if (pair > 0 && q.b[v] != 0xff) r.ptr[pair + v] = ptrs.p[q.b[v]];
     }
     most = std::max<uint64_t>(most, hi - lo);
     start = end;
@@ -223,8 +257,18 @@ void describe_regs(int dtype, int op, const RankPtrs& ptrs, int P, const RegPlan
   (void)P;
   const uint32_t E = dtype == kF32 || dtype == kI32 ? 4u : (dtype == kI8 ? 1u : 2u);
   uint64_t most = 0;
-  if (rp.form == kRegTree) most = fill(new (k->args) RegTreeCall, ptrs, rp, count, phase, E);
-  else most = fill(new (k->args) RegFoldCall, ptrs, rp, count, phase, E);
+  uint32_t form = rp.form;
+  if (form == kRegTree) {
+    bool pairs = false;
+    for (const RegRegion& q : rp.regions)
+      for (uint32_t v = 0; v < rp.n; ++v) pairs = pairs || q.b[v] != 0xff;
+    if (!pairs) form = kRegTreeSingles;
+    else if (rp.n <= uint32_t(RegShape<kRegTreeSmall>::leaves)) form = kRegTreeSmall;
+  }
+  if (form == kRegTree) most = fill(new (k->args) RegTreeCall, ptrs, rp, count, phase, E, RegShape<kRegTree>::pair);
+  else
+    most = fill(new (k->args) RegFoldCall, ptrs, rp, count, phase, E,
+                form == kRegTreeSmall ? uint32_t(RegShape<kRegTreeSmall>::pair) : 0u);
   // at least one lane per element a region takes one by one (fewer than 16
   // at each end of a region)
   const uint64_t lanes = std::max<uint64_t>(most, 16);
@@ -234,11 +278,11 @@ void describe_regs(int dtype, int op, const RankPtrs& ptrs, int P, const RegPlan
   k->block = dim3(block);
   k->shared_bytes = 0;
   switch (dtype) {
-    case kF32: k->func = regs_op<kF32>(op, rp.form); break;
-    case kF16: k->func = regs_op<kF16>(op, rp.form); break;
-    case kBF16: k->func = regs_op<kBF16>(op, rp.form); break;
-    case kI32: k->func = regs_op<kI32>(op, rp.form); break;
-    default: k->func = regs_op<kI8>(op, rp.form); break;
+    case kF32: k->func = regs_op<kF32>(op, form); break;
+    case kF16: k->func = regs_op<kF16>(op, form); break;
+    case kBF16: k->func = regs_op<kBF16>(op, form); break;
+    case kI32: k->func = regs_op<kI32>(op, form); break;
+    default: k->func = regs_op<kI8>(op, form); break;
   }
   k->bind();
 }
