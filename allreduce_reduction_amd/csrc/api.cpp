@@ -241,7 +241,6 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
     for (void* m : kv.second->retired)
       if (hipFree(m) != hipSuccess) st = HBMC_ERR_HIP;
   }
-  if (comm->flow_timeouts && hipFree(comm->flow_timeouts) != hipSuccess) st = HBMC_ERR_HIP;
   delete comm;
   return st;
 }

@@ -241,6 +241,7 @@ hbmc_status_t flow_host(hbmc_comm* c, Plan* p, uint64_t count, uint32_t e) {
   if (p->flow_mem) {
     // launches already enqueued and graphs built earlier may still read it
     p->retired.push_back(p->flow_mem);
+    p->flow_old.push_back(p->flow_mem);
     p->flow_mem = nullptr;
   }
   p->flow_ok = build_flow(p->sched, count, e, col, &p->flow);
@@ -249,21 +250,16 @@ hbmc_status_t flow_host(hbmc_comm* c, Plan* p, uint64_t count, uint32_t e) {
   return HBMC_OK;
 }
 
-hbmc_status_t upload_flow(hbmc_comm* c, Plan* p) {
-  if (!c->flow_timeouts) {
-    void* m = nullptr;
-    if (hipMalloc(&m, 256) != hipSuccess) return HBMC_ERR_NOMEM;
-    const std::vector<uint32_t> zero(64, 0);
-    if (hipMemcpy(m, zero.data(), 256, hipMemcpyHostToDevice) != hipSuccess) {
-      (void)hipFree(m);
-      return HBMC_ERR_HIP;
-    }
-    c->flow_timeouts = static_cast<uint32_t*>(m);
-  }
+// Byte offsets in a plan's flow allocation: the control block, the count
+// of waits that gave up, then the column counters, tiles and chunks.
+constexpr size_t kFlowTimeoutsAt = 128;
+constexpr size_t kFlowHeadBytes = 256;
+
+hbmc_status_t upload_flow(Plan* p) {
   if (p->flow_mem) return HBMC_OK;
   const FlowTable& f = p->flow;
   auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
-  const size_t b_ctrl = 256;
+  const size_t b_ctrl = kFlowHeadBytes;
   const size_t b_prog = up(size_t(f.ncols) * sizeof(uint32_t) + 4);
   const size_t b_tiles = up(f.tiles.size() * sizeof(FlowTile) + 16);
   const size_t b_chunks = up(f.chunks.size() * sizeof(FlowChunk) + 16);
@@ -281,6 +277,7 @@ hbmc_status_t upload_flow(hbmc_comm* c, Plan* p) {
   }
   p->flow_mem = mem;
   p->dev_fctrl = reinterpret_cast<FlowCtrl*>(base);
+  p->dev_ftimeouts = reinterpret_cast<uint32_t*>(base + kFlowTimeoutsAt);
   p->dev_fprog = reinterpret_cast<uint32_t*>(base + b_ctrl);
   p->dev_ftiles = reinterpret_cast<FlowTile*>(base + b_ctrl + b_prog);
   p->dev_fchunks = reinterpret_cast<FlowChunk*>(base + b_ctrl + b_prog + b_tiles);
@@ -289,10 +286,22 @@ hbmc_status_t upload_flow(hbmc_comm* c, Plan* p) {
 
 hbmc_status_t flow_timeouts(hbmc_comm* c, uint32_t* count) {
   *count = 0;
-  if (!c->flow_timeouts) return HBMC_OK;
-  if (hipMemcpy(count, c->flow_timeouts, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return HBMC_ERR_HIP;
   const uint32_t zero = 0;
-  if (hipMemcpy(c->flow_timeouts, &zero, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess) return HBMC_ERR_HIP;
+  for (auto& kv : c->plans) {
+    Plan* p = kv.second.get();
+    std::vector<void*> blocks = p->flow_old;
+    if (p->flow_mem) blocks.push_back(p->flow_mem);
+    for (void* m : blocks) {
+      // the counter lives on the plan's device; unified addressing lets the
+      // copies find it from the pointer
+      uint32_t* t = reinterpret_cast<uint32_t*>(static_cast<char*>(m) + kFlowTimeoutsAt);
+      uint32_t n = 0;
+      if (hipMemcpy(&n, t, sizeof(n), hipMemcpyDeviceToHost) != hipSuccess ||
+          hipMemcpy(t, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+        return HBMC_ERR_HIP;
+      *count += n;
+    }
+  }
   return HBMC_OK;
 }
 
@@ -977,7 +986,7 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
   }
   if (mode == kExecFlow) {
     // the whole call as one flow-kernel launch
-    st = upload_flow(c, p);
+    st = upload_flow(p);
     if (st != HBMC_OK) return st;
     const FlowTable& f = p->flow;
     const uint32_t grid = std::max<uint32_t>(1, compute_units() * std::max<uint32_t>(1, c->flow_wgs_per_cu));
@@ -985,7 +994,7 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     const uint32_t flags = c->flow_flags | (f.max_step_write > kCacheBytes ? kFlowNtStores : 0u);
     KernelDesc k;
     describe_flow(dtype, op, ptrs, p->dev_ftiles, p->dev_fchunks, static_cast<uint32_t>(f.tiles.size()),
-                  p->dev_fctrl, p->dev_fprog, f.ncols, c->flow_timeouts, phase, flags, ticks,
+                  p->dev_fctrl, p->dev_fprog, f.ncols, p->dev_ftimeouts, phase, flags, ticks,
                   std::max<uint32_t>(1, c->flow_batch), grid, &k);
     launches->push_back(k);
     return HBMC_OK;

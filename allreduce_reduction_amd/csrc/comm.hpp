@@ -110,13 +110,17 @@ struct Plan {
   std::vector<DevItem> host_table;
   bool host_table_built = false;
   // the flow kernel: its host table for the communicator's tile length, and
-  // one device allocation holding the control block, the column counters,
-  // the tiles and the chunks (built on first launch)
+  // one device allocation (on the plan's device) holding the control block,
+  // the count of waits that gave up, the column counters, the tiles and the
+  // chunks (built on first launch); the allocations of earlier tile lengths,
+  // whose counts are still read
   FlowTable flow;
   bool flow_built = false;
   bool flow_ok = false;  // the schedule fits the flow records
   void* flow_mem = nullptr;
+  std::vector<void*> flow_old;
   FlowCtrl* dev_fctrl = nullptr;
+  uint32_t* dev_ftimeouts = nullptr;
   uint32_t* dev_fprog = nullptr;
   FlowTile* dev_ftiles = nullptr;
   FlowChunk* dev_fchunks = nullptr;
@@ -145,14 +149,12 @@ struct hbmc_comm {
   uint64_t column_bytes = 0;   // column length in bytes; 0: chosen per call
   bool xcd_split = false;
   // the flow kernel: tile length per rank buffer (bytes), workgroups per
-  // compute unit, wait bound, flags (kFlowUnreachable) and the device
-  // counter of waits that gave up (allocated on first use)
+  // compute unit, wait bound, flags (kFlowUnreachable)
   uint64_t flow_tile_bytes = uint64_t(16) << 10;
   uint32_t flow_wgs_per_cu = 8;
   uint32_t flow_wait_us = 1000000;
   uint32_t flow_flags = 0;
   uint32_t flow_batch = 1;  // tiles per ticket
-  uint32_t* flow_timeouts = nullptr;
   // (topology index, coll, root, count, dtype) -> plan
   std::map<std::tuple<int, int, int, uint64_t, int>, std::unique_ptr<hbmc::Plan>> plans;
   // AUTO: (coll, root, count, dtype) -> chosen topology index
@@ -214,12 +216,11 @@ hbmc_status_t lds_host_tables(Plan* p, int P, uint64_t count, uint32_t e);
 // The flow kernel's host table of plan p for the communicator's tile length
 // (count elements of e bytes), built once per length; sets p->flow_ok.
 hbmc_status_t flow_host(hbmc_comm* c, Plan* p, uint64_t count, uint32_t e);
-// Upload it to the current device with zeroed counters (again after the
-// tile length changed; the old tables are retired, not freed), and allocate
-// the communicator's timeout counter.
-hbmc_status_t upload_flow(hbmc_comm* c, Plan* p);
-// Read the communicator's count of flow waits that gave up, and clear it
-// (synchronous; 0 when no flow launch ran).
+// Upload it to the plan's device with zeroed counters (again after the
+// tile length changed; the old tables are retired, not freed).
+hbmc_status_t upload_flow(Plan* p);
+// The number of flow waits that gave up in all of the communicator's plans,
+// then cleared (synchronous; 0 when no flow launch ran).
 hbmc_status_t flow_timeouts(hbmc_comm* c, uint32_t* count);
 // Bytes a launch of steps [first, last) in form `mode` moves between the
 // compute units and memory (see hbmc_exec_bytes).

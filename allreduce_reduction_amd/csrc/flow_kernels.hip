@@ -19,8 +19,8 @@
 // which a running workgroup already holds (tickets are taken by running
 // workgroups only, at most one ahead of the tile a workgroup runs), so the
 // smallest unfinished ticket can always proceed.  Every wait is bounded in
-// wall-clock time all the same: a wait past the bound counts a timeout in a
-// per-communicator counter, raises the launch's give-up flag and skips its
+// wall-clock time all the same: a wait past the bound counts a timeout in the
+// plan's counter, raises the launch's give-up flag and skips its
 // tile; waits that see the flag give up at once, so every workgroup reaches
 // the exit.  The last workgroup to leave resets the ticket and column
 // counters for the next launch.

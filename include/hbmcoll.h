@@ -241,8 +241,9 @@ hbmc_status_t hbmc_comm_set_fused_limit(hbmc_comm_t comm, uint64_t max_bytes);
 #define HBMC_FLOW_UNREACHABLE 1u
 hbmc_status_t hbmc_comm_set_flow(hbmc_comm_t comm, uint64_t tile_bytes, uint32_t wgs_per_cu,
                                  uint32_t tiles_per_ticket, uint32_t wait_us, uint32_t flags);
-/* The number of flow-form waits that gave up since the last call, then
- * reset to 0 (waits for the device: call it after the launches in
+/* The number of flow-form waits that gave up since the last call, over all
+ * of the communicator's plans (each counts in its own device allocation),
+ * then reset to 0 (waits for the device: call it after the launches in
  * question have completed). */
 hbmc_status_t hbmc_comm_flow_timeouts(hbmc_comm_t comm, uint32_t* count);
 /* column_bytes: 0, or 16 .. 2^31 (rounded down to a multiple of 16). */

@@ -142,24 +142,33 @@ def test_flow_graph_replays():
 def test_flow_gives_up_when_forced_and_recovers():
     """Every wait made unreachable from the host: each tile with an earlier
     tile gives up after the 50 us bound, the launch ends normally and counts
-    timeouts; the next call, with reachable waits, is exact."""
+    timeouts; the next calls, with reachable waits, are exact, also after the
+    tile length changed (the counts of the earlier tables are still read)."""
     P, L, dtype = 8, 50_000, "fp32"
     xs = make_inputs(dtype, "sum", P, L, 21)
-    dev = [to_dev(x, dtype) for x in xs]
+    want = [x.copy() for x in xs]
+    oracle.run("allreduce", "ring", want, dtype, "sum")
     with hc.Comm(P, "ring") as c:
         c.set_exec_mode("flow")
         c.set_flow(1024, wait_us=50, unreachable=True)
+        dev = [to_dev(x, dtype) for x in xs]
         say("case flow give-up forced")
         c.allreduce(dev, dtype, "sum")
         torch.cuda.synchronize()
         assert c.flow_timeouts() >= 1
         assert c.flow_timeouts() == 0  # read and cleared
-        c.set_flow(1024)
-        dev = [to_dev(x, dtype) for x in xs]
-        say("case flow after give-up")
-        c.allreduce(dev, dtype, "sum")
-        torch.cuda.synchronize()
+        for tile in (1024, 2048):
+            if tile == 2048:  # a give-up under the old length, then a new length
+                c.set_flow(1024, wait_us=50, unreachable=True)
+                dev = [to_dev(x, dtype) for x in xs]
+                c.allreduce(dev, dtype, "sum")
+                torch.cuda.synchronize()
+            c.set_flow(tile)
+            dev = [to_dev(x, dtype) for x in xs]
+            say(f"case flow after give-up, tile {tile}")
+            c.allreduce(dev, dtype, "sum")
+            torch.cuda.synchronize()
+            _check(dev, want, dtype, f"flow after give-up, tile {tile}")
+            n = c.flow_timeouts()
+            assert (n >= 1) if tile == 2048 else (n == 0)
         assert c.flow_timeouts() == 0
-    want = [x.copy() for x in xs]
-    oracle.run("allreduce", "ring", want, dtype, "sum")
-    _check(dev, want, dtype, "flow after give-up")
