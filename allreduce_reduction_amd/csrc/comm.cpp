@@ -797,7 +797,12 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
     if (aligned && busy > 1 && whole) {
       hbmc_status_t st = flow_host(c, p, count, e);
       if (st != HBMC_OK) return st;
-      if (p->flow_ok) *mode = kExecFlow;
+      // the ticket counter runs to the tiles plus one batch per workgroup
+      // past them (and one more taken ahead): it must not wrap
+      const uint64_t tickets = uint64_t(p->flow.tiles.size()) + uint64_t(compute_units()) *
+                                                                   std::max<uint32_t>(1, c->flow_wgs_per_cu) *
+                                                                   std::max<uint32_t>(1, c->flow_batch) * 2;
+      if (p->flow_ok && tickets < UINT32_MAX) *mode = kExecFlow;
     }
     return HBMC_OK;
   }
