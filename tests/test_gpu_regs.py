@@ -60,14 +60,16 @@ def test_regs_parity(algo, P, dtype):
     assert forms == {"regs"}
 
 
-@pytest.mark.parametrize("algo,P", [("ring", 8), ("rhd", 5)])
-def test_regs_phases(algo, P):
+@pytest.mark.parametrize("algo,P,coll", [("ring", 8, "allreduce"), ("rhd", 5, "allreduce"),
+                                         ("ring", 6, "reduce_scatter"), ("ring", 7, "all_gather"),
+                                         ("rhd", 6, "all_gather")])
+def test_regs_phases(algo, P, coll):
     """Rank buffers at one shared 16-byte phase other than 0: the head and
-    tail elements go element by element."""
+    tail elements go element by element (fold and tree; prefix and copy)."""
     for dtype in ("fp16", "int8", "fp32"):
         e = np.dtype(refops.STORAGE[dtype]).itemsize
         for ph in range(0, 16 // e):
-            assert run_regs(algo, P, 2000 + ph, dtype, "sum", seed=ph, offsets=[ph] * P) == "regs"
+            assert run_regs(algo, P, 2000 + ph, dtype, "sum", seed=ph, offsets=[ph] * P, coll=coll) == "regs"
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
