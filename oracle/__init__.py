@@ -125,7 +125,7 @@ def num_steps(coll: str, algo: str, P: int, S: int = 1, M: int = 1) -> int:
 
 def threads_available() -> int:
     """Host threads a parallel replay uses: the CPUs this process may run on,
-    at most 16 (a GPU machine's share of its host)."""
+    at most 16 (a single GPU's usual share of a multi-GPU host's cores)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
