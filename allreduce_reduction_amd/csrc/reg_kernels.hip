@@ -270,9 +270,14 @@ void describe_regs(int dtype, int op, const RankPtrs& ptrs, int P, const RegPlan
     most = fill(new (k->args) RegFoldCall, ptrs, rp, count, phase, E,
                 form == kRegTreeSmall ? uint32_t(RegShape<kRegTreeSmall>::pair) : 0u);
   // at least one lane per element a region takes one by one (fewer than 16
-  // at each end of a region)
+  // at each end of a region); one-wave workgroups, which measured as fast or
+  // faster than 128 or 256 lanes everywhere (MI355X, graphs of ten calls:
+  // 8-rank RHD bf16 at 4-64 KiB per rank 2.91-3.00 against 3.11-3.28 us,
+  // 16-rank RHD fp16 at 16 KiB 3.06 against 3.52 us, 16-rank ring fp16 at
+  // 4 MiB 21.9 against 23.5 us; a capped grid whose lanes walk several
+  // positions was slower still)
   const uint64_t lanes = std::max<uint64_t>(most, 16);
-  const uint32_t block = lanes <= 64 ? 64u : (lanes <= 128 ? 128u : uint32_t(kRegThreads));
+  const uint32_t block = 64u;
   k->kind = KernelDesc::kRegs;
   k->grid = dim3(static_cast<uint32_t>((lanes + block - 1) / block), static_cast<uint32_t>(rp.regions.size()));
   k->block = dim3(block);
