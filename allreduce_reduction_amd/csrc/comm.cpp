@@ -916,7 +916,19 @@ hbmc_status_t exec_bytes(hbmc_comm* c, Plan* p, int first, int last, uint64_t co
       p->regs_built = true;
     }
     if (!p->regs.ok) return HBMC_ERR_INVALID_ARG;
-    *bytes = uint64_t(p->regs.loads + p->regs.stores) * count * e;
+    if (p->regs.form != kRegNodes) {
+      *bytes = uint64_t(p->regs.loads + p->regs.stores) * count * e;
+      return HBMC_OK;
+    }
+    // the node form: every rank loaded; per region, the ranks that receive a node
+    *bytes = uint64_t(p->regs.loads) * count * e;
+    uint64_t start = 0;
+    for (const RegRegion& q : p->regs.regions) {
+      uint64_t st = 0;
+      for (uint32_t v = 0; v < p->regs.n; ++v) st += q.lvl[v] != 0 && q.lvl[v] != 0xff;
+      *bytes += st * (q.end - start) * e;
+      start = q.end;
+    }
     return HBMC_OK;
   }
   if (mode != kExecLds) return HBMC_ERR_INVALID_ARG;

@@ -152,12 +152,15 @@ constexpr uint32_t kFlowNtStores = 2u;
 // region's elements outside them [el_lo[i], el_hi[i]), and the address of
 // element 0 of every operand: for the fold ptr[0..n) in fold order, for the
 // tree ptr[v] and ptr[16 + v] the two ranks of leaf v (nullptr for a leaf of
-// one rank).  Every operand is also a destination.
+// one rank).  Every operand is also a destination, except in the node form,
+// where leaf v's rank receives the tree node of level lvl[v] above it (0: it
+// keeps its input).
 constexpr int kRegThreads = 256;
 template <int NP>
 struct RegRegionArg {
   uint32_t vec_lo, vec_hi;
   uint32_t el_lo[2], el_hi[2];
+  uint8_t lvl[kRegMaxLeaves];
   unsigned char* ptr[NP];
 };
 template <int NP, int NR>

@@ -3,8 +3,8 @@
 // one 16-byte position of the vector, loads every operand there into
 // registers at once, evaluates the schedule's expression in its grouping --
 // a left fold over a rank sequence, a complete pairwise tree over single
-// ranks and merged pairs, a copy of one rank, or the prefixes of a fold --
-// and stores every rank the schedule writes there.  A region's
+// ranks and merged pairs, a copy of one rank, the prefixes of a fold, or the
+// nodes of a tree -- and stores every rank the schedule writes there.  A region's
 // operand addresses travel in its record in the kernel arguments, so a
 // workgroup waits on one round of scalar loads (its record) and one round of
 // data loads: no table in device memory, no LDS, no barrier.  The region's
@@ -106,10 +106,29 @@ __device__ __forceinline__ void store_all(uint32_t n, unsigned char* const* ptr,
 }
 
 // One position (a 16-byte vector, or one element) of a region: the
-// operands loaded, combined and stored as the form says.
+// operands loaded, combined and stored as the form says (lvl: the node
+// form's store levels).
 template <int FORM, typename V, typename Load, typename Op, typename Store>
-__device__ __forceinline__ void position(uint32_t n, unsigned char* const* ptr, Load load, Op op, Store store) {
-  if constexpr (FORM == kRegCopy) {
+__device__ __forceinline__ void position(uint32_t n, unsigned char* const* ptr, const uint8_t* lvl, Load load,
+                                         Op op, Store store) {
+  if constexpr (FORM == kRegNodes) {
+    // the tree level by level; after level l, every leaf whose rank holds
+    // the level-l node above it stores that node
+    V x[kRegMaxLeaves];
+#pragma unroll
+    for (uint32_t v = 0; v < kRegMaxLeaves; ++v)
+      if (v < n) x[v] = load(ptr[v]);
+    uint32_t l = 1;
+#pragma unroll
+    for (uint32_t w = 1; w < kRegMaxLeaves; w *= 2, ++l) {
+#pragma unroll
+      for (uint32_t v = 0; v + w < kRegMaxLeaves; v += 2 * w)
+        if (v + w < n) x[v] = op(x[v], x[v + w]);
+#pragma unroll
+      for (uint32_t v = 0; v < kRegMaxLeaves; ++v)
+        if (v < n && lvl[v] == l) store(ptr[v], x[v & ~(2 * w - 1)]);
+    }
+  } else if constexpr (FORM == kRegCopy) {
     const V v = load(ptr[0]);
 #pragma unroll
     for (uint32_t i = 1; i < kRegMaxLeaves; ++i)
@@ -146,10 +165,15 @@ plan_regs(Call c) {
   const auto& R0 = c.r[blockIdx.y];
   struct {
     uint32_t vec_lo, vec_hi, el_lo[2], el_hi[2];
+    uint8_t lvl[kRegMaxLeaves];
     unsigned char* ptr[NP];
   } R;
   R.vec_lo = R0.vec_lo;
   R.vec_hi = R0.vec_hi;
+  if constexpr (FORM == kRegNodes) {
+#pragma unroll
+    for (int i = 0; i < kRegMaxLeaves; ++i) R.lvl[i] = R0.lvl[i];
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     R.el_lo[i] = R0.el_lo[i];
@@ -163,7 +187,7 @@ plan_regs(Call c) {
   if (k < R.vec_hi) {
     const uint64_t off = (head + k * EPV) * E;
     position<FORM, u32x4>(
-        n, R.ptr, [&](const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p + off); },
+        n, R.ptr, R.lvl, [&](const unsigned char* p) { return *reinterpret_cast<const u32x4*>(p + off); },
         [](u32x4 a, u32x4 b) { return op_vec<DT, OP>(a, b); },
         [&](unsigned char* p, u32x4 v) { store_vec(reinterpret_cast<u32x4*>(p + off), v); });
   }
@@ -174,7 +198,7 @@ plan_regs(Call c) {
       if (e < R.el_hi[part]) {
         const uint64_t off = e * E;
         position<FORM, uint32_t>(
-            n, R.ptr, [&](const unsigned char* p) { return load_elem<E>(p + off); },
+            n, R.ptr, R.lvl, [&](const unsigned char* p) { return load_elem<E>(p + off); },
             [](uint32_t a, uint32_t b) { return op_word<DT, OP>(a, b); },
             [&](unsigned char* p, uint32_t v) { store_elem<E>(p + off, v); });
       }
@@ -188,6 +212,7 @@ const void* regs_fn(uint32_t form) {
     case kRegTree: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTree, RegTreeCall>);
     case kRegTreeSingles: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTreeSingles, RegFoldCall>);
     case kRegTreeSmall: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegTreeSmall, RegFoldCall>);
+    case kRegNodes: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegNodes, RegFoldCall>);
     case kRegCopy: return reinterpret_cast<const void*>(plan_regs<DT, kSum, kRegCopy, RegFoldCall>);
     case kRegPrefix: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegPrefix, RegFoldCall>);
     default: return reinterpret_cast<const void*>(plan_regs<DT, OP, kRegFold, RegFoldCall>);
@@ -242,6 +267,7 @@ uint64_t fill(Call* c, const RankPtrs& ptrs, const RegPlan& rp, uint64_t count, 
     }
     for (uint32_t v = 0; v < rp.n; ++v) {
       r.ptr[v] = ptrs.p[q.a[v]];
+      r.lvl[v] = q.lvl[v] == 0xff ? 0 : q.lvl[v];
       if (pair > 0 && q.b[v] != 0xff) r.ptr[pair + v] = ptrs.p[q.b[v]];
     }
     most = std::max<uint64_t>(most, hi - lo);

@@ -162,7 +162,7 @@ void derive_regs(const Schedule& s, int P, uint64_t count, RegPlan* out) {
   std::vector<RegRegion> regs;
   auto push = [&](uint64_t end, const RegRegion& r) {
     if (!regs.empty() && std::memcmp(regs.back().a, r.a, sizeof(r.a)) == 0 &&
-        std::memcmp(regs.back().b, r.b, sizeof(r.b)) == 0) {
+        std::memcmp(regs.back().b, r.b, sizeof(r.b)) == 0 && std::memcmp(regs.back().lvl, r.lvl, sizeof(r.lvl)) == 0) {
       regs.back().end = end;
       return;
     }
@@ -187,29 +187,78 @@ void derive_regs(const Schedule& s, int P, uint64_t count, RegPlan* out) {
     for (int r = 1; r < P; ++r) same = same && val[t * P + r] == expr[t];
   }
   if (!same) {
+    if (P > kRegMaxLeaves) return;
     // prefixes of one fold: the first rank holding a fold over all P ranks
     // names the sequence; rank seq[0] keeps its input and rank seq[i] holds
     // the fold over seq[0..i]
-    if (P > kRegMaxLeaves) return;
-    for (size_t t = 0; t < nint; ++t) {
-      const int* v = &val[t * P];
-      bool found = false;
-      for (int r = 0; r < P && !found; ++r) found = as_fold(X, v[r], &seq) && seq.size() == size_t(P);
-      if (!found) return;
-      // the first two operands of a fold commute: the one that keeps its input goes first
-      if (v[seq[0]] != seq[0]) std::swap(seq[0], seq[1]);
-      if (v[seq[0]] != seq[0]) return;
-      int pre = seq[0];
-      for (int i = 1; i < P; ++i) {
-        pre = X.op(pre, seq[i]);
-        if (v[seq[i]] != pre) return;
+    auto prefix = [&]() {
+      for (size_t t = 0; t < nint; ++t) {
+        const int* v = &val[t * P];
+        bool found = false;
+        for (int r = 0; r < P && !found; ++r) found = as_fold(X, v[r], &seq) && seq.size() == size_t(P);
+        if (!found) return false;
+        // the first two operands of a fold commute: the one that keeps its input goes first
+        if (v[seq[0]] != seq[0]) std::swap(seq[0], seq[1]);
+        if (v[seq[0]] != seq[0]) return false;
+        int pre = seq[0];
+        for (int i = 1; i < P; ++i) {
+          pre = X.op(pre, seq[i]);
+          if (v[seq[i]] != pre) return false;
+        }
+        RegRegion r;
+        std::memset(&r, 0xff, sizeof(r));
+        for (int i = 0; i < P; ++i) r.a[i] = static_cast<uint8_t>(seq[i]);
+        push(cut[t + 1], r);
       }
-      RegRegion r;
-      std::memset(&r, 0xff, sizeof(r));
-      for (int i = 0; i < P; ++i) r.a[i] = static_cast<uint8_t>(seq[i]);
-      push(cut[t + 1], r);
+      return true;
+    };
+    // nodes of one complete tree of single ranks over all P ranks: every rank
+    // keeps its input or holds a node above its own leaf (how many ranks
+    // receive a node may differ between intervals: `stores` is the most)
+    uint32_t stores = 0;
+    auto nodes = [&]() {
+      if (P & (P - 1)) return false;
+      int k = 0;
+      while ((1 << k) < P) ++k;
+      for (size_t t = 0; t < nint; ++t) {
+        const int* v = &val[t * P];
+        bool found = false;
+        for (int r = 0; r < P && !found; ++r) {
+          if (!as_tree(X, v[r], &leaves) || leaves.size() != size_t(P)) continue;
+          found = true;
+          for (const auto& lf : leaves) found = found && lf.second == 0xff;
+        }
+        if (!found) return false;
+        // node ids level by level, as the kernel pairs them
+        std::vector<std::vector<int>> lv(k + 1);
+        for (const auto& lf : leaves) lv[0].push_back(lf.first);
+        for (int l = 1; l <= k; ++l)
+          for (size_t j = 0; j + 1 < lv[l - 1].size(); j += 2) lv[l].push_back(X.op(lv[l - 1][j], lv[l - 1][j + 1]));
+        RegRegion r;
+        std::memset(&r, 0xff, sizeof(r));
+        uint32_t n_st = 0;
+        for (int i = 0; i < P; ++i) {
+          const int rank = lv[0][i];
+          r.a[i] = static_cast<uint8_t>(rank);
+          int got = -1;
+          if (v[rank] == rank) got = 0;
+          for (int l = 1; l <= k && got < 0; ++l)
+            if (lv[l][i >> l] == v[rank]) got = l;
+          if (got < 0) return false;
+          r.lvl[i] = static_cast<uint8_t>(got);
+          n_st += got > 0;
+        }
+        stores = std::max(stores, n_st);
+        push(cut[t + 1], r);
+      }
+      return true;
+    };
+    if (prefix()) {
+      finish(kRegPrefix, static_cast<uint32_t>(P), static_cast<uint32_t>(P), static_cast<uint32_t>(P - 1));
+      return;
     }
-    finish(kRegPrefix, static_cast<uint32_t>(P), static_cast<uint32_t>(P), static_cast<uint32_t>(P - 1));
+    regs.clear();
+    if (nodes()) finish(kRegNodes, static_cast<uint32_t>(P), static_cast<uint32_t>(P), stores);
     return;
   }
   bool copy = true;

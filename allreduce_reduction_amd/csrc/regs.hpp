@@ -16,6 +16,9 @@
 //   - or the ranks end with the prefixes of one left fold over all P ranks,
 //     each rank holding the prefix that ends with its own input (the ring's
 //     reduce-scatter),
+//   - or, for a complete pairwise tree over all P ranks (P a power of two),
+//     every rank ends with its own input or with a node of that tree above
+//     its own leaf (RHD's reduce-scatter and Reduce),
 // one kernel evaluates it in registers: every operand loaded once, the
 // operations in the schedule's grouping, and every rank's result stored.
 // The element ops are commutative bit for bit (IEEE sum / product, wrapping
@@ -34,26 +37,30 @@ constexpr int kRegMaxLeaves = 16;       // fold length / tree leaves
 constexpr int kRegMaxFoldRegions = 16;  // intervals of distinct parameters, fold form
 constexpr int kRegMaxTreeRegions = 8;   // and tree form (each region's addresses travel in
                                         // the kernel arguments)
-enum RegForm : uint32_t { kRegFold = 0, kRegTree = 1, kRegCopy = 2, kRegPrefix = 3 };
+enum RegForm : uint32_t { kRegFold = 0, kRegTree = 1, kRegCopy = 2, kRegPrefix = 3, kRegNodes = 6 };
 
 // Elements [previous region's end, end) take: for kRegFold the left fold over
 // a[0..n), stored to every rank; for kRegTree the tree over leaves v < n =
 // 2^k, leaf v being rank a[v], or a[v] op b[v] when b[v] != 0xff, stored to
 // every rank; for kRegCopy rank a[0]'s value, stored to ranks a[1..n); for
 // kRegPrefix the left fold over a[0..n), rank a[i] (i >= 1) receiving the
-// fold over a[0..i].
+// fold over a[0..i]; for kRegNodes the tree over leaves a[0..n) (n = 2^k),
+// rank a[v] receiving the node of level lvl[v] whose leaves include v (the
+// nodes of level l pair those of level l - 1: (0,1), (2,3), ...), or keeping
+// its input when lvl[v] is 0.
 struct RegRegion {
   uint64_t end;
   uint8_t a[kRegMaxLeaves];
   uint8_t b[kRegMaxLeaves];
+  uint8_t lvl[kRegMaxLeaves];
 };
-static_assert(sizeof(RegRegion) == 40, "register-form region");
+static_assert(sizeof(RegRegion) == 56, "register-form region");
 
 struct RegPlan {
   bool ok = false;  // the whole collective can run in the register form
   RegForm form = kRegFold;
   uint32_t n = 0;   // operands (fold length, tree leaves; one value for all regions)
-  uint32_t loads = 0, stores = 0;  // per element position, every region
+  uint32_t loads = 0, stores = 0;  // per element position (kRegNodes: stores is the most of any region)
   std::vector<RegRegion> regions;
 };
 

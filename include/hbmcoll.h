@@ -172,9 +172,11 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    with one rank's input (all-gathers of ring, RHD and pipeline, RHD's
  *    broadcast); or the ranks hold the prefixes of one left fold over all
  *    ranks (the ring's reduce-scatter, whose other segments keep the
- *    schedule's partial sums).  At most 16 folded terms, tree leaves or
- *    copies, and at most 16 (fold, copy, prefix) or 8 (tree) intervals of
- *    distinct parameters.  One lane per 16-byte position loads every
+ *    schedule's partial sums); or, for P a power of two, every rank keeps its
+ *    input or holds a node of one pairwise tree above its own leaf (RHD's
+ *    reduce-scatter and Reduce).  At most 16 folded terms, tree leaves or
+ *    copies, and at most 16 (fold, copy, prefix, nodes) or 8 (tree)
+ *    intervals of distinct parameters.  One lane per 16-byte position loads every
  *    operand once, evaluates the expression and stores every rank the
  *    schedule writes there ([RHD] "耗时计算": every step pays alpha, which
  *    this form pays once);
@@ -267,7 +269,9 @@ hbmc_status_t hbmc_exec_choice(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
  *    communicator would use;
  *  - REGS: every operand loaded once and every written rank stored once:
  *    2 P count e for an AllReduce, P count e for a copy (one load, P - 1
- *    stores), (2 P - 1) count e for the ring's reduce-scatter.
+ *    stores), (2 P - 1) count e for the ring's reduce-scatter, (P + P/2)
+ *    count e for RHD's reduce-scatter (P/2 ranks receive a node per
+ *    element), counted region by region for RHD's Reduce.
  * HBMC_ERR_INVALID_ARG for a bad step range, for LDS when no column length
  * fits one workgroup's LDS, and for REGS when the call has no register form
  * or the range is not all of its steps.  Otherwise the figure does not

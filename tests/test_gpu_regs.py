@@ -35,6 +35,8 @@ def run_regs(algo, P, L, dtype, op, seed, offsets=None, coll="allreduce", S=0, M
         say(f"case regs {algo} {coll} P={P} L={L} {dtype} {op} offsets={offsets} -> {form}")
         if coll == "broadcast":
             c.broadcast(dev, dtype, root=root)
+        elif coll == "reduce":
+            c.reduce(dev, dtype, op, root=root)
         else:
             getattr(c, coll)(dev, dtype, op)
         torch.cuda.synchronize()
@@ -62,7 +64,7 @@ def test_regs_parity(algo, P, dtype):
 
 @pytest.mark.parametrize("algo,P,coll", [("ring", 8, "allreduce"), ("rhd", 5, "allreduce"),
                                          ("ring", 6, "reduce_scatter"), ("ring", 7, "all_gather"),
-                                         ("rhd", 6, "all_gather")])
+                                         ("rhd", 6, "all_gather"), ("rhd", 8, "reduce_scatter")])
 def test_regs_phases(algo, P, coll):
     """Rank buffers at one shared 16-byte phase other than 0: the head and
     tail elements go element by element (fold and tree; prefix and copy)."""
@@ -78,14 +80,18 @@ def test_regs_phases(algo, P, coll):
                                              ("ring", 5, "all_gather", 0, 0), ("rhd", 8, "all_gather", 0, 0),
                                              ("rhd", 6, "all_gather", 0, 0), ("rhd", 5, "broadcast", 0, 0),
                                              ("pipeline", 8, "all_gather", 2, 4), ("tree", 5, "allreduce", 0, 2),
-                                             ("tree", 3, "allreduce", 0, 2), ("rhd", 17, "allreduce", 0, 0)])
+                                             ("tree", 3, "allreduce", 0, 2), ("rhd", 17, "allreduce", 0, 0),
+                                             ("rhd", 4, "reduce_scatter", 0, 0), ("rhd", 8, "reduce_scatter", 0, 0),
+                                             ("rhd", 16, "reduce_scatter", 0, 0), ("rhd", 8, "reduce", 0, 0),
+                                             ("rhd", 16, "reduce", 0, 0), ("rhd", 4, "reduce", 0, 0)])
 def test_regs_other_collectives(algo, P, coll, S, M, dtype):
     """Copies (all-gather, broadcast), prefixes of one fold (the ring's
-    reduce-scatter, whose other segments keep the schedule's partials) and a
-    small tree AllReduce whose nesting is a fold: every rank's whole buffer
-    against the oracle."""
+    reduce-scatter, whose other segments keep the schedule's partials), nodes
+    of one tree (RHD's reduce-scatter and Reduce: every rank keeps its input or
+    holds the subtree it last kept) and a small tree AllReduce whose nesting
+    is a fold: every rank's whole buffer against the oracle."""
     forms = set()
-    for i, op in enumerate(OPS if coll in ("reduce_scatter", "allreduce") else ["sum"]):
+    for i, op in enumerate(OPS if coll in ("reduce_scatter", "allreduce", "reduce") else ["sum"]):
         for L in (7, 1001, 3 * 4096 + 5, 40_000 + 3):
             forms.add(run_regs(algo, P, L, dtype, op, seed=77 * i + L, coll=coll, S=S, M=M, root=P - 2))
     assert forms == {"regs"}

@@ -37,10 +37,10 @@ def test_auto_small_rhd_many_ranks_prefers_the_single_workgroup():
         assert c.exec_choice("allreduce", 8 << 10, "fp16") == "lds"
     # over 16 ranks the register form takes the whole tree (on MI355X, graphs
     # of ten: 7.0-7.1 us against 14.2 us in the LDS form and 15.4 us in the
-    # single workgroup); its reduce-scatter keeps the LDS form
+    # single workgroup), and its reduce-scatter as the tree's nodes
     with hc.Comm(16, "rhd") as c:
         assert c.exec_choice("allreduce", 512, "fp16") == "regs"
-        assert c.exec_choice("reduce_scatter", 512, "fp16") != "regs"
+        assert c.exec_choice("reduce_scatter", 512, "fp16") == "regs"
 
 
 def test_auto_prefers_steps_where_launches_are_few_and_bytes_many():
@@ -198,10 +198,15 @@ def test_regs_only_where_the_expression_is_a_fold_tree_copy_or_prefix():
         assert c.exec_choice("allreduce", 10_000, "fp32") == "steps"
     with hc.Comm(8, "rhd") as c:
         c.set_exec_mode("regs")
-        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "steps"  # partial trees
-        assert c.exec_choice("reduce", 10_000, "fp32", root=3) == "steps"
+        # partial trees: every rank holds its input or a node of the tree above its own leaf
+        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "regs"
+        assert c.exec_choice("reduce", 10_000, "fp32", root=3) == "regs"
         assert c.exec_choice("all_gather", 10_000, "fp32") == "regs"
         assert c.exec_choice("broadcast", 10_000, "fp32", root=3) == "regs"
+    with hc.Comm(6, "rhd") as c:  # not a power of two: merged pairs under partial trees
+        c.set_exec_mode("regs")
+        assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "steps"
+        assert c.exec_choice("reduce", 10_000, "fp32", root=3) == "steps"
     with hc.Comm(8, "ring") as c:
         c.set_exec_mode("regs")
         assert c.exec_choice("reduce_scatter", 10_000, "fp32") == "regs"
@@ -231,3 +236,7 @@ def test_regs_offered_for_folds_and_trees(algo, P):
         if algo == "ring" and P > 2:
             assert c.exec_bytes("reduce_scatter", 1001, "bf16", "regs") == (2 * P - 1) * 1001 * 2
             assert c.exec_bytes("all_gather", 1001, "bf16", "regs") == P * 1001 * 2
+        if algo == "rhd" and P & (P - 1) == 0 and P > 2:
+            # every rank loaded; per element, P/2 ranks receive a node (the owner
+            # the root, the others the subtrees they kept)
+            assert c.exec_bytes("reduce_scatter", 1001, "bf16", "regs") == (P + P // 2) * 1001 * 2
