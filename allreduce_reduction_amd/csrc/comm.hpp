@@ -64,7 +64,7 @@ struct LdsHost {
 struct Plan {
   Schedule sched;
   int coll = 0;                    // the collective it implements
-  // the register form of a whole AllReduce, derived on first use
+  // the register form of the whole call, derived on first use
   bool regs_built = false;
   RegPlan regs;
   std::vector<size_t> first_item;  // offset of each step's items in the device table

@@ -310,8 +310,8 @@ void describe_columns_lds(int dtype, int op, const RankPtrs& ptrs, const DevColC
                           const DevColStore* stores, const uint32_t* col_run, const uint32_t* st_off,
                           const uint64_t* col_load, KernelDesc* k);
 
-// The register-form kernel of a whole AllReduce of P ranks over `count`
-// elements whose rank buffers share the 16-byte `phase` (rp.ok).
+// The register-form kernel of a whole call of P ranks over `count` elements
+// whose rank buffers share the 16-byte `phase` (rp.ok).
 void describe_regs(int dtype, int op, const RankPtrs& ptrs, int P, const RegPlan& rp, uint64_t count,
                    uint32_t phase, KernelDesc* k);
 
