@@ -78,7 +78,7 @@ def parse():
     ap.add_argument("--suite", action="store_true", help="time the other workloads instead")
     ap.add_argument("--max-sweep-bytes", type=int, default=1 << 30)
     ap.add_argument("--workloads", default="rhd_small,sweep,forms,algorithms,pipe",
-                    help="suite workloads to run (comma-separated; also sweep_steps, flow)")
+                    help="suite workloads to run (comma-separated; also sweep_steps, flow, cold_steps)")
     ap.add_argument("--sweep-sizes", default=f"{16 << 20},{256 << 20},{1 << 30}",
                     help="sweep_steps: bytes per rank (comma-separated)")
     return ap.parse_args()
@@ -263,6 +263,43 @@ def suite(a):
                              launch_form="steps", steps=rows)
             del bufs, pristine
             torch.cuda.empty_cache()
+
+    if "cold_steps" in workloads:
+        # the benchmark AllReduce's 14 step kernels, each timed alone: warm
+        # (right after the previous run of the same step, so part of its
+        # reads may come from the 256 MiB memory-side cache), and cold (after
+        # a 512 MiB read pass that fills that cache and the L2s with other,
+        # clean data, so the step's reads come from HBM and no write-back of
+        # other data gets in the way); HIP events around the step alone
+        P, L = 8, 64 << 20
+        bufs = upload("ring_p8_fp32_grad", P, L)
+        scrub_r = torch.ones((512 << 20) // 4, dtype=torch.float32, device="cuda")
+        rows = []
+        with hc.Comm(P, "ring") as c:
+            c.set_exec_mode("steps")
+            n = c.plan_info("allreduce", L, "fp32")["nsteps"]
+            for st in range(n):
+                si = c.step_info("allreduce", L, "fp32", st)
+                warm = time_calls(lambda: c.run_steps("allreduce", bufs, st, st + 1, "fp32", "sum"), 5, 1)
+                cold = []
+                for _ in range(7):
+                    float(scrub_r.sum())  # read pass, and the device is idle after it
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    c.run_steps("allreduce", bufs, st, st + 1, "fp32", "sum")
+                    b.record()
+                    b.synchronize()
+                    cold.append(a.elapsed_time(b) * 1e-3)
+                cold.sort()
+                tc = cold[len(cold) // 2]
+                rows.append(dict(step=st, hbm_bytes=si["hbm_bytes"], warm_us=round(warm * 1e6, 2),
+                                 cold_us=round(tc * 1e6, 2), warm_frac=round(si["hbm_bytes"] / warm / HBM_PEAK, 4),
+                                 cold_frac=round(si["hbm_bytes"] / tc / HBM_PEAK, 4)))
+        emit(workload="ring_p8_fp32_cold_steps", P=P, elems_per_rank=L, steps=rows,
+             warm_us=round(sum(r["warm_us"] for r in rows), 1), cold_us=round(sum(r["cold_us"] for r in rows), 1))
+        del bufs, scrub_r
+        torch.cuda.empty_cache()
 
     if "flow" in workloads:
         # the flow form (all steps in one persistent launch, tiles in step
@@ -572,7 +609,9 @@ def main():
                                       "calibrated on a 256 MiB device copy); a read served by the 256 MiB "
                                       "memory-side cache counts like one from HBM, and each step writes 256 MiB "
                                       "with plain stores, so part of the next step's reads of those blocks "
-                                      "come from that cache rather than from HBM")},
+                                      "come from that cache rather than from HBM; with that cache holding "
+                                      "other data before each step, the reduce step measured 0.80-0.81 of "
+                                      "peak (bench.py --suite --workloads cold_steps)")},
     }
     if ag_ms:
         ag_bytes = comm.step_info("allreduce", L, dtype, ag_steps[0])["hbm_bytes"]
