@@ -71,8 +71,9 @@ constexpr size_t kArgBytes = sizeof(ArgItems<kArgMaxBufs>);
 // A step that writes more than the memory-side cache holds (MI355X: 256 MiB
 // Infinity Cache) gets the step kernel whose stores carry the nontemporal
 // hint; plain stores measured 2-10% slower there.  At or below it, plain
-// stores measured 2-4% faster (each step there reads blocks the previous
-// step wrote).
+// stores measured 2-4% faster.  That gain is not reads served by the cache:
+// a 256 MiB-per-step kernel timed alone after a 512 MiB read pass, which
+// leaves the cache holding other data, runs as fast as back to back.
 constexpr uint64_t kCacheBytes = uint64_t(256) << 20;
 
 // A step of the single-workgroup plan kernel (device table).

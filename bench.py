@@ -265,15 +265,43 @@ def suite(a):
             torch.cuda.empty_cache()
 
     if "cold_steps" in workloads:
-        # the benchmark AllReduce's 14 step kernels, each timed alone: warm
-        # (right after the previous run of the same step, so part of its
-        # reads may come from the 256 MiB memory-side cache), and cold (after
-        # a 512 MiB read pass that fills that cache and the L2s with other,
-        # clean data, so the step's reads come from HBM and no write-back of
-        # other data gets in the way); HIP events around the step alone
+        # Whether the benchmark AllReduce's step kernels gain from the 256 MiB
+        # memory-side cache.  First a check that a 512 MiB read pass empties
+        # that cache of a buffer: torch's sum over 256 MiB, back to back (the
+        # cache holds it), after the read pass, and right after a fill of the
+        # buffer (the cache holds what was just written).  Then each of the
+        # 14 step kernels alone: back to back (after a run of the same step)
+        # and after the read pass.  Timed with HIP events; the read pass is
+        # still running while the host queues the events and the timed call,
+        # so the host's launch time stays outside.  The kernel trace of this
+        # workload gives the kernel-only durations.
         P, L = 8, 64 << 20
-        bufs = upload("ring_p8_fp32_grad", P, L)
         scrub_r = torch.ones((512 << 20) // 4, dtype=torch.float32, device="cuda")
+
+        def after_scrub(fn, reps, prep=None):
+            out = []
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                scrub_r.sum()  # read pass, queued ahead of the timed call
+                if prep is not None:
+                    prep()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                b.synchronize()
+                out.append(a.elapsed_time(b) * 1e-3)
+            out.sort()
+            return out[len(out) // 2]
+
+        x = torch.ones((256 << 20) // 4, dtype=torch.float32, device="cuda")
+        probe = dict(bytes=x.numel() * 4,
+                     back_to_back_us=round(time_calls(lambda: x.sum(), 8, 1) * 1e6, 2),
+                     after_read_pass_us=round(after_scrub(lambda: x.sum(), 7) * 1e6, 2),
+                     after_fill_us=round(after_scrub(lambda: x.sum(), 7, prep=lambda: x.fill_(2.0)) * 1e6, 2))
+        del x
+        bufs = upload("ring_p8_fp32_grad", P, L)
         rows = []
         with hc.Comm(P, "ring") as c:
             c.set_exec_mode("steps")
@@ -281,22 +309,11 @@ def suite(a):
             for st in range(n):
                 si = c.step_info("allreduce", L, "fp32", st)
                 warm = time_calls(lambda: c.run_steps("allreduce", bufs, st, st + 1, "fp32", "sum"), 5, 1)
-                cold = []
-                for _ in range(7):
-                    float(scrub_r.sum())  # read pass, and the device is idle after it
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    c.run_steps("allreduce", bufs, st, st + 1, "fp32", "sum")
-                    b.record()
-                    b.synchronize()
-                    cold.append(a.elapsed_time(b) * 1e-3)
-                cold.sort()
-                tc = cold[len(cold) // 2]
+                tc = after_scrub(lambda: c.run_steps("allreduce", bufs, st, st + 1, "fp32", "sum"), 7)
                 rows.append(dict(step=st, hbm_bytes=si["hbm_bytes"], warm_us=round(warm * 1e6, 2),
                                  cold_us=round(tc * 1e6, 2), warm_frac=round(si["hbm_bytes"] / warm / HBM_PEAK, 4),
                                  cold_frac=round(si["hbm_bytes"] / tc / HBM_PEAK, 4)))
-        emit(workload="ring_p8_fp32_cold_steps", P=P, elems_per_rank=L, steps=rows,
+        emit(workload="ring_p8_fp32_cold_steps", P=P, elems_per_rank=L, cache_probe_sum_256MiB=probe, steps=rows,
              warm_us=round(sum(r["warm_us"] for r in rows), 1), cold_us=round(sum(r["cold_us"] for r in rows), 1))
         del bufs, scrub_r
         torch.cuda.empty_cache()
@@ -569,11 +586,16 @@ def main():
 
     # cold pass: the first reduce step alone, 5 times, each after a 512 MiB
     # read pass that fills the memory-side cache and the L2s with other,
-    # clean data, so its reads come from HBM (HIP events around the step only)
+    # clean data, so its reads come from HBM (HIP events around the step
+    # only).  The read pass is left running while the host queues the events
+    # and the step, so the first event marks its end and the step starts
+    # after the usual gap between two queued kernels, not after the host's
+    # launch time.
     scrub = torch.ones((512 << 20) // 4, dtype=torch.float32, device=bufs[0].device)
     cold_ms = []
     for _ in range(5):
-        float(scrub.sum())
+        torch.cuda.synchronize()
+        scrub.sum()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record(stream)
         comm.run_steps("allreduce", bufs, rs_steps[0], rs_steps[0] + 1, dtype, "sum")
@@ -624,15 +646,16 @@ def main():
                      "hbm_only": {"launch_us": round(cold_rs_ms * 1e3, 2),
                                   "achieved": round(rs_bytes / (cold_rs_ms / 1e3) / 1e9, 1),
                                   "frac": round(rs_bytes / (cold_rs_ms / 1e3) / HBM_PEAK, 4),
-                                  "how": "the reduce step alone after a 512 MiB read pass has filled the "
-                                         "memory-side cache and the L2s with other data; median of 5"},
+                                  "how": "the reduce step alone, queued behind a 512 MiB read pass that fills the "
+                                         "memory-side cache and the L2s with other data; HIP events from the end "
+                                         "of that pass to the end of the step; median of 5"},
                      "traffic_note": ("counted at the L2-to-fabric interface (FETCH_SIZE x 1.9998 + WRITE_SIZE, "
                                       "calibrated on a 256 MiB device copy); a read served by the 256 MiB "
-                                      "memory-side cache counts like one from HBM, and each step writes 256 MiB "
-                                      "with plain stores, so part of the next step's reads of those blocks "
-                                      "come from that cache rather than from HBM; with that cache holding "
-                                      "other data before each step, the reduce step measured 0.80-0.81 of "
-                                      "peak (bench.py --suite --workloads cold_steps)")},
+                                      "memory-side cache would count like one from HBM, but timed alone after "
+                                      "a 512 MiB read pass that leaves that cache holding other data, the "
+                                      "step kernels run as fast as in the AllReduce (kernel trace: reduce "
+                                      "steps 0.877-0.886 of peak, all-gather steps 0.887-0.890; bench.py "
+                                      "--suite --workloads cold_steps), so their reads come from HBM")},
     }
     if ag_ms:
         ag_bytes = comm.step_info("allreduce", L, dtype, ag_steps[0])["hbm_bytes"]
