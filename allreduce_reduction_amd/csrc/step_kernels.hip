@@ -21,7 +21,8 @@
 // global_store_dwordx4, with that hint only in steps that write more than the
 // memory-side cache holds): one wave per workgroup and one vector per lane per
 // operand, i.e. 1 KiB tiles of every operand per workgroup, which measured
-// fastest for streams far larger than the caches; the few head / tail
+// fastest for streams far larger than the caches (copy steps of at most
+// 32 MiB take four vectors per lane, see arg_kernel); the few head / tail
 // elements are done one by one.  Buffers with different phases take an
 // element-wise kernel.
 //
@@ -42,8 +43,9 @@ namespace {
 using namespace dev;
 
 constexpr int kThreads = 64;        // vector kernel: one wave per workgroup
-constexpr int kVecPerThread = 1;    // 16-byte vectors per lane per operand
-constexpr uint64_t kTileVecs = uint64_t(kThreads) * kVecPerThread;
+constexpr uint64_t kTileVecs = kThreads;  // one 16-byte vector per lane per operand
+constexpr int kWideVecs = 4;  // vectors per lane of the small copy steps (arg_kernel)
+constexpr uint64_t kWideMinItemBytes = uint64_t(1) << 20;  // ... whose items reach this size
 constexpr int kElemThreads = 256;   // element-wise kernel
 // Items per grid row when a step's items do not fit grid.y alone (below the
 // device's reported grid.y and grid.z limits of 65536).
@@ -97,7 +99,8 @@ __device__ __forceinline__ void xcd_tile(uint32_t* item, uint32_t* tile) {
 // issued before any combine); 0 takes ns / nd.
 // NT: stores with the nontemporal hint (a compile-time choice: the compiler
 // merges the two stores of a run-time branch into one plain store).  PL: the
-// loads without the nontemporal hint.
+// loads without the nontemporal hint.  VPL: 16-byte vectors per lane per
+// operand, the tile being kThreads * VPL vectors.
 // A 16-byte load: with the nontemporal hint, or plain (PL).
 template <bool PL>
 __device__ __forceinline__ u32x4 ld(const u32x4* p) {
@@ -105,7 +108,7 @@ __device__ __forceinline__ u32x4 ld(const u32x4* p) {
   else return load_vec(p);
 }
 
-template <int DT, int OP, int MODE, int NS, int ND, bool NT, bool PL, typename B>
+template <int DT, int OP, int MODE, int NS, int ND, bool NT, bool PL, int VPL, typename B>
 __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t count, uint32_t phase,
                                          uint32_t tile, int ns, int nd) {
   constexpr uint32_t E = Width<DT>::bytes;
@@ -125,13 +128,14 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
   const uint64_t nvec = (count - head) * E / 16;
   const uint64_t body_end = head + nvec * (16 / E);
 
-  const uint64_t v0 = uint64_t(tile) * kTileVecs + threadIdx.x;
-  if (uint64_t(tile) * kTileVecs < nvec) {
+  constexpr uint64_t TV = kTileVecs * VPL;
+  const uint64_t v0 = uint64_t(tile) * TV + threadIdx.x;
+  if (uint64_t(tile) * TV < nvec) {
     const uint64_t base = (begin + head) * E;
-    u32x4 acc[kVecPerThread];
+    u32x4 acc[VPL];
     if constexpr (NS > 0) {
       // all loads of the tile first, then the combines in schedule order
-      u32x4 x[NS][kVecPerThread];
+      u32x4 x[NS][VPL];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const unsigned char* src;
@@ -139,13 +143,13 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
         else src = bufs(s);
         const u32x4* p = reinterpret_cast<const u32x4*>(src + base);
 #pragma unroll
-        for (int u = 0; u < kVecPerThread; ++u) {
+        for (int u = 0; u < VPL; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
           if (v < nvec) x[s][u] = ld<PL>(p + v);
         }
       }
 #pragma unroll
-      for (int u = 0; u < kVecPerThread; ++u) {
+      for (int u = 0; u < VPL; ++u) {
         if constexpr (MODE == kCopy || NS == 1) {
           acc[u] = x[0][u];
         } else if constexpr (MODE == kFold) {
@@ -164,7 +168,7 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
       {
         const u32x4* p = reinterpret_cast<const u32x4*>(bufs(first) + base);
 #pragma unroll
-        for (int u = 0; u < kVecPerThread; ++u) {
+        for (int u = 0; u < VPL; ++u) {
           const uint64_t v = v0 + uint64_t(u) * kThreads;
           if (v < nvec) acc[u] = ld<PL>(p + v);
         }
@@ -173,7 +177,7 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
         for (int s = first + 1; s < ns; ++s) {
           const u32x4* p = reinterpret_cast<const u32x4*>(bufs(s) + base);
 #pragma unroll
-          for (int u = 0; u < kVecPerThread; ++u) {
+          for (int u = 0; u < VPL; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
             if (v < nvec) acc[u] = op_vec<DT, OP>(acc[u], ld<PL>(p + v));
           }
@@ -181,7 +185,7 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
         if constexpr (MODE == kRecvFold) {
           const u32x4* p = reinterpret_cast<const u32x4*>(bufs(0) + base);
 #pragma unroll
-          for (int u = 0; u < kVecPerThread; ++u) {
+          for (int u = 0; u < VPL; ++u) {
             const uint64_t v = v0 + uint64_t(u) * kThreads;
             if (v < nvec) acc[u] = op_vec<DT, OP>(ld<PL>(p + v), acc[u]);
           }
@@ -195,7 +199,7 @@ __device__ __forceinline__ void vec_item(const B& bufs, uint64_t begin, uint64_t
       else dst = bufs(ns + d);
       u32x4* q = reinterpret_cast<u32x4*>(dst + base);
 #pragma unroll
-      for (int u = 0; u < kVecPerThread; ++u) {
+      for (int u = 0; u < VPL; ++u) {
         const uint64_t v = v0 + uint64_t(u) * kThreads;
         if (v < nvec) {
           if constexpr (NT) store_vec_nt(q + v, acc[u]);
@@ -227,20 +231,20 @@ step_vec(const DevItem* __restrict__ items, uint32_t phase, uint32_t flags, Rank
   const DevItem* it = items + item;
   const int ns = NS > 0 ? NS : static_cast<int>(it->nsrc);
   const int nd = ND > 0 ? ND : static_cast<int>(it->ndst);
-  vec_item<DT, OP, MODE, NS, ND, NT, false>(ItemBufs{ptrs, it}, it->begin, it->count, phase, tile, ns, nd);
+  vec_item<DT, OP, MODE, NS, ND, NT, false, 1>(ItemBufs{ptrs, it}, it->begin, it->count, phase, tile, ns, nd);
 }
 
 // Vector kernel, items resolved into the kernel arguments (compile-time
 // shapes, plain stores): the operand addresses already point at the item's
-// first element, whose 16-byte phase they carry.
-template <int DT, int OP, int MODE, int NS, int ND, bool PL>
+// first element, whose 16-byte phase they carry.  VPL vectors per lane.
+template <int DT, int OP, int MODE, int NS, int ND, bool PL, int VPL>
 __global__ void __launch_bounds__(kThreads)
 step_arg(uint32_t flags, ArgItems<NS + ND> args) {
   uint32_t item = blockIdx.y, tile = blockIdx.x;
   if (flags & kFlagXcdSplit) xcd_tile(&item, &tile);
   const ArgItem<NS + ND>* a = &args.it[item];
   const uint32_t phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(a->buf[0]) & 15u);
-  vec_item<DT, OP, MODE, NS, ND, false, PL>(ArgBufs<NS + ND>{a}, 0, a->count, phase, tile, NS, ND);
+  vec_item<DT, OP, MODE, NS, ND, false, PL, VPL>(ArgBufs<NS + ND>{a}, 0, a->count, phase, tile, NS, ND);
 }
 
 // Element-wise kernel for buffers whose 16-byte phases differ.
@@ -298,7 +302,7 @@ const void* vector_kernel(const StepLaunch& s) {
 // operands resolved, into k->args and return the kernel (plain loads for
 // `plain`).
 template <int DT, int OP, int MODE, int NS, int ND>
-const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k, bool plain) {
+const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k, bool plain, bool wide) {
   constexpr int NB = NS + ND;
   constexpr uint32_t E = Width<DT>::bytes;
   static_assert(NB <= kArgMaxBufs && sizeof(ArgItems<NB>) <= kArgBytes, "argument items");
@@ -308,7 +312,10 @@ const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k, 
     for (int b = 0; b < NB; ++b) a->it[i].buf[b] = ptrs.p[it.rank[b]] + it.begin * E;
     a->it[i].count = it.count;
   }
-  return plain ? fn(step_arg<DT, OP, MODE, NS, ND, true>) : fn(step_arg<DT, OP, MODE, NS, ND, false>);
+  if constexpr (MODE == kCopy) {
+    if (wide) return fn(step_arg<DT, OP, MODE, NS, ND, true, kWideVecs>);
+  }
+  return plain ? fn(step_arg<DT, OP, MODE, NS, ND, true, 1>) : fn(step_arg<DT, OP, MODE, NS, ND, false, 1>);
 }
 
 // The kernel-argument form for a step of at most kArgItems items of a
@@ -322,28 +329,44 @@ const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k, 
 // rank no change (ring 790.0 / 790.1, RHD 754.4 / 753.9).  A limit of 64 MiB
 // made the 16-rank ring at 64 MiB 1% slower; plain loads in the reduce steps
 // as well gained at 8 ranks and lost at 16.
+// Such a copy of items of at least 1 MiB also moves kWideVecs vectors per
+// lane (4 KiB tiles): its one-wave workgroups of 1 KiB are so short that the
+// rate at which the hardware starts workgroups (about 3.3 per ns) bounds it.
+// Measured on MI355X, one launch per step, fp16 max, same session, three
+// runs each, us per AllReduce (1 KiB tiles / 4 KiB tiles): 16-rank ring at
+// 16 MiB per rank 235.7-235.8 / 224.0-226.3, 8-rank fp32 ring at 16 MiB
+// 101.9-102.4 / 100.8-100.9; RHD lost a little (16 ranks at 16 MiB
+// 199.7-200.2 / 201.1-201.8, at 4 MiB 58.0-58.3 / 59.7-59.8), 2 KiB tiles
+// lost more, and copies of smaller items lost 0.8-1.4 us per step, hence
+// the item bound.  The 2-read reduce gained nothing from wider tiles, and
+// at 8 items of 32 MiB 1 KiB tiles stay fastest.  `*tile_vecs` receives the
+// kernel's vectors per tile.
 template <int DT, int OP>
-const void* arg_kernel(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
+const void* arg_kernel(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k, uint64_t* tile_vecs) {
+  *tile_vecs = kTileVecs;
   if (!s.host_items || s.nitems > kArgItems || s.write_bytes > kCacheBytes || s.ndst != 1) return nullptr;
   const bool pl = s.mode == kCopy && s.write_bytes <= kPlainLoadCopyBytes;  // a copy reads what it writes
+  const bool wide = pl && s.max_count * Width<DT>::bytes >= kWideMinItemBytes;
   if (s.mode == kRecvFold) {
     switch (s.nsrc) {
-      case 2: return arg_items<DT, OP, kRecvFold, 2, 1>(s, ptrs, k, pl);
-      case 3: return arg_items<DT, OP, kRecvFold, 3, 1>(s, ptrs, k, pl);
-      case 5: return arg_items<DT, OP, kRecvFold, 5, 1>(s, ptrs, k, pl);
-      case 9: return arg_items<DT, OP, kRecvFold, 9, 1>(s, ptrs, k, pl);
+      case 2: return arg_items<DT, OP, kRecvFold, 2, 1>(s, ptrs, k, pl, false);
+      case 3: return arg_items<DT, OP, kRecvFold, 3, 1>(s, ptrs, k, pl, false);
+      case 5: return arg_items<DT, OP, kRecvFold, 5, 1>(s, ptrs, k, pl, false);
+      case 9: return arg_items<DT, OP, kRecvFold, 9, 1>(s, ptrs, k, pl, false);
       default: return nullptr;
     }
   }
   if (s.mode == kFold) {
     switch (s.nsrc) {
-      case 2: return arg_items<DT, OP, kFold, 2, 1>(s, ptrs, k, pl);
-      case 4: return arg_items<DT, OP, kFold, 4, 1>(s, ptrs, k, pl);
-      case 8: return arg_items<DT, OP, kFold, 8, 1>(s, ptrs, k, pl);
+      case 2: return arg_items<DT, OP, kFold, 2, 1>(s, ptrs, k, pl, false);
+      case 4: return arg_items<DT, OP, kFold, 4, 1>(s, ptrs, k, pl, false);
+      case 8: return arg_items<DT, OP, kFold, 8, 1>(s, ptrs, k, pl, false);
       default: return nullptr;
     }
   }
-  return s.nsrc == 1 ? arg_items<DT, kSum, kCopy, 1, 1>(s, ptrs, k, pl) : nullptr;
+  if (s.nsrc != 1) return nullptr;
+  if (wide) *tile_vecs = kTileVecs * kWideVecs;  // the grid follows the kernel's tile
+  return arg_items<DT, kSum, kCopy, 1, 1>(s, ptrs, k, pl, wide);
 }
 
 // Grid of `gx` tiles by `nitems` items: items along y, and along z as well
@@ -377,14 +400,16 @@ void describe_typed(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k) {
   }
   // body vectors of the largest item (a head of fewer than 16 bytes only
   // shortens the body); tile 0 of each item also takes the head and tail
+  uint64_t tv = kTileVecs;
+  const void* af = arg_kernel<DT, OP>(s, ptrs, k, &tv);
   const uint64_t vecs = s.max_count * E / 16;
-  const uint64_t gx = vecs > kTileVecs ? (vecs + kTileVecs - 1) / kTileVecs : 1;
+  const uint64_t gx = vecs > tv ? (vecs + tv - 1) / tv : 1;
   k->grid = item_grid(static_cast<uint32_t>(gx), s.nitems);
   k->block = dim3(kThreads);
   k->flags = (s.xcd_split && k->grid.z == 1 && (gx * s.nitems) % 8 == 0) ? kFlagXcdSplit : 0u;
-  if (const void* f = arg_kernel<DT, OP>(s, ptrs, k)) {
+  if (af) {
     k->kind = KernelDesc::kVectorArgs;
-    k->func = f;
+    k->func = af;
     return;
   }
   k->kind = KernelDesc::kVector;

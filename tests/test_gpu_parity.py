@@ -220,6 +220,37 @@ def test_parity_items_past_grid_y():
     check_case("pipeline", "allreduce", "bf16", "sum", P, L, seed=11, loop_bytes=1024, exec_mode="steps")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_parity_wide_copy_tiles(dtype):
+    """Copy steps whose items reach 1 MiB and that write at most 32 MiB move
+    4 KiB tiles: ring and RHD AllReduce and all-gather with items just below,
+    at and above 1 MiB, ragged item ends, and all rank buffers at a shared
+    nonzero 16-byte phase (head and tail elements beside the wide body)."""
+    e = np.dtype(refops.STORAGE[dtype]).itemsize
+    for algo, P in (("ring", 4), ("rhd", 8)):
+        for L in ((P << 20) // e - 64, (P << 20) // e, (P << 20) // e + 7, (3 * P << 20) // e + 33):
+            for coll in ("allreduce", "all_gather"):
+                check_case(algo, coll, dtype, "max", P, L, seed=L % 97, exec_mode="steps")
+    P, L = 4, (4 << 20) // e + 5
+    offs = [max(1, 16 // e - 1)] * P if e < 16 else [0] * P
+    say(f"case wide copy tiles, shared phase {offs[0] * e} bytes, dtype={dtype} P={P} L={L}")
+    xs = make_inputs(dtype, "sum", P, L, seed=29)
+    views, backing = strided_buffers(xs, dtype, offs)
+    with hc.Comm(P, "ring") as comm:
+        comm.set_exec_mode("steps")
+        comm.allreduce(views, dtype, "sum")
+        torch.cuda.synchronize()
+    want = [x.copy() for x in xs]
+    oracle.run("allreduce", "ring", want, dtype, "sum")
+    for r in range(P):
+        refops.assert_same(dtype, to_host(views[r], dtype), want[r], f"rank {r}")
+    mask = torch.ones_like(backing, dtype=torch.bool)
+    for v in views:
+        off = (v.data_ptr() - backing.data_ptr()) // e
+        mask[off:off + L] = False
+    assert int((backing[mask] != 0).sum()) == 0
+
+
 @pytest.mark.parametrize("algo", ["ring", "rhd", "pipeline"])
 def test_parity_small_and_empty_segments(algo):
     for P in (3, 5, 8, 16):
