@@ -21,9 +21,9 @@
 // global_store_dwordx4, with that hint only in steps that write more than the
 // memory-side cache holds): one wave per workgroup and one vector per lane per
 // operand, i.e. 1 KiB tiles of every operand per workgroup, which measured
-// fastest for streams far larger than the caches (copy steps of at most
-// 32 MiB take four vectors per lane, see arg_kernel); the few head / tail
-// elements are done one by one.  Buffers with different phases take an
+// fastest for streams far larger than the caches (copy steps that write at
+// most 32 MiB and whose items reach 1 MiB take four vectors per lane, see
+// arg_kernel); the few head / tail elements are done one by one.  Buffers with different phases take an
 // element-wise kernel.
 //
 // Element ops: fp16 / bf16 lanes are widened to fp32, combined and rounded
@@ -300,7 +300,7 @@ const void* vector_kernel(const StepLaunch& s) {
 
 // Kernel-argument form of a compile-time shape: write the step's items,
 // operands resolved, into k->args and return the kernel (plain loads for
-// `plain`).
+// `plain`; for a copy, kWideVecs vectors per lane for `wide`).
 template <int DT, int OP, int MODE, int NS, int ND>
 const void* arg_items(const StepLaunch& s, const RankPtrs& ptrs, KernelDesc* k, bool plain, bool wide) {
   constexpr int NB = NS + ND;
