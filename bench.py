@@ -654,7 +654,7 @@ def main():
                                       "memory-side cache would count like one from HBM, but timed alone after "
                                       "a 512 MiB read pass that leaves that cache holding other data, the "
                                       "step kernels run as fast as in the AllReduce (kernel trace: reduce "
-                                      "steps 0.877-0.886 of peak, all-gather steps 0.887-0.890; bench.py "
+                                      "steps 0.875-0.886 of peak, all-gather steps 0.886-0.890; bench.py "
                                       "--suite --workloads cold_steps), so their reads come from HBM")},
     }
     if ag_ms:
