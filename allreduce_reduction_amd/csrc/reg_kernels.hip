@@ -114,16 +114,20 @@ __device__ __forceinline__ void position(uint32_t n, unsigned char* const* ptr, 
   if constexpr (FORM == kRegNodes) {
     // the tree level by level; after level l, every leaf whose rank holds
     // the level-l node above it stores that node
+    // (fixed trip counts throughout, so that once unrolled every index is a
+    // constant and x stays in registers)
     V x[kRegMaxLeaves];
 #pragma unroll
     for (uint32_t v = 0; v < kRegMaxLeaves; ++v)
       if (v < n) x[v] = load(ptr[v]);
-    uint32_t l = 1;
+    constexpr uint32_t kLevels = __builtin_ctz(kRegMaxLeaves);
+    static_assert((1u << kLevels) == kRegMaxLeaves, "leaves: a power of two");
 #pragma unroll
-    for (uint32_t w = 1; w < kRegMaxLeaves; w *= 2, ++l) {
+    for (uint32_t l = 1; l <= kLevels; ++l) {
+      const uint32_t w = 1u << (l - 1);
 #pragma unroll
-      for (uint32_t v = 0; v + w < kRegMaxLeaves; v += 2 * w)
-        if (v + w < n) x[v] = op(x[v], x[v + w]);
+      for (uint32_t v = 0; v < kRegMaxLeaves; ++v)
+        if ((v & (2 * w - 1)) == 0 && v + w < n) x[v] = op(x[v], x[v + w]);
 #pragma unroll
       for (uint32_t v = 0; v < kRegMaxLeaves; ++v)
         if (v < n && lvl[v] == l) store(ptr[v], x[v & ~(2 * w - 1)]);
@@ -192,17 +196,21 @@ plan_regs(Call c) {
         [&](unsigned char* p, u32x4 v) { store_vec(reinterpret_cast<u32x4*>(p + off), v); });
   }
   if (blockIdx.x == 0) {
-#pragma unroll
-    for (int part = 0; part < 2; ++part) {
-      const uint64_t e = uint64_t(R.el_lo[part]) + threadIdx.x;
-      if (e < R.el_hi[part]) {
+    // the region's head and tail elements; the body written out twice (not
+    // a loop over the two parts: int8's is too large to unroll, and an index
+    // into R would move all of R, operand addresses included, to scratch)
+    auto part = [&](uint32_t lo, uint32_t hi) __attribute__((always_inline)) {
+      const uint64_t e = uint64_t(lo) + threadIdx.x;
+      if (e < hi) {
         const uint64_t off = e * E;
         position<FORM, uint32_t>(
             n, R.ptr, R.lvl, [&](const unsigned char* p) { return load_elem<E>(p + off); },
             [](uint32_t a, uint32_t b) { return op_word<DT, OP>(a, b); },
             [&](unsigned char* p, uint32_t v) { store_elem<E>(p + off, v); });
       }
-    }
+    };
+    part(R.el_lo[0], R.el_hi[0]);
+    part(R.el_lo[1], R.el_hi[1]);
   }
 }
 
