@@ -124,7 +124,7 @@ def load_library():
         L.hbmc_comm_flow_timeouts.restype = ci
         L.hbmc_comm_flow_timeouts.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
         L.hbmc_plan_flow.restype = ci
-        L.hbmc_plan_flow.argtypes = [vp, ci, ci, sz, ci, ctypes.c_uint64, ctypes.POINTER(FlowTile), sz,
+        L.hbmc_plan_flow.argtypes = [vp, ci, ci, sz, ci, ci, ci, ctypes.c_uint64, ctypes.POINTER(FlowTile), sz,
                                      ctypes.POINTER(sz), ctypes.POINTER(FlowChunk), sz, ctypes.POINTER(sz)]
         L.hbmc_comm_set_exec_mode.restype = ci
         L.hbmc_comm_set_exec_mode.argtypes = [vp, ci]
@@ -385,17 +385,19 @@ class Comm:
         return [dict(begin=c.begin, count=c.count, item=c.item, step=c.step, deps=list(deps[c.dep_lo:c.dep_hi]))
                 for c in arr[:n.value]]
 
-    def plan_flow(self, coll: str, count: int, dtype: str, tile_bytes: int, root: int = 0):
-        """Flow-kernel tables (host only): tiles in ticket order (dicts: col, seq,
-        step, chunks) and chunks (dicts: begin, count, item)."""
+    def plan_flow(self, coll: str, count: int, dtype: str, tile_bytes: int, root: int = 0, first: int = 0,
+                  last: int = -1):
+        """Flow-kernel tables of steps [first, last) (host only): tiles in ticket
+        order (dicts: col, seq, step, chunks) and chunks (dicts: begin, count,
+        item)."""
         L = load_library()
         nt, nc = ctypes.c_size_t(), ctypes.c_size_t()
-        _check(L.hbmc_plan_flow(self._h, COLL[coll], root, count, DTYPE[dtype], tile_bytes, None, 0,
+        _check(L.hbmc_plan_flow(self._h, COLL[coll], root, count, DTYPE[dtype], first, last, tile_bytes, None, 0,
                                 ctypes.byref(nt), None, 0, ctypes.byref(nc)), "hbmc_plan_flow")
         tiles = (FlowTile * max(nt.value, 1))()
         chunks = (FlowChunk * max(nc.value, 1))()
-        _check(L.hbmc_plan_flow(self._h, COLL[coll], root, count, DTYPE[dtype], tile_bytes, tiles, nt.value,
-                                ctypes.byref(nt), chunks, nc.value, ctypes.byref(nc)), "hbmc_plan_flow")
+        _check(L.hbmc_plan_flow(self._h, COLL[coll], root, count, DTYPE[dtype], first, last, tile_bytes, tiles,
+                                nt.value, ctypes.byref(nt), chunks, nc.value, ctypes.byref(nc)), "hbmc_plan_flow")
         return ([dict(col=t.col, seq=t.seq, step=t.step, chunks=range(t.c_lo, t.c_hi)) for t in tiles[:nt.value]],
                 [dict(begin=c.begin, count=c.count, item=c.item) for c in chunks[:nc.value]])
 

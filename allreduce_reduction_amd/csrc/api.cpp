@@ -237,7 +237,8 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm) {
     if (kv.second->dev && hipFree(kv.second->dev) != hipSuccess) st = HBMC_ERR_HIP;
     if (kv.second->cols_mem && hipFree(kv.second->cols_mem) != hipSuccess) st = HBMC_ERR_HIP;
     if (kv.second->lds_mem && hipFree(kv.second->lds_mem) != hipSuccess) st = HBMC_ERR_HIP;
-    if (kv.second->flow_mem && hipFree(kv.second->flow_mem) != hipSuccess) st = HBMC_ERR_HIP;
+    for (auto& f : kv.second->flow)
+      if (f.second.mem && hipFree(f.second.mem) != hipSuccess) st = HBMC_ERR_HIP;
     for (void* m : kv.second->retired)
       if (hipFree(m) != hipSuccess) st = HBMC_ERR_HIP;
   }
@@ -366,16 +367,21 @@ hbmc_status_t hbmc_plan_chunks(hbmc_comm_t comm, hbmc_coll_t coll, int root, siz
 }
 
 hbmc_status_t hbmc_plan_flow(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
-                             uint64_t tile_bytes, hbmc_flow_tile_t* tiles, size_t cap, size_t* n_tiles,
-                             hbmc_flow_chunk_t* chunks, size_t ccap, size_t* n_chunks) {
+                             int first_step, int last_step, uint64_t tile_bytes, hbmc_flow_tile_t* tiles,
+                             size_t cap, size_t* n_tiles, hbmc_flow_chunk_t* chunks, size_t ccap,
+                             size_t* n_chunks) {
   return no_throw([&]() -> hbmc_status_t {
     if (tile_bytes < 16 || tile_bytes > (uint64_t(1) << 31)) return HBMC_ERR_INVALID_ARG;
     Plan* p = nullptr;
     hbmc_status_t st = get_plan(comm, coll, root, count, dtype, &p);
     if (st != HBMC_OK) return st;
+    const int nsteps = static_cast<int>(p->sched.steps.size());
+    const int last = last_step < 0 ? nsteps : last_step;
+    if (first_step < 0 || first_step > last || last > nsteps) return HBMC_ERR_INVALID_ARG;
     const uint32_t e = elem_bytes(dtype);
     FlowTable f;
-    if (!build_flow(p->sched, count, e, tile_bytes / 16 * 16 / e, &f)) return HBMC_ERR_UNSUPPORTED;
+    if (!build_flow(p->sched, first_step, last, count, e, tile_bytes / 16 * 16 / e, &f))
+      return HBMC_ERR_UNSUPPORTED;
     for (size_t i = 0; tiles && i < f.tiles.size() && i < cap; ++i) {
       const FlowTile& t = f.tiles[i];
       tiles[i] = hbmc_flow_tile_t{t.col, t.seq, f.tile_step[i], t.c_lo, t.c_hi, 0};

@@ -235,18 +235,20 @@ hbmc_status_t upload_columns(Plan* p) {
   return HBMC_OK;
 }
 
-hbmc_status_t flow_host(hbmc_comm* c, Plan* p, uint64_t count, uint32_t e) {
+hbmc_status_t flow_host(hbmc_comm* c, Plan* p, int first, int last, uint64_t count, uint32_t e, FlowSet** out) {
   const uint64_t col = std::max<uint64_t>(16, c->flow_tile_bytes / 16 * 16) / e;
-  if (p->flow_built && p->flow.col_elems == col) return HBMC_OK;
-  if (p->flow_mem) {
+  FlowSet& f = p->flow[std::make_pair(first, last)];
+  *out = &f;
+  if (f.built && f.table.col_elems == col) return HBMC_OK;
+  if (f.mem) {
     // launches already enqueued and graphs built earlier may still read it
-    p->retired.push_back(p->flow_mem);
-    p->flow_old.push_back(p->flow_mem);
-    p->flow_mem = nullptr;
+    p->retired.push_back(f.mem);
+    p->flow_old.push_back(f.mem);
+    f.mem = nullptr;
   }
-  p->flow_ok = build_flow(p->sched, count, e, col, &p->flow);
-  p->flow.col_elems = col;
-  p->flow_built = true;
+  f.ok = build_flow(p->sched, first, last, count, e, col, &f.table);
+  f.table.col_elems = col;
+  f.built = true;
   return HBMC_OK;
 }
 
@@ -255,9 +257,9 @@ hbmc_status_t flow_host(hbmc_comm* c, Plan* p, uint64_t count, uint32_t e) {
 constexpr size_t kFlowTimeoutsAt = 128;
 constexpr size_t kFlowHeadBytes = 256;
 
-hbmc_status_t upload_flow(Plan* p) {
-  if (p->flow_mem) return HBMC_OK;
-  const FlowTable& f = p->flow;
+hbmc_status_t upload_flow(Plan*, FlowSet* fs) {
+  if (fs->mem) return HBMC_OK;
+  const FlowTable& f = fs->table;
   auto up = [](size_t b) { return (b + 255) & ~size_t(255); };
   const size_t b_ctrl = kFlowHeadBytes;
   const size_t b_prog = up(size_t(f.ncols) * sizeof(uint32_t) + 4);
@@ -275,12 +277,12 @@ hbmc_status_t upload_flow(Plan* p) {
     (void)hipFree(mem);
     return HBMC_ERR_HIP;
   }
-  p->flow_mem = mem;
-  p->dev_fctrl = reinterpret_cast<FlowCtrl*>(base);
-  p->dev_ftimeouts = reinterpret_cast<uint32_t*>(base + kFlowTimeoutsAt);
-  p->dev_fprog = reinterpret_cast<uint32_t*>(base + b_ctrl);
-  p->dev_ftiles = reinterpret_cast<FlowTile*>(base + b_ctrl + b_prog);
-  p->dev_fchunks = reinterpret_cast<FlowChunk*>(base + b_ctrl + b_prog + b_tiles);
+  fs->mem = mem;
+  fs->ctrl = reinterpret_cast<FlowCtrl*>(base);
+  fs->timeouts = reinterpret_cast<uint32_t*>(base + kFlowTimeoutsAt);
+  fs->prog = reinterpret_cast<uint32_t*>(base + b_ctrl);
+  fs->tiles = reinterpret_cast<FlowTile*>(base + b_ctrl + b_prog);
+  fs->chunks = reinterpret_cast<FlowChunk*>(base + b_ctrl + b_prog + b_tiles);
   return HBMC_OK;
 }
 
@@ -290,7 +292,8 @@ hbmc_status_t flow_timeouts(hbmc_comm* c, uint32_t* count) {
   for (auto& kv : c->plans) {
     Plan* p = kv.second.get();
     std::vector<void*> blocks = p->flow_old;
-    if (p->flow_mem) blocks.push_back(p->flow_mem);
+    for (auto& f : p->flow)
+      if (f.second.mem) blocks.push_back(f.second.mem);
     for (void* m : blocks) {
       // the counter lives on the plan's device; unified addressing lets the
       // copies find it from the pointer
@@ -793,16 +796,17 @@ hbmc_status_t choose_exec(hbmc_comm* c, Plan* p, int first, int last, uint64_t c
   }
   *mode = kExecSteps;
   if (c->exec_mode == kExecFlow) {
-    // a whole call of two or more busy steps, every item within the records
-    if (aligned && busy > 1 && whole) {
-      hbmc_status_t st = flow_host(c, p, count, e);
+    // a step range of two or more busy steps, every item within the records
+    if (aligned && busy > 1) {
+      FlowSet* f = nullptr;
+      hbmc_status_t st = flow_host(c, p, first, last, count, e, &f);
       if (st != HBMC_OK) return st;
       // the ticket counter runs to the tiles plus one batch per workgroup
       // past them (and one more taken ahead): it must not wrap
-      const uint64_t tickets = uint64_t(p->flow.tiles.size()) + uint64_t(compute_units()) *
-                                                                   std::max<uint32_t>(1, c->flow_wgs_per_cu) *
-                                                                   std::max<uint32_t>(1, c->flow_batch) * 2;
-      if (p->flow_ok && tickets < UINT32_MAX) *mode = kExecFlow;
+      const uint64_t tickets = uint64_t(f->table.tiles.size()) + uint64_t(compute_units()) *
+                                                                    std::max<uint32_t>(1, c->flow_wgs_per_cu) *
+                                                                    std::max<uint32_t>(1, c->flow_batch) * 2;
+      if (f->ok && tickets < UINT32_MAX) *mode = kExecFlow;
     }
     return HBMC_OK;
   }
@@ -1002,16 +1006,17 @@ hbmc_status_t prepare(hbmc_comm* c, int coll, int root, void* const bufs[], size
     return HBMC_OK;
   }
   if (mode == kExecFlow) {
-    // the whole call as one flow-kernel launch
-    st = upload_flow(p);
+    // the step range as one flow-kernel launch
+    FlowSet* fs = &p->flow.at(std::make_pair(first, last));  // made by choose_exec
+    st = upload_flow(p, fs);
     if (st != HBMC_OK) return st;
-    const FlowTable& f = p->flow;
+    const FlowTable& f = fs->table;
     const uint32_t grid = std::max<uint32_t>(1, compute_units() * std::max<uint32_t>(1, c->flow_wgs_per_cu));
     const uint64_t ticks = uint64_t(c->flow_wait_us) * wall_clock_khz() / 1000;
     const uint32_t flags = c->flow_flags | (f.max_step_write > kCacheBytes ? kFlowNtStores : 0u);
     KernelDesc k;
-    describe_flow(dtype, op, ptrs, p->dev_ftiles, p->dev_fchunks, static_cast<uint32_t>(f.tiles.size()),
-                  p->dev_fctrl, p->dev_fprog, f.ncols, p->dev_ftimeouts, phase, flags, ticks,
+    describe_flow(dtype, op, ptrs, fs->tiles, fs->chunks, static_cast<uint32_t>(f.tiles.size()),
+                  fs->ctrl, fs->prog, f.ncols, fs->timeouts, phase, flags, ticks,
                   std::max<uint32_t>(1, c->flow_batch), grid, &k);
     launches->push_back(k);
     return HBMC_OK;

@@ -60,6 +60,22 @@ struct LdsHost {
   bool stores_fit = false;  // launches of all steps use the store records
 };
 
+// The flow kernel's state for one step range of a plan: its host table for
+// the communicator's tile length, and one device allocation (on the plan's
+// device) holding the control block, the count of waits that gave up, the
+// column counters, the tiles and the chunks (built on first launch).
+struct FlowSet {
+  FlowTable table;
+  bool built = false;
+  bool ok = false;  // the steps fit the flow records
+  void* mem = nullptr;
+  FlowCtrl* ctrl = nullptr;
+  uint32_t* timeouts = nullptr;
+  uint32_t* prog = nullptr;
+  FlowTile* tiles = nullptr;
+  FlowChunk* chunks = nullptr;
+};
+
 // A cached schedule and its device item table (uploaded on first use).
 struct Plan {
   Schedule sched;
@@ -109,21 +125,10 @@ struct Plan {
   // every call
   std::vector<DevItem> host_table;
   bool host_table_built = false;
-  // the flow kernel: its host table for the communicator's tile length, and
-  // one device allocation (on the plan's device) holding the control block,
-  // the count of waits that gave up, the column counters, the tiles and the
-  // chunks (built on first launch); the allocations of earlier tile lengths,
-  // whose counts are still read
-  FlowTable flow;
-  bool flow_built = false;
-  bool flow_ok = false;  // the schedule fits the flow records
-  void* flow_mem = nullptr;
+  // the flow kernel, per step range [first, last) launched in that form; and
+  // the allocations of earlier tile lengths, whose counts are still read
+  std::map<std::pair<int, int>, FlowSet> flow;
   std::vector<void*> flow_old;
-  FlowCtrl* dev_fctrl = nullptr;
-  uint32_t* dev_ftimeouts = nullptr;
-  uint32_t* dev_fprog = nullptr;
-  FlowTile* dev_ftiles = nullptr;
-  FlowChunk* dev_fchunks = nullptr;
   // device tables of earlier column lengths: graphs built or captured before
   // the length changed still point at them, so they are kept until the
   // communicator is destroyed
@@ -213,12 +218,13 @@ hbmc_status_t lds_layout(hbmc_comm* c, Plan* p, int P, uint64_t count, uint32_t 
 hbmc_status_t upload_lds_tables(Plan* p, int P, uint64_t count, uint32_t e);
 // The same tables built on the host only (p->lh), once per column length.
 hbmc_status_t lds_host_tables(Plan* p, int P, uint64_t count, uint32_t e);
-// The flow kernel's host table of plan p for the communicator's tile length
-// (count elements of e bytes), built once per length; sets p->flow_ok.
-hbmc_status_t flow_host(hbmc_comm* c, Plan* p, uint64_t count, uint32_t e);
-// Upload it to the plan's device with zeroed counters (again after the
-// tile length changed; the old tables are retired, not freed).
-hbmc_status_t upload_flow(Plan* p);
+// The flow kernel's host table of steps [first, last) of plan p for the
+// communicator's tile length (count elements of e bytes), built once per
+// range and length; *out receives the range's state (ok: the steps fit).
+hbmc_status_t flow_host(hbmc_comm* c, Plan* p, int first, int last, uint64_t count, uint32_t e, FlowSet** out);
+// Upload a range's table to the plan's device with zeroed counters (again
+// after the tile length changed; the old tables are retired, not freed).
+hbmc_status_t upload_flow(Plan* p, FlowSet* f);
 // The number of flow waits that gave up in all of the communicator's plans,
 // then cleared (synchronous; 0 when no flow launch ran).
 hbmc_status_t flow_timeouts(hbmc_comm* c, uint32_t* count);

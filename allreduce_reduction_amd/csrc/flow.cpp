@@ -6,9 +6,11 @@
 
 namespace hbmc {
 
-bool build_flow(const Schedule& sched, uint64_t count, uint32_t esize, uint64_t col_elems, FlowTable* out) {
+bool build_flow(const Schedule& sched, int first, int last, uint64_t count, uint32_t esize, uint64_t col_elems,
+                FlowTable* out) {
   *out = FlowTable();
   if (col_elems == 0 || col_elems > UINT32_MAX) return false;
+  if (first < 0 || last > static_cast<int>(sched.steps.size()) || first > last) return false;
   const uint64_t ncols = (count + col_elems - 1) / col_elems;
   if (ncols > UINT32_MAX) return false;
   out->col_elems = col_elems;
@@ -20,7 +22,8 @@ bool build_flow(const Schedule& sched, uint64_t count, uint32_t esize, uint64_t 
   };
   std::vector<Cut> cuts;
   uint32_t item_base = 0;
-  for (size_t s = 0; s < sched.steps.size(); ++s) {
+  for (int s = 0; s < first; ++s) item_base += static_cast<uint32_t>(sched.steps[s].items.size());
+  for (int s = first; s < last; ++s) {
     const Step& st = sched.steps[s];
     cuts.clear();
     uint64_t write = 0;

@@ -24,9 +24,11 @@ struct FlowTable {
   uint64_t max_step_write = 0;       // most bytes one step writes (chooses the store hint)
 };
 
-// Build the table of `sched` over `count` elements of `esize` bytes; false
-// when an item has more than kFlowOperands operands or a count does not fit
-// the records.
-bool build_flow(const Schedule& sched, uint64_t count, uint32_t esize, uint64_t col_elems, FlowTable* out);
+// Build the table of steps [first, last) of `sched` over `count` elements of
+// `esize` bytes (seq then counts from 0 within the range; items keep their
+// numbers over all steps); false when an item has more than kFlowOperands
+// operands or a count does not fit the records.
+bool build_flow(const Schedule& sched, int first, int last, uint64_t count, uint32_t esize, uint64_t col_elems,
+                FlowTable* out);
 
 }  // namespace hbmc

@@ -180,7 +180,8 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    operand once, evaluates the expression and stores every rank the
  *    schedule writes there ([RHD] "耗时计算": every step pays alpha, which
  *    this form pays once);
- *  - HBMC_EXEC_FLOW: a whole call in one launch of a persistent kernel
+ *  - HBMC_EXEC_FLOW: a call, or a hbmc_run_steps range, in one launch of a
+ *    persistent kernel
  *    that runs every step's work as the step kernels do (each step reads
  *    and writes its own bytes in the rank buffers) but lets consecutive steps
  *    overlap: items are cut into tiles at multiples of the tile length
@@ -189,8 +190,9 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  *    elements are done ([RING-RHD] "Ring AllReduce带宽最优的环形流水线": no
  *    rank waits for a whole step).  Only when set explicitly (AUTO does not
  *    pick it).  Launches of one communicator's call of the same collective,
- *    count and dtype share the plan's counters: they must not overlap in
- *    time (one stream, or ordered; graphs order such nodes themselves);
+ *    count, dtype and step range share that range's counters: they must not
+ *    overlap in time (one stream, or ordered; graphs order such nodes
+ *    themselves);
  *  - HBMC_EXEC_AUTO (default, or the environment variable HBMC_EXEC = auto,
  *    steps, fused, columns, lds, regs or flow): per call the eligible form of least
  *    modelled time, with constants measured on MI355X: steps sum over the
@@ -216,8 +218,8 @@ hbmc_status_t hbmc_comm_destroy(hbmc_comm_t comm);
  * needs, and a column of every rank buffer plus 160 bytes per chunk of the
  * longest column within one workgroup's LDS; REGS needs what COLUMNS needs,
  * all of the call's steps, and the expression forms above; FLOW needs rank
- * buffers of one 16-byte phase, all of the call's steps, two or more busy
- * steps and at most 32 ranks per item.  The
+ * buffers of one 16-byte phase, two or more busy steps in the range and at
+ * most 32 ranks per item.  The
  * element ops commute bit for bit, so every form gives the same bits.  The
  * forms apply to
  * every call, hbmc_run_steps ranges and graph nodes.  Host only.
@@ -459,14 +461,17 @@ typedef struct {
   uint32_t count, item;
 } hbmc_flow_chunk_t;
 
-/* The flow kernel's tables for tiles of tile_bytes per rank buffer (rounded
- * as hbmc_comm_set_flow does), host only: tiles in the order the kernel hands
- * them out (step after step, columns ascending), at most `cap` tiles and
- * `ccap` chunks written, totals in *n_tiles / *n_chunks.
+/* The flow kernel's tables for steps [first_step, last_step) (last_step -1:
+ * through the last step) and tiles of tile_bytes per rank buffer (rounded as
+ * hbmc_comm_set_flow does), host only: tiles in the order the kernel hands
+ * them out (step after step, columns ascending; seq counts within the
+ * range), at most `cap` tiles and `ccap` chunks written, totals in *n_tiles /
+ * *n_chunks.  HBMC_ERR_INVALID_ARG for a range outside the schedule;
  * HBMC_ERR_UNSUPPORTED when an item has more than 32 ranks. */
 hbmc_status_t hbmc_plan_flow(hbmc_comm_t comm, hbmc_coll_t coll, int root, size_t count, hbmc_dtype_t dtype,
-                             uint64_t tile_bytes, hbmc_flow_tile_t* tiles, size_t cap, size_t* n_tiles,
-                             hbmc_flow_chunk_t* chunks, size_t ccap, size_t* n_chunks);
+                             int first_step, int last_step, uint64_t tile_bytes, hbmc_flow_tile_t* tiles,
+                             size_t cap, size_t* n_tiles, hbmc_flow_chunk_t* chunks, size_t ccap,
+                             size_t* n_chunks);
 
 /*
  * Graph mode ([RING-RHD] section "Ascend950的AIVAICPU通信引擎与图模式": a

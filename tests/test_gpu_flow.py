@@ -7,8 +7,8 @@ pipeline, Flat, tree, hierarchical; AllReduce, reduce-scatter, all-gather,
 Reduce, Broadcast), every dtype and op, tiles from 16 bytes (many tiles per
 item, ragged tails) to 16 KiB, one or several tiles per ticket, rank buffers
 at a shared 16-byte phase other than 0, calls repeated back to back (the counters reset by the kernel itself),
-graphs that replay it, a 16-rank ring of 16 MiB per rank compared whole, and
-the give-up path forced from the host.
+graphs that replay it, a 16-rank ring of 16 MiB per rank compared whole, step
+ranges run one launch each, and the give-up path forced from the host.
 """
 import numpy as np
 import pytest
@@ -107,6 +107,35 @@ def test_flow_ring_16_ranks_16MiB():
         for per in (1, 16):
             assert run_flow((P, algo), {}, "allreduce", L, dtype, "sum", seed=16, tile=16 << 10,
                             per_ticket=per) == "flow"
+
+
+@pytest.mark.parametrize("sched", [SCHEDS[0], SCHEDS[2], SCHEDS[3], SCHEDS[4], SCHEDS[7]],
+                         ids=["ring-P8", "rhd-P8", "rhd-P6", "pipeline-P8", "hier-P6"])
+def test_flow_step_ranges(sched):
+    """hbmc_run_steps ranges in the flow form: the steps cut into three
+    ranges, each run as one flow launch (a range of one step takes the step
+    kernel), every rank's whole buffer compared with the oracle's replay of
+    the same steps after each range; then the same ranges again, repeated."""
+    args, kw, colls = sched
+    P, dtype, op, L = args[0], "bf16", "sum", 3 * 4096 + 77
+    xs = make_inputs(dtype, op, P, L, seed=P + 40)
+    dev = [to_dev(x, dtype) for x in xs]
+    want = [x.copy() for x in xs]
+    with hc.Comm(*args) as c:
+        c.set_exec_mode("flow")
+        c.set_flow(512)
+        n = c.plan_info("allreduce", L, dtype)["nsteps"]
+        cuts = sorted({0, 1, n // 2, n})
+        for rep in range(2):
+            for a, b in zip(cuts, cuts[1:]):
+                form = c.exec_choice("allreduce", L, dtype, first=a, last=b)
+                say(f"case flow steps [{a}, {b}) of {n} {args} rep {rep} -> {form}")
+                assert form == ("flow" if b - a > 1 else "steps")
+                c.run_steps("allreduce", dev, a, b, dtype, op)
+                torch.cuda.synchronize()
+                oracle.run("allreduce", args[1], want, dtype, op, first_step=a, last_step=b, **kw)
+                _check(dev, want, dtype, f"flow {args} steps [{a}, {b}) rep {rep}")
+        assert c.flow_timeouts() == 0
 
 
 def test_flow_graph_replays():

@@ -258,10 +258,15 @@ def test_flow_argument_checks():
             with pytest.raises(hc.HbmcError):
                 comm.set_flow(**kw)
         comm.set_flow(64 << 10, 4, 1000)
-        # forced flow: whole calls of two or more steps on one 16-byte phase
+        # forced flow: calls and step ranges of two or more busy steps on one
+        # 16-byte phase
         comm.set_exec_mode("flow")
         assert comm.exec_choice("allreduce", 1000, "fp32") == "flow"
-        assert comm.exec_choice("allreduce", 1000, "fp32", first=0, last=3) == "steps"
+        assert comm.exec_choice("allreduce", 1000, "fp32", first=0, last=3) == "flow"
+        assert comm.exec_choice("allreduce", 1000, "fp32", first=2, last=3) == "steps"  # one step
+        for first, last in ((-1, 2), (2, 1), (0, 7)):
+            with pytest.raises(hc.HbmcError):
+                comm.plan_flow("allreduce", 1000, "fp32", 64, first=first, last=last)
         assert comm.exec_bytes("allreduce", 1000, "fp32", "flow") == comm.exec_bytes("allreduce", 1000, "fp32", "steps")
     with hc.Comm(2, "ring") as comm:
         comm.set_exec_mode("flow")
@@ -274,3 +279,57 @@ def test_flow_argument_checks():
     # AUTO never picks the flow form
     with hc.Comm(16, "ring") as comm:
         assert comm.exec_choice("allreduce", 8 << 20, "fp16") == "steps"
+
+
+RANGE_CASES = [(CASES[3], 5, 19), (CASES[4], 1, 5), (CASES[5], 0, 4), (CASES[10], 1, 4), (CASES[13], 1, 3)]
+RANGE_IDS = [f"{c[0][1]}-P{c[3]}-steps{a}-{b}" for c, a, b in RANGE_CASES]
+
+
+def _range_tables(case, first, last, dtype="int32"):
+    args, kw, coll, P, L, tile = case
+    with hc.Comm(*args) as comm:
+        n = comm.plan_info(coll, L, dtype, root=1 % P)["nsteps"]
+        assert 0 <= first < last <= n
+        return comm.plan_flow(coll, L, dtype, tile, root=1 % P, first=first, last=last)
+
+
+@pytest.mark.parametrize("case,first,last", RANGE_CASES, ids=RANGE_IDS)
+def test_range_tables_are_the_whole_tables_steps_renumbered(case, first, last):
+    """A step range's table holds the whole call's tiles of those steps, in
+    the same order and with the same chunks, each column's seq counted from 0
+    within the range."""
+    items, tiles, chunks, ce = _tables(case)
+    rt, rc = _range_tables(case, first, last)
+    sel = [t for t in tiles if first <= t["step"] < last]
+    assert len(rt) == len(sel)
+    seen = {}
+    for a, b in zip(rt, sel):
+        assert (a["col"], a["step"]) == (b["col"], b["step"])
+        assert a["seq"] == seen.get(a["col"], 0)
+        seen[a["col"]] = a["seq"] + 1
+        assert [rc[i] for i in a["chunks"]] == [chunks[i] for i in b["chunks"]]
+
+
+@pytest.mark.parametrize("case,first,last", RANGE_CASES, ids=RANGE_IDS)
+def test_range_protocol_gives_the_oracle_step_range(case, first, last):
+    """The protocol model over a range's table, from the state the oracle
+    reaches after steps [0, first), ends with the oracle's state after steps
+    [0, last), for several residencies."""
+    args, kw, coll, P, L, tile = case
+    dtype, op = "int32", "sum"
+    items, _, _, ce = _tables(case)
+    rt, rc = _range_tables(case, first, last)
+    ncols = (L + ce - 1) // ce
+    xs = _inputs(dtype, P, L, seed=P + first)
+    start = [x.copy() for x in xs]
+    oracle.run(coll, args[1], start, dtype, op, root=1 % P, first_step=0, last_step=first, **kw)
+    want = [x.copy() for x in start]
+    oracle.run(coll, args[1], want, dtype, op, root=1 % P, first_step=first, last_step=last, **kw)
+    rng = np.random.default_rng(first * 31 + last)
+    for groups, resident, batch in ((1, 1, 1), (5, 2, 2), (len(rt) + 2, len(rt) + 2, 1), (6, 6, 3)):
+        got, tmo, ctrl, progress = simulate(start, dtype, op, items, rt, rc, ncols, groups=groups, resident=resident,
+                                            rng=rng, batch=batch)
+        assert tmo == 0
+        assert ctrl == dict(next=0, done=0, abort=0) and not any(progress)
+        for r in range(P):
+            assert np.array_equal(got[r], want[r]), f"rank {r}, {groups} workgroups, {resident} resident"
