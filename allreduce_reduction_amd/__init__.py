@@ -24,6 +24,7 @@ ALGO_NAME = {v: k for k, v in ALGO.items()}
 COLL = {"allreduce": 0, "reduce_scatter": 1, "all_gather": 2, "reduce": 3, "broadcast": 4}
 MODE = {0: "copy", 1: "fold", 2: "recv_fold"}
 EXEC = {"auto": 0, "steps": 1, "fused": 2, "columns": 3, "lds": 4, "regs": 5, "flow": 6}
+_EXEC_NAME = {v: k for k, v in EXEC.items()}
 
 # every symbol include/hbmcoll.h declares
 EXPORTS = ("hbmc_comm_create", "hbmc_comm_destroy", "hbmc_allreduce", "hbmc_reduce_scatter",
@@ -296,7 +297,7 @@ class Comm:
         m = ctypes.c_int()
         _check(load_library().hbmc_exec_choice(self._h, COLL[coll], root, count, DTYPE[dtype], first, last,
                                                ctypes.byref(m)), "hbmc_exec_choice")
-        return {v: k for k, v in EXEC.items()}[m.value]
+        return _EXEC_NAME[m.value]
 
     def exec_bytes(self, coll: str, count: int, dtype: str, mode: str = "auto", root: int = 0,
                    first: int = 0, last: int = 0) -> int:
