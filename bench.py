@@ -693,6 +693,10 @@ def main():
 
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(a, P, L, D, dtype, recipe)
+    prop = torch.cuda.get_device_properties(bufs[0].device)
+    out["device"] = {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""),
+                     "compute_units": prop.multi_processor_count,
+                     "memory_GiB": round(prop.total_memory / 2 ** 30, 1)}
     comm.close()
     print(json.dumps(out), flush=True)
 
