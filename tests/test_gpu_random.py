@@ -99,3 +99,43 @@ def test_random_cases(batch):
             if op in ("max", "min") and dtype in refops.FLOATS:
                 assert np.array_equal(to_host(dev[r], dtype).view(np.uint8), want[r].view(np.uint8))
         del dev, keep
+
+
+def test_random_large_cases():
+    """Larger seeded cases (1-3 MiB of every rank per segment or block): ring,
+    RHD and pipeline AllReduce / reduce-scatter / all-gather, one launch per
+    step or AUTO, aligned buffers or one shared 16-byte phase; copy steps of
+    items of 1 MiB or more take 4 KiB tiles here.  Whole buffers compared."""
+    rng = np.random.default_rng(777)
+    for i in range(12):
+        algo = str(rng.choice(["ring", "rhd", "pipeline"]))
+        if algo == "pipeline":
+            S, M = int(rng.integers(2, 5)), int(rng.choice([2, 4]))
+            P, args, kw = S * M, (S * M, "pipeline", S, M, 0), dict(S=S, M=M, loop_bytes=0)
+        else:
+            P = int(rng.integers(2, 17))
+            args, kw = (P, algo), {}
+        coll = str(rng.choice(["allreduce", "reduce_scatter", "all_gather"]))
+        if algo == "rhd" and coll != "allreduce" and P & (P - 1):
+            coll = "allreduce"
+        dtype = str(rng.choice(DTYPES))
+        op = str(rng.choice(["sum", "max", "min"]))
+        e = np.dtype(refops.STORAGE[dtype]).itemsize
+        L = int(rng.integers(P * (1 << 20) // e // 2, P * (3 << 20) // e)) + int(rng.integers(0, 64))
+        mode = str(rng.choice(["auto", "steps"]))
+        phase = str(rng.choice(["aligned", "same"]))
+        say(f"case large {i}: {algo} P={P} {coll} {dtype} {op} L={L} mode={mode} phase={phase}")
+        xs = make_inputs(dtype, op, P, L, 1000 + i)
+        if phase == "aligned":
+            dev, keep = [to_dev(x, dtype) for x in xs], None
+        else:
+            dev, keep = strided_buffers(xs, dtype, [1 % max(1, 16 // e)] * P)
+        with hc.Comm(*args) as comm:
+            comm.set_exec_mode(mode)
+            getattr(comm, coll)(dev, dtype, op)
+            torch.cuda.synchronize()
+        want = [x.copy() for x in xs]
+        oracle.run_parallel(coll, algo, want, dtype, op, **kw)
+        for r in range(P):
+            refops.assert_same(dtype, to_host(dev[r], dtype), want[r], f"large case {i} rank {r}")
+        del dev, keep
